@@ -1,0 +1,330 @@
+"""block_scaled_fp4_04_amd -- NVFP4 / MXFP4 block-scaled 4-bit quantization and
+the quantized linear-layer GEMMs it feeds, on AMD Instinct MI355X (gfx950).
+
+This module is a thin binding over the C ABI of ``libfp4blk.so`` (declared in
+``include/fp4blk.h``): it checks tensors, hands device pointers and torch's
+current stream to the library, and maps status codes to exceptions.  Every step
+of the computation runs in the library's HIP kernels; there is no fallback.  If
+the library is not built, importing the functions raises.
+
+Formats ("NVFP4", newton.com.tw wiki, section "Technical principle"; edge-FP4
+article, eefocus.com, section "FP4 as the next core standard"):
+
+* NVFP4: E2M1 codes, two per byte (even column in the low nibble), one E4M3
+  scale byte per 16 elements, one FP32 scale per tensor (or per row for
+  dynamically quantized activations): 4.5 bits per value.
+* MXFP4: E2M1 codes, one E8M0 byte per 32 elements: 4.25 bits per value.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "_lib", "libfp4blk.so")
+
+FP4_F32, FP4_BF16 = 0, 1
+PER_TENSOR, PER_ROW = 0, 1
+MX_OCP_FLOOR, MX_CEIL = 0, 1
+
+_EXPORTS = {
+    # name: (restype, argtypes)
+}
+
+
+class Fp4Error(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+_lib = None
+
+
+def _declare(L):
+    p, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "fp4_status_str": (ctypes.c_char_p, [i32]),
+        "fp4blk_version": (i32, []),
+        "fp4blk_check_device": (i32, []),
+        "nvfp4_quantize_workspace": (sz, [i64, i64, i32]),
+        "nvfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, p, i32, p, sz, p, p]),
+        "nvfp4_dequantize": (i32, [p, p, p, i32, i64, i64, p, i32, i64, p]),
+        "gemm_w4a16": (i32, [p, i64, i64, i64, p, p, p, i64, p, i32, i64, p]),
+        "gemm_w4a4_workspace": (sz, [i64, i64, i32]),
+        "gemm_w4a4_workspace_offsets": (None, [i64, i64, p, p, p]),
+        "gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p, sz, p]),
+        "gemm_nvfp4_w4a4_prequant": (i32, [p, p, p, i32, i64, i64, p, p, p, i64, p, i32, i64, p]),
+        "mxfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, i32, p, p]),
+        "mxfp4_dequantize": (i32, [p, p, i64, i64, p, i32, i64, p]),
+        "mxfp4_gemm_w4a4_workspace": (sz, [i64, i64]),
+        "mxfp4_gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
+        "mxfp4_gemm_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    return sig
+
+
+def lib():
+    """The loaded libfp4blk (ctypes handle).  Raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'` "
+                "(hipcc, gfx950); there is no fallback path")
+        # torch first: the library links against torch's HIP runtime, which must
+        # be the single HIP runtime in this process
+        L = ctypes.CDLL(LIB_PATH)
+        _EXPORTS.update(_declare(L))
+        _lib = L
+    return _lib
+
+
+def exported_names():
+    lib()
+    return sorted(_EXPORTS)
+
+
+def status_str(s: int) -> str:
+    return lib().fp4_status_str(int(s)).decode()
+
+
+def _check(s: int):
+    if s != 0:
+        raise Fp4Error(s, status_str(s))
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def _dt(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return FP4_F32
+    if t.dtype == torch.bfloat16:
+        return FP4_BF16
+    raise TypeError(f"expected float32 or bfloat16, got {t.dtype}")
+
+
+def _out_dt(dtype) -> int:
+    return FP4_F32 if dtype == torch.float32 else FP4_BF16
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libfp4blk takes device tensors")
+
+
+def _mode(m) -> int:
+    if m in ("tensor", PER_TENSOR):
+        return PER_TENSOR
+    if m in ("row", PER_ROW):
+        return PER_ROW
+    raise ValueError(f"scale mode must be 'tensor' or 'row', got {m!r}")
+
+
+def _rule(r) -> int:
+    if r in ("ocp", MX_OCP_FLOOR):
+        return MX_OCP_FLOOR
+    if r in ("ceil", MX_CEIL):
+        return MX_CEIL
+    raise ValueError(f"MX rule must be 'ocp' or 'ceil', got {r!r}")
+
+
+def _ld(t: torch.Tensor) -> int:
+    if t.dim() != 2 or t.stride(1) != 1:
+        raise ValueError("expected a 2-D tensor with unit stride along its rows")
+    return t.stride(0)
+
+
+@dataclasses.dataclass
+class PackedNVFP4:
+    """NVFP4 tensor [rows, cols]: codes uint8 [rows, cols/2], scales uint8
+    [rows, cols/16] (E4M3FN), tscale float32 [1] or [rows]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+    rows: int
+    cols: int
+    per_row: bool = False
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel() + 4 * self.tscale.numel()
+
+
+@dataclasses.dataclass
+class PackedMXFP4:
+    """MXFP4 tensor [rows, cols]: codes uint8 [rows, cols/2], scales uint8 [rows, cols/32] (E8M0)."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+
+    def nbytes(self) -> int:
+        return self.codes.numel() + self.scales.numel()
+
+
+# --------------------------------------------------------------- NVFP4 -----
+
+def nvfp4_quantize(x: torch.Tensor, mode="tensor", nonfinite: torch.Tensor | None = None,
+                   out: PackedNVFP4 | None = None, workspace: torch.Tensor | None = None) -> PackedNVFP4:
+    """Quantize a 2-D fp32/bf16 device tensor to NVFP4 (blocks along its rows)."""
+    L = lib()
+    _need_cuda(x, nonfinite)
+    rows, cols = x.shape
+    m = _mode(mode)
+    dev = x.device
+    if out is None:
+        out = PackedNVFP4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
+                          torch.empty(rows, cols // 16, dtype=torch.uint8, device=dev),
+                          torch.empty(rows if m == PER_ROW else 1, dtype=torch.float32, device=dev),
+                          rows, cols, m == PER_ROW)
+    wsb = L.nvfp4_quantize_workspace(rows, cols, m)
+    if workspace is None and wsb:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    _check(L.nvfp4_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
+                            _ptr(out.tscale), m, _ptr(workspace), wsb, _ptr(nonfinite), _stream()))
+    return out
+
+
+def nvfp4_dequantize(p: PackedNVFP4, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    L = lib()
+    if out is None:
+        out = torch.empty(p.rows, p.cols, dtype=dtype, device=p.codes.device)
+    _check(L.nvfp4_dequantize(_ptr(p.codes), _ptr(p.scales), _ptr(p.tscale),
+                              PER_ROW if p.per_row else PER_TENSOR, p.rows, p.cols, _ptr(out),
+                              _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+def gemm_w4a16(a: torch.Tensor, w: PackedNVFP4, dtype=torch.bfloat16,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A . W^T with bf16 A [M, K] and NVFP4 W [N, K] (per-tensor scale)."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("gemm_w4a16 takes bfloat16 activations")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    _check(L.gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                        _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+def gemm_w4a4_workspace(M: int, K: int, a_mode="row", device="cuda") -> torch.Tensor:
+    n = lib().gemm_w4a4_workspace(M, K, _mode(a_mode))
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def w4a4_packed_a(ws: torch.Tensor, M: int, K: int, a_mode="row") -> PackedNVFP4:
+    """Views of A's NVFP4 form inside a gemm_w4a4 workspace."""
+    co, so, to = ctypes.c_size_t(), ctypes.c_size_t(), ctypes.c_size_t()
+    lib().gemm_w4a4_workspace_offsets(M, K, ctypes.byref(co), ctypes.byref(so), ctypes.byref(to))
+    per_row = _mode(a_mode) == PER_ROW
+    codes = ws[co.value:co.value + M * K // 2].view(M, K // 2)
+    scales = ws[so.value:so.value + M * K // 16].view(M, K // 16)
+    nt = M if per_row else 1
+    tscale = ws[to.value:to.value + 4 * nt].view(torch.float32)
+    return PackedNVFP4(codes, scales, tscale, M, K, per_row)
+
+
+def gemm_w4a4(a: torch.Tensor, w: PackedNVFP4, a_mode="row", dtype=torch.bfloat16,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """NVFP4 W4A4: quantize bf16 A on the device (per row by default), then C = A_q . W^T."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("gemm_w4a4 takes bfloat16 activations")
+    M, K = a.shape
+    m = _mode(a_mode)
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    if workspace is None:
+        workspace = gemm_w4a4_workspace(M, K, m, a.device)
+    _check(L.gemm_w4a4(_ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                       _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                       _stream()))
+    return out
+
+
+def gemm_nvfp4_prequant(a: PackedNVFP4, w: PackedNVFP4, dtype=torch.bfloat16,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    L = lib()
+    if out is None:
+        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.gemm_nvfp4_w4a4_prequant(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
+                                      PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
+                                      _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
+                                      _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+# --------------------------------------------------------------- MXFP4 -----
+
+def mxfp4_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None = None,
+                   out: PackedMXFP4 | None = None) -> PackedMXFP4:
+    L = lib()
+    _need_cuda(x, nonfinite)
+    rows, cols = x.shape
+    if out is None:
+        out = PackedMXFP4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device),
+                          torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device), rows, cols)
+    _check(L.mxfp4_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
+                            _rule(rule), _ptr(nonfinite), _stream()))
+    return out
+
+
+def mxfp4_dequantize(p: PackedMXFP4, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    L = lib()
+    if out is None:
+        out = torch.empty(p.rows, p.cols, dtype=dtype, device=p.codes.device)
+    _check(L.mxfp4_dequantize(_ptr(p.codes), _ptr(p.scales), p.rows, p.cols, _ptr(out),
+                              _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a4(a: torch.Tensor, w: PackedMXFP4, rule="ocp", dtype=torch.bfloat16,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("mxfp4_gemm_w4a4 takes bfloat16 activations")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    if workspace is None:
+        workspace = torch.empty(L.mxfp4_gemm_w4a4_workspace(M, K), dtype=torch.uint8, device=a.device)
+    _check(L.mxfp4_gemm_w4a4(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
+                             _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                             _stream()))
+    return out
+
+
+def mxfp4_packed_a(ws: torch.Tensor, M: int, K: int) -> PackedMXFP4:
+    """Views of A's MXFP4 form inside an mxfp4_gemm_w4a4 workspace."""
+    cb = (M * (K // 2) + 255) // 256 * 256
+    return PackedMXFP4(ws[:M * K // 2].view(M, K // 2), ws[cb:cb + M * K // 32].view(M, K // 32), M, K)
+
+
+def mxfp4_gemm_prequant(a: PackedMXFP4, w: PackedMXFP4, dtype=torch.bfloat16,
+                        out: torch.Tensor | None = None) -> torch.Tensor:
+    L = lib()
+    if out is None:
+        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.mxfp4_gemm_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
+                                 _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
+                                 _stream()))
+    return out

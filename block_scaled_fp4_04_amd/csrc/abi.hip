@@ -1,0 +1,347 @@
+// abi.hip -- the extern "C" entry points of libfp4blk: argument validation,
+// workspace layout and dispatch to the kernels.  Validation happens on the host
+// before anything is launched, so an error leaves every output untouched.
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "fp4blk.h"
+#include "internal.h"
+
+using namespace fp4k;
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_dev_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+
+fp4_status check_device()
+{
+    int dev = 0;
+    int count = 0;
+    if (hipGetDeviceCount(&count) != hipSuccess || count <= 0) {
+        (void)hipGetLastError();
+        return FP4_ERR_NO_DEVICE;
+    }
+    if (hipGetDevice(&dev) != hipSuccess) return FP4_ERR_NO_DEVICE;
+    if (dev < 0 || dev >= kMaxDevices) return FP4_ERR_UNSUPPORTED_DEVICE;
+    int st = g_dev_state[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t p;
+        if (hipGetDeviceProperties(&p, dev) != hipSuccess) return FP4_ERR_HIP;
+        st = std::strncmp(p.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_dev_state[dev].store(st, std::memory_order_relaxed);
+    }
+    return st == 1 ? FP4_OK : FP4_ERR_UNSUPPORTED_DEVICE;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+size_t dsize(fp4_dtype t) { return t == FP4_F32 ? 4 : 2; }
+
+bool valid_dtype(int t) { return t == FP4_F32 || t == FP4_BF16; }
+
+// rows x cols input with leading dimension ld (elements of size es): rows stay
+// 16-byte aligned when the base is and ld * es is a multiple of 16.
+fp4_status check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld, size_t es)
+{
+    if (!p) return FP4_ERR_NULL;
+    if (rows <= 0 || cols <= 0) return FP4_ERR_SHAPE;
+    if (ld < cols) return FP4_ERR_LAYOUT;
+    if (!aligned16(p) || ((uint64_t)ld * es) % 16 != 0) return FP4_ERR_LAYOUT;
+    return FP4_OK;
+}
+
+// packed operand (codes, scales): codes rows are cols/2 bytes, scale rows
+// cols/block bytes; base pointers 16-byte aligned.
+fp4_status check_packed(const uint8_t *codes, const uint8_t *scales)
+{
+    if (!codes || !scales) return FP4_ERR_NULL;
+    if (!aligned16(codes) || !aligned16(scales)) return FP4_ERR_LAYOUT;
+    return FP4_OK;
+}
+
+#define FP4_TRY(expr)                          \
+    do {                                       \
+        const fp4_status _s = (expr);          \
+        if (_s != FP4_OK) return _s;           \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *fp4_status_str(int s)
+{
+    switch (s) {
+    case FP4_OK: return "FP4_OK";
+    case FP4_ERR_NULL: return "FP4_ERR_NULL: a required pointer is null";
+    case FP4_ERR_SHAPE: return "FP4_ERR_SHAPE: size <= 0, too large, or not a whole number of blocks";
+    case FP4_ERR_LAYOUT: return "FP4_ERR_LAYOUT: leading dimension too small or pointer/row not 16-byte aligned";
+    case FP4_ERR_DTYPE: return "FP4_ERR_DTYPE: unknown dtype, scale mode or MX rule";
+    case FP4_ERR_WORKSPACE: return "FP4_ERR_WORKSPACE: workspace null or too small";
+    case FP4_ERR_NO_DEVICE: return "FP4_ERR_NO_DEVICE: no HIP device visible";
+    case FP4_ERR_UNSUPPORTED_DEVICE: return "FP4_ERR_UNSUPPORTED_DEVICE: current device is not gfx950";
+    case FP4_ERR_HIP: return "FP4_ERR_HIP: a HIP call or kernel launch failed";
+    default: return "unknown fp4_status";
+    }
+}
+
+int fp4blk_version(void) { return 10000; }
+
+fp4_status fp4blk_check_device(void) { return check_device(); }
+
+// ------------------------------------------------------------------ NVFP4 --
+
+size_t nvfp4_quantize_workspace(int64_t rows, int64_t cols, fp4_scale_mode mode)
+{
+    (void)rows;
+    (void)cols;
+    return mode == FP4_SCALE_PER_TENSOR ? kAmaxPartials * sizeof(float) : 0;
+}
+
+fp4_status nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *codes, uint8_t *scales, float *tscale, fp4_scale_mode mode,
+                          void *ws, size_t ws_bytes, int32_t *nonfinite, hipStream_t stream)
+{
+    if (!valid_dtype(xt) || (mode != FP4_SCALE_PER_TENSOR && mode != FP4_SCALE_PER_ROW))
+        return FP4_ERR_DTYPE;
+    FP4_TRY(check_matrix(x, rows, cols, ldx, dsize(xt)));
+    if (cols % 16 != 0) return FP4_ERR_SHAPE;
+    if (rows * cols > kMaxFlatElems) return FP4_ERR_SHAPE;
+    if (!tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_packed(codes, scales));
+    if (mode == FP4_SCALE_PER_TENSOR &&
+        (!ws || ws_bytes < nvfp4_quantize_workspace(rows, cols, mode)))
+        return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    return launch_nvfp4_quantize(x, xt, rows, cols, ldx, codes, scales, tscale, mode, ws, nonfinite,
+                                 stream);
+}
+
+fp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tscale,
+                            fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
+                            fp4_dtype yt, int64_t ldy, hipStream_t stream)
+{
+    if (!valid_dtype(yt) || (mode != FP4_SCALE_PER_TENSOR && mode != FP4_SCALE_PER_ROW))
+        return FP4_ERR_DTYPE;
+    FP4_TRY(check_matrix(y, rows, cols, ldy, dsize(yt)));
+    if (cols % 16 != 0) return FP4_ERR_SHAPE;
+    if (rows * cols > kMaxFlatElems) return FP4_ERR_SHAPE;
+    if (!tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_packed(codes, scales));
+    FP4_TRY(check_device());
+    return launch_nvfp4_dequantize(codes, scales, tscale, mode, rows, cols, y, yt, ldy, stream);
+}
+
+static fp4_status check_gemm_common(int64_t M, int64_t K, int64_t N, int kblock, const void *c,
+                                    fp4_dtype ct, int64_t ldc)
+{
+    if (!valid_dtype(ct)) return FP4_ERR_DTYPE;
+    if (M <= 0 || N <= 0 || K <= 0 || K % kblock != 0) return FP4_ERR_SHAPE;
+    if (M > INT32_MAX / 2 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP4_ERR_SHAPE;
+    if (!c) return FP4_ERR_NULL;
+    if (ldc < N) return FP4_ERR_LAYOUT;
+    return FP4_OK;
+}
+
+fp4_status gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes,
+                      const uint8_t *w_scales, const float *w_tscale, int64_t N, void *c,
+                      fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 16, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!w_tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_device());
+    NvGemmArgs g{};
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.w_tscale = w_tscale;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_nvfp4_gemm(g, stream);
+}
+
+void gemm_w4a4_workspace_offsets(int64_t M, int64_t K, size_t *codes_off, size_t *scales_off,
+                                 size_t *tscale_off)
+{
+    const size_t cb = align256((size_t)M * (size_t)(K / 2));
+    const size_t sb = align256((size_t)M * (size_t)(K / 16));
+    if (codes_off) *codes_off = 0;
+    if (scales_off) *scales_off = cb;
+    if (tscale_off) *tscale_off = cb + sb;
+}
+
+size_t gemm_w4a4_workspace(int64_t M, int64_t K, fp4_scale_mode a_mode)
+{
+    if (M <= 0 || K <= 0) return 0;
+    size_t t;
+    gemm_w4a4_workspace_offsets(M, K, nullptr, nullptr, &t);
+    const size_t ts = align256((size_t)(a_mode == FP4_SCALE_PER_ROW ? M : 1) * sizeof(float));
+    // the per-tensor amax partials follow the tensor scale
+    const size_t amax = a_mode == FP4_SCALE_PER_TENSOR ? kAmaxPartials * sizeof(float) : 0;
+    return t + ts + amax;
+}
+
+fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    const float *a_tscale, fp4_scale_mode a_mode, int64_t M,
+                                    int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+                                    const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
+                                    int64_t ldc, hipStream_t stream)
+{
+    if (a_mode != FP4_SCALE_PER_TENSOR && a_mode != FP4_SCALE_PER_ROW) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, 16, c, ct, ldc));
+    FP4_TRY(check_packed(a_codes, a_scales));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!a_tscale || !w_tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_device());
+    NvGemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.a_tscale = a_tscale;
+    g.a_per_row = a_mode == FP4_SCALE_PER_ROW;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.w_tscale = w_tscale;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_nvfp4_gemm(g, stream);
+}
+
+fp4_status gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale,
+                     int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
+                     hipStream_t stream)
+{
+    if (a_mode != FP4_SCALE_PER_TENSOR && a_mode != FP4_SCALE_PER_ROW) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, 16, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!w_tscale) return FP4_ERR_NULL;
+    if (!ws || !aligned16(ws) || ws_bytes < gemm_w4a4_workspace(M, K, a_mode))
+        return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    size_t co, so, to;
+    gemm_w4a4_workspace_offsets(M, K, &co, &so, &to);
+    uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+    uint8_t *ac = base + co;
+    uint8_t *as = base + so;
+    float *at = reinterpret_cast<float *>(base + to);
+    void *amax_ws = base + to + align256((size_t)(a_mode == FP4_SCALE_PER_ROW ? M : 1) * sizeof(float));
+    FP4_TRY(launch_nvfp4_quantize(a, FP4_BF16, M, K, lda, ac, as, at, a_mode, amax_ws, nullptr,
+                                  stream));
+    NvGemmArgs g{};
+    g.a_codes = ac;
+    g.a_scales = as;
+    g.a_tscale = at;
+    g.a_per_row = a_mode == FP4_SCALE_PER_ROW;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.w_tscale = w_tscale;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_nvfp4_gemm(g, stream);
+}
+
+// ------------------------------------------------------------------ MXFP4 --
+
+fp4_status mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *codes, uint8_t *scales, fp4_mx_rule rule, int32_t *nonfinite,
+                          hipStream_t stream)
+{
+    if (!valid_dtype(xt) || (rule != FP4_MX_OCP_FLOOR && rule != FP4_MX_CEIL)) return FP4_ERR_DTYPE;
+    FP4_TRY(check_matrix(x, rows, cols, ldx, dsize(xt)));
+    if (cols % 32 != 0) return FP4_ERR_SHAPE;
+    if (rows * cols > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(codes, scales));
+    FP4_TRY(check_device());
+    return launch_mxfp4_quantize(x, xt, rows, cols, ldx, codes, scales, rule, nonfinite, stream);
+}
+
+fp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int64_t cols, void *y, fp4_dtype yt, int64_t ldy, hipStream_t stream)
+{
+    if (!valid_dtype(yt)) return FP4_ERR_DTYPE;
+    FP4_TRY(check_matrix(y, rows, cols, ldy, dsize(yt)));
+    if (cols % 32 != 0) return FP4_ERR_SHAPE;
+    if (rows * cols > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(codes, scales));
+    FP4_TRY(check_device());
+    return launch_mxfp4_dequantize(codes, scales, rows, cols, y, yt, ldy, stream);
+}
+
+size_t mxfp4_gemm_w4a4_workspace(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0) return 0;
+    return align256((size_t)M * (size_t)(K / 2)) + align256((size_t)M * (size_t)(K / 32));
+}
+
+fp4_status mxfp4_gemm_prequant(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M,
+                               int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+                               int64_t N, void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 32, c, ct, ldc));
+    FP4_TRY(check_packed(a_codes, a_scales));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    FP4_TRY(check_device());
+    MxGemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_mxfp4_gemm(g, stream);
+}
+
+fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                           const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                           fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
+                           hipStream_t stream)
+{
+    if (rule != FP4_MX_OCP_FLOOR && rule != FP4_MX_CEIL) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, 32, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!ws || !aligned16(ws) || ws_bytes < mxfp4_gemm_w4a4_workspace(M, K)) return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
+    uint8_t *as = ac + align256((size_t)M * (size_t)(K / 2));
+    FP4_TRY(launch_mxfp4_quantize(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
+    MxGemmArgs g{};
+    g.a_codes = ac;
+    g.a_scales = as;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_mxfp4_gemm(g, stream);
+}
+
+}  // extern "C"

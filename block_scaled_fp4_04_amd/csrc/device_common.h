@@ -1,0 +1,107 @@
+// device_common.h -- gfx950 device helpers shared by the libfp4blk kernels:
+// E2M1 / E4M3 / E8M0 codecs, lane reductions and small vector types.
+//
+// Formats: "NVFP4" (newton.com.tw wiki), section "Technical principle" (E2M1
+// elements, E4M3 block scales, FP32 tensor scale); edge-FP4 article
+// (eefocus.com), section "FP4 as the next core standard" (E8M0 MX scales).
+// E4M3 is the OCP E4M3FN variant (bias 7, largest finite 448, no infinities).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fp4k {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs here are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// |q| rounded onto the E2M1 magnitudes {0,0.5,1,1.5,2,3,4,6}: each decision
+// point is the midpoint of two neighbours; at a midpoint the neighbour whose
+// mantissa bit is 0 (0, 1, 2, 4) wins, hence ">" at 0.25/1.25/2.5/5 and ">=" at
+// 0.75/1.75/3.5.  Magnitudes above 6 saturate to index 7.  The sign bit of q
+// becomes code bit 3, so a negative value rounding to 0 keeps code 0x8.
+__device__ __forceinline__ uint32_t e2m1_code(float q)
+{
+    const float a = __builtin_fabsf(q);
+    uint32_t m = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                 (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                 (uint32_t)(a > 5.0f);
+    return m | ((__float_as_uint(q) >> 28) & 8u);
+}
+
+// Non-negative fp32 -> E4M3FN byte, round to nearest even, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code_sat(float q)
+{
+    if (!(q < 448.0f)) return 0x7Eu;                            // >= 448 or +inf
+    if (q < 0x1p-6f) return (uint32_t)__builtin_rintf(q * 512.0f); // subnormal: m * 2^-9, m in 0..8
+    const uint32_t u = __float_as_uint(q);
+    const uint32_t mant = u & 0x7FFFFFu;
+    // keep 3 mantissa bits, round half to even; a carry out of the mantissa
+    // lands in the exponent field by the addition below
+    const uint32_t r = (mant + 0x7FFFFu + ((mant >> 20) & 1u)) >> 20;
+    const uint32_t code = ((((u >> 23) & 0xFFu) - 120u) << 3) + r;  // biased exponent - 127 + 7
+    return code > 0x7Eu ? 0x7Eu : code;
+}
+
+// E4M3FN byte -> fp32 (sign honoured; 0x7F/0xFF are never produced by the quantizer).
+__device__ __forceinline__ float e4m3_value(uint32_t b)
+{
+    const uint32_t e = (b >> 3) & 15u, m = b & 7u;
+    const float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
+    return (b & 0x80u) ? -mag : mag;
+}
+
+// E2M1 code (4 bits) -> fp32, exact.
+__device__ __forceinline__ float e2m1_value(uint32_t c)
+{
+    const uint32_t i = c & 7u;
+    // magnitudes 0, 0.5 by index; 1..6 as 2^(e-1) * (1 + m/2) with e = i>>1, m = i&1
+    const uint32_t normal_bits = (((i >> 1) + 126u) << 23) | ((i & 1u) << 22);
+    const float mag = i >= 2u ? __uint_as_float(normal_bits) : (i ? 0.5f : 0.0f);
+    return (c & 8u) ? -mag : mag;
+}
+
+// lane exchange with lane ^ 1 and lane ^ 2 (DPP quad permutes)
+__device__ __forceinline__ float xor1(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xor2(float v)
+{
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ float wave_max(float v)
+{
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, kWave));
+    return v;
+}
+
+// 32-bit division by a run-time constant (Granlund-Montgomery round-up method;
+// exact for n, d < 2^31).
+struct FastDiv {
+    uint32_t d, m, s;
+};
+
+__device__ __forceinline__ uint32_t fdiv(uint32_t n, const FastDiv &f)
+{
+    return (__umulhi(n, f.m) + n) >> f.s;
+}
+
+}  // namespace fp4k

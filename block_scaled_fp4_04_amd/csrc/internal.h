@@ -1,0 +1,86 @@
+// internal.h -- declarations shared by the libfp4blk translation units (not
+// part of the public C ABI; see include/fp4blk.h for that).
+#pragma once
+
+#include <stdint.h>
+
+#include "fp4blk.h"
+
+namespace fp4k {
+
+struct FastDiv;
+
+// Number of per-workgroup partial maxima the per-tensor amax pass writes; the
+// per-tensor quantize workspace holds this many floats.
+constexpr unsigned kAmaxPartials = 1024;
+
+// Largest element count a flat (rows * cols) kernel indexes with 32-bit units
+// of 8 elements.
+constexpr int64_t kMaxFlatElems = (int64_t(1) << 31) * 8 - 8;
+
+inline size_t align256(size_t n) { return (n + 255) & ~size_t(255); }
+
+fp4_status launch_nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *codes, uint8_t *scales, float *tscale,
+                                 fp4_scale_mode mode, void *ws, int32_t *nonfinite,
+                                 hipStream_t st);
+fp4_status launch_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tscale,
+                                   fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
+                                   fp4_dtype yt, int64_t ldy, hipStream_t st);
+fp4_status launch_mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *codes, uint8_t *scales, fp4_mx_rule rule,
+                                 int32_t *nonfinite, hipStream_t st);
+fp4_status launch_mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                   int64_t cols, void *y, fp4_dtype yt, int64_t ldy,
+                                   hipStream_t st);
+
+// NVFP4 GEMMs.  A is bf16 (a_codes == nullptr) or NVFP4 (a_codes/a_scales/a_tscale).
+struct NvGemmArgs {
+    const uint16_t *a;      // bf16 [M][lda] (W4A16)
+    int64_t lda;
+    const uint8_t *a_codes; // NVFP4 A (W4A4): codes [M][K/2], scales [M][K/16], tscale
+    const uint8_t *a_scales;
+    const float *a_tscale;
+    int a_per_row;
+    const uint8_t *w_codes;  // W [N][K/2]
+    const uint8_t *w_scales; // W [N][K/16]
+    const float *w_tscale;   // [1]
+    int64_t M, N, K;
+    void *c;
+    int c_bf16;
+    int64_t ldc;
+};
+
+fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st);
+
+struct MxGemmArgs {
+    const uint8_t *a_codes;  // [M][K/2]
+    const uint8_t *a_scales; // [M][K/32]
+    const uint8_t *w_codes;  // [N][K/2]
+    const uint8_t *w_scales; // [N][K/32]
+    int64_t M, N, K;
+    void *c;
+    int c_bf16;
+    int64_t ldc;
+};
+
+fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st);
+
+}  // namespace fp4k
+
+// host-side construction of the device divider
+#include "device_common.h"
+
+namespace fp4k {
+inline FastDiv make_fastdiv(uint32_t d)
+{
+    uint32_t s = 0;
+    while ((uint64_t(1) << s) < d) ++s;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << s) - d)) / d + 1;
+    FastDiv f;
+    f.d = d;
+    f.m = (uint32_t)m;
+    f.s = s;
+    return f;
+}
+}  // namespace fp4k

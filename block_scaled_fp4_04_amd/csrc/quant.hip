@@ -1,0 +1,389 @@
+// quant.hip -- NVFP4 and MXFP4 quantize / dequantize kernels for gfx950.
+//
+// NVFP4 ("NVFP4", newton.com.tw wiki, section "Technical principle"): a tensor
+// is cut into 16-value micro-blocks along its rows; each block gets one E4M3
+// scale byte and the tensor one FP32 scale; elements are E2M1.
+// MXFP4 (edge-FP4 article, eefocus.com, section "FP4 as the next core
+// standard"): 32-element blocks, one E8M0 byte each, E2M1 elements.
+//
+// Work unit: one lane owns 8 consecutive elements of a row (one or two 16-byte
+// loads), so a wave reads 512 contiguous elements per instruction pair and
+// writes its 8 codes as one 32-bit store.  A 16-block is a lane pair, a
+// 32-block a lane quad; block maxima are exchanged with DPP quad permutes.
+//
+// All fp32 arithmetic here is IEEE round-to-nearest-even: the library is built
+// with correctly rounded fp32 division, no contraction, denormals kept.
+#include "device_common.h"
+#include "internal.h"
+
+#pragma clang fp contract(off)
+
+namespace fp4k {
+
+template <typename T>
+struct Vec8;
+
+template <>
+struct Vec8<float> {
+    static __device__ __forceinline__ void load(const float *p, float v[8])
+    {
+        const float4 a = *reinterpret_cast<const float4 *>(p);
+        const float4 b = *reinterpret_cast<const float4 *>(p + 4);
+        v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+        v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    }
+};
+
+template <>
+struct Vec8<uint16_t> {
+    static __device__ __forceinline__ void load(const uint16_t *p, float v[8])
+    {
+        const uint4 a = *reinterpret_cast<const uint4 *>(p);
+        const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] = __uint_as_float(w[i] << 16);
+            v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+        }
+    }
+};
+
+__device__ __forceinline__ float amax8(const float v[8], int &bad)
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float a = __builtin_fabsf(v[i]);
+        bad |= !__builtin_isfinite(a);
+        m = fmaxf(m, a);
+    }
+    return m;
+}
+
+// Codes of 8 values under divisor d (d == 0: signed zeros), nibble i = value i.
+__device__ __forceinline__ uint32_t nvfp4_codes8(const float v[8], float d)
+{
+    uint32_t w = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t c = d == 0.0f ? ((__float_as_uint(v[i]) >> 28) & 8u) : e2m1_code(v[i] / d);
+        w |= c << (4 * i);
+    }
+    return w;
+}
+
+// ------------------------------------------------------------------ amax --
+
+// Per-block maxima of |x| over the whole tensor; partial[blockIdx.x].
+template <typename T>
+__global__ __launch_bounds__(256) void k_amax_partial(const T *__restrict__ x, uint32_t units,
+                                                      FastDiv cv, int64_t ldx,
+                                                      float *__restrict__ partial,
+                                                      int32_t *__restrict__ nonfinite)
+{
+    float m = 0.0f;
+    int bad = 0;
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
+        float v[8];
+        Vec8<T>::load(x + (int64_t)r * ldx + (int64_t)c8 * 8, v);
+        m = fmaxf(m, amax8(v, bad));
+    }
+    m = wave_max(m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    if (bad && nonfinite) *nonfinite = 1;
+    __syncthreads();
+    if (threadIdx.x == 0) partial[blockIdx.x] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// tscale[0] = fl32(max(partial) / 2688).
+__global__ __launch_bounds__(256) void k_tscale_finalize(const float *__restrict__ partial, int n,
+                                                         float *__restrict__ tscale)
+{
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < n; i += 256) m = fmaxf(m, partial[i]);
+    m = wave_max(m);
+    __shared__ float red[4];
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) tscale[0] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3])) / 2688.0f;
+}
+
+// --------------------------------------------------------- NVFP4 quantize --
+
+// One 8-element unit under tensor scale s: lanes (2i, 2i+1) hold one 16-block.
+__device__ __forceinline__ void nvfp4_unit(const float v[8], float s, float six_s,
+                                           uint32_t *code_word, uint8_t *scale_byte, bool even)
+{
+    int dummy = 0;
+    float bm = amax8(v, dummy);
+    bm = fmaxf(bm, xor1(bm));
+    const uint32_t b = bm == 0.0f ? 0u : e4m3_code_sat(bm / six_s);
+    const float d = e4m3_value(b) * s;
+    *code_word = nvfp4_codes8(v, d);
+    if (even) *scale_byte = (uint8_t)b;
+}
+
+// Per-tensor mode: tensor scale read from device memory (written by
+// k_tscale_finalize on the same stream).
+template <typename T>
+__global__ __launch_bounds__(256) void k_nvfp4_quant_tensor(const T *__restrict__ x, uint32_t units,
+                                                            FastDiv cv, int64_t ldx, int64_t cols,
+                                                            const float *__restrict__ tscale,
+                                                            uint8_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales)
+{
+    const float s = tscale[0];
+    const float six_s = 6.0f * s;
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
+        float v[8];
+        Vec8<T>::load(x + (int64_t)r * ldx + (int64_t)c8 * 8, v);
+        uint32_t w;
+        uint8_t *sp = scales + (int64_t)r * (cols / 16) + (c8 >> 1);
+        nvfp4_unit(v, s, six_s, &w, sp, (c8 & 1u) == 0u);
+        *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
+    }
+}
+
+// Per-row mode: one workgroup per row; pass 1 finds the row amax, pass 2
+// re-reads the row (from cache) and quantizes it.
+template <typename T>
+__global__ __launch_bounds__(256) void k_nvfp4_quant_rows(const T *__restrict__ x, int64_t rows,
+                                                          int64_t cols, int64_t ldx,
+                                                          uint8_t *__restrict__ codes,
+                                                          uint8_t *__restrict__ scales,
+                                                          float *__restrict__ tscale,
+                                                          int32_t *__restrict__ nonfinite)
+{
+    __shared__ float red[4];
+    const int64_t units = cols / 8;
+    for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+        const T *xr = x + r * ldx;
+        float m = 0.0f;
+        int bad = 0;
+        for (int64_t u = threadIdx.x; u < units; u += 256) {
+            float v[8];
+            Vec8<T>::load(xr + u * 8, v);
+            m = fmaxf(m, amax8(v, bad));
+        }
+        if (bad && nonfinite) *nonfinite = 1;
+        m = wave_max(m);
+        if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+        __syncthreads();
+        const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        __syncthreads();
+        const float s = amax / 2688.0f;
+        const float six_s = 6.0f * s;
+        if (threadIdx.x == 0) tscale[r] = s;
+        for (int64_t u = threadIdx.x; u < units; u += 256) {
+            float v[8];
+            Vec8<T>::load(xr + u * 8, v);
+            uint32_t w;
+            nvfp4_unit(v, s, six_s, &w, scales + r * (cols / 16) + (u >> 1), (u & 1) == 0);
+            *reinterpret_cast<uint32_t *>(codes + r * (cols / 2) + u * 4) = w;
+        }
+    }
+}
+
+// ------------------------------------------------------- NVFP4 dequantize --
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_nvfp4_dequant(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ scales,
+                                                       const float *__restrict__ tscale,
+                                                       int per_row, uint32_t units, FastDiv cv,
+                                                       int64_t cols, void *__restrict__ y,
+                                                       int64_t ldy)
+{
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
+        const float bs = e4m3_value(scales[(int64_t)r * (cols / 16) + (c8 >> 1)]);
+        const float s = tscale[per_row ? r : 0];
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = (e2m1_value(w >> (4 * i)) * bs) * s;  // first product exact
+        const int64_t off = (int64_t)r * ldy + (int64_t)c8 * 8;
+        if (OUT_BF16) {
+            uint4 p;
+            p.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+            p.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+            p.z = f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16);
+            p.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(y) + off) = p;
+        } else {
+            float *yp = reinterpret_cast<float *>(y) + off;
+            *reinterpret_cast<float4 *>(yp) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4 *>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+    }
+}
+
+// --------------------------------------------------------- MXFP4 quantize --
+
+// Lanes (4i .. 4i+3) hold one 32-block.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, uint32_t units,
+                                                     FastDiv cv, int64_t ldx, int64_t cols,
+                                                     int rule, uint8_t *__restrict__ codes,
+                                                     uint8_t *__restrict__ scales,
+                                                     int32_t *__restrict__ nonfinite)
+{
+    int bad = 0;
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
+        float v[8];
+        Vec8<T>::load(x + (int64_t)r * ldx + (int64_t)c8 * 8, v);
+        float bm = amax8(v, bad);
+        bm = fmaxf(bm, xor1(bm));
+        bm = fmaxf(bm, xor2(bm));
+        uint32_t w = 0, byte = 0;
+        if (bm == 0.0f) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
+        } else {
+            const int E = __builtin_amdgcn_frexp_expf(bm) - 1;        // floor(log2 bm), exact
+            int k = E - 2;                                             // E2M1's top exponent is 2
+            if (rule == 1 && __builtin_amdgcn_frexp_mantf(bm) > 0.75f) k = E - 1;  // 6*2^(E-2) < bm
+            k = k < -127 ? -127 : (k > 127 ? 127 : k);
+            byte = (uint32_t)(k + 127);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= e2m1_code(__builtin_amdgcn_ldexpf(v[i], -k)) << (4 * i);
+        }
+        *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
+        if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
+    }
+    if (bad && nonfinite) *nonfinite = 1;
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(256) void k_mxfp4_dequant(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ scales,
+                                                       uint32_t units, FastDiv cv, int64_t cols,
+                                                       void *__restrict__ y, int64_t ldy)
+{
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
+        const int k = (int)scales[(int64_t)r * (cols / 32) + (c8 >> 2)] - 127;
+        float o[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_ldexpf(e2m1_value(w >> (4 * i)), k);
+        const int64_t off = (int64_t)r * ldy + (int64_t)c8 * 8;
+        if (OUT_BF16) {
+            uint4 p;
+            p.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
+            p.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
+            p.z = f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16);
+            p.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
+            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(y) + off) = p;
+        } else {
+            float *yp = reinterpret_cast<float *>(y) + off;
+            *reinterpret_cast<float4 *>(yp) = make_float4(o[0], o[1], o[2], o[3]);
+            *reinterpret_cast<float4 *>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
+        }
+    }
+}
+
+// ------------------------------------------------------------- launchers --
+
+static unsigned grid_for(uint64_t units, unsigned cap)
+{
+    uint64_t g = (units + 255) / 256;
+    if (g > cap) g = cap;
+    return g ? (unsigned)g : 1u;
+}
+
+fp4_status launch_nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *codes, uint8_t *scales, float *tscale,
+                                 fp4_scale_mode mode, void *ws, int32_t *nonfinite,
+                                 hipStream_t st)
+{
+    const bool bf = xt == FP4_BF16;
+    if (mode == FP4_SCALE_PER_ROW) {
+        const unsigned g = rows > 65536 ? 65536u : (unsigned)rows;
+        if (bf)
+            hipLaunchKernelGGL(k_nvfp4_quant_rows<uint16_t>, dim3(g), dim3(256), 0, st,
+                               (const uint16_t *)x, rows, cols, ldx, codes, scales, tscale, nonfinite);
+        else
+            hipLaunchKernelGGL(k_nvfp4_quant_rows<float>, dim3(g), dim3(256), 0, st,
+                               (const float *)x, rows, cols, ldx, codes, scales, tscale, nonfinite);
+        return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+    }
+    const uint32_t units = (uint32_t)(rows * (cols / 8));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const unsigned gp = grid_for(units, kAmaxPartials);
+    float *partial = reinterpret_cast<float *>(ws);
+    if (bf)
+        hipLaunchKernelGGL(k_amax_partial<uint16_t>, dim3(gp), dim3(256), 0, st, (const uint16_t *)x,
+                           units, cv, ldx, partial, nonfinite);
+    else
+        hipLaunchKernelGGL(k_amax_partial<float>, dim3(gp), dim3(256), 0, st, (const float *)x,
+                           units, cv, ldx, partial, nonfinite);
+    hipLaunchKernelGGL(k_tscale_finalize, dim3(1), dim3(256), 0, st, partial, (int)gp, tscale);
+    const unsigned gq = grid_for(units, 8192);
+    if (bf)
+        hipLaunchKernelGGL(k_nvfp4_quant_tensor<uint16_t>, dim3(gq), dim3(256), 0, st,
+                           (const uint16_t *)x, units, cv, ldx, cols, tscale, codes, scales);
+    else
+        hipLaunchKernelGGL(k_nvfp4_quant_tensor<float>, dim3(gq), dim3(256), 0, st,
+                           (const float *)x, units, cv, ldx, cols, tscale, codes, scales);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tscale,
+                                   fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
+                                   fp4_dtype yt, int64_t ldy, hipStream_t st)
+{
+    const uint32_t units = (uint32_t)(rows * (cols / 8));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const unsigned g = grid_for(units, 16384);
+    const int pr = mode == FP4_SCALE_PER_ROW;
+    if (yt == FP4_BF16)
+        hipLaunchKernelGGL(k_nvfp4_dequant<true>, dim3(g), dim3(256), 0, st, codes, scales, tscale,
+                           pr, units, cv, cols, y, ldy);
+    else
+        hipLaunchKernelGGL(k_nvfp4_dequant<false>, dim3(g), dim3(256), 0, st, codes, scales, tscale,
+                           pr, units, cv, cols, y, ldy);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *codes, uint8_t *scales, fp4_mx_rule rule,
+                                 int32_t *nonfinite, hipStream_t st)
+{
+    const uint32_t units = (uint32_t)(rows * (cols / 8));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const unsigned g = grid_for(units, 16384);
+    if (xt == FP4_BF16)
+        hipLaunchKernelGGL(k_mxfp4_quant<uint16_t>, dim3(g), dim3(256), 0, st, (const uint16_t *)x,
+                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
+    else
+        hipLaunchKernelGGL(k_mxfp4_quant<float>, dim3(g), dim3(256), 0, st, (const float *)x,
+                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                                   int64_t cols, void *y, fp4_dtype yt, int64_t ldy, hipStream_t st)
+{
+    const uint32_t units = (uint32_t)(rows * (cols / 8));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const unsigned g = grid_for(units, 16384);
+    if (yt == FP4_BF16)
+        hipLaunchKernelGGL(k_mxfp4_dequant<true>, dim3(g), dim3(256), 0, st, codes, scales, units, cv,
+                           cols, y, ldy);
+    else
+        hipLaunchKernelGGL(k_mxfp4_dequant<false>, dim3(g), dim3(256), 0, st, codes, scales, units,
+                           cv, cols, y, ldy);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+}  // namespace fp4k

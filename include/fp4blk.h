@@ -1,0 +1,192 @@
+/*
+ * fp4blk.h -- C ABI of libfp4blk: block-scaled 4-bit (NVFP4, MXFP4)
+ * quantization and the quantized linear-layer GEMMs it feeds, for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Formats (pages cited by title and section):
+ *  - NVFP4: "NVFP4" (newton.com.tw wiki), section "Technical principle".
+ *    E2M1 elements (1 sign, 2 exponent, 1 mantissa bit; values
+ *    {0, 0.5, 1, 1.5, 2, 3, 4, 6} and their negatives), 16-element micro-blocks
+ *    each with one E4M3 (OCP E4M3FN: bias 7, largest 448, no infinities) scale
+ *    byte, and one FP32 scale per tensor: 4.5 bits per value.
+ *  - MXFP4: edge-FP4 article (eefocus.com), section "FP4 as the next core
+ *    standard".  OCP MX block floating point: 32-element blocks, one E8M0 byte
+ *    (2^(byte-127)) per block, E2M1 elements: 4.25 bits per value.
+ *  - W4A16 / W4A4: Unsloth Dynamic NVFP4 article (aixq.cc), section "Core
+ *    difference: W4A4 vs W4A16".  W4A16 multiplies 4-bit weights, widened to
+ *    16 bits, by 16-bit activations; W4A4 quantizes the activations to 4 bits
+ *    as well.
+ *
+ * Packed layout (every packed tensor, row-major, blocks along the last axis):
+ *  - codes  uint8 [rows][cols/2]: element (r, c) is in byte r*cols/2 + c/2, in
+ *           the low nibble when c is even and the high nibble when c is odd;
+ *           nibble = sign<<3 | magnitude index into the grid above.
+ *  - scales uint8 [rows][cols/16] (NVFP4, E4M3FN bytes) or [rows][cols/32]
+ *           (MXFP4, E8M0 bytes).
+ *  - tscale float32 [1] (per tensor) or [rows] (per row): the NVFP4 second-level
+ *           scale; value = E2M1(code) * E4M3(scale byte) * tscale.
+ * A GEMM computes C[m][n] = sum_k A[m][k] * W[n][k] (C = A . W^T) with W [N][K]
+ * packed as above and blocks running along K.
+ *
+ * Quantization recipe (NVFP4):
+ *   tscale    = fl32(amax / 2688)                      (2688 = 6 * 448)
+ *   scale[b]  = E4M3 round-to-nearest-even, saturating at 448, of
+ *               fl32(block_amax / fl32(6 * tscale)); 0x00 for an all-zero block
+ *   code      = E2M1 round-to-nearest-even (ties to the even mantissa bit),
+ *               saturating at 6, of fl32(x / fl32(E4M3(scale[b]) * tscale));
+ *               a signed zero when that divisor is zero
+ * MXFP4: k = floor(log2 block_amax) - 2 (FP4_MX_OCP_FLOOR) or the smallest k
+ * with 6 * 2^k >= block_amax (FP4_MX_CEIL), clamped to [-127, 127]; scale byte
+ * k + 127 (0 for an all-zero block); code = E2M1-RNE-saturating(x * 2^-k).
+ *
+ * Conventions:
+ *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
+ *    allocates and frees nothing and keeps no mutable global state apart from a
+ *    per-device "is this a gfx950" cache; calls are thread-safe.
+ *  - Every call is asynchronous on `stream` (0 = the null stream) and never
+ *    synchronizes the host.
+ *  - Arguments are validated on the host before anything is launched; on an
+ *    error nothing is launched and the outputs are untouched.  Validation:
+ *    non-null pointers, all sizes > 0, leading dimensions >= the row length,
+ *    cols (or K) a multiple of 16 (NVFP4) / 32 (MXFP4), 16-byte aligned base
+ *    pointers and leading dimensions that keep every row 16-byte aligned,
+ *    workspace at least the queried size.
+ *  - Launch failures return FP4_ERR_HIP.  Non-finite inputs (NaN, Inf) violate
+ *    a precondition: outputs are unspecified and, if `nonfinite` is non-null,
+ *    the device int it points to is set to 1 (it is never cleared by the
+ *    library).
+ *  - No C++ exception crosses this interface.
+ */
+#ifndef FP4BLK_H
+#define FP4BLK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    FP4_OK = 0,
+    FP4_ERR_NULL = 1,               /* a required pointer is null */
+    FP4_ERR_SHAPE = 2,              /* a size is <= 0, or not a whole number of blocks */
+    FP4_ERR_LAYOUT = 3,             /* leading dimension too small, or misaligned pointer/row */
+    FP4_ERR_DTYPE = 4,              /* unknown dtype / mode / rule value */
+    FP4_ERR_WORKSPACE = 5,          /* workspace null or smaller than the queried size */
+    FP4_ERR_NO_DEVICE = 6,          /* no HIP device is visible */
+    FP4_ERR_UNSUPPORTED_DEVICE = 7, /* the current device is not gfx950 */
+    FP4_ERR_HIP = 8                 /* a HIP call or kernel launch failed */
+} fp4_status;
+
+typedef enum { FP4_F32 = 0, FP4_BF16 = 1 } fp4_dtype;
+typedef enum { FP4_SCALE_PER_TENSOR = 0, FP4_SCALE_PER_ROW = 1 } fp4_scale_mode;
+typedef enum { FP4_MX_OCP_FLOOR = 0, FP4_MX_CEIL = 1 } fp4_mx_rule;
+
+/* Human-readable name of a status code (static string; never null). */
+const char *fp4_status_str(int status);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+int fp4blk_version(void);
+
+/* FP4_OK if the current HIP device is a gfx950, else NO_DEVICE / UNSUPPORTED_DEVICE. */
+fp4_status fp4blk_check_device(void);
+
+/* ------------------------------------------------------------ NVFP4 ------ */
+
+/* Workspace bytes nvfp4_quantize needs (0 for FP4_SCALE_PER_ROW). */
+size_t nvfp4_quantize_workspace(int64_t rows, int64_t cols, fp4_scale_mode mode);
+
+/* NVFP4 quantize ("NVFP4", Technical principle: two-level micro-block scaling).
+ *  x        [rows][ldx] fp32 or bf16 (xt), cols % 16 == 0, read only.
+ *  codes    [rows][cols/2] out; scales [rows][cols/16] out (E4M3FN bytes).
+ *  tscale   out: [1] for FP4_SCALE_PER_TENSOR (amax over the whole tensor),
+ *           [rows] for FP4_SCALE_PER_ROW (each row is its own tensor).
+ *  ws       device scratch of nvfp4_quantize_workspace() bytes (per-tensor mode).
+ *  nonfinite optional device int32 flag, set to 1 if x holds NaN/Inf.
+ * Codes and scale bytes equal the recipe above bit for bit. */
+fp4_status nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *codes, uint8_t *scales, float *tscale, fp4_scale_mode mode,
+                          void *ws, size_t ws_bytes, int32_t *nonfinite, hipStream_t stream);
+
+/* NVFP4 dequantize: y = fl32(fl32(E2M1(c) * E4M3(s)) * tscale) (the inner
+ * product is exact), stored as fp32 or rounded to nearest even into bf16 (yt).
+ *  y [rows][ldy] out. */
+fp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tscale,
+                            fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
+                            fp4_dtype yt, int64_t ldy, hipStream_t stream);
+
+/* W4A16 GEMM (aixq.cc article, "Core difference: W4A4 vs W4A16"): C = A . W^T.
+ *  a        [M][lda] bf16 activations.
+ *  w_*      W [N][K] NVFP4 with a per-tensor scale (w_tscale[1]).
+ *  c        [M][ldc] out, fp32 or bf16 (ct; bf16 by round to nearest even).
+ * Each weight is widened exactly to E2M1 * E4M3 in bfloat16, products are
+ * accumulated in fp32 and the sum is multiplied by w_tscale.  |C - C_exact|
+ * stays within 2e-3 * sum_k |a w| (C_exact: fp64 over the dequantized W). */
+fp4_status gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes,
+                      const uint8_t *w_scales, const float *w_tscale, int64_t N, void *c,
+                      fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
+/* Workspace bytes gemm_w4a4 needs: A's codes | scales | tscale, each starting
+ * at a 256-byte boundary, in that order (offsets by gemm_w4a4_workspace_offsets). */
+size_t gemm_w4a4_workspace(int64_t M, int64_t K, fp4_scale_mode a_mode);
+void gemm_w4a4_workspace_offsets(int64_t M, int64_t K, size_t *codes_off, size_t *scales_off,
+                                 size_t *tscale_off);
+
+/* W4A4 NVFP4 GEMM (aixq.cc article, "Core difference"): the bf16 activations
+ * are quantized to NVFP4 on the device (a_mode: per row, each row its own
+ * tensor, or per tensor) into `ws`, then C = A_q . W^T with both operands
+ * widened exactly to bfloat16, fp32 accumulation, and the epilogue multiplies
+ * by the activation scale (per row) and the weight tensor scale.  After the call
+ * `ws` holds A's packed NVFP4 form (codes, scales, tscale) at the documented
+ * offsets.  Same tolerance as gemm_w4a16, against fp64 over the two dequantized
+ * operands. */
+fp4_status gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale,
+                     int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
+                     hipStream_t stream);
+
+/* The GEMM half of gemm_w4a4 on an already-quantized A (codes [M][K/2],
+ * scales [M][K/16], a_tscale [1] or [M] per a_mode). */
+fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    const float *a_tscale, fp4_scale_mode a_mode, int64_t M,
+                                    int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+                                    const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
+                                    int64_t ldc, hipStream_t stream);
+
+/* ------------------------------------------------------------ MXFP4 ------ */
+
+/* MXFP4 quantize (eefocus.com article, "FP4 as the next core standard").
+ *  x [rows][ldx] fp32 or bf16, cols % 32 == 0; codes [rows][cols/2] out;
+ *  scales [rows][cols/32] E8M0 out; rule FP4_MX_OCP_FLOOR or FP4_MX_CEIL. */
+fp4_status mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *codes, uint8_t *scales, fp4_mx_rule rule, int32_t *nonfinite,
+                          hipStream_t stream);
+
+/* MXFP4 dequantize: y = E2M1(c) * 2^(s-127) (exact when in range), fp32 or bf16. */
+fp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
+                            int64_t cols, void *y, fp4_dtype yt, int64_t ldy, hipStream_t stream);
+
+/* Workspace bytes mxfp4_gemm_w4a4 needs: A's codes | scales, 256-byte aligned. */
+size_t mxfp4_gemm_w4a4_workspace(int64_t M, int64_t K);
+
+/* MXFP4 W4A4 GEMM: A (bf16) is quantized to MXFP4 with `rule` into `ws`, then
+ * C = A_q . W^T on gfx950's block-scaled FP4 matrix instruction (E8M0 scale per
+ * 32 K-elements per row, the MX block), fp32 accumulation.  W [N][K] MXFP4. */
+fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                           const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                           fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
+                           hipStream_t stream);
+
+/* The GEMM half of mxfp4_gemm_w4a4 on an already-quantized A. */
+fp4_status mxfp4_gemm_prequant(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M,
+                               int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+                               int64_t N, void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FP4BLK_H */
