@@ -69,72 +69,95 @@ __device__ __forceinline__ uint4 ld_u128(const uint8_t *p)
 }
 
 // ============================================================ decode =======
-// M <= 16.  Workgroup = 4 waves = one 16-row N-tile (x NT); wave w owns a quarter
-// of the K steps (128 K per step).  Lane l = (n = l % 16, g = l / 16) loads 32
-// consecutive codes (16 bytes) of W row n at k0 + 32 g and their two scale bytes,
-// and feeds them to four 16x16x32 MFMAs; MFMA j contracts the K values
-// k0 + 32 g + 8 j + [0, 8) of every lane group g (a permutation of K that A and
-// W share, so the sum is unchanged).  The four waves' partial tiles are added
-// in LDS and the epilogue multiplies by the tensor scale.
+// M <= 16, HBM-bound: the kernel's job is to keep the whole weight streaming.
+// Workgroup = 4 waves over 32 W rows (two 16-row N-tiles); wave w owns a
+// quarter of the K steps (128 K per step).  Lane l = (n = l % 16, g = l / 16)
+// reads, for each of its steps and tiles, the 32 consecutive codes (16 bytes) of
+// W row n at k0 + 32 g and their two scale bytes; all of these loads are issued
+// before any arithmetic, so the full weight is in flight at once.  Each 16-byte
+// run feeds four 16x16x32 MFMAs: MFMA j contracts the K values
+// k0 + 32 g + 8 j + [0, 8) of every lane group g (a permutation of K that A and W
+// share, so the sum is unchanged); one A fragment serves both N-tiles.  The
+// four waves' partial tiles are added in LDS and the epilogue multiplies by the
+// tensor scale.  At K = 5120 a wave holds its 10 steps x 2 tiles of codes in
+// registers, so 544 workgroups (all resident at 3 waves per SIMD) have the whole
+// weight in flight.
 
-constexpr int kDecNT = 1;  // N-tiles (16 rows) per workgroup
+constexpr int kDecNT = 2;      // N-tiles (16 rows) per workgroup
+constexpr int kDecWaves = 4;   // waves per workgroup, splitting K
+constexpr int kDecMaxS = 10;   // K steps a wave keeps in flight
 
 template <bool ALIGNED>
-__global__ __launch_bounds__(256) void k_nv_decode(const uint16_t *__restrict__ a, int64_t lda,
+__global__ __launch_bounds__(256, 3) void k_nv_decode_generic(const uint16_t *__restrict__ a, int64_t lda,
                                                    const uint8_t *__restrict__ wc,
                                                    const uint8_t *__restrict__ wsc,
                                                    const float *__restrict__ wts, int M, int N,
                                                    int K, void *__restrict__ c, int c_bf16,
                                                    int64_t ldc)
 {
-    __shared__ f32x4 part[4][kDecNT][64];
+    __shared__ f32x4 part[kDecWaves][kDecNT][64];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int ln = lane & 15, g = lane >> 4;
     const int n_base = blockIdx.x * 16 * kDecNT;
     const int nsteps = (K + 127) / 128;
-    const int s_begin = (nsteps * wave) / 4, s_end = (nsteps * (wave + 1)) / 4;
-    const int am = ln;  // A row this lane feeds
-    const bool a_ok = am < M;
+    const int s_begin = (nsteps * wave) / kDecWaves, s_end = (nsteps * (wave + 1)) / kDecWaves;
+    const bool a_ok = ln < M;
+    const uint16_t *arow = a + (int64_t)(a_ok ? ln : 0) * lda;
 
     f32x4 acc[kDecNT];
 #pragma unroll
     for (int t = 0; t < kDecNT; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    for (int s = s_begin; s < s_end; ++s) {
-        const int kb = s * 128 + g * 32;  // first K of this lane's 32
-        uint4 cw[kDecNT];
-        uint32_t sw[kDecNT];
+    for (int s0 = s_begin; s0 < s_end; s0 += kDecMaxS) {
+        const int ns = min(kDecMaxS, s_end - s0);
+        uint4 cw[kDecMaxS][kDecNT];
+        uint32_t sw[kDecMaxS][kDecNT];
+        // issue every weight load of this chunk first
 #pragma unroll
-        for (int t = 0; t < kDecNT; ++t) {
-            const int n = n_base + t * 16 + ln;
-            cw[t] = uint4{0u, 0u, 0u, 0u};
-            sw[t] = 0;
-            if (n < N) {
-                const uint8_t *cp = wc + (int64_t)n * (K / 2) + kb / 2;
-                const uint8_t *sp = wsc + (int64_t)n * (K / 16) + kb / 16;
-                if (kb + 32 <= K) {
-                    cw[t] = ld_u128<ALIGNED>(cp);
-                    sw[t] = ALIGNED ? (uint32_t)*reinterpret_cast<const uint16_t *>(sp)
-                                    : ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8));
-                } else if (kb + 16 <= K) {
-                    cw[t].x = ld_u32<false>(cp);
-                    cw[t].y = ld_u32<false>(cp + 4);
-                    sw[t] = sp[0];
+        for (int i = 0; i < kDecMaxS; ++i) {
+#pragma unroll
+            for (int t = 0; t < kDecNT; ++t) {
+                cw[i][t] = uint4{0u, 0u, 0u, 0u};
+                sw[i][t] = 0;
+                const int n = n_base + t * 16 + ln;
+                const int kb = (s0 + i) * 128 + g * 32;
+                if (i < ns && n < N) {
+                    const uint8_t *cp = wc + (int64_t)n * (K / 2) + kb / 2;
+                    const uint8_t *sp = wsc + (int64_t)n * (K / 16) + kb / 16;
+                    if (kb + 32 <= K) {
+                        cw[i][t] = ld_u128<ALIGNED>(cp);
+                        sw[i][t] = ALIGNED ? (uint32_t)*reinterpret_cast<const uint16_t *>(sp)
+                                           : ((uint32_t)sp[0] | ((uint32_t)sp[1] << 8));
+                    } else if (kb + 16 <= K) {
+                        cw[i][t].x = ld_u32<false>(cp);
+                        cw[i][t].y = ld_u32<false>(cp + 4);
+                        sw[i][t] = sp[0];
+                    }
                 }
             }
         }
-        const uint16_t *ap = a + (int64_t)am * lda + kb;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            uint4 av = uint4{0u, 0u, 0u, 0u};
-            if (a_ok && kb + 8 * j < K) av = *reinterpret_cast<const uint4 *>(ap + 8 * j);
-            const bf16x8 A = as_bf16x8(av);
+        for (int i = 0; i < kDecMaxS; ++i) {
+            if (i < ns) {
+                const int kb = (s0 + i) * 128 + g * 32;
+                float bs[kDecNT][2];
 #pragma unroll
-            for (int t = 0; t < kDecNT; ++t) {
-                const uint32_t cwj = j == 0 ? cw[t].x : j == 1 ? cw[t].y : j == 2 ? cw[t].z : cw[t].w;
-                const float bs = e4m3_value((sw[t] >> (j < 2 ? 0 : 8)) & 0xFFu);
-                const bf16x8 B = as_bf16x8(dq8_bf16(cwj, bs));
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
+                for (int t = 0; t < kDecNT; ++t) {
+                    bs[t][0] = e4m3_value(sw[i][t] & 0xFFu);
+                    bs[t][1] = e4m3_value((sw[i][t] >> 8) & 0xFFu);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint4 av = uint4{0u, 0u, 0u, 0u};
+                    if (a_ok && kb + 8 * j < K) av = *reinterpret_cast<const uint4 *>(arow + kb + 8 * j);
+                    const bf16x8 A = as_bf16x8(av);
+#pragma unroll
+                    for (int t = 0; t < kDecNT; ++t) {
+                        const uint32_t cwj = j == 0 ? cw[i][t].x : j == 1 ? cw[i][t].y : j == 2 ? cw[i][t].z : cw[i][t].w;
+                        const bf16x8 B = as_bf16x8(dq8_bf16(cwj, bs[t][j >> 1]));
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc[t], 0, 0, 0);
+                    }
+                }
             }
         }
     }
@@ -142,12 +165,15 @@ __global__ __launch_bounds__(256) void k_nv_decode(const uint16_t *__restrict__ 
     for (int t = 0; t < kDecNT; ++t) part[wave][t][lane] = acc[t];
     __syncthreads();
     const float wt = wts[0];
-    // 256 threads; each (t, lane, r) output: thread -> lane = tid & 63, r = tid >> 6
-    for (int idx = threadIdx.x; idx < kDecNT * 64 * 4; idx += 256) {
-        const int t = idx / 256, rem = idx % 256;
+    // kDecNT * 64 lanes * 4 slots outputs; slot r of lane l is C row 4 (l / 16) + r,
+    // column l % 16 of the tile
+    for (int idx = threadIdx.x; idx < kDecNT * 256; idx += 64 * kDecWaves) {
+        const int t = idx >> 8, rem = idx & 255;
         const int l = rem & 63, r = rem >> 6;
-        const float v = part[0][t][l][r] + part[1][t][l][r] + part[2][t][l][r] + part[3][t][l][r];
-        const int m = (l >> 4) * 4 + r;  // C row of accumulator slot r in lane l
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kDecWaves; ++w) v += part[w][t][l][r];
+        const int m = (l >> 4) * 4 + r;
         const int n = n_base + t * 16 + (l & 15);
         if (m < M && n < N) {
             const float o = v * wt;
@@ -157,6 +183,406 @@ __global__ __launch_bounds__(256) void k_nv_decode(const uint16_t *__restrict__ 
                 reinterpret_cast<float *>(c)[(int64_t)m * ldc + n] = o;
         }
     }
+}
+
+// Decode kernel for K % 128 == 0 (the common case).  Workgroup = 4 waves on 16
+// W rows; wave w owns a quarter of the K steps and walks it in passes of up to
+// 5 steps (640 K).  A pass's codes are read with coalesced 16-byte loads -- the
+// 64 lanes cover consecutive 16-byte chunks of the 16 rows' pass segments -- and
+// its scale bytes with coalesced 32-bit loads; the wave then writes them to its
+// own LDS region in the order the MFMA wants and reads them back (no other wave
+// touches that region, so a wave-scope fence is the only synchronization).  The
+// chunk of row r holding K values [32 c, 32 c + 32) of the pass feeds MFMA
+// lane r + 16 (c % 4) in step c / 4: a permutation of K shared with A.  Loads of
+// pass p + 1 are issued before pass p is computed.
+
+constexpr int kDecP = 5;                      // steps (128 K) per pass
+constexpr int kDecChunks = kDecP * 4 * 16 / 64;   // 16-byte code chunks per lane per pass = 5
+constexpr int kDecSDw = (kDecP * 8 * 16 + 255) / 256;  // scale dwords per lane per pass = 3
+
+struct DecPass {
+    u32x4 c[kDecChunks];
+    uint32_t s[kDecSDw];
+};
+
+__device__ __forceinline__ void dec_load(DecPass &p, const uint8_t *__restrict__ wc,
+                                         const uint8_t *__restrict__ wsc, int n0, int N, int K,
+                                         int kpass, int steps, int lane)
+{
+    const int seg = steps * 4;  // 16-byte chunks per row in this pass
+#pragma unroll
+    for (int i = 0; i < kDecChunks; ++i) {
+        const int q = i * 64 + lane;
+        const int row = q / (kDecP * 4), c = q % (kDecP * 4);
+        p.c[i] = u32x4{0u, 0u, 0u, 0u};
+        if (c < seg && n0 + row < N)
+            p.c[i] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4 *>(wc + (int64_t)(n0 + row) * (K / 2) + kpass / 2) + c);
+    }
+    // scale bytes of the pass: 16 rows x (steps * 8) bytes, as dwords
+    const int sdw = steps * 2;  // dwords per row
+#pragma unroll
+    for (int i = 0; i < kDecSDw; ++i) {
+        const int q = i * 64 + lane;
+        const int row = q / (kDecP * 2), d = q % (kDecP * 2);
+        p.s[i] = 0;
+        if (row < 16 && d < sdw && n0 + row < N)
+            p.s[i] = reinterpret_cast<const uint32_t *>(wsc + (int64_t)(n0 + row) * (K / 16) + kpass / 16)[d];
+    }
+}
+
+__device__ __forceinline__ void dec_stage(uint8_t *lds, const DecPass &p, int lane)
+{
+    // codes: chunk (row, c) -> slot (c / 4) * 64 + row + 16 (c % 4); scales: [row][kDecP * 8]
+#pragma unroll
+    for (int i = 0; i < kDecChunks; ++i) {
+        const int q = i * 64 + lane;
+        const int row = q / (kDecP * 4), c = q % (kDecP * 4);
+        reinterpret_cast<u32x4 *>(lds)[(c >> 2) * 64 + row + 16 * (c & 3)] = p.c[i];
+    }
+#pragma unroll
+    for (int i = 0; i < kDecSDw; ++i) {
+        const int q = i * 64 + lane;
+        if (q < 16 * kDecP * 2) reinterpret_cast<uint32_t *>(lds + kDecP * 64 * 16)[q] = p.s[i];
+    }
+}
+
+// E4M3FN byte (sign clear) -> fp32: the byte placed at fp32 bit 20 reads as
+// 2^(e-127) (1 + m/8) (or the denormal m * 2^-129 when e == 0); times 2^120 that
+// is exactly the E4M3 value (2^(e-7) (1 + m/8), or m * 2^-9).
+__device__ __forceinline__ float e4m3_fast(uint32_t byte_at_bit20)
+{
+    return __uint_as_float(byte_at_bit20) * 0x1p120f;
+}
+
+// One pass of the decode kernel over `steps` (compile-time) steps.
+template <int STEPS>
+__device__ __forceinline__ void dec_compute(f32x4 &acc, const uint8_t *lds, const uint16_t *arow,
+                                            int kpass, int lane, int i0)
+{
+    const int ln = lane & 15, g = lane >> 4;
+    const uint32_t *sp = reinterpret_cast<const uint32_t *>(lds + kDecP * 64 * 16);
+#pragma unroll
+    for (int ii = 0; ii < STEPS; ++ii) {
+        const int i = i0 + ii;
+        const u32x4 cw = reinterpret_cast<const u32x4 *>(lds)[i * 64 + lane];
+        // scale bytes of this lane's two 16-blocks: row ln, bytes 8 i + 2 g, 8 i + 2 g + 1
+        const uint32_t sw = sp[ln * (kDecP * 2) + 2 * i + (g >> 1)] >> (16 * (g & 1));
+        const float bs0 = e4m3_fast((sw << 20) & 0x0FF00000u);
+        const float bs1 = e4m3_fast((sw << 12) & 0x0FF00000u);
+        const uint16_t *ap = arow + kpass + i * 128 + g * 32;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const bf16x8 A = *reinterpret_cast<const bf16x8 *>(ap + 8 * j);
+            const bf16x8 B = as_bf16x8(dq8_bf16(cw[j], j < 2 ? bs0 : bs1));
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, acc, 0, 0, 0);
+        }
+    }
+}
+
+__device__ __forceinline__ void dec_pass(f32x4 &acc, uint8_t *lds, const DecPass &p,
+                                         const uint16_t *arow, int kpass, int steps, int lane)
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    dec_stage(lds, p, lane);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (steps == kDecP) {
+        dec_compute<kDecP>(acc, lds, arow, kpass, lane, 0);
+    } else {
+        for (int i = 0; i < steps; ++i) dec_compute<1>(acc, lds, arow, kpass, lane, i);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+}
+
+__global__ __launch_bounds__(256) void k_nv_decode(const uint16_t *__restrict__ a, int64_t lda,
+                                                   const uint8_t *__restrict__ wc,
+                                                   const uint8_t *__restrict__ wsc,
+                                                   const float *__restrict__ wts, int M, int N,
+                                                   int K, void *__restrict__ c, int c_bf16,
+                                                   int64_t ldc)
+{
+    constexpr int kRegion = kDecP * 64 * 16 + 16 * kDecP * 8;  // codes + scale bytes per wave
+    __shared__ __align__(16) uint8_t stage[4][kRegion];
+    __shared__ f32x4 part[4][64];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int ln = lane & 15;
+    const int n0 = blockIdx.x * 16;
+    const int nsteps = K / 128;
+    const int s_begin = (nsteps * wave) / 4, s_end = (nsteps * (wave + 1)) / 4;
+    // lanes feeding A rows >= M read row M - 1 instead: those MFMA output rows are
+    // never stored, and no other output row depends on them
+    const uint16_t *arow = a + (int64_t)min(ln, M - 1) * lda;
+    uint8_t *lds = stage[wave];
+
+    f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+    DecPass p0, p1;
+    int s0 = s_begin;
+    if (s0 < s_end) dec_load(p0, wc, wsc, n0, N, K, s0 * 128, min(kDecP, s_end - s0), lane);
+    while (s0 < s_end) {
+        const int st0 = min(kDecP, s_end - s0);
+        const int s1 = s0 + st0;
+        if (s1 < s_end) dec_load(p1, wc, wsc, n0, N, K, s1 * 128, min(kDecP, s_end - s1), lane);
+        dec_pass(acc, lds, p0, arow, s0 * 128, st0, lane);
+        if (s1 >= s_end) break;
+        const int st1 = min(kDecP, s_end - s1);
+        const int s2 = s1 + st1;
+        if (s2 < s_end) dec_load(p0, wc, wsc, n0, N, K, s2 * 128, min(kDecP, s_end - s2), lane);
+        dec_pass(acc, lds, p1, arow, s1 * 128, st1, lane);
+        s0 = s2;
+    }
+    part[wave][lane] = acc;
+    __syncthreads();
+    const float wt = wts[0];
+    {
+        const int l = threadIdx.x & 63, r = threadIdx.x >> 6;
+        const float v = part[0][l][r] + part[1][l][r] + part[2][l][r] + part[3][l][r];
+        const int m = (l >> 4) * 4 + r;
+        const int n = n0 + (l & 15);
+        if (m < M && n < N) {
+            const float o = v * wt;
+            if (c_bf16)
+                reinterpret_cast<uint16_t *>(c)[(int64_t)m * ldc + n] = (uint16_t)f32_to_bf16_rne(o);
+            else
+                reinterpret_cast<float *>(c)[(int64_t)m * ldc + n] = o;
+        }
+    }
+}
+
+// Persistent decode kernel for K = 1024 S (S = 1..8 steps of 128 K per wave).
+// One workgroup per CU, 8 waves; workgroup b owns W rows [N b / G, N (b+1) / G),
+// so every CU streams the same number of weight bytes.  Wave w owns K slice
+// [128 S w, 128 S (w+1)): it loads its A fragments once (S x 4 16-byte loads per
+// lane, kept in registers for the whole kernel) and then walks the workgroup's
+// 16-row tiles.  A tile's codes and scale bytes for the slice are copied into a
+// per-wave LDS ring (depth D) by global->LDS DMA loads that read whole 128-byte
+// lines: instruction t, lane i fetches row-major chunk 64 t + (i ^ ((i >> 4) & 3))
+// of the tile (16 rows x 4 S chunks of 16 bytes) and lands in LDS slot 64 t + i.
+// The MFMA lane (n, g) then reads chunk (n, 4 s + g) at slot 64 t + (o ^ ((o >> 4)
+// & 3)) (o = q % 64, t = q / 64, q = 4 S n + 4 s + g), which for odd S puts the 16
+// lanes of a group on 16 different bank groups.  The ring keeps D - 1 tiles in
+// flight; waits are exact vmcnt counts of the DMA loads issued after the tile
+// being consumed.  The eight K-slice partial tiles are summed in LDS at the end.
+
+constexpr int kPersistWaves = 8;
+constexpr int kPersistMaxT = 5;   // 16-row tiles per workgroup
+
+__device__ __forceinline__ void waitcnt_vm(int n)
+{
+    // s_waitcnt with vmcnt = n (n < 64), expcnt and lgkmcnt left at their maxima
+    switch (n) {
+#define FP4K_WC(N) case N: __builtin_amdgcn_s_waitcnt(((N) & 0xF) | (((N) >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
+        FP4K_WC(0) FP4K_WC(1) FP4K_WC(2) FP4K_WC(3) FP4K_WC(4) FP4K_WC(5) FP4K_WC(6) FP4K_WC(7)
+        FP4K_WC(8) FP4K_WC(9) FP4K_WC(10) FP4K_WC(11) FP4K_WC(12) FP4K_WC(13) FP4K_WC(14) FP4K_WC(15)
+        FP4K_WC(16) FP4K_WC(17) FP4K_WC(18) FP4K_WC(19) FP4K_WC(20) FP4K_WC(21) FP4K_WC(22) FP4K_WC(23)
+        FP4K_WC(24) FP4K_WC(25) FP4K_WC(26) FP4K_WC(27) FP4K_WC(28) FP4K_WC(29) FP4K_WC(30) FP4K_WC(31)
+#undef FP4K_WC
+    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;  // vmcnt(0)
+    }
+}
+
+template <int S>
+struct PersistCfg {
+    static constexpr int kCodeBytes = 16 * S * 64;               // 16 rows x S steps x 64 bytes
+    static constexpr int kCodeInstr = kCodeBytes / 1024;         // 16-byte DMA instructions = S
+    static constexpr int kScaleDw = 16 * S * 2;                  // scale dwords of a tile slice
+    static constexpr int kScaleInstr = (kScaleDw + 63) / 64;     // 4-byte DMA instructions
+    static constexpr int kUnitBytes = kCodeBytes + kScaleInstr * 256;
+    static constexpr int D = S <= 5 ? 3 : 2;                     // ring depth (tiles)
+    static constexpr int kLoads = kCodeInstr + kScaleInstr;      // vmem instructions per tile
+    static constexpr size_t kRing = (size_t)kPersistWaves * D * kUnitBytes;
+    static constexpr size_t kReduce = (size_t)kPersistWaves * kPersistMaxT * 64 * 16;  // partial tiles
+    static constexpr size_t kLds = kRing > kReduce ? kRing : kReduce;
+};
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Per-lane byte offsets of a tile's DMA sources, relative to the tile's first row
+// (computed once; a tile adds a wave-uniform base).
+template <int S>
+struct PersistLane {
+    uint32_t code_off[PersistCfg<S>::kCodeInstr];
+    uint32_t scale_off[PersistCfg<S>::kScaleInstr];
+    uint8_t code_row[PersistCfg<S>::kCodeInstr];
+    uint8_t scale_row[PersistCfg<S>::kScaleInstr];
+};
+
+template <int S>
+__device__ __forceinline__ void persist_lane_init(PersistLane<S> &pl, int K, int kslice, int lane)
+{
+    using C = PersistCfg<S>;
+    const int o = lane ^ ((lane >> 4) & 3);
+#pragma unroll
+    for (int t = 0; t < C::kCodeInstr; ++t) {
+        const int q = 64 * t + o;
+        const int row = q / (4 * S), cc = q % (4 * S);
+        pl.code_row[t] = (uint8_t)row;
+        pl.code_off[t] = (uint32_t)(row * (K / 2) + kslice / 2 + cc * 16);
+    }
+#pragma unroll
+    for (int t = 0; t < C::kScaleInstr; ++t) {
+        const int q = min(64 * t + lane, C::kScaleDw - 1);
+        const int row = q / (2 * S), d = q % (2 * S);
+        pl.scale_row[t] = (uint8_t)row;
+        pl.scale_off[t] = (uint32_t)(row * (K / 16) + kslice / 16 + 4 * d);
+    }
+}
+
+// DMA one tile (rows t0 .. t0 + 15, clamped to n_hi - 1) of the wave's K slice into buf.
+template <int S>
+__device__ __forceinline__ void persist_issue(uint8_t *buf, const uint8_t *__restrict__ wc,
+                                              const uint8_t *__restrict__ wsc, int t0, int n_hi,
+                                              int K, const PersistLane<S> &pl)
+{
+    using C = PersistCfg<S>;
+    const uint8_t *cbase = wc + (int64_t)t0 * (K / 2);
+    const uint8_t *sbase = wsc + (int64_t)t0 * (K / 16);
+    if (t0 + 16 <= n_hi) {
+#pragma unroll
+        for (int t = 0; t < C::kCodeInstr; ++t)
+            __builtin_amdgcn_global_load_lds(cbase + pl.code_off[t], (lds_void *)(buf + t * 1024), 16, 0, 0);
+#pragma unroll
+        for (int t = 0; t < C::kScaleInstr; ++t)
+            __builtin_amdgcn_global_load_lds(sbase + pl.scale_off[t],
+                                             (lds_void *)(buf + C::kCodeBytes + t * 256), 4, 0, 0);
+    } else {
+        // partial last tile: rows past n_hi re-read row n_hi - 1 (never stored)
+        const int last = n_hi - 1 - t0;
+#pragma unroll
+        for (int t = 0; t < C::kCodeInstr; ++t) {
+            const int back = max((int)pl.code_row[t] - last, 0);
+            __builtin_amdgcn_global_load_lds(cbase + pl.code_off[t] - (int64_t)back * (K / 2),
+                                             (lds_void *)(buf + t * 1024), 16, 0, 0);
+        }
+#pragma unroll
+        for (int t = 0; t < C::kScaleInstr; ++t) {
+            const int back = max((int)pl.scale_row[t] - last, 0);
+            __builtin_amdgcn_global_load_lds(sbase + pl.scale_off[t] - (int64_t)back * (K / 16),
+                                             (lds_void *)(buf + C::kCodeBytes + t * 256), 4, 0, 0);
+        }
+    }
+}
+
+template <int S>
+__global__ __launch_bounds__(512, 1) void k_nv_decode_persist(const uint16_t *__restrict__ a,
+                                                              int64_t lda,
+                                                              const uint8_t *__restrict__ wc,
+                                                              const uint8_t *__restrict__ wsc,
+                                                              const float *__restrict__ wts, int M,
+                                                              int N, int K, void *__restrict__ c,
+                                                              int c_bf16, int64_t ldc)
+{
+    using C = PersistCfg<S>;
+    extern __shared__ __align__(16) uint8_t psmem[];
+    const int lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int ln = lane & 15, g = lane >> 4;
+    const int n_lo = (int)((int64_t)N * blockIdx.x / gridDim.x);
+    const int n_hi = (int)((int64_t)N * (blockIdx.x + 1) / gridDim.x);
+    const int ntiles = (n_hi - n_lo + 15) / 16;
+    const int kslice = wave * S * 128;
+    uint8_t *ring = psmem + (size_t)wave * C::D * C::kUnitBytes;
+
+    // A fragments of this wave's K slice (rows >= M read row M - 1: their MFMA
+    // output rows are never stored and no stored row depends on them)
+    bf16x8 af[S][4];
+    {
+        const uint16_t *ap = a + (int64_t)min(ln, M - 1) * lda + kslice + g * 32;
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) af[s][j] = *reinterpret_cast<const bf16x8 *>(ap + s * 128 + j * 8);
+    }
+    PersistLane<S> pl;
+    persist_lane_init<S>(pl, K, kslice, lane);
+    if (ntiles > 0) persist_issue<S>(ring, wc, wsc, n_lo, n_hi, K, pl);
+    if (C::D > 2 && ntiles > 1) persist_issue<S>(ring + C::kUnitBytes, wc, wsc, n_lo + 16, n_hi, K, pl);
+
+    // LDS offsets this lane reads: code slot of step s, scale dword and shift
+    uint32_t code_slot[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        const int q = 4 * S * ln + 4 * s + g;
+        code_slot[s] = (uint32_t)(((q & ~63) | ((q & 63) ^ (((q & 63) >> 4) & 3))) * 16);
+    }
+    const uint32_t scale_base = (uint32_t)(C::kCodeBytes + (ln * 2 * S + (g >> 1)) * 4);
+    const uint32_t scale_shift = 16u * (g & 1);
+
+    f32x4 acc[kPersistMaxT];
+#pragma unroll
+    for (int u = 0; u < kPersistMaxT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+    for (int u = 0; u < kPersistMaxT; ++u) {
+        if (u < ntiles) {
+            const int ahead = u + C::D - 1;  // tile issued now, into the slot tile u - 1 used
+            __builtin_amdgcn_s_waitcnt((0x3F & 0xF) | (0x3 << 14) | (0x7 << 4));  // lgkmcnt(0)
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            if (ahead < ntiles)
+                persist_issue<S>(ring + (ahead % C::D) * C::kUnitBytes, wc, wsc, n_lo + 16 * ahead, n_hi,
+                                 K, pl);
+            // tiles issued after tile u: min(D - 1, ntiles - 1 - u)
+            waitcnt_vm(min(C::D - 1, ntiles - 1 - u) * C::kLoads);
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            const uint8_t *buf = ring + (u % C::D) * C::kUnitBytes;
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                const u32x4 cw = *reinterpret_cast<const u32x4 *>(buf + code_slot[s]);
+                const uint32_t sw = *reinterpret_cast<const uint32_t *>(buf + scale_base + 8 * s) >> scale_shift;
+                const float bs0 = e4m3_fast((sw << 20) & 0x0FF00000u);
+                const float bs1 = e4m3_fast((sw << 12) & 0x0FF00000u);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const bf16x8 B = as_bf16x8(dq8_bf16(cw[j], j < 2 ? bs0 : bs1));
+                    acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][j], B, acc[u], 0, 0, 0);
+                }
+            }
+        }
+    }
+
+    // sum the eight K-slice partials (the rings are free now)
+    __syncthreads();
+    f32x4 *part = reinterpret_cast<f32x4 *>(psmem);  // [wave][tile][lane]
+#pragma unroll
+    for (int u = 0; u < kPersistMaxT; ++u)
+        if (u < ntiles) part[(wave * kPersistMaxT + u) * 64 + lane] = acc[u];
+    __syncthreads();
+    const float wt = wts[0];
+    for (int idx = threadIdx.x; idx < ntiles * 256; idx += 64 * kPersistWaves) {
+        const int u = idx >> 8, l = idx & 63, r = (idx >> 6) & 3;
+        float v = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kPersistWaves; ++w) v += part[(w * kPersistMaxT + u) * 64 + l][r];
+        const int m = (l >> 4) * 4 + r;
+        const int n = n_lo + 16 * u + (l & 15);
+        if (m < M && n < n_hi) {
+            const float o = v * wt;
+            if (c_bf16)
+                reinterpret_cast<uint16_t *>(c)[(int64_t)m * ldc + n] = (uint16_t)f32_to_bf16_rne(o);
+            else
+                reinterpret_cast<float *>(c)[(int64_t)m * ldc + n] = o;
+        }
+    }
+}
+
+template <int S>
+static fp4_status launch_decode_persist(const NvGemmArgs &g, hipStream_t st)
+{
+    using C = PersistCfg<S>;
+    static bool attr_set = false;  // benign race: every setter writes the same value
+    if (!attr_set) {
+        if (hipFuncSetAttribute((const void *)k_nv_decode_persist<S>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds) != hipSuccess)
+            return FP4_ERR_HIP;
+        attr_set = true;
+    }
+    // enough workgroups that none owns more than kPersistMaxT tiles, at least one per CU
+    int64_t grid = (g.N + 16 * kPersistMaxT - 1) / (16 * kPersistMaxT);
+    if (grid < 256) grid = 256;
+    if (grid > (g.N + 15) / 16) grid = (g.N + 15) / 16;
+    hipLaunchKernelGGL(k_nv_decode_persist<S>, dim3((unsigned)grid), dim3(64 * kPersistWaves), C::kLds,
+                       st, g.a, g.lda, g.w_codes, g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K,
+                       g.c, g.c_bf16, g.ldc);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
 // =========================================================== prefill =======
@@ -385,13 +811,33 @@ fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
 {
     const bool aligned = (g.K % 64) == 0;
     if (!g.a_codes && g.M <= 16) {
+        if (g.K % 1024 == 0 && g.K <= 8192) {
+            switch (g.K / 1024) {
+            case 1: return launch_decode_persist<1>(g, st);
+            case 2: return launch_decode_persist<2>(g, st);
+            case 3: return launch_decode_persist<3>(g, st);
+            case 4: return launch_decode_persist<4>(g, st);
+            case 5: return launch_decode_persist<5>(g, st);
+            case 6: return launch_decode_persist<6>(g, st);
+            case 7: return launch_decode_persist<7>(g, st);
+            default: return launch_decode_persist<8>(g, st);
+            }
+        }
+        if (g.K % 128 == 0) {
+            hipLaunchKernelGGL(k_nv_decode, dim3((unsigned)((g.N + 15) / 16)), dim3(256), 0, st, g.a, g.lda,
+                               g.w_codes, g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K, g.c,
+                               g.c_bf16, g.ldc);
+            return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+        }
         const int nwg = (int)((g.N + 16 * kDecNT - 1) / (16 * kDecNT));
         if (aligned)
-            hipLaunchKernelGGL(k_nv_decode<true>, dim3(nwg), dim3(256), 0, st, g.a, g.lda, g.w_codes,
-                               g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K, g.c, g.c_bf16, g.ldc);
+            hipLaunchKernelGGL(k_nv_decode_generic<true>, dim3(nwg), dim3(64 * kDecWaves), 0, st, g.a,
+                               g.lda, g.w_codes, g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K,
+                               g.c, g.c_bf16, g.ldc);
         else
-            hipLaunchKernelGGL(k_nv_decode<false>, dim3(nwg), dim3(256), 0, st, g.a, g.lda, g.w_codes,
-                               g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K, g.c, g.c_bf16, g.ldc);
+            hipLaunchKernelGGL(k_nv_decode_generic<false>, dim3(nwg), dim3(64 * kDecWaves), 0, st, g.a,
+                               g.lda, g.w_codes, g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K,
+                               g.c, g.c_bf16, g.ldc);
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
     if (g.a_codes)

@@ -85,8 +85,15 @@ def lib():
         L.fp4o_mxfp4_dequantize.argtypes = [p, p, i64, i64, p]
         L.fp4o_mxfp4_to_f64.argtypes = [p, p, i64, i64, p]
         L.fp4o_gemm_f64.argtypes = [p, p, i64, i64, i64, p, p]
+        L.fp4o_num_threads.restype = ctypes.c_int
+        L.fp4o_num_threads.argtypes = []
         _lib = L
     return _lib
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(lib().fp4o_num_threads())
 
 
 def _ptr(a: np.ndarray):

@@ -361,3 +361,11 @@ void fp4o_gemm_f64(const double *a, const double *w, int64_t M, int64_t N, int64
             if (t) t[m * N + n] = abs_acc;
         }
 }
+
+/* threads an OpenMP region of this library uses (for reporting the CPU baseline) */
+#ifdef _OPENMP
+#include <omp.h>
+int fp4o_num_threads(void) { return omp_get_max_threads(); }
+#else
+int fp4o_num_threads(void) { return 1; }
+#endif
