@@ -18,11 +18,249 @@
 
 namespace fp4k {
 
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+
 constexpr int MBM = 256, MBN = 256, MBK = 128;        // MBK in elements
 constexpr int kRowBytes = MBK / 2;                    // 64 code bytes per row per step
 constexpr int kMxGroupM = 8;
+constexpr int kMxStages = 4;                          // LDS ring depth (K steps)
+constexpr int kMxTile = MBM * kRowBytes;              // 16 KiB of codes per operand per step
+constexpr int kMxStage = 2 * kMxTile + (MBM + MBN) * 4;   // codes A, codes W, scale dwords A, W
+constexpr int kMxDmaPerWave = 2 * (kMxTile / 1024 / 4) + 2 * (MBM * 4 / 256 / 4);  // 8 + 2
 
+typedef __attribute__((address_space(3))) void mx_lds_void;
+
+// LDS slot (16-byte units) of code chunk c (0..3) of tile row r: the chunk index is
+// XORed with bits 2..3 of the row so that the 16 lanes of an MFMA fragment read
+// (16 consecutive rows, one chunk) hit 16 different bank groups.
 __device__ __forceinline__ int mswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
+
+__device__ __forceinline__ int mx_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
+
+__device__ __forceinline__ void mx_tile_of(int b, int nb, int tiles_m, int tiles_n, int &tm, int &tn)
+{
+    const int per = (nb + 7) / 8;
+    const int xcd = b % 8, idx = b / 8;
+    const int full = nb % 8;
+    const int logical = (full == 0 || xcd < full) ? xcd * per + idx
+                                                  : full * per + (xcd - full) * (per - 1) + idx;
+    const int group = logical / (kMxGroupM * tiles_n);
+    const int first_m = group * kMxGroupM;
+    const int gsz = min(kMxGroupM, tiles_m - first_m);
+    const int in = logical % (kMxGroupM * tiles_n);
+    tm = first_m + in % gsz;
+    tn = in / gsz;
+}
+
+// DMA one K step (k0) of both operands into stage buffer `st`.  Wave w copies
+// code slots [256 w, 256 w + 256) of each operand (4 instructions of 64 lanes x
+// 16 bytes; a tile is 256 rows x 4 chunks = 1024 slots) and the scale dwords of
+// rows [64 w, 64 w + 64).  Rows past the matrix edge re-read the last row: their
+// products land only in output rows / columns that are never stored.
+template <bool ALIGNED>
+__device__ __forceinline__ void mx_dma(uint8_t *st, const MxGemmArgs &g, int64_t m0, int64_t n0,
+                                       int k0, int wave, int lane)
+{
+    const int K = (int)g.K;
+    const int64_t M = g.M, N = g.N;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int slot = 256 * wave + 64 * i + lane;  // this lane's destination slot
+        const int r = slot >> 2;
+        const int c = (slot & 3) ^ ((r >> 2) & 3);
+        const int k = k0 + 32 * c;  // < K: K % 128 == 0 on this path
+        const int64_t ma = min(m0 + r, M - 1), nw = min(n0 + r, N - 1);
+        __builtin_amdgcn_global_load_lds(g.a_codes + ma * (K / 2) + k / 2,
+                                         (mx_lds_void *)(st + 16 * (256 * wave + 64 * i)), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(g.w_codes + nw * (K / 2) + k / 2,
+                                         (mx_lds_void *)(st + kMxTile + 16 * (256 * wave + 64 * i)), 16, 0, 0);
+    }
+    {
+        const int r = 64 * wave + lane;
+        const int64_t ma = min(m0 + r, M - 1), nw = min(n0 + r, N - 1);
+        // 4 scale bytes (MX blocks k0/32 .. k0/32 + 3) of the row; K % 128 == 0 here
+        __builtin_amdgcn_global_load_lds(g.a_scales + ma * (K / 32) + k0 / 32,
+                                         (mx_lds_void *)(st + 2 * kMxTile + 4 * 64 * wave), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(g.w_scales + nw * (K / 32) + k0 / 32,
+                                         (mx_lds_void *)(st + 2 * kMxTile + 4 * MBM + 4 * 64 * wave), 4, 0, 0);
+    }
+}
+
+__device__ __forceinline__ void mx_waitcnt(int n)
+{
+    switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
+    case 10: __builtin_amdgcn_s_waitcnt((10 & 0xF) | (0x7 << 4) | (0xF << 8)); break;
+    case 20: __builtin_amdgcn_s_waitcnt((20 & 0xF) | ((20 >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
+    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
+    }
+}
+
+// Epilogue of the MX GEMM: each wave's 128 x 128 fp32 block (4 x 4 tiles of
+// 32 x 32, accumulator slot e of tile (i, j) = row 32 i + 8 (e / 4) + 4 (lane / 32)
+// + e % 4, column 32 j + lane % 32) is converted and staged through LDS 64 rows at
+// a time (row stride padded by 16 bytes), then written with 16-byte
+// row-contiguous stores.  `stage` holds 64 x (128 * 4 + 16) bytes for this wave.
+constexpr int kMxStageRows = 64;
+constexpr int kMxStagePitch = 128 * 4 + 16;
+
+__device__ __forceinline__ void mx_store_block(const f32x16 (&acc)[4][4], uint8_t *stage, void *c,
+                                               int c_bf16, int64_t ldc, int64_t r0, int64_t c0,
+                                               int64_t M, int64_t N, int lane)
+{
+    const int es = c_bf16 ? 2 : 4;
+    const int cpr = 128 * es / 16;  // 16-byte chunks per row
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int r = 32 * ii + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+                    const int col = 32 * j + (lane & 31);
+                    const float v = acc[2 * h + ii][j][e];
+                    if (c_bf16)
+                        *reinterpret_cast<uint16_t *>(stage + r * kMxStagePitch + 2 * col) = (uint16_t)f32_to_bf16_rne(v);
+                    else
+                        *reinterpret_cast<float *>(stage + r * kMxStagePitch + 4 * col) = v;
+                }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        for (int q = lane; q < kMxStageRows * cpr; q += 64) {
+            const int r = q / cpr, ch = q % cpr;
+            const int64_t m = r0 + 64 * h + r, n = c0 + ch * (16 / es);
+            if (m >= M) continue;
+            const uint4 v = *reinterpret_cast<const uint4 *>(stage + r * kMxStagePitch + ch * 16);
+            uint8_t *dst = reinterpret_cast<uint8_t *>(c) + (m * ldc + n) * es;
+            if (n + 16 / es <= N && ((reinterpret_cast<uintptr_t>(dst) & 15) == 0)) {
+                *reinterpret_cast<uint4 *>(dst) = v;
+            } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                for (int t = 0; t < 16 / es; ++t) {
+                    if (n + t >= N) break;
+                    if (es == 2) reinterpret_cast<uint16_t *>(dst)[t] = (uint16_t)(w[t >> 1] >> (16 * (t & 1)));
+                    else reinterpret_cast<uint32_t *>(dst)[t] = w[t];
+                }
+            }
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+}
+
+// MXFP4 GEMM for K % 128 == 0: 4-stage LDS ring fed by DMA three steps ahead.
+__global__ __launch_bounds__(256) void k_mx_gemm_ring(MxGemmArgs g)
+{
+    extern __shared__ __align__(16) uint8_t msmem[];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+    const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + MBN - 1) / MBN;
+    int tm, tn;
+    mx_tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * MBM, n0 = (int64_t)tn * MBN;
+    const int nk = K / MBK;
+
+    // per-lane DMA sources at k0 = 0 (a step adds k0 / 2, or k0 / 32 for scales)
+    const uint8_t *a_src[4], *w_src[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int slot = 256 * wave + 64 * i + lane;
+        const int r = slot >> 2;
+        const int c = (slot & 3) ^ ((r >> 2) & 3);
+        a_src[i] = g.a_codes + min(m0 + r, (int64_t)M - 1) * (K / 2) + 16 * c;
+        w_src[i] = g.w_codes + min(n0 + r, (int64_t)N - 1) * (K / 2) + 16 * c;
+    }
+    const uint8_t *as_src = g.a_scales + min(m0 + 64 * wave + lane, (int64_t)M - 1) * (K / 32);
+    const uint8_t *ws_src = g.w_scales + min(n0 + 64 * wave + lane, (int64_t)N - 1) * (K / 32);
+    auto dma = [&](int stage, int k0) {
+        uint8_t *st = msmem + stage * kMxStage;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_global_load_lds(a_src[i] + k0 / 2, (mx_lds_void *)(st + 16 * (256 * wave + 64 * i)), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(w_src[i] + k0 / 2, (mx_lds_void *)(st + kMxTile + 16 * (256 * wave + 64 * i)), 16, 0, 0);
+        }
+        __builtin_amdgcn_global_load_lds(as_src + k0 / 32, (mx_lds_void *)(st + 2 * kMxTile + 256 * wave), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(ws_src + k0 / 32, (mx_lds_void *)(st + 2 * kMxTile + 4 * MBM + 256 * wave), 4, 0, 0);
+    };
+
+    // LDS offsets this lane reads: fragment (i, ks) of A and W, scale dwords
+    const int x = ((lane & 31) >> 2) & 3;   // row bits 2..3 (tile rows start at multiples of 32)
+    const int half = lane >> 5;
+    uint32_t a_off[2][4], w_off[2][4];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int ch = (2 * ks + half) ^ x;
+            a_off[ks][i] = 16 * (4 * (wm * 128 + i * 32 + (lane & 31)) + ch);
+            w_off[ks][i] = kMxTile + 16 * (4 * (wn * 128 + i * 32 + (lane & 31)) + ch);
+        }
+    const uint32_t as_off = 2 * kMxTile + 4 * (wm * 128 + (lane & 31));
+    const uint32_t ws_off = 2 * kMxTile + 4 * MBM + 4 * (wn * 128 + (lane & 31));
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+#pragma unroll
+    for (int p = 0; p < kMxStages - 1; ++p)
+        if (p < nk) dma(p, p * MBK);
+
+    for (int kt = 0; kt < nk; ++kt) {
+        mx_waitcnt(min(kMxStages - 2, nk - 1 - kt) * kMxDmaPerWave);
+        __syncthreads();  // every wave's share of stage kt landed; stage kt-1 fully consumed
+        if (kt + kMxStages - 1 < nk) dma((kt + kMxStages - 1) % kMxStages, (kt + kMxStages - 1) * MBK);
+        const uint8_t *st = msmem + (kt % kMxStages) * kMxStage;
+        uint32_t sa4[4], sw4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sa4[i] = *reinterpret_cast<const uint32_t *>(st + as_off + 128 * i);
+            sw4[i] = *reinterpret_cast<const uint32_t *>(st + ws_off + 128 * i);
+        }
+        i32x4 af[2][4], wf[2][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[0][i] = *reinterpret_cast<const i32x4 *>(st + a_off[0][i]);
+            wf[0][i] = *reinterpret_cast<const i32x4 *>(st + w_off[0][i]);
+        }
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            if (ks == 0) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    af[1][i] = *reinterpret_cast<const i32x4 *>(st + a_off[1][i]);
+                    wf[1][i] = *reinterpret_cast<const i32x4 *>(st + w_off[1][i]);
+                }
+            }
+            const int sh = 8 * (2 * ks + half);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        __builtin_shufflevector(af[ks][i], af[ks][i], 0, 1, 2, 3, -1, -1, -1, -1),
+                        __builtin_shufflevector(wf[ks][j], wf[ks][j], 0, 1, 2, 3, -1, -1, -1, -1),
+                        acc[i][j], 4, 4, 0, (int)((sa4[i] >> sh) & 0xFFu), 0, (int)((sw4[j] >> sh) & 0xFFu));
+        }
+    }
+
+    __syncthreads();  // rings free: reuse them to stage the output
+    mx_store_block(acc, msmem + (size_t)wave * kMxStageRows * kMxStagePitch, g.c, g.c_bf16, g.ldc,
+                   m0 + wm * 128, n0 + wn * 128, M, N, lane);
+}
+
+constexpr size_t kMxRingLds = (size_t)kMxStages * kMxStage;
+static_assert(kMxRingLds >= (size_t)4 * kMxStageRows * kMxStagePitch, "output staging must fit the ring");
+
+// ---- generic path (K % 128 != 0): double-buffered register prefetch ----
 
 struct MxPrefetch {
     uint4 a[4], w[4];
@@ -76,21 +314,6 @@ __device__ __forceinline__ void mx_store(uint8_t *As, uint8_t *Ws, uint32_t *Sa,
     }
     Sa[tid] = p.sa;
     Sw[tid] = p.sw;
-}
-
-__device__ __forceinline__ void mx_tile_of(int b, int nb, int tiles_m, int tiles_n, int &tm, int &tn)
-{
-    const int per = (nb + 7) / 8;
-    const int xcd = b % 8, idx = b / 8;
-    const int full = nb % 8;
-    const int logical = (full == 0 || xcd < full) ? xcd * per + idx
-                                                  : full * per + (xcd - full) * (per - 1) + idx;
-    const int group = logical / (kMxGroupM * tiles_n);
-    const int first_m = group * kMxGroupM;
-    const int gsz = min(kMxGroupM, tiles_m - first_m);
-    const int in = logical % (kMxGroupM * tiles_n);
-    tm = first_m + in % gsz;
-    tn = in / gsz;
 }
 
 template <bool ALIGNED>
@@ -202,7 +425,19 @@ static fp4_status launch_mx(const MxGemmArgs &g, hipStream_t st)
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)
 {
-    return (g.K % MBK) == 0 ? launch_mx<true>(g, st) : launch_mx<false>(g, st);
+    if (g.K % MBK == 0) {
+        static bool attr_set = false;  // benign race: every setter writes the same value
+        if (!attr_set) {
+            if (hipFuncSetAttribute((const void *)k_mx_gemm_ring, hipFuncAttributeMaxDynamicSharedMemorySize,
+                                    (int)kMxRingLds) != hipSuccess)
+                return FP4_ERR_HIP;
+            attr_set = true;
+        }
+        const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
+        hipLaunchKernelGGL(k_mx_gemm_ring, dim3(tiles), dim3(256), kMxRingLds, st, g);
+        return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+    }
+    return launch_mx<false>(g, st);
 }
 
 }  // namespace fp4k
