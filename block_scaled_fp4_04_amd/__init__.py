@@ -54,6 +54,8 @@ def _declare(L):
         "nvfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, p, i32, p, sz, p, p]),
         "nvfp4_dequantize": (i32, [p, p, p, i32, i64, i64, p, i32, i64, p]),
         "gemm_w4a16": (i32, [p, i64, i64, i64, p, p, p, i64, p, i32, i64, p]),
+        "nvfp4_pack_decode": (i32, [p, p, i64, i64, p, p, p]),
+        "gemm_w4a16_decode": (i32, [p, i64, i64, i64, p, p, p, i64, p, i32, i64, p]),
         "gemm_w4a4_workspace": (sz, [i64, i64, i32]),
         "gemm_w4a4_workspace_offsets": (None, [i64, i64, p, p, p]),
         "gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p, sz, p]),
@@ -221,6 +223,48 @@ def gemm_w4a16(a: torch.Tensor, w: PackedNVFP4, dtype=torch.bfloat16,
         out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
     _check(L.gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                         _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+@dataclasses.dataclass
+class DecodeNVFP4:
+    """An NVFP4 weight [rows, cols] in the decode layout (see nvfp4_pack_decode):
+    codes [cols/128, rows, 64], scales [cols/128, rows, 8], tscale [1]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+    rows: int
+    cols: int
+
+
+def nvfp4_pack_decode(w: PackedNVFP4, out: DecodeNVFP4 | None = None) -> DecodeNVFP4:
+    """Rewrite a per-tensor NVFP4 weight into the decode layout (segment-major)."""
+    L = lib()
+    if w.per_row:
+        raise ValueError("the decode layout holds weights with a per-tensor scale")
+    N, K = w.rows, w.cols
+    if out is None:
+        dev = w.codes.device
+        out = DecodeNVFP4(torch.empty(K // 128, N, 64, dtype=torch.uint8, device=dev),
+                          torch.empty(K // 128, N, 8, dtype=torch.uint8, device=dev),
+                          w.tscale, N, K)
+    _check(L.nvfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
+                               _stream()))
+    return out
+
+
+def gemm_w4a16_decode(a: torch.Tensor, w: DecodeNVFP4, dtype=torch.bfloat16,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode GEMV C = A . W^T for bf16 A [M <= 16, K] and W in the decode layout."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("gemm_w4a16_decode takes bfloat16 activations")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    _check(L.gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                               _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
 
 

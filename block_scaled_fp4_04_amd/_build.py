@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIBDIR = os.path.join(PKG, "_lib")
 LIB = os.path.join(LIBDIR, "libfp4blk.so")
-SOURCES = ["abi.hip", "quant.hip", "gemm_nv.hip", "gemm_mx.hip"]
+SOURCES = ["abi.hip", "quant.hip", "gemm_nv.hip", "gemv_nv.hip", "gemm_mx.hip"]
 HEADERS = ["device_common.h", "internal.h"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -170,6 +170,41 @@ fp4_status gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const ui
     return launch_nvfp4_gemm(g, stream);
 }
 
+fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                             uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream)
+{
+    if (N <= 0 || K <= 0 || K % 128 != 0 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(codes, scales));
+    FP4_TRY(check_packed(codes_p, scales_p));
+    FP4_TRY(check_device());
+    return launch_nvfp4_pack_decode(codes, scales, N, K, codes_p, scales_p, stream);
+}
+
+fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
+                             const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
+                             fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    if (M > 16 || K > 8192) return FP4_ERR_SHAPE;
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    FP4_TRY(check_packed(w_codes_p, w_scales_p));
+    if (!w_tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_device());
+    GemvArgs g{};
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    g.w_codes = w_codes_p;
+    g.w_scales = w_scales_p;
+    g.w_tscale = w_tscale;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_nvfp4_gemv_decode(g, stream);
+}
+
 void gemm_w4a4_workspace_offsets(int64_t M, int64_t K, size_t *codes_off, size_t *scales_off,
                                  size_t *tscale_off)
 {

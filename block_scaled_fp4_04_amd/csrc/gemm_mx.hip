@@ -9,10 +9,10 @@
 // are exact; the matrix core accumulates in fp32.
 //
 // Tiling: 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (4 x 4
-// MFMA tiles of 32 x 32), BK = 128 K-elements (64 code bytes per row).  Packed
-// codes are staged in LDS unchanged (64-byte rows, 16-byte chunk c of row r at
-// chunk c ^ ((r >> 2) & 3)); each row's 4 scale bytes of the step are one LDS
-// dword.  Global loads of step k+1 are in flight during the MFMAs of step k.
+// MFMA tiles of 32 x 32).  Packed codes and scale bytes are staged in LDS
+// unchanged.  K % 256 == 0 takes the staged kernel (two 256-element LDS stages
+// filled by global-to-LDS DMA); other K take a register-prefetch kernel with
+// 128-element steps that masks the K tail.
 #include "device_common.h"
 #include "internal.h"
 
@@ -20,13 +20,9 @@ namespace fp4k {
 
 typedef int i32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int MBM = 256, MBN = 256, MBK = 128;        // MBK in elements
+constexpr int MBM = 256, MBN = 256, MBK = 128;        // MBK: K elements per step of the prefetch kernel
 constexpr int kRowBytes = MBK / 2;                    // 64 code bytes per row per step
 constexpr int kMxGroupM = 8;
-constexpr int kMxStages = 4;                          // LDS ring depth (K steps)
-constexpr int kMxTile = MBM * kRowBytes;              // 16 KiB of codes per operand per step
-constexpr int kMxStage = 2 * kMxTile + (MBM + MBN) * 4;   // codes A, codes W, scale dwords A, W
-constexpr int kMxDmaPerWave = 2 * (kMxTile / 1024 / 4) + 2 * (MBM * 4 / 256 / 4);  // 8 + 2
 
 typedef __attribute__((address_space(3))) void mx_lds_void;
 
@@ -35,7 +31,6 @@ typedef __attribute__((address_space(3))) void mx_lds_void;
 // (16 consecutive rows, one chunk) hit 16 different bank groups.
 __device__ __forceinline__ int mswz(int row, int chunk) { return row * kRowBytes + ((chunk ^ ((row >> 2) & 3)) << 4); }
 
-__device__ __forceinline__ int mx_slot(int r, int c) { return 4 * r + (c ^ ((r >> 2) & 3)); }
 
 __device__ __forceinline__ void mx_tile_of(int b, int nb, int tiles_m, int tiles_n, int &tm, int &tn)
 {
@@ -50,50 +45,6 @@ __device__ __forceinline__ void mx_tile_of(int b, int nb, int tiles_m, int tiles
     const int in = logical % (kMxGroupM * tiles_n);
     tm = first_m + in % gsz;
     tn = in / gsz;
-}
-
-// DMA one K step (k0) of both operands into stage buffer `st`.  Wave w copies
-// code slots [256 w, 256 w + 256) of each operand (4 instructions of 64 lanes x
-// 16 bytes; a tile is 256 rows x 4 chunks = 1024 slots) and the scale dwords of
-// rows [64 w, 64 w + 64).  Rows past the matrix edge re-read the last row: their
-// products land only in output rows / columns that are never stored.
-template <bool ALIGNED>
-__device__ __forceinline__ void mx_dma(uint8_t *st, const MxGemmArgs &g, int64_t m0, int64_t n0,
-                                       int k0, int wave, int lane)
-{
-    const int K = (int)g.K;
-    const int64_t M = g.M, N = g.N;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int slot = 256 * wave + 64 * i + lane;  // this lane's destination slot
-        const int r = slot >> 2;
-        const int c = (slot & 3) ^ ((r >> 2) & 3);
-        const int k = k0 + 32 * c;  // < K: K % 128 == 0 on this path
-        const int64_t ma = min(m0 + r, M - 1), nw = min(n0 + r, N - 1);
-        __builtin_amdgcn_global_load_lds(g.a_codes + ma * (K / 2) + k / 2,
-                                         (mx_lds_void *)(st + 16 * (256 * wave + 64 * i)), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(g.w_codes + nw * (K / 2) + k / 2,
-                                         (mx_lds_void *)(st + kMxTile + 16 * (256 * wave + 64 * i)), 16, 0, 0);
-    }
-    {
-        const int r = 64 * wave + lane;
-        const int64_t ma = min(m0 + r, M - 1), nw = min(n0 + r, N - 1);
-        // 4 scale bytes (MX blocks k0/32 .. k0/32 + 3) of the row; K % 128 == 0 here
-        __builtin_amdgcn_global_load_lds(g.a_scales + ma * (K / 32) + k0 / 32,
-                                         (mx_lds_void *)(st + 2 * kMxTile + 4 * 64 * wave), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(g.w_scales + nw * (K / 32) + k0 / 32,
-                                         (mx_lds_void *)(st + 2 * kMxTile + 4 * MBM + 4 * 64 * wave), 4, 0, 0);
-    }
-}
-
-__device__ __forceinline__ void mx_waitcnt(int n)
-{
-    switch (n) {
-    case 0: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
-    case 10: __builtin_amdgcn_s_waitcnt((10 & 0xF) | (0x7 << 4) | (0xF << 8)); break;
-    case 20: __builtin_amdgcn_s_waitcnt((20 & 0xF) | ((20 >> 4) << 14) | (0x7 << 4) | (0xF << 8)); break;
-    default: __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8)); break;
-    }
 }
 
 // Epilogue of the MX GEMM: each wave's 128 x 128 fp32 block (4 x 4 tiles of
@@ -152,10 +103,246 @@ __device__ __forceinline__ void mx_store_block(const f32x16 (&acc)[4][4], uint8_
     }
 }
 
-// MXFP4 GEMM for K % 128 == 0: 4-stage LDS ring fed by DMA three steps ahead.
-__global__ __launch_bounds__(256) void k_mx_gemm_ring(MxGemmArgs g)
+// ---- main path (K % 256 == 0): two LDS stages of 256 K-elements fed by DMA ----
+//
+// Each stage holds, for both operands, 256 tile rows x 128 code bytes (16-byte
+// chunk c of row r at slot 8 r + (c ^ ((r >> 1) & 7)), so the 16 lanes of an MFMA
+// fragment read hit 16 different bank groups) and 256 rows x 8 E8M0 bytes.  The
+// two stages are separate LDS objects: the compiler can then tell a DMA into one
+// from a read of the other and does not wait for the DMA before the read.  Stage
+// kt + 1 is copied while stage kt is multiplied; the barrier that publishes it
+// sits in the middle of the last 64-element step of stage kt, and the fragments of
+// the next step are read while the MFMAs of the current one run.
+constexpr int kSK = 256;                          // K elements per stage
+constexpr int kSRow = kSK / 2;                    // 128 code bytes per tile row
+constexpr int kSTile = MBM * kSRow;               // 32 KiB of codes per operand
+constexpr int kSScl = MBM * (kSK / 32);           // 2 KiB of scale bytes per operand
+constexpr int kSStage = 2 * kSTile + 2 * kSScl;   // 69,632 bytes
+static_assert(2 * kMxStageRows * kMxStagePitch <= kSStage, "two waves' output staging must fit a stage");
+
+// Per-lane byte offsets (from the matrix base at k0 = 0) of the 20 DMA transfers a
+// wave issues per stage: 8 x 16 bytes of A codes, 8 of W codes, 2 x 4 bytes of
+// scales per operand.  Code slot q = 512 wave + 64 i + lane is row q / 8, chunk
+// (q % 8) ^ ((row >> 1) & 7); scale dword q = 128 wave + 64 i + lane is row q / 2,
+// bytes 4 (q % 2) .. +3.  Rows past the matrix edge re-read the last row: their
+// products land only in outputs that are never stored.  The copies are buffer
+// loads into LDS: a 32-bit per-lane offset, the stage's K offset as the scalar
+// offset, and a descriptor per matrix whose size bound makes the hardware return
+// zeros for any address past the matrix.  A stage that does not exist is
+// "copied" through descriptors of size 0: the hardware writes zeros and reads
+// nothing, so every stage runs the same code.
+struct Mx2Dma {
+    __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
+    uint32_t a[8], w[8], as[2], ws[2];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx2_rsrc(const uint8_t *base, int64_t bytes)
 {
-    extern __shared__ __align__(16) uint8_t msmem[];
+    // dword 3: data format 32 bits (a raw byte-addressed buffer; stride 0)
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t *>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void mx2_dma(uint8_t *st, const Mx2Dma &d, int k0, int wave)
+{
+    // d's descriptors are chosen by the caller (matrix or empty)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + 16 * (512 * wave + 64 * i)), 16,
+                                                 (int)d.a[i], k0 / 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kSTile + 16 * (512 * wave + 64 * i)), 16,
+                                                 (int)d.w[i], k0 / 2, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (mx_lds_void *)(st + 2 * kSTile + 4 * (128 * wave + 64 * i)), 4,
+                                                 (int)d.as[i], k0 / 32, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsw,
+                                                 (mx_lds_void *)(st + 2 * kSTile + kSScl + 4 * (128 * wave + 64 * i)), 4,
+                                                 (int)d.ws[i], k0 / 32, 0, 0);
+    }
+}
+
+// LDS offsets one lane reads within a stage: fragment (i, ks) of A is at
+// la[ks] + 4096 i, of W at lw[ks] + 4096 j; the 8 scale bytes of A row i at
+// lsa + 256 i, of W row j at lsw + 256 j.
+struct Mx2Lds {
+    uint32_t la[4], lw[4], lsa, lsw, sel;
+};
+
+struct Mx2Frag {
+    i32x4 a[4], w[4];
+};
+
+__device__ __forceinline__ void mx2_frags(const uint8_t *st, uint32_t la, uint32_t lw, Mx2Frag &f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f.a[i] = *reinterpret_cast<const i32x4 *>(st + la + 4096 * i);
+        f.w[i] = *reinterpret_cast<const i32x4 *>(st + lw + 4096 * i);
+    }
+}
+
+// The lane's MFMA scale operand for step ks is byte ks of one dword: lanes 0..31
+// supply blocks 0, 2, 4, 6 of the row's 8 blocks in the stage, lanes 32..63
+// blocks 1, 3, 5, 7 (the K-half of the 32 x 32 x 64 instruction each half covers).
+__device__ __forceinline__ void mx2_scales(const uint8_t *st, const Mx2Lds &o, uint32_t (&sa)[4], uint32_t (&sw)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint2 va = *reinterpret_cast<const uint2 *>(st + o.lsa + 256 * i);
+        const uint2 vw = *reinterpret_cast<const uint2 *>(st + o.lsw + 256 * i);
+        sa[i] = __builtin_amdgcn_perm(va.y, va.x, o.sel);
+        sw[i] = __builtin_amdgcn_perm(vw.y, vw.x, o.sel);
+    }
+}
+
+__device__ __forceinline__ i32x8 mx2_wide(i32x4 v) { return __builtin_shufflevector(v, v, 0, 1, 2, 3, -1, -1, -1, -1); }
+
+// acc[i][j] accumulates the transposed 32 x 32 block W_j A_i^T: lane l then holds
+// output row 32 i + l % 32 and the 4 consecutive columns 32 j + 8 g + 4 (l / 32)
+// + 0..3 in slots 4 g .. 4 g + 3, which the epilogue writes as one 8- or 16-byte
+// piece.
+template <int KS, int I0, int I1>
+__device__ __forceinline__ void mx2_mfma(f32x16 (&acc)[4][4], const Mx2Frag &f, const uint32_t (&sa)[4],
+                                         const uint32_t (&sw)[4])
+{
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx2_wide(f.w[j]), mx2_wide(f.a[i]), acc[i][j],
+                                                                        4, 4, KS, (int)sw[j], KS, (int)sa[i]);
+}
+
+// Interleave the LDS reads of the next step with the MFMAs of this one: pairs of
+// MFMAs alternate with single reads, so neither the reads' latency nor their
+// registers pile up.
+template <int N_READ, int N_MFMA>
+__device__ __forceinline__ void mx2_interleave()
+{
+#pragma unroll
+    for (int t = 0; t < N_READ; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, N_MFMA / N_READ, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage: multiply the 256 K-elements in `cur` while the next stage lands in
+// `oth`; then read step 0 of the next stage into f0 / sa / sw and start copying
+// the stage after next into `cur` (`dn` holds the matrix descriptors, or empty
+// ones when that stage does not exist).  Where no next stage exists the reads of
+// `oth` fetch stale bytes that are never used.  The stage is one basic block
+// whose instruction order the scheduling groups fix.
+__device__ __forceinline__ void mx2_stage(uint8_t *cur, uint8_t *oth, int k_next2, const Mx2Dma &dn,
+                                          const Mx2Lds &o, int wave, f32x16 (&acc)[4][4], Mx2Frag &f0,
+                                          Mx2Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[4])
+{
+    mx2_frags(cur, o.la[1], o.lw[1], f1);
+    mx2_mfma<0, 0, 4>(acc, f0, sa, sw);
+    mx2_interleave<8, 16>();
+    mx2_frags(cur, o.la[2], o.lw[2], f0);
+    mx2_mfma<1, 0, 4>(acc, f1, sa, sw);
+    mx2_interleave<8, 16>();
+    mx2_frags(cur, o.la[3], o.lw[3], f1);
+    mx2_mfma<2, 0, 4>(acc, f0, sa, sw);
+    mx2_interleave<8, 16>();
+    mx2_mfma<3, 0, 2>(acc, f1, sa, sw);
+    __builtin_amdgcn_sched_barrier(0);
+    // this wave's copy into `oth` has landed and its reads of `cur` returned; after
+    // the barrier the same holds for every wave
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    uint32_t na[4], nw[4];
+    mx2_scales(oth, o, na, nw);
+    mx2_frags(oth, o.la[0], o.lw[0], f0);
+    mx2_dma(cur, dn, k_next2, wave);
+    mx2_mfma<3, 2, 4>(acc, f1, sa, sw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sa[i] = na[i];
+        sw[i] = nw[i];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Epilogue of the staged kernel.  The output tile passes through LDS so that
+// every store instruction writes whole 512-byte (bf16) or 1 KiB (fp32) row
+// runs.  Rows are padded by 16 bytes.  bf16: waves with wm = 0 stage tile rows
+// 0..127 in s0 and waves with wm = 1 rows 128..255 in s1, in one round; fp32: the
+// same split, 64 rows per wave pair per round, two rounds.
+template <typename T>
+__device__ __forceinline__ void mx2_put(uint8_t *row, int col, const f32x16 &a, int g)
+{
+    if constexpr (sizeof(T) == 2) {
+        typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+        const bf16x4 v = {(__bf16)a[4 * g], (__bf16)a[4 * g + 1], (__bf16)a[4 * g + 2], (__bf16)a[4 * g + 3]};
+        *reinterpret_cast<bf16x4 *>(row + 2 * col) = v;
+    } else {
+        *reinterpret_cast<f32x4 *>(row + 4 * col) = f32x4{a[4 * g], a[4 * g + 1], a[4 * g + 2], a[4 * g + 3]};
+    }
+}
+
+// Store `rows` staged rows of width 256 elements (pitch bytes apart in `st`) to
+// output rows m_first.. and columns n0..; threads take 16-byte chunks in order.
+template <typename T>
+__device__ __forceinline__ void mx2_flush(const uint8_t *st, int pitch, int rows, const MxGemmArgs &g, int m_first,
+                                          int n0, int tid)
+{
+    constexpr int kPer = 16 / (int)sizeof(T);              // elements per chunk
+    constexpr int kChunks = 256 / kPer;                    // chunks per row
+    const int M = (int)g.M, N = (int)g.N;
+    for (int q = tid; q < rows * kChunks; q += 256) {
+        const int r = q / kChunks, ch = q % kChunks;
+        const int m = m_first + r, n = n0 + ch * kPer;
+        if (m >= M || n >= N) continue;
+        const uint4 v = *reinterpret_cast<const uint4 *>(st + r * pitch + 16 * ch);
+        T *dst = reinterpret_cast<T *>(g.c) + (int64_t)m * g.ldc + n;
+        if (n + kPer <= N) {
+            *reinterpret_cast<uint4 *>(dst) = v;
+        } else {
+            T e[kPer];
+            __builtin_memcpy(e, &v, 16);
+#pragma unroll
+            for (int t = 0; t < kPer; ++t)
+                if (n + t < N) dst[t] = e[t];
+        }
+    }
+}
+
+template <typename T>
+__device__ __forceinline__ void mx2_epilogue(const f32x16 (&acc)[4][4], uint8_t *s0, uint8_t *s1, const MxGemmArgs &g,
+                                             int m0, int n0, int wm, int wn, int lane, int tid)
+{
+    constexpr int pitch = 256 * (int)sizeof(T) + 16;
+    constexpr int rounds = sizeof(T) == 2 ? 1 : 2;
+    constexpr int rows = 128 / rounds;                     // staged rows per wave pair per round
+    static_assert(rows * pitch <= kSStage, "a staged half tile must fit one stage buffer");
+    uint8_t *mine = wm ? s1 : s0;
+#pragma unroll
+    for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+        for (int i = rd * (4 / rounds); i < (rd + 1) * (4 / rounds); ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    mx2_put<T>(mine + (i * 32 - rd * rows + (lane & 31)) * pitch,
+                               wn * 128 + j * 32 + 8 * gq + 4 * (lane >> 5), acc[i][j], gq);
+                __builtin_amdgcn_sched_barrier(0);  // convert block by block: few live VGPRs
+            }
+        __syncthreads();
+        mx2_flush<T>(s0, pitch, rows, g, m0 + rd * rows, n0, tid);
+        mx2_flush<T>(s1, pitch, rows, g, m0 + 128 + rd * rows, n0, tid);
+        if (rd + 1 < rounds) __syncthreads();
+    }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void k_mx_gemm_2s(MxGemmArgs g)
+{
+    __shared__ __align__(16) uint8_t s0[kSStage];
+    __shared__ __align__(16) uint8_t s1[kSStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1;
@@ -163,46 +350,43 @@ __global__ __launch_bounds__(256) void k_mx_gemm_ring(MxGemmArgs g)
     const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + MBN - 1) / MBN;
     int tm, tn;
     mx_tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int64_t m0 = (int64_t)tm * MBM, n0 = (int64_t)tn * MBN;
-    const int nk = K / MBK;
+    const int m0 = tm * MBM, n0 = tn * MBN;
+    const int nk = K / kSK;
 
-    // per-lane DMA sources at k0 = 0 (a step adds k0 / 2, or k0 / 32 for scales)
-    const uint8_t *a_src[4], *w_src[4];
+    Mx2Dma d, dz;
+    d.ra = mx2_rsrc(g.a_codes, g.M * (g.K / 2));
+    d.rw = mx2_rsrc(g.w_codes, g.N * (g.K / 2));
+    d.rsa = mx2_rsrc(g.a_scales, g.M * (g.K / 32));
+    d.rsw = mx2_rsrc(g.w_scales, g.N * (g.K / 32));
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int slot = 256 * wave + 64 * i + lane;
-        const int r = slot >> 2;
-        const int c = (slot & 3) ^ ((r >> 2) & 3);
-        a_src[i] = g.a_codes + min(m0 + r, (int64_t)M - 1) * (K / 2) + 16 * c;
-        w_src[i] = g.w_codes + min(n0 + r, (int64_t)N - 1) * (K / 2) + 16 * c;
+    for (int i = 0; i < 8; ++i) {
+        const int q = 512 * wave + 64 * i + lane;
+        const int r = q >> 3;
+        const int c = (q & 7) ^ ((r >> 1) & 7);
+        d.a[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)(K / 2) + 16 * c;
+        d.w[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)(K / 2) + 16 * c;
     }
-    const uint8_t *as_src = g.a_scales + min(m0 + 64 * wave + lane, (int64_t)M - 1) * (K / 32);
-    const uint8_t *ws_src = g.w_scales + min(n0 + 64 * wave + lane, (int64_t)N - 1) * (K / 32);
-    auto dma = [&](int stage, int k0) {
-        uint8_t *st = msmem + stage * kMxStage;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_global_load_lds(a_src[i] + k0 / 2, (mx_lds_void *)(st + 16 * (256 * wave + 64 * i)), 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(w_src[i] + k0 / 2, (mx_lds_void *)(st + kMxTile + 16 * (256 * wave + 64 * i)), 16, 0, 0);
-        }
-        __builtin_amdgcn_global_load_lds(as_src + k0 / 32, (mx_lds_void *)(st + 2 * kMxTile + 256 * wave), 4, 0, 0);
-        __builtin_amdgcn_global_load_lds(ws_src + k0 / 32, (mx_lds_void *)(st + 2 * kMxTile + 4 * MBM + 256 * wave), 4, 0, 0);
-    };
-
-    // LDS offsets this lane reads: fragment (i, ks) of A and W, scale dwords
-    const int x = ((lane & 31) >> 2) & 3;   // row bits 2..3 (tile rows start at multiples of 32)
-    const int half = lane >> 5;
-    uint32_t a_off[2][4], w_off[2][4];
+    for (int i = 0; i < 2; ++i) {
+        const int q = 128 * wave + 64 * i + lane;
+        d.as[i] = (uint32_t)min(m0 + (q >> 1), M - 1) * (uint32_t)(K / 32) + 4 * (q & 1);
+        d.ws[i] = (uint32_t)min(n0 + (q >> 1), N - 1) * (uint32_t)(K / 32) + 4 * (q & 1);
+    }
+    Mx2Lds o;
+    const int half = lane >> 5, x = ((lane & 31) >> 1) & 7;
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int ch = (2 * ks + half) ^ x;
-            a_off[ks][i] = 16 * (4 * (wm * 128 + i * 32 + (lane & 31)) + ch);
-            w_off[ks][i] = kMxTile + 16 * (4 * (wn * 128 + i * 32 + (lane & 31)) + ch);
-        }
-    const uint32_t as_off = 2 * kMxTile + 4 * (wm * 128 + (lane & 31));
-    const uint32_t ws_off = 2 * kMxTile + 4 * MBM + 4 * (wn * 128 + (lane & 31));
+    for (int ks = 0; ks < 4; ++ks) {
+        o.la[ks] = 128 * (wm * 128 + (lane & 31)) + 16 * ((2 * ks + half) ^ x);
+        o.lw[ks] = kSTile + 128 * (wn * 128 + (lane & 31)) + 16 * ((2 * ks + half) ^ x);
+    }
+    o.lsa = 2 * kSTile + 8 * (wm * 128 + (lane & 31));
+    o.lsw = 2 * kSTile + kSScl + 8 * (wn * 128 + (lane & 31));
+    o.sel = half ? 0x07050301u : 0x06040200u;
+    dz = d;
+    dz.ra = mx2_rsrc(g.a_codes, 0);
+    dz.rw = mx2_rsrc(g.w_codes, 0);
+    dz.rsa = mx2_rsrc(g.a_scales, 0);
+    dz.rsw = mx2_rsrc(g.w_scales, 0);
 
     f32x16 acc[4][4];
 #pragma unroll
@@ -210,55 +394,31 @@ __global__ __launch_bounds__(256) void k_mx_gemm_ring(MxGemmArgs g)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
-#pragma unroll
-    for (int p = 0; p < kMxStages - 1; ++p)
-        if (p < nk) dma(p, p * MBK);
-
-    for (int kt = 0; kt < nk; ++kt) {
-        mx_waitcnt(min(kMxStages - 2, nk - 1 - kt) * kMxDmaPerWave);
-        __syncthreads();  // every wave's share of stage kt landed; stage kt-1 fully consumed
-        if (kt + kMxStages - 1 < nk) dma((kt + kMxStages - 1) % kMxStages, (kt + kMxStages - 1) * MBK);
-        const uint8_t *st = msmem + (kt % kMxStages) * kMxStage;
-        uint32_t sa4[4], sw4[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            sa4[i] = *reinterpret_cast<const uint32_t *>(st + as_off + 128 * i);
-            sw4[i] = *reinterpret_cast<const uint32_t *>(st + ws_off + 128 * i);
-        }
-        i32x4 af[2][4], wf[2][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            af[0][i] = *reinterpret_cast<const i32x4 *>(st + a_off[0][i]);
-            wf[0][i] = *reinterpret_cast<const i32x4 *>(st + w_off[0][i]);
-        }
-#pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            if (ks == 0) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    af[1][i] = *reinterpret_cast<const i32x4 *>(st + a_off[1][i]);
-                    wf[1][i] = *reinterpret_cast<const i32x4 *>(st + w_off[1][i]);
-                }
-            }
-            const int sh = 8 * (2 * ks + half);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        __builtin_shufflevector(af[ks][i], af[ks][i], 0, 1, 2, 3, -1, -1, -1, -1),
-                        __builtin_shufflevector(wf[ks][j], wf[ks][j], 0, 1, 2, 3, -1, -1, -1, -1),
-                        acc[i][j], 4, 4, 0, (int)((sa4[i] >> sh) & 0xFFu), 0, (int)((sw4[j] >> sh) & 0xFFu));
-        }
+    // Stages t = 0 .. T-1 with T = nk rounded up to even: with nk odd, stage 0 is
+    // an all-zero stage (its products add +0 to accumulators that start at +0)
+    // and stage t holds K-elements [256 (t - 1), 256 t).
+    const int ph = nk & 1, T = nk + ph;
+    auto stage_k = [&](int t) { return max(t - ph, 0) * kSK; };
+    auto stage_d = [&](int t) -> const Mx2Dma & { return (t >= ph && t < T) ? d : dz; };
+    mx2_dma(s0, stage_d(0), stage_k(0), wave);
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    mx2_dma(s1, stage_d(1), stage_k(1), wave);
+    Mx2Frag f0, f1;
+    uint32_t sa[4], sw[4];
+    mx2_scales(s0, o, sa, sw);
+    mx2_frags(s0, o.la[0], o.lw[0], f0);
+    for (int t = 0; t < T; t += 2) {
+        mx2_stage(s0, s1, stage_k(t + 2), stage_d(t + 2), o, wave, acc, f0, f1, sa, sw);
+        mx2_stage(s1, s0, stage_k(t + 3), stage_d(t + 3), o, wave, acc, f0, f1, sa, sw);
     }
 
-    __syncthreads();  // rings free: reuse them to stage the output
-    mx_store_block(acc, msmem + (size_t)wave * kMxStageRows * kMxStagePitch, g.c, g.c_bf16, g.ldc,
-                   m0 + wm * 128, n0 + wn * 128, M, N, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // the empty copies issued by the last stages have landed
+    __syncthreads();  // both stages free: stage the output in them
+    // the lane index is recomputed rather than kept live through the main loop
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    mx2_epilogue<OutT>(acc, s0, s1, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
 }
-
-constexpr size_t kMxRingLds = (size_t)kMxStages * kMxStage;
-static_assert(kMxRingLds >= (size_t)4 * kMxStageRows * kMxStagePitch, "output staging must fit the ring");
 
 // ---- generic path (K % 128 != 0): double-buffered register prefetch ----
 
@@ -425,16 +585,13 @@ static fp4_status launch_mx(const MxGemmArgs &g, hipStream_t st)
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)
 {
-    if (g.K % MBK == 0) {
-        static bool attr_set = false;  // benign race: every setter writes the same value
-        if (!attr_set) {
-            if (hipFuncSetAttribute((const void *)k_mx_gemm_ring, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                    (int)kMxRingLds) != hipSuccess)
-                return FP4_ERR_HIP;
-            attr_set = true;
-        }
+    // the staged kernel addresses a matrix with 32-bit byte offsets
+    if (g.K % kSK == 0 && g.M * (g.K / 2) < (int64_t(1) << 32) && g.N * (g.K / 2) < (int64_t(1) << 32)) {
         const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
-        hipLaunchKernelGGL(k_mx_gemm_ring, dim3(tiles), dim3(256), kMxRingLds, st, g);
+        if (g.c_bf16)
+            hipLaunchKernelGGL(k_mx_gemm_2s<__bf16>, dim3(tiles), dim3(256), 0, st, g);
+        else
+            hipLaunchKernelGGL(k_mx_gemm_2s<float>, dim3(tiles), dim3(256), 0, st, g);
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
     return launch_mx<false>(g, st);

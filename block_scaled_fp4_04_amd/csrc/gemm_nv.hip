@@ -18,35 +18,6 @@
 
 namespace fp4k {
 
-// ------------------------------------------------------------ dequant -----
-
-// 8 E2M1 codes (nibble i = element i) times block scale bs -> 8 bf16 (4 dwords,
-// element 2i in the low half of dword i).  The hardware FP4 -> fp32 conversion
-// applies only the exponent of its scale operand, so it runs with scale 1 and
-// the E4M3 value is applied by an fp32 multiply.  Exact: each product has at
-// most 6 significant bits, so its fp32 bits truncate to bf16 without rounding.
-__device__ __forceinline__ uint4 dq8_bf16(uint32_t codes, float bs)
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 0);
-    const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 1);
-    const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 2);
-    const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(codes, 1.0f, 3);
-    uint4 r;
-    r.x = __builtin_amdgcn_perm(__float_as_uint(p0[1] * bs), __float_as_uint(p0[0] * bs), 0x07060302u);
-    r.y = __builtin_amdgcn_perm(__float_as_uint(p1[1] * bs), __float_as_uint(p1[0] * bs), 0x07060302u);
-    r.z = __builtin_amdgcn_perm(__float_as_uint(p2[1] * bs), __float_as_uint(p2[0] * bs), 0x07060302u);
-    r.w = __builtin_amdgcn_perm(__float_as_uint(p3[1] * bs), __float_as_uint(p3[0] * bs), 0x07060302u);
-    return r;
-}
-
-__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
-{
-    bf16x8 r;
-    __builtin_memcpy(&r, &v, 16);
-    return r;
-}
-
 // ------------------------------------------------------ byte-safe loads ---
 
 template <bool ALIGNED>
@@ -247,13 +218,6 @@ __device__ __forceinline__ void dec_stage(uint8_t *lds, const DecPass &p, int la
     }
 }
 
-// E4M3FN byte (sign clear) -> fp32: the byte placed at fp32 bit 20 reads as
-// 2^(e-127) (1 + m/8) (or the denormal m * 2^-129 when e == 0); times 2^120 that
-// is exactly the E4M3 value (2^(e-7) (1 + m/8), or m * 2^-9).
-__device__ __forceinline__ float e4m3_fast(uint32_t byte_at_bit20)
-{
-    return __uint_as_float(byte_at_bit20) * 0x1p120f;
-}
 
 // One pass of the decode kernel over `steps` (compile-time) steps.
 template <int STEPS>

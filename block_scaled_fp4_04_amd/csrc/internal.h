@@ -53,6 +53,24 @@ struct NvGemmArgs {
 
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st);
 
+// W4A16 decode GEMV over weights in the decode layout (gemv_nv.hip)
+struct GemvArgs {
+    const uint16_t *a;        // bf16 [M][lda]
+    int64_t lda;
+    const uint8_t *w_codes;   // [K/128][N][64]
+    const uint8_t *w_scales;  // [K/128][N][8]
+    const float *w_tscale;    // [1]
+    int M, N, K;
+    int rows_per_wg;          // set by the launcher
+    void *c;
+    int c_bf16;
+    int64_t ldc;
+};
+
+fp4_status launch_nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                                    uint8_t *codes_p, uint8_t *scales_p, hipStream_t st);
+fp4_status launch_nvfp4_gemv_decode(GemvArgs g, hipStream_t st);
+
 struct MxGemmArgs {
     const uint8_t *a_codes;  // [M][K/2]
     const uint8_t *a_scales; // [M][K/32]

@@ -129,6 +129,27 @@ fp4_status gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const ui
                       const uint8_t *w_scales, const float *w_tscale, int64_t N, void *c,
                       fp4_dtype ct, int64_t ldc, hipStream_t stream);
 
+/* Decode layout of an NVFP4 weight (for gemm_w4a16_decode).  K is cut into
+ * 128-element segments; the layout stores them segment-major,
+ *   codes_p  uint8 [K/128][N][64]: byte (s*N + n)*64 + b = codes[n][64*s + b]
+ *   scales_p uint8 [K/128][N][8]:  byte (s*N + n)*8 + b  = scales[n][8*s + b]
+ * so the 16 rows of a matrix-core tile at one segment are 1 KiB of
+ * consecutive bytes.  Same bytes and byte count as the row-major form (4.5 bits
+ * a value); only the order differs.  The tensor scale is unchanged.
+ * nvfp4_pack_decode rewrites row-major codes [N][K/2] / scales [N][K/16] into
+ * it (K % 128 == 0; outputs of N*K/2 and N*K/16 bytes, not overlapping the
+ * inputs). */
+fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                             uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream);
+
+/* W4A16 decode GEMV (aixq.cc article, "Core difference: W4A4 vs W4A16") on a
+ * weight in the decode layout: C = A . W^T for 1 <= M <= 16, K % 128 == 0,
+ * K <= 8192.  Same arithmetic and tolerance as gemm_w4a16 (each weight widened
+ * exactly to E2M1 * E4M3 in bfloat16, fp32 accumulation, times w_tscale). */
+fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
+                             const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
+                             fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
 /* Workspace bytes gemm_w4a4 needs: A's codes | scales | tscale, each starting
  * at a 256-byte boundary, in that order (offsets by gemm_w4a4_workspace_offsets). */
 size_t gemm_w4a4_workspace(int64_t M, int64_t K, fp4_scale_mode a_mode);

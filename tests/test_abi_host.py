@@ -144,6 +144,40 @@ def test_gemm_validation(L):
         assert g4() == NO_DEVICE
 
 
+def test_decode_layout_validation(L):
+    import torch
+
+    def pk(**kw):
+        a = dict(codes=FAKE, scales=FAKE, N=32, K=256, cp=FAKE, sp=FAKE, stream=None)
+        a.update(kw)
+        return L.nvfp4_pack_decode(*a.values())
+
+    assert pk(codes=None) == NULL
+    assert pk(sp=None) == NULL
+    assert pk(K=192) == SHAPE          # not whole 128-element segments
+    assert pk(N=0) == SHAPE
+    assert pk(cp=FAKE + 8) == LAYOUT
+    if not torch.cuda.is_available():
+        assert pk() == NO_DEVICE
+
+    def gd(**kw):
+        a = dict(a=FAKE, M=4, K=256, lda=256, wc=FAKE, ws=FAKE, wt=FAKE, N=32, c=FAKE, ct=1, ldc=32,
+                 stream=None)
+        a.update(kw)
+        return L.gemm_w4a16_decode(*a.values())
+
+    assert gd(a=None) == NULL
+    assert gd(wt=None) == NULL
+    assert gd(M=17) == SHAPE           # decode takes at most 16 rows
+    assert gd(K=192, lda=192) == SHAPE
+    assert gd(K=8320, lda=8320) == SHAPE
+    assert gd(lda=128) == LAYOUT
+    assert gd(ws=FAKE + 4) == LAYOUT
+    assert gd(ct=9) == DTYPE
+    if not torch.cuda.is_available():
+        assert gd() == NO_DEVICE
+
+
 def test_mxfp4_validation(L):
     import torch
 

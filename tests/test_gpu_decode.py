@@ -1,0 +1,127 @@
+"""GPU parity of the decode layout and the decode GEMV.
+
+nvfp4_pack_decode only reorders bytes: its output must equal, byte for byte, the
+segment-major rearrangement of the oracle's row-major codes and scales, written
+here with numpy reshapes.  gemm_w4a16_decode must meet the GEMM bound
+|C - C_ref| <= 2e-3 * sum_k |a w| against the oracle's fp64 product, over
+shapes that cover one and many 16-row tiles, ragged row counts per workgroup,
+waves with no K segment (K / 128 < 8), the largest K (8192), more workgroups
+than CUs, and the full decode workload; with grid-valued operands the fp32
+result is exact and must equal the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from helpers import assert_gemm_close, bf16bits_to_dev, dev, log
+from synthetic import WORKLOADS, activations_f32, to_bf16_bits, weights
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU visible")
+
+
+def fp4():
+    import block_scaled_fp4_04_amd as m
+
+    return m
+
+
+def _packed_nv(codes, scales, tscale):
+    return fp4().PackedNVFP4(torch.from_numpy(codes).to(dev()), torch.from_numpy(scales).to(dev()),
+                             torch.from_numpy(tscale).to(dev()), codes.shape[0], codes.shape[1] * 2, False)
+
+
+def _segment_major(codes, scales):
+    """codes [N][K/2] -> [K/128][N][64]; scales [N][K/16] -> [K/128][N][8]."""
+    N, half = codes.shape
+    nseg = half // 64
+    cp = codes.reshape(N, nseg, 64).transpose(1, 0, 2)
+    sp = scales.reshape(N, nseg, 8).transpose(1, 0, 2)
+    return np.ascontiguousarray(cp), np.ascontiguousarray(sp)
+
+
+@pytest.mark.parametrize("N,K", [(1, 128), (16, 256), (300, 1024), (17408, 5120)])
+def test_pack_decode_layout(N, K):
+    log(f"nvfp4_pack_decode N={N} K={K}")
+    w = weights(N, K, 0.02, 0.001, 20.0, seed=N + K)
+    oc, os_, ot = oracle.nvfp4_quantize(w)
+    d = fp4().nvfp4_pack_decode(_packed_nv(oc, os_, ot))
+    torch.cuda.synchronize()
+    cp, sp = _segment_major(oc, os_)
+    assert np.array_equal(d.codes.cpu().numpy(), cp)
+    assert np.array_equal(d.scales.cpu().numpy(), sp)
+
+
+SHAPES = [
+    (1, 16, 128), (1, 100, 1024), (2, 33, 5120), (4, 517, 5120), (16, 300, 1024), (5, 40, 384),
+    (3, 1000, 8192), (1, 4097, 2048), (16, 1, 128), (7, 40000, 256), (16, 2000, 1152),
+]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_decode_gemv(M, N, K, out):
+    log(f"gemm_w4a16_decode M={M} N={N} K={K} out={out}")
+    w = weights(N, K, 0.02, 0.001, 20.0, seed=7 * M + N + K)
+    a = to_bf16_bits(activations_f32(M, K, 0.005, 30.0, seed=M + 2 * N + K))
+    oc, os_, ot = oracle.nvfp4_quantize(w)
+    d = fp4().nvfp4_pack_decode(_packed_nv(oc, os_, ot))
+    c = fp4().gemm_w4a16_decode(bf16bits_to_dev(a), d, dtype=torch.bfloat16 if out == "bf16" else torch.float32)
+    torch.cuda.synchronize()
+    ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot)
+    assert_gemm_close(c, ref, tol, f"decode {M}x{N}x{K}")
+
+
+def _grid_vals(rng, shape, top_every):
+    """E2M1 grid values with a +-6 every `top_every` elements (so every 16-block of
+    the weight gets the same scale byte)."""
+    g = rng.integers(0, 16, shape).astype(np.uint8)
+    g[..., ::top_every] = (g[..., ::top_every] & 8) | 7
+    mag = np.array([0, .5, 1, 1.5, 2, 3, 4, 6])
+    return np.where(g & 8, -1.0, 1.0) * mag[g & 7]
+
+
+@pytest.mark.parametrize("M,N,K", [(1, 64, 512), (16, 300, 1024), (4, 520, 5120)])
+def test_decode_exact_when_operands_are_grid_values(M, N, K):
+    """W = grid * 448 * 2^-9 (every block byte 0x7E), A = grid * 4: products are
+    448 * n with |n| <= 144 and partial sums stay far below 2^24 units of 448, so
+    fp32 C is exact in any summation order and must equal fp64 C."""
+    rng = np.random.default_rng(M + N + K)
+    wv = (_grid_vals(rng, (N, K), 16) * 448 * 2.0 ** -9).astype(np.float32)
+    av = (_grid_vals(rng, (M, K), 10 ** 9) * 4.0).astype(np.float32)
+    oc, os_, ot = oracle.nvfp4_quantize(wv)
+    assert ot[0] == 2.0 ** -9 and np.all(os_ == 0x7E)
+    a = to_bf16_bits(av)
+    d = fp4().nvfp4_pack_decode(_packed_nv(oc, os_, ot))
+    c = fp4().gemm_w4a16_decode(bf16bits_to_dev(a), d, dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, _ = oracle.gemm_w4a16_ref(a, oc, os_, ot)
+    assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
+
+
+_cache = {}
+
+
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_gemv_full_size(M):
+    wl = WORKLOADS["decode_gemv_k5120_n17408"]
+    log(f"decode GEMV (decode layout) full size M={M} N=17408 K=5120")
+    if "nv" not in _cache:
+        _cache["nv"] = oracle.nvfp4_quantize(wl.weights())
+    oc, os_, ot = _cache["nv"]
+    a = wl.activations_bf16(M)
+    d = fp4().nvfp4_pack_decode(_packed_nv(oc, os_, ot))
+    c = fp4().gemm_w4a16_decode(bf16bits_to_dev(a), d, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot)
+    assert_gemm_close(c, ref, tol, f"decode layout M={M}")
+    # the row-major path gives the same numbers up to summation order
+    c2 = fp4().gemm_w4a16(bf16bits_to_dev(a), _packed_nv(oc, os_, ot), dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_gemm_close(c2, ref, tol, f"row-major M={M}")

@@ -89,8 +89,11 @@ def test_w4a4(M, N, K, a_mode):
     assert_gemm_close(c, ref, tol, f"w4a4 {M}x{N}x{K}")
 
 
+# K % 256 == 0 takes the two-stage kernel (K / 256 odd adds a leading zero stage);
+# other K the prefetch kernel with a masked K tail.
 @pytest.mark.parametrize("M,N,K", [(1, 32, 64), (5, 100, 96), (16, 300, 1056), (17, 260, 1024),
-                                   (300, 520, 5120), (513, 130, 160), (256, 256, 128)])
+                                   (300, 520, 5120), (513, 130, 160), (256, 256, 128),
+                                   (70, 300, 768), (257, 513, 1280), (9, 40, 256)])
 @pytest.mark.parametrize("rule", ["ocp", "ceil"])
 def test_mxfp4_w4a4(M, N, K, rule):
     log(f"mxfp4_gemm_w4a4 M={M} N={N} K={K} rule={rule}")
@@ -152,7 +155,7 @@ def test_w4a4_exact_when_operands_are_grid_values(M, N, K):
     assert np.array_equal(c4.cpu().numpy().astype(np.float64), ref4)
 
 
-@pytest.mark.parametrize("M,N,K", [(32, 64, 256), (300, 260, 1024)])
+@pytest.mark.parametrize("M,N,K", [(32, 64, 256), (300, 260, 1024), (40, 300, 768)])
 def test_mxfp4_exact_when_scales_are_powers_of_two(M, N, K):
     rng = np.random.default_rng(K)
     av = _grid_vals(rng, (M, K), 32).astype(np.float32) * np.float32(2.0 ** 3)
