@@ -54,10 +54,46 @@ __global__ __launch_bounds__(256) void k_nv_pack_decode(const uint8_t *__restric
         *reinterpret_cast<const uint2 *>(scales + (int64_t)r * (K / 16) + 8 * s);
 }
 
-template <int S, int D>
-__global__ __launch_bounds__(512, 1) void k_nv_gemv_dec(GemvArgs g)
+// Buffer descriptor over `bytes` bytes at `base` (raw, byte-addressed; dword 3
+// selects 32-bit data format).  A load whose offset is at or past `bytes`
+// returns zeros and reads nothing, which is how rows past the workgroup's range,
+// K segments a wave does not own and activation rows past M are skipped without
+// any branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, uint32_t bytes)
 {
-    __shared__ f32x4 red[kGvMaxT][kGvWaves][64];
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+constexpr uint32_t kGvOut = 0x80000000u;  // an offset past every descriptor's size
+
+template <int S>
+struct GvTile {
+    u32x4 c[S];     // 32 codes of row n, K 32 grp .. 32 grp + 31 of each segment
+    uint32_t s[S];  // their two E4M3 scale bytes
+};
+
+// E2M1 x 4 (two code bytes, low nibble first) -> bf16 x 4, unscaled (exact).
+__device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half)
+{
+    const bf16x2 lo = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)
+                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
+    const bf16x2 hi = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3)
+                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    return bf16x4{lo[0], lo[1], hi[0], hi[1]};
+}
+
+// M4: M <= 4 variant.  Sixteen 4x4x4 bf16 MFMA blocks: block b = l / 4 multiplies
+// activation rows 0..3 (lane 4 b + i supplies row i) by W rows 4 (b % 4) + j
+// (lane 4 b + j, so lane l still owns W row l % 16) over K-quarter b / 4 of the
+// segment, 4 K values per instruction.  The codes enter unscaled (E2M1 exactly
+// in bf16); each NVFP4 block's four steps accumulate from zero and the partial is
+// multiplied by the lane's E4M3 scale, so the scale costs 4 FMAs per 16 codes
+// instead of a multiply per code.  The four K-quarters are summed across lanes
+// at the end of the tile.
+template <int S, int D, bool M4, int W>
+__global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
+{
+    __shared__ f32x4 red[kGvMaxT][W][64];
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, grp = lane >> 4;
@@ -69,68 +105,114 @@ __global__ __launch_bounds__(512, 1) void k_nv_gemv_dec(GemvArgs g)
     const int r_hi = min(r_lo + g.rows_per_wg, N);
     const int nt = (r_hi - r_lo + 15) >> 4;
 
-    // activation fragments: A row n (zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8)
-    bf16x8 af[S][4];
-#pragma unroll
-    for (int s = 0; s < S; ++s)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            bf16x8 v = {};
-            if (s < ns && n < M)
-                v = *reinterpret_cast<const bf16x8 *>(g.a + (int64_t)n * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j);
-            af[s][j] = v;
-        }
+    const __amdgpu_buffer_rsrc_t ra = gv_rsrc(g.a, (uint32_t)((int64_t)(M - 1) * g.lda * 2 + g.K * 2));
+    const __amdgpu_buffer_rsrc_t rc = gv_rsrc(g.w_codes, (uint32_t)((int64_t)nseg * N * 64));
+    const __amdgpu_buffer_rsrc_t rs = gv_rsrc(g.w_scales, (uint32_t)((int64_t)nseg * N * 8));
 
-    u32x4 wc[D][S];
-    uint32_t wsc[D][S];
-    auto issue = [&](int t, int b) {
-        const int row = r_lo + 16 * t + n;
-        const bool ok = row < r_hi;
+    // byte offsets of this lane's codes / scales at tile 0, segment seg0 (kGvOut where skipped)
+    uint32_t oc[S], os[S];
 #pragma unroll
-        for (int s = 0; s < S; ++s) {
-            u32x4 c = {0u, 0u, 0u, 0u};
-            uint32_t sc = 0;
-            if (s < ns && ok) {
-                const int64_t e = (int64_t)(seg0 + s) * N + row;
-                c = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(g.w_codes + e * 64 + 16 * grp));
-                sc = *reinterpret_cast<const uint16_t *>(g.w_scales + e * 8 + 2 * grp);
-            }
-            wc[b][s] = c;
-            wsc[b][s] = sc;
-        }
+    for (int s = 0; s < S; ++s) {
+        const int64_t e = (int64_t)(seg0 + s) * N + r_lo + n;
+        oc[s] = s < ns ? (uint32_t)(e * 64 + 16 * grp) : kGvOut;
+        os[s] = s < ns ? (uint32_t)(e * 8 + 2 * grp) : kGvOut;
+    }
+    auto issue_seg = [&](int t, int s, GvTile<S> &b) {
+        const bool ok = r_lo + 16 * t + n < r_hi;
+        b.c[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(ok ? oc[s] + 1024 * t : kGvOut), 0, 0);
+        b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? os[s] + 128 * t : kGvOut), 0, 0);
     };
 
+    // activation fragments: A row n (M4: row l % 4; zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8),
+    // loaded segment by segment between tile 0's weight loads so the first math
+    // waits only for its own segment
+    const int arow = M4 ? (lane & 3) : n;
+    bf16x8 af[S][4];
+    GvTile<S> buf[D];
 #pragma unroll
-    for (int t = 0; t < D - 1; ++t)
-        if (t < nt) issue(t, t);
+    for (int s = 0; s < S; ++s) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const uint32_t off = (s < ns && arow < M)
+                ? (uint32_t)(((int64_t)arow * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j) * 2) : kGvOut;
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
+            __builtin_memcpy(&af[s][j], &v, 16);
+        }
+        issue_seg(0, s, buf[0]);
+    }
+#pragma unroll
+    for (int k = 1; k < D - 1; ++k)
+#pragma unroll
+        for (int s = 0; s < S; ++s) issue_seg(k, s, buf[k]);
+
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    // one segment of a tile, M <= 4 variant
+    auto seg4 = [&](int s, const GvTile<S> &b, f32x4 &acc) {
+        const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)b.s[s], false);
+#pragma unroll
+        for (int blk = 0; blk < 2; ++blk) {
+            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const int q = 4 * blk + st;  // K values 4 q .. 4 q + 3 of the lane's 32
+                const bf16x8 a8 = af[s][q >> 1];
+                const bf16x4 a4 = (q & 1) ? bf16x4{a8[4], a8[5], a8[6], a8[7]} : bf16x4{a8[0], a8[1], a8[2], a8[3]};
+                part = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(b.c[s][q >> 1], q & 1), part, 0, 0, 0);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(part[i], bs[blk], acc[i]);
+        }
+    };
+    // one segment of a tile, 16x16x32 variant (two accumulator chains)
+    auto seg16 = [&](int s, const GvTile<S> &b, f32x4 &acc0, f32x4 &acc1) {
+        // the two E4M3 block scales of the lane's 32 codes (OCP E4M3FN conversion)
+        const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)b.s[s], false);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][0], as_bf16x8(dq8_bf16(b.c[s][0], bs[0])), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][1], as_bf16x8(dq8_bf16(b.c[s][1], bs[0])), acc1, 0, 0, 0);
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][2], as_bf16x8(dq8_bf16(b.c[s][2], bs[1])), acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][3], as_bf16x8(dq8_bf16(b.c[s][3], bs[1])), acc1, 0, 0, 0);
+    };
+
+    // D tiles in flight.  The tile loop is unrolled completely, so every buffer is
+    // a fixed register set and no load in flight crosses a loop back edge.  The
+    // loads of tile t + D - 1 are spread over tile t's segments, one segment's
+    // loads before each segment's math, so the wave keeps loads in flight while it
+    // computes; loads for tiles at or past nt read nothing.
 #pragma unroll
     for (int t = 0; t < kGvMaxT; ++t) {
         if (t < nt) {
-            if (t + D - 1 < nt) issue(t + D - 1, (t + D - 1) % D);
-            const int b = t % D;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                if (s < ns) {
-                    // the two E4M3 block scales of the lane's 32 codes (OCP E4M3FN conversion)
-                    typedef float f32x2 __attribute__((ext_vector_type(2)));
-                    const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)wsc[b][s], false);
-#pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            af[s][j], as_bf16x8(dq8_bf16(wc[b][s][j], j < 2 ? bs[0] : bs[1])), acc, 0, 0, 0);
-                }
+                if (t + D - 1 < kGvMaxT) issue_seg(t + D - 1, s, buf[(t + D - 1) % D]);
+                __builtin_amdgcn_sched_barrier(0);
+                if (M4)
+                    seg4(s, buf[t % D], acc0);
+                else
+                    seg16(s, buf[t % D], acc0, acc1);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            red[t][wave][lane] = acc;
+            if (M4) {
+                // sum the four K-quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    acc0[i] += __shfl_xor(acc0[i], 16);
+                    acc0[i] += __shfl_xor(acc0[i], 32);
+                }
+                red[t][wave][lane] = acc0;
+            } else {
+                red[t][wave][lane] = acc0 + acc1;
+            }
         }
     }
     __syncthreads();
 
-    // wave w finishes tile w: lane (n, grp) holds rows 4 grp + i of output column r_lo + 16 w + n
+    // wave w finishes tile w: lane (n, grp) holds rows 4 grp + i of output column
+    // r_lo + 16 w + n (M4: lanes with grp = 0 hold rows 0..3)
     if (wave < nt) {
         f32x4 sum = red[wave][0][lane];
 #pragma unroll
-        for (int w = 1; w < kGvWaves; ++w) sum += red[wave][w][lane];
+        for (int w = 1; w < W; ++w) sum += red[wave][w][lane];
         const float ts = *g.w_tscale;
         const int col = r_lo + 16 * wave + n;
         if (col < r_hi) {
@@ -163,7 +245,14 @@ template <int S>
 static void launch_gemv(const GemvArgs &g, unsigned grid, hipStream_t st)
 {
     constexpr int D = S <= 5 ? 3 : 2;  // tiles in flight, bounded by registers
-    hipLaunchKernelGGL((k_nv_gemv_dec<S, D>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    // the M <= 4 variant's extra registers do not fit beside 8 segments' fragments
+    if constexpr (S < 8) {
+        if (g.M <= 4) {
+            hipLaunchKernelGGL((k_nv_gemv_dec<S, D, true, kGvWaves>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+            return;
+        }
+    }
+    hipLaunchKernelGGL((k_nv_gemv_dec<S, D, false, kGvWaves>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
 }
 
 static int cu_count()
