@@ -94,6 +94,7 @@ template <int S, int D, bool M4, int W>
 __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
 {
     __shared__ f32x4 red[kGvMaxT][W][64];
+    __shared__ __align__(16) uint16_t alds[M4 ? 4 * 1024 * S : 8];  // M4: A rows 0..3, K <= 1024 S
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, grp = lane >> 4;
@@ -123,45 +124,83 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
         b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? os[s] + 128 * t : kGvOut), 0, 0);
     };
 
-    // activation fragments: A row n (M4: row l % 4; zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8),
-    // loaded segment by segment between tile 0's weight loads so the first math
-    // waits only for its own segment
+    // activation fragments: A row n (M4: row l % 4; zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8)
     const int arow = M4 ? (lane & 3) : n;
     bf16x8 af[S][4];
     GvTile<S> buf[D];
+    if constexpr (M4) {
+        // M <= 4: lanes 4 p + i (p = 0..3) need the same activation bytes, so the
+        // workgroup stages A ([4][K] bf16, rows past M zero) in LDS once and every
+        // wave reads its fragments from there.  The A loads go out first, then
+        // the first tiles' weight loads, so waiting for A does not wait for them.
+        constexpr int kAChunks = S;  // 16-byte chunks per thread: 4 * K / 8 <= 4 * 1024 S / 8 = 512 S
+        const int cpr = g.K >> 3;    // chunks per row
+        u32x4 ach[kAChunks];
 #pragma unroll
-    for (int s = 0; s < S; ++s) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const uint32_t off = (s < ns && arow < M)
-                ? (uint32_t)(((int64_t)arow * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j) * 2) : kGvOut;
-            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-            __builtin_memcpy(&af[s][j], &v, 16);
+        for (int c = 0; c < kAChunks; ++c) {
+            const int idx = (int)threadIdx.x + 64 * W * c;
+            const int row = idx / cpr, col = idx - row * cpr;
+            const uint32_t off = (row < M && row < 4) ? (uint32_t)(((int64_t)row * g.lda + 8 * col) * 2) : kGvOut;
+            ach[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
         }
-        issue_seg(0, s, buf[0]);
+#pragma unroll
+        for (int k = 0; k < D - 1; ++k)
+#pragma unroll
+            for (int s = 0; s < S; ++s) issue_seg(k, s, buf[k]);
+#pragma unroll
+        for (int c = 0; c < kAChunks; ++c) {
+            const int idx = (int)threadIdx.x + 64 * W * c;
+            if (idx < 4 * cpr) *reinterpret_cast<u32x4 *>(alds + 8 * idx) = ach[c];
+        }
+        __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0): this wave's A stores done
+        asm volatile("s_barrier" ::: "memory");
+#pragma unroll
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                bf16x8 v = {};
+                if (s < ns) v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * (seg0 + s) + 32 * grp + 8 * j);
+                af[s][j] = v;
+            }
+    } else {
+        // loaded segment by segment between tile 0's weight loads so the first
+        // math waits only for its own segment
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t off = (s < ns && arow < M)
+                    ? (uint32_t)(((int64_t)arow * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j) * 2) : kGvOut;
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
+                __builtin_memcpy(&af[s][j], &v, 16);
+            }
+            issue_seg(0, s, buf[0]);
+        }
+#pragma unroll
+        for (int k = 1; k < D - 1; ++k)
+#pragma unroll
+            for (int s = 0; s < S; ++s) issue_seg(k, s, buf[k]);
     }
-#pragma unroll
-    for (int k = 1; k < D - 1; ++k)
-#pragma unroll
-        for (int s = 0; s < S; ++s) issue_seg(k, s, buf[k]);
 
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     // one segment of a tile, M <= 4 variant
     auto seg4 = [&](int s, const GvTile<S> &b, f32x4 &acc) {
         const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)b.s[s], false);
+        // the two NVFP4 blocks' MFMA chains interleaved, so each hides the other's latency
+        f32x4 part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-        for (int blk = 0; blk < 2; ++blk) {
-            f32x4 part = {0.f, 0.f, 0.f, 0.f};
+        for (int st = 0; st < 4; ++st)
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
+            for (int blk = 0; blk < 2; ++blk) {
                 const int q = 4 * blk + st;  // K values 4 q .. 4 q + 3 of the lane's 32
                 const bf16x8 a8 = af[s][q >> 1];
                 const bf16x4 a4 = (q & 1) ? bf16x4{a8[4], a8[5], a8[6], a8[7]} : bf16x4{a8[0], a8[1], a8[2], a8[3]};
-                part = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(b.c[s][q >> 1], q & 1), part, 0, 0, 0);
+                part[blk] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(b.c[s][q >> 1], q & 1), part[blk], 0, 0, 0);
             }
 #pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(part[i], bs[blk], acc[i]);
-        }
+        for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(part[blk][i], bs[blk], acc[i]);
     };
     // one segment of a tile, 16x16x32 variant (two accumulator chains)
     auto seg16 = [&](int s, const GvTile<S> &b, f32x4 &acc0, f32x4 &acc1) {
