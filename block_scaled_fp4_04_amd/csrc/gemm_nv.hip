@@ -754,6 +754,290 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
     }
 }
 
+// ---------------------------------------------- prefill, DMA ring (K % 64) --
+//
+// The same 256 x 256 tile and 2 x 2 waves, restructured around what moves:
+//  - Operands travel HBM -> LDS by buffer-to-LDS DMA, in their stored form: bf16
+//    A tiles (W4A16) or packed codes + E4M3 bytes (W4A4 A, and W always).  LDS
+//    holds W at 4.5 bits a value, not widened, so a stage is 41 KiB (W4A16) or
+//    18 KiB (W4A4) and three stages are in flight.
+//  - Each wave widens the W (and W4A4 A) fragments it multiplies straight from
+//    LDS into registers (exact E2M1 x E4M3 in bf16), between MFMAs.
+//  - The K order inside a 64-element stage is permuted the same way for both
+//    operands: MFMA step ks, lane half h contracts K = 32 h + 8 ks + [0, 8), so a
+//    lane's 16 code bytes of a row feed its four steps.
+//  - MFMA computes W_j A_i^T, so each lane ends with 4 consecutive output columns
+//    of one row, which the epilogue stages through LDS into whole-row stores.
+// Stages are three separate LDS objects (the compiler then never waits for a DMA
+// into one before reading another), rotated by unrolling the K loop 3 times;
+// stages past K are copied through size-0 descriptors (zeros, nothing read) and
+// add +0 to the accumulators.
+constexpr int kRK = 64;  // K elements per stage
+
+template <bool A_FP4>
+struct NvRing {
+    // byte offsets inside a stage
+    static constexpr int kA = 0;                                // bf16 [256][64] or codes [256][32]
+    static constexpr int kAS = A_FP4 ? 256 * 32 : 0;            // A scales [256][4] (W4A4)
+    static constexpr int kW = A_FP4 ? kAS + 1024 : 256 * 128;   // W codes [256][32]
+    static constexpr int kWS = kW + 256 * 32;                   // W scales [256][4]
+    static constexpr int kUsed = kWS + 1024;
+    static constexpr int kEpi = 64 * (256 * 2 + 16);            // epilogue staging of one wave pair
+    static constexpr int kStage = kUsed > kEpi ? kUsed : kEpi;
+    static constexpr int kDma = A_FP4 ? 6 : 11;                 // DMA instructions per wave per stage
+};
+
+struct NvRingDma {
+    __amdgpu_buffer_rsrc_t ra, ras, rw, rws;
+    uint32_t a[8], as, w[2], ws;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)(uint32_t)bytes, 0x00020000);
+}
+
+typedef __attribute__((address_space(3))) void nv_lds_void;
+constexpr uint32_t kNvOut = 0x80000000u;  // an offset past every descriptor's size
+
+// codes chunk h of tile row r sits at 32 r + 16 (h ^ ((r >> 3) & 1)); bf16 chunk c
+// of A row r at 128 r + 16 (c ^ ((r >> 1) & 7)): conflict-free 16-lane reads
+template <bool A_FP4>
+__device__ __forceinline__ void nv_ring_dma(uint8_t *st, const NvRingDma &d, int k0, int wave)
+{
+    using C = NvRing<A_FP4>;
+    if constexpr (A_FP4) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (nv_lds_void *)(st + C::kA + 16 * (128 * wave + 64 * i)), 16,
+                                                     (int)d.a[i], k0 / 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ras, (nv_lds_void *)(st + C::kAS + 4 * 64 * wave), 4, (int)d.as,
+                                                 k0 / 16, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (nv_lds_void *)(st + C::kA + 16 * (512 * wave + 64 * i)), 16,
+                                                     (int)d.a[i], 2 * k0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (nv_lds_void *)(st + C::kW + 16 * (128 * wave + 64 * i)), 16,
+                                                 (int)d.w[i], k0 / 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rws, (nv_lds_void *)(st + C::kWS + 4 * 64 * wave), 4, (int)d.ws,
+                                             k0 / 16, 0, 0);
+}
+
+// Four bf16 fragments (steps ks = 0..3) of one packed row: 16 code bytes and the
+// two E4M3 bytes of the lane's K half.
+__device__ __forceinline__ void nv_frags_fp4(const uint8_t *codes, const uint8_t *scl, bf16x8 (&f)[4])
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const u32x4 c = *reinterpret_cast<const u32x4 *>(codes);
+    const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)*reinterpret_cast<const uint16_t *>(scl), false);
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) f[ks] = as_bf16x8(dq8_bf16(c[ks], ks < 2 ? bs[0] : bs[1]));
+}
+
+template <bool A_FP4>
+__device__ __forceinline__ void nv_ring_stage(const uint8_t *st, int wm, int wn, int lane, f32x16 (&acc)[4][4])
+{
+    using C = NvRing<A_FP4>;
+    const int half = lane >> 5;
+    bf16x8 wf[4][4], af[4][4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = wn * 128 + 32 * j + (lane & 31);
+        nv_frags_fp4(st + C::kW + 32 * r + 16 * (half ^ ((r >> 3) & 1)), st + C::kWS + 4 * r + 2 * half, wf[j]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = wm * 128 + 32 * i + (lane & 31);
+        if constexpr (A_FP4) {
+            nv_frags_fp4(st + C::kA + 32 * r + 16 * (half ^ ((r >> 3) & 1)), st + C::kAS + 4 * r + 2 * half, af[i]);
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks)
+                af[i][ks] = *reinterpret_cast<const bf16x8 *>(st + C::kA + 128 * r + 16 * ((4 * half + ks) ^ ((r >> 1) & 7)));
+        }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][ks], af[i][ks], acc[i][j], 0, 0, 0);
+}
+
+__device__ __forceinline__ void nv_ring_wait(int n)
+{
+    // vmcnt(n) for the per-wave DMA counts used here
+    switch (n) {
+    case 6: __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8)); break;
+    case 11: __builtin_amdgcn_s_waitcnt(11 | (7 << 4) | (15 << 8)); break;
+    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+    }
+}
+
+// One stage: wait for stage t (this wave's copies of stage t + 1 may still be in
+// flight), barrier (every wave's copies of stage t landed; stage t - 1 read by
+// all), start copying stage t + 2 into `dst`, multiply stage t from `cur`.
+template <bool A_FP4>
+__device__ __forceinline__ void nv_ring_step(const uint8_t *cur, uint8_t *dst, int t, int nk, const NvRingDma &d,
+                                             const NvRingDma &dz, int wave, int wm, int wn, int lane,
+                                             f32x16 (&acc)[4][4])
+{
+    nv_ring_wait(NvRing<A_FP4>::kDma);
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0): reads of stage t - 1 done
+    asm volatile("s_barrier" ::: "memory");
+    nv_ring_dma<A_FP4>(dst, t + 2 < nk ? d : dz, (t + 2 < nk ? t + 2 : 0) * kRK, wave);
+    __builtin_amdgcn_sched_barrier(0);  // copies go out before this stage's work
+    nv_ring_stage<A_FP4>(cur, wm, wn, lane, acc);
+}
+
+// Epilogue: lane l of wave (wm, wn) holds output row wm 128 + 32 i + l % 32,
+// columns wn 128 + 32 j + 8 g + 4 (l / 32) + 0..3 in slots 4 g .. 4 g + 3 of
+// acc[i][j].  Rounds of R rows per wave pair go through LDS (wm = 0 in `s0`,
+// wm = 1 in `s1`, rows padded by 16 bytes) and leave as whole-row 16-byte stores.
+template <typename T, bool A_FP4>
+__device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[4][4], uint8_t *s0, uint8_t *s1,
+                                                 const NvGemmArgs &g, int m0, int n0, int wm, int wn, int lane,
+                                                 int tid)
+{
+    constexpr int es = (int)sizeof(T);
+    constexpr int pitch = 256 * es + 16;
+    constexpr int R = es == 2 ? 64 : 32;      // rows per wave pair per round
+    constexpr int kPer = 16 / es, kChunks = 256 / kPer;
+    const int M = (int)g.M, N = (int)g.N;
+    const float wt = g.w_tscale[0];
+    uint8_t *mine = wm ? s1 : s0;
+#pragma unroll
+    for (int rd = 0; rd < 128 / R; ++rd) {
+#pragma unroll
+        for (int i = rd * R / 32; i < (rd + 1) * R / 32; ++i) {
+            const int m = m0 + wm * 128 + 32 * i + (lane & 31);
+            float sc = wt;
+            if (A_FP4) sc = (m < M ? g.a_tscale[g.a_per_row ? m : 0] : 0.f) * wt;
+            uint8_t *row = mine + (32 * i - rd * R + (lane & 31)) * pitch;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                    const int col = wn * 128 + 32 * j + 8 * gq + 4 * (lane >> 5);
+                    const f32x16 &a = acc[i][j];
+                    if constexpr (es == 2) {
+                        const bf16x4 v = {(__bf16)(a[4 * gq] * sc), (__bf16)(a[4 * gq + 1] * sc),
+                                          (__bf16)(a[4 * gq + 2] * sc), (__bf16)(a[4 * gq + 3] * sc)};
+                        *reinterpret_cast<bf16x4 *>(row + 2 * col) = v;
+                    } else {
+                        *reinterpret_cast<f32x4 *>(row + 4 * col) =
+                            f32x4{a[4 * gq] * sc, a[4 * gq + 1] * sc, a[4 * gq + 2] * sc, a[4 * gq + 3] * sc};
+                    }
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const uint8_t *st = half ? s1 : s0;
+            const int mrow0 = m0 + 128 * half + rd * R;
+            for (int q = tid; q < R * kChunks; q += 256) {
+                const int r = q / kChunks, ch = q % kChunks;
+                const int m = mrow0 + r, n = n0 + ch * kPer;
+                if (m >= M || n >= N) continue;
+                const uint4 v = *reinterpret_cast<const uint4 *>(st + r * pitch + 16 * ch);
+                T *dstp = reinterpret_cast<T *>(g.c) + (int64_t)m * g.ldc + n;
+                if (n + kPer <= N) {
+                    *reinterpret_cast<uint4 *>(dstp) = v;
+                } else {
+                    T e[kPer];
+                    __builtin_memcpy(e, &v, 16);
+#pragma unroll
+                    for (int tt = 0; tt < kPer; ++tt)
+                        if (n + tt < N) dstp[tt] = e[tt];
+                }
+            }
+        }
+        __syncthreads();
+    }
+}
+
+template <bool A_FP4, typename OutT>
+__global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
+{
+    using C = NvRing<A_FP4>;
+    __shared__ __align__(16) uint8_t s0[C::kStage];
+    __shared__ __align__(16) uint8_t s1[C::kStage];
+    __shared__ __align__(16) uint8_t s2[C::kStage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    int tm, tn;
+    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * BM, n0 = tn * BN;
+    const int nk = K / kRK;
+
+    NvRingDma d, dz;
+    d.rw = nv_rsrc(g.w_codes, (int64_t)N * (K / 2));
+    d.rws = nv_rsrc(g.w_scales, (int64_t)N * (K / 16));
+    if constexpr (A_FP4) {
+        d.ra = nv_rsrc(g.a_codes, (int64_t)M * (K / 2));
+        d.ras = nv_rsrc(g.a_scales, (int64_t)M * (K / 16));
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int q = 128 * wave + 64 * i + lane;
+            const int r = q >> 1, h = (q & 1) ^ ((r >> 3) & 1);
+            d.a[i] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
+        }
+        const int qa = 64 * wave + lane;
+        d.as = m0 + qa < M ? (uint32_t)(m0 + qa) * (uint32_t)(K / 16) : kNvOut;
+    } else {
+        d.ra = nv_rsrc(g.a, ((int64_t)(M - 1) * g.lda + K) * 2);
+        d.ras = d.ra;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int q = 512 * wave + 64 * i + lane;
+            const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+            d.a[i] = m0 + r < M ? (uint32_t)(((int64_t)(m0 + r) * g.lda + 8 * c) * 2) : kNvOut;
+        }
+        d.as = kNvOut;
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = 128 * wave + 64 * i + lane;
+        const int r = q >> 1, h = (q & 1) ^ ((r >> 3) & 1);
+        d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
+    }
+    const int qw = 64 * wave + lane;
+    d.ws = n0 + qw < N ? (uint32_t)(n0 + qw) * (uint32_t)(K / 16) : kNvOut;
+    dz = d;
+    dz.ra = nv_rsrc(g.a_codes ? (const void *)g.a_codes : (const void *)g.a, 0);
+    dz.ras = dz.ra;
+    dz.rw = nv_rsrc(g.w_codes, 0);
+    dz.rws = nv_rsrc(g.w_scales, 0);
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    nv_ring_dma<A_FP4>(s0, d, 0, wave);
+    nv_ring_dma<A_FP4>(s1, nk > 1 ? d : dz, nk > 1 ? kRK : 0, wave);
+    for (int t = 0; t < nk; t += 3) {
+        nv_ring_step<A_FP4>(s0, s2, t, nk, d, dz, wave, wm, wn, lane, acc);
+        nv_ring_step<A_FP4>(s1, s0, t + 1, nk, d, dz, wave, wm, wn, lane, acc);
+        nv_ring_step<A_FP4>(s2, s1, t + 2, nk, d, dz, wave, wm, wn, lane, acc);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
+    __syncthreads();
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    nv_ring_epilogue<OutT, A_FP4>(acc, s0, s1, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
+}
+
 constexpr size_t kGemmLds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);  // 128 KiB
 
 template <bool A_FP4, bool ALIGNED>
@@ -802,6 +1086,20 @@ fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
             hipLaunchKernelGGL(k_nv_decode_generic<false>, dim3(nwg), dim3(64 * kDecWaves), 0, st, g.a,
                                g.lda, g.w_codes, g.w_scales, g.w_tscale, (int)g.M, (int)g.N, (int)g.K,
                                g.c, g.c_bf16, g.ldc);
+        return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+    }
+    // the ring kernel addresses operands with 32-bit byte offsets
+    const bool ring = aligned && g.M * g.K * 2 < (int64_t(1) << 31) && g.N * (g.K / 2) < (int64_t(1) << 31) &&
+                      (g.a_codes || g.M * g.lda * 2 < (int64_t(1) << 31));
+    if (ring) {
+        const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
+        if (g.a_codes) {
+            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<true, __bf16>), dim3(tiles), dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((k_nv_gemm_ring<true, float>), dim3(tiles), dim3(256), 0, st, g);
+        } else {
+            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<false, __bf16>), dim3(tiles), dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((k_nv_gemm_ring<false, float>), dim3(tiles), dim3(256), 0, st, g);
+        }
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
     if (g.a_codes)

@@ -52,6 +52,8 @@ SHAPES = [
     (1, 16, 64), (1, 100, 1040), (2, 33, 5120), (4, 517, 5120), (7, 64, 80), (16, 300, 1024),
     (16, 17408, 5120), (17, 260, 1040), (64, 256, 256), (300, 520, 5120), (513, 130, 96),
     (257, 1000, 2048),
+    # prefill with K a multiple of 64: one to five 64-wide K stages, ragged M and N
+    (40, 70, 64), (300, 300, 128), (257, 513, 192), (513, 260, 320),
 ]
 
 
@@ -69,7 +71,8 @@ def test_w4a16(M, N, K, out):
 
 
 @pytest.mark.parametrize("M,N,K", [(1, 48, 64), (4, 517, 5120), (16, 300, 1040), (17, 260, 1040),
-                                   (300, 520, 5120), (513, 130, 96)])
+                                   (300, 520, 5120), (513, 130, 96),
+                                   (40, 70, 64), (257, 513, 192), (513, 260, 320)])
 @pytest.mark.parametrize("a_mode", ["row", "tensor"])
 def test_w4a4(M, N, K, a_mode):
     log(f"gemm_w4a4 M={M} N={N} K={K} a_mode={a_mode}")
