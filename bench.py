@@ -51,6 +51,8 @@ def parse():
     ap.add_argument("--skip-components", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
     ap.add_argument("--only-decode", action="store_true", help="decode step only (profiling runs)")
+    ap.add_argument("--only-components", action="store_true",
+                    help="quantize / dequantize / prefill GEMM components only (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -134,6 +136,10 @@ def main():
     w32 = torch.from_numpy(w_np).to(dev)
     wq = fp4.nvfp4_quantize(w32)
     torch.cuda.synchronize()
+    if args.only_components:
+        print(json.dumps({"components": components(args, torch, fp4, T, dev, w32, wq)}))
+        return
+
     R = max(1, args.rotate)
     copies = [wq] + [fp4.PackedNVFP4(wq.codes.clone(), wq.scales.clone(), wq.tscale.clone(), N, K)
                      for _ in range(R - 1)]

@@ -773,6 +773,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 // stages past K are copied through size-0 descriptors (zeros, nothing read) and
 // add +0 to the accumulators.
 constexpr int kRK = 64;  // K elements per stage
+constexpr int kNvL16 = 1;  // wave layout of the W4A16 tile (see NvWaves)
 
 template <bool A_FP4>
 struct NvRing {
@@ -838,92 +839,201 @@ __device__ __forceinline__ void nv_frags_fp4(const uint8_t *codes, const uint8_t
     for (int ks = 0; ks < 4; ++ks) f[ks] = as_bf16x8(dq8_bf16(c[ks], ks < 2 ? bs[0] : bs[1]));
 }
 
-template <bool A_FP4>
-__device__ __forceinline__ void nv_ring_stage(const uint8_t *st, int wm, int wn, int lane, f32x16 (&acc)[4][4])
+// Wave layout of the 256 x 256 tile: L = 0 splits it 2 x 2 (128 x 128 per wave),
+// L = 1 splits N four ways (wave w: all 256 rows x columns 64 w .. 64 w + 63), so
+// no two waves widen the same W rows.
+template <int L>
+struct NvWaves {
+    static constexpr int NI = L ? 8 : 4;  // 32-row MFMA tiles per wave
+    static constexpr int NJ = L ? 2 : 4;  // 32-column MFMA tiles per wave
+    __device__ static int row0(int wave) { return L ? 0 : (wave >> 1) * 128; }
+    __device__ static int col0(int wave) { return L ? 64 * wave : (wave & 1) * 128; }
+};
+
+// Per-wave operand state.  A stage's packed rows (16 code bytes and two E4M3
+// scales per lane and row) are read from LDS once; each MFMA step ks widens its
+// fragments from them (bf16 A fragments are read from LDS per step instead).
+// Rows r0 + 32 i + l % 32 share the swizzle terms of l % 32, so every row's LDS
+// offset is a per-lane base plus a constant.
+template <bool A_FP4, int L>
+struct NvPipe {
+    static constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
+    static constexpr int NA = A_FP4 ? NI : 1;
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    u32x4 wc[NJ];
+    f32x2 wsc[NJ];
+    u32x4 ac[NA];
+    f32x2 asc[NA];
+    uint32_t wb, wsb;  // W codes / scales of MFMA tile 0
+    uint32_t ab, asb;  // A codes / scales (W4A4) or bf16 row (W4A16) of MFMA tile 0
+    uint32_t ak[4];    // W4A16: swizzled 16-byte chunk of step ks in a bf16 A row
+};
+
+template <bool A_FP4, int L>
+__device__ __forceinline__ void nv_pipe_init(NvPipe<A_FP4, L> &p, int wave, int lane)
+{
+    const int half = lane >> 5, l = lane & 31;
+    const int r0 = NvWaves<L>::row0(wave), c0 = NvWaves<L>::col0(wave);
+    const int hsw = 16 * (half ^ ((l >> 3) & 1));
+    p.wb = 32 * (c0 + l) + hsw;
+    p.wsb = 4 * (c0 + l) + 2 * half;
+    if (A_FP4) {
+        p.ab = 32 * (r0 + l) + hsw;
+        p.asb = 4 * (r0 + l) + 2 * half;
+    } else {
+        p.ab = 128 * (r0 + l);
+        p.asb = 0;
+    }
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) p.ak[ks] = 16 * ((4 * half + ks) ^ ((l >> 1) & 7));
+}
+
+// read the stage's packed rows (codes + scales) into registers
+template <bool A_FP4, int L>
+__device__ __forceinline__ void nv_pipe_raw(NvPipe<A_FP4, L> &p, const uint8_t *st)
 {
     using C = NvRing<A_FP4>;
-    const int half = lane >> 5;
-    bf16x8 wf[4][4], af[4][4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = wn * 128 + 32 * j + (lane & 31);
-        nv_frags_fp4(st + C::kW + 32 * r + 16 * (half ^ ((r >> 3) & 1)), st + C::kWS + 4 * r + 2 * half, wf[j]);
+    for (int j = 0; j < NvPipe<A_FP4, L>::NJ; ++j) {
+        p.wc[j] = *reinterpret_cast<const u32x4 *>(st + C::kW + p.wb + 1024 * j);
+        p.wsc[j] = __builtin_amdgcn_cvt_pk_f32_fp8(
+            (int)*reinterpret_cast<const uint16_t *>(st + C::kWS + p.wsb + 128 * j), false);
     }
+    if constexpr (A_FP4) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int r = wm * 128 + 32 * i + (lane & 31);
-        if constexpr (A_FP4) {
-            nv_frags_fp4(st + C::kA + 32 * r + 16 * (half ^ ((r >> 3) & 1)), st + C::kAS + 4 * r + 2 * half, af[i]);
-        } else {
-#pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                af[i][ks] = *reinterpret_cast<const bf16x8 *>(st + C::kA + 128 * r + 16 * ((4 * half + ks) ^ ((r >> 1) & 7)));
+        for (int i = 0; i < NvPipe<A_FP4, L>::NI; ++i) {
+            p.ac[i] = *reinterpret_cast<const u32x4 *>(st + C::kA + p.ab + 1024 * i);
+            p.asc[i] = __builtin_amdgcn_cvt_pk_f32_fp8(
+                (int)*reinterpret_cast<const uint16_t *>(st + C::kAS + p.asb + 128 * i), false);
         }
     }
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j][ks], af[i][ks], acc[i][j], 0, 0, 0);
 }
 
-__device__ __forceinline__ void nv_ring_wait(int n)
+// fragments of step ks: lane half h holds K = 32 h + 8 ks + [0, 8) of the stage
+template <bool A_FP4, int L, int KS>
+__device__ __forceinline__ void nv_pipe_frags(const NvPipe<A_FP4, L> &p, const uint8_t *st,
+                                              bf16x8 (&wf)[NvWaves<L>::NJ], bf16x8 (&af)[NvWaves<L>::NI])
 {
-    // vmcnt(n) for the per-wave DMA counts used here
-    switch (n) {
-    case 6: __builtin_amdgcn_s_waitcnt(6 | (7 << 4) | (15 << 8)); break;
-    case 11: __builtin_amdgcn_s_waitcnt(11 | (7 << 4) | (15 << 8)); break;
-    default: __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8)); break;
+    using C = NvRing<A_FP4>;
+#pragma unroll
+    for (int j = 0; j < NvWaves<L>::NJ; ++j)
+        wf[j] = as_bf16x8(dq8_bf16(p.wc[j][KS], KS < 2 ? p.wsc[j][0] : p.wsc[j][1]));
+#pragma unroll
+    for (int i = 0; i < NvWaves<L>::NI; ++i) {
+        if constexpr (A_FP4)
+            af[i] = as_bf16x8(dq8_bf16(p.ac[i][KS], KS < 2 ? p.asc[i][0] : p.asc[i][1]));
+        else
+            af[i] = *reinterpret_cast<const bf16x8 *>(st + C::kA + p.ab + p.ak[KS] + 4096 * i);
     }
 }
 
-// One stage: wait for stage t (this wave's copies of stage t + 1 may still be in
-// flight), barrier (every wave's copies of stage t landed; stage t - 1 read by
-// all), start copying stage t + 2 into `dst`, multiply stage t from `cur`.
-template <bool A_FP4>
-__device__ __forceinline__ void nv_ring_step(const uint8_t *cur, uint8_t *dst, int t, int nk, const NvRingDma &d,
-                                             const NvRingDma &dz, int wave, int wm, int wn, int lane,
-                                             f32x16 (&acc)[4][4])
+template <int L>
+__device__ __forceinline__ void nv_pipe_mfma(f32x16 (&acc)[NvWaves<L>::NI][NvWaves<L>::NJ],
+                                             const bf16x8 (&wf)[NvWaves<L>::NJ], const bf16x8 (&af)[NvWaves<L>::NI])
 {
-    nv_ring_wait(NvRing<A_FP4>::kDma);
-    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0): reads of stage t - 1 done
-    asm volatile("s_barrier" ::: "memory");
-    nv_ring_dma<A_FP4>(dst, t + 2 < nk ? d : dz, (t + 2 < nk ? t + 2 : 0) * kRK, wave);
-    __builtin_amdgcn_sched_barrier(0);  // copies go out before this stage's work
-    nv_ring_stage<A_FP4>(cur, wm, wn, lane, acc);
+#pragma unroll
+    for (int i = 0; i < NvWaves<L>::NI; ++i)
+#pragma unroll
+        for (int j = 0; j < NvWaves<L>::NJ; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
-// Epilogue: lane l of wave (wm, wn) holds output row wm 128 + 32 i + l % 32,
-// columns wn 128 + 32 j + 8 g + 4 (l / 32) + 0..3 in slots 4 g .. 4 g + 3 of
-// acc[i][j].  Rounds of R rows per wave pair go through LDS (wm = 0 in `s0`,
-// wm = 1 in `s1`, rows padded by 16 bytes) and leave as whole-row 16-byte stores.
-template <typename T, bool A_FP4>
-__device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[4][4], uint8_t *s0, uint8_t *s1,
-                                                 const NvGemmArgs &g, int m0, int n0, int wm, int wn, int lane,
-                                                 int tid)
+// Spread the 16 MFMAs of a step over the widening (NV VALU) and the reads (ND)
+// of the next step.  NR reads and NB copies (global-to-LDS) go out first, then P
+// MFMAs cover the latency of those reads before any VALU work uses them.
+template <int NV, int ND, int NR = 0, int NB = 0, int P = 0>
+__device__ __forceinline__ void nv_pipe_interleave()
 {
+    constexpr int per = (NV + 15 - P) / (16 - P);
+    if (NR) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS read
+    if (NB) __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // VMEM read
+    if (P) __builtin_amdgcn_sched_group_barrier(0x008, P, 0);    // MFMA
+#pragma unroll
+    for (int t = P; t < 16; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        if (per) __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // VALU
+        if (ND && t % (16 / ND) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int N>
+__device__ __forceinline__ void nv_wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// One stage t (in `cur`; stage t + 1 in `nxt`).  Entering, f holds step 0's
+// fragments.  Steps 0-2 multiply while the next step's fragments are formed; then
+// the wave waits until its copies of stage t + 1 landed and its reads of `cur`
+// returned, and a barrier extends both to every wave, so `cur` is free: the copy
+// of stage t + 3 starts into it.  Step 3 multiplies while stage t + 1's packed
+// rows and step-0 fragments are read from `nxt`.  One basic block per stage.
+template <bool A_FP4, int L>
+__device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, int t, int nk, const NvRingDma &d,
+                                              const NvRingDma &dz, int wave, NvPipe<A_FP4, L> &p,
+                                              f32x16 (&acc)[NvWaves<L>::NI][NvWaves<L>::NJ],
+                                              bf16x8 (&wf)[NvWaves<L>::NJ], bf16x8 (&af)[NvWaves<L>::NI])
+{
+    constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
+    constexpr int NV = 16 * (NJ + (A_FP4 ? NI : 0));      // VALU per step's widening, about
+    constexpr int ND = A_FP4 ? 0 : NI;                     // DS reads per step
+    bf16x8 wf1[NJ], af1[NI];
+    nv_pipe_frags<A_FP4, L, 1>(p, cur, wf1, af1);
+    nv_pipe_mfma<L>(acc, wf, af);
+    nv_pipe_interleave<NV, ND>();
+    nv_pipe_frags<A_FP4, L, 2>(p, cur, wf, af);
+    nv_pipe_mfma<L>(acc, wf1, af1);
+    nv_pipe_interleave<NV, ND>();
+    nv_pipe_frags<A_FP4, L, 3>(p, cur, wf1, af1);
+    nv_pipe_mfma<L>(acc, wf, af);
+    nv_pipe_interleave<NV, ND>();
+    nv_wait_vm<NvRing<A_FP4>::kDma>();
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    nv_pipe_raw<A_FP4, L>(p, nxt);
+    nv_ring_dma<A_FP4>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
+    nv_pipe_frags<A_FP4, L, 0>(p, nxt, wf, af);
+    nv_pipe_mfma<L>(acc, wf1, af1);
+    nv_pipe_interleave<NV, ND, 2 * (A_FP4 ? NI + NJ : NJ), NvRing<A_FP4>::kDma, 4>();
+}
+
+// Epilogue: lane l holds output row r0 + 32 i + l % 32, columns
+// c0 + 32 j + 8 g + 4 (l / 32) + 0..3 in slots 4 g .. 4 g + 3 of acc[i][j].  In
+// round rd, tile rows rd R + [0, R) go through `s0` and rows 128 + rd R + [0, R)
+// through `s1` (rows padded by 16 bytes), then leave as whole-row 16-byte stores.
+template <typename T, bool A_FP4, int L>
+__device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[NvWaves<L>::NI][NvWaves<L>::NJ],
+                                                 uint8_t *s0, uint8_t *s1, const NvGemmArgs &g, int m0, int n0,
+                                                 int wave, int lane, int tid)
+{
+    constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
     constexpr int es = (int)sizeof(T);
     constexpr int pitch = 256 * es + 16;
-    constexpr int R = es == 2 ? 64 : 32;      // rows per wave pair per round
+    constexpr int R = es == 2 ? 64 : 32;      // rows per staging buffer per round
     constexpr int kPer = 16 / es, kChunks = 256 / kPer;
     const int M = (int)g.M, N = (int)g.N;
     const float wt = g.w_tscale[0];
-    uint8_t *mine = wm ? s1 : s0;
+    const int r0 = NvWaves<L>::row0(wave), c0 = NvWaves<L>::col0(wave);
 #pragma unroll
     for (int rd = 0; rd < 128 / R; ++rd) {
 #pragma unroll
-        for (int i = rd * R / 32; i < (rd + 1) * R / 32; ++i) {
-            const int m = m0 + wm * 128 + 32 * i + (lane & 31);
+        for (int i = 0; i < NI; ++i) {
+            // rows of MFMA tile i: r0 + 32 i + [0, 32), one staging buffer, one round
+            const int rr = L ? (32 * i) % 128 : 32 * i;  // row within its half of the tile
+            if (rr / R != rd) continue;
+            const int row_t = r0 + 32 * i + (lane & 31);
+            const int m = m0 + row_t;
             float sc = wt;
             if (A_FP4) sc = (m < M ? g.a_tscale[g.a_per_row ? m : 0] : 0.f) * wt;
-            uint8_t *row = mine + (32 * i - rd * R + (lane & 31)) * pitch;
+            uint8_t *buf = (L ? 32 * i : r0) >= 128 ? s1 : s0;
+            uint8_t *row = buf + (rr - rd * R + (lane & 31)) * pitch;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < NJ; ++j) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
-                    const int col = wn * 128 + 32 * j + 8 * gq + 4 * (lane >> 5);
+                    const int col = c0 + 32 * j + 8 * gq + 4 * (lane >> 5);
                     const f32x16 &a = acc[i][j];
                     if constexpr (es == 2) {
                         const bf16x4 v = {(__bf16)(a[4 * gq] * sc), (__bf16)(a[4 * gq + 1] * sc),
@@ -963,16 +1073,16 @@ __device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[4][4], uint
     }
 }
 
-template <bool A_FP4, typename OutT>
+template <bool A_FP4, int L, typename OutT>
 __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 {
     using C = NvRing<A_FP4>;
+    constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
     __shared__ __align__(16) uint8_t s0[C::kStage];
     __shared__ __align__(16) uint8_t s1[C::kStage];
     __shared__ __align__(16) uint8_t s2[C::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
     const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
     const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
     int tm, tn;
@@ -1019,23 +1129,31 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
     dz.rw = nv_rsrc(g.w_codes, 0);
     dz.rws = nv_rsrc(g.w_scales, 0);
 
-    f32x16 acc[4][4];
+    f32x16 acc[NI][NJ];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
+    NvPipe<A_FP4, L> p;
+    nv_pipe_init(p, wave, lane);
     nv_ring_dma<A_FP4>(s0, d, 0, wave);
     nv_ring_dma<A_FP4>(s1, nk > 1 ? d : dz, nk > 1 ? kRK : 0, wave);
+    nv_ring_dma<A_FP4>(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kRK : 0, wave);
+    nv_wait_vm<2 * C::kDma>();
+    asm volatile("s_barrier" ::: "memory");
+    bf16x8 wf[NJ], af[NI];
+    nv_pipe_raw<A_FP4, L>(p, s0);
+    nv_pipe_frags<A_FP4, L, 0>(p, s0, wf, af);
     for (int t = 0; t < nk; t += 3) {
-        nv_ring_step<A_FP4>(s0, s2, t, nk, d, dz, wave, wm, wn, lane, acc);
-        nv_ring_step<A_FP4>(s1, s0, t + 1, nk, d, dz, wave, wm, wn, lane, acc);
-        nv_ring_step<A_FP4>(s2, s1, t + 2, nk, d, dz, wave, wm, wn, lane, acc);
+        nv_pipe_stage<A_FP4, L>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<A_FP4, L>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<A_FP4, L>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    nv_ring_epilogue<OutT, A_FP4>(acc, s0, s1, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
+    nv_ring_epilogue<OutT, A_FP4, L>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e);
 }
 
 constexpr size_t kGemmLds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);  // 128 KiB
@@ -1094,11 +1212,11 @@ fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
     if (ring) {
         const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
         if (g.a_codes) {
-            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<true, __bf16>), dim3(tiles), dim3(256), 0, st, g);
-            else hipLaunchKernelGGL((k_nv_gemm_ring<true, float>), dim3(tiles), dim3(256), 0, st, g);
+            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<true, 0, __bf16>), dim3(tiles), dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((k_nv_gemm_ring<true, 0, float>), dim3(tiles), dim3(256), 0, st, g);
         } else {
-            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<false, __bf16>), dim3(tiles), dim3(256), 0, st, g);
-            else hipLaunchKernelGGL((k_nv_gemm_ring<false, float>), dim3(tiles), dim3(256), 0, st, g);
+            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<false, kNvL16, __bf16>), dim3(tiles), dim3(256), 0, st, g);
+            else hipLaunchKernelGGL((k_nv_gemm_ring<false, kNvL16, float>), dim3(tiles), dim3(256), 0, st, g);
         }
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
