@@ -756,11 +756,12 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 
 // ---------------------------------------------- prefill, DMA ring (K % 64) --
 //
-// The same 256 x 256 tile and 2 x 2 waves, restructured around what moves:
+// TM x TN output tile (256 x 256, or 128 x 128 for a last partial round), four
+// waves, built around what moves:
 //  - Operands travel HBM -> LDS by buffer-to-LDS DMA, in their stored form: bf16
 //    A tiles (W4A16) or packed codes + E4M3 bytes (W4A4 A, and W always).  LDS
-//    holds W at 4.5 bits a value, not widened, so a stage is 41 KiB (W4A16) or
-//    18 KiB (W4A4) and three stages are in flight.
+//    holds W at 4.5 bits a value, not widened, so a 256 x 256 stage is 41 KiB
+//    (W4A16) or 18 KiB (W4A4) and three stages are in flight.
 //  - Each wave widens the W (and W4A4 A) fragments it multiplies straight from
 //    LDS into registers (exact E2M1 x E4M3 in bf16), between MFMAs.
 //  - The K order inside a 64-element stage is permuted the same way for both
@@ -773,19 +774,38 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 // stages past K are copied through size-0 descriptors (zeros, nothing read) and
 // add +0 to the accumulators.
 constexpr int kRK = 64;  // K elements per stage
-constexpr int kNvL16 = 1;  // wave layout of the W4A16 tile (see NvWaves)
+constexpr int kNvL16 = 1;  // wave layout of the W4A16 256 x 256 tile (see NvTile)
 
-template <bool A_FP4>
-struct NvRing {
+// Tile geometry.  Wave layout L = 0 splits the tile 2 x 2; L = 1 splits N four
+// ways (each wave all TM rows), so no two waves widen the same W rows.
+template <bool A_FP4, int L, int TM, int TN>
+struct NvTile {
+    static_assert((TM == 128 || TM == 256) && (TN == 128 || TN == 256), "tile");
+    static constexpr int WM = L ? TM : TM / 2;      // rows per wave
+    static constexpr int WN = L ? TN / 4 : TN / 2;  // columns per wave
+    static constexpr int NI = WM / 32, NJ = WN / 32;
+    static_assert(NI * 32 == WM && NJ * 32 == WN && NJ >= 1, "wave tile");
+    __device__ static int row0(int wave) { return L ? 0 : (wave >> 1) * WM; }
+    __device__ static int col0(int wave) { return L ? WN * wave : (wave & 1) * WN; }
     // byte offsets inside a stage
-    static constexpr int kA = 0;                                // bf16 [256][64] or codes [256][32]
-    static constexpr int kAS = A_FP4 ? 256 * 32 : 0;            // A scales [256][4] (W4A4)
-    static constexpr int kW = A_FP4 ? kAS + 1024 : 256 * 128;   // W codes [256][32]
-    static constexpr int kWS = kW + 256 * 32;                   // W scales [256][4]
-    static constexpr int kUsed = kWS + 1024;
-    static constexpr int kEpi = 64 * (256 * 2 + 16);            // epilogue staging of one wave pair
+    static constexpr int kA = 0;                             // bf16 [TM][64] or codes [TM][32]
+    static constexpr int kAS = A_FP4 ? TM * 32 : 0;          // A scales [TM][4] (W4A4)
+    static constexpr int kW = A_FP4 ? kAS + TM * 4 : TM * 128;  // W codes [TN][32]
+    static constexpr int kWS = kW + TN * 32;                 // W scales [TN][4]
+    static constexpr int kUsed = kWS + TN * 4;
+    // copies per wave per stage: 16-byte chunks (8 per bf16 row, 2 per packed
+    // row) and one 4-byte scale word per row
+    static constexpr int nA = A_FP4 ? TM * 2 / 256 : TM * 8 / 256;
+    static constexpr int nW = TN * 2 / 256;
+    static constexpr int kDma = nA + nW + 1 + (A_FP4 ? 1 : 0);
+    // epilogue: the two row halves of the tile are staged through two stage
+    // buffers, R rows at a time (rows padded by 16 bytes)
+    static constexpr int H = TM / 2;
+    static constexpr int epi_rows(int es) { return (es == 2 ? 64 : 32) < H ? (es == 2 ? 64 : 32) : H; }
+    static constexpr int epi_pitch(int es) { return TN * es + 16; }
+    static constexpr int kEpi = epi_rows(2) * epi_pitch(2) > epi_rows(4) * epi_pitch(4)
+                                    ? epi_rows(2) * epi_pitch(2) : epi_rows(4) * epi_pitch(4);
     static constexpr int kStage = kUsed > kEpi ? kUsed : kEpi;
-    static constexpr int kDma = A_FP4 ? 6 : 11;                 // DMA instructions per wave per stage
 };
 
 struct NvRingDma {
@@ -801,67 +821,48 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void *base, int6
 typedef __attribute__((address_space(3))) void nv_lds_void;
 constexpr uint32_t kNvOut = 0x80000000u;  // an offset past every descriptor's size
 
-// codes chunk h of tile row r sits at 32 r + 16 (h ^ ((r >> 3) & 1)); bf16 chunk c
-// of A row r at 128 r + 16 (c ^ ((r >> 1) & 7)): conflict-free 16-lane reads
-template <bool A_FP4>
+// Copy-lane assignment.  16-byte chunk q of a wave's share: codes chunk h of row
+// r lands at 32 r + 16 (h ^ ((r >> 3) & 1)); bf16 chunk c of A row r at
+// 128 r + 16 (c ^ ((r >> 1) & 7)): conflict-free 16-lane fragment reads.  Scale
+// word of row r at 4 r; with fewer than 256 rows the upper waves repeat the lower
+// waves' rows (same bytes to the same place).
+template <bool A_FP4, int L, int TM, int TN>
 __device__ __forceinline__ void nv_ring_dma(uint8_t *st, const NvRingDma &d, int k0, int wave)
 {
-    using C = NvRing<A_FP4>;
+    using S = NvTile<A_FP4, L, TM, TN>;
     if constexpr (A_FP4) {
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (nv_lds_void *)(st + C::kA + 16 * (128 * wave + 64 * i)), 16,
-                                                     (int)d.a[i], k0 / 2, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ras, (nv_lds_void *)(st + C::kAS + 4 * 64 * wave), 4, (int)d.as,
-                                                 k0 / 16, 0, 0);
+        for (int i = 0; i < S::nA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                d.ra, (nv_lds_void *)(st + S::kA + 16 * (64 * S::nA * wave + 64 * i)), 16, (int)d.a[i], k0 / 2, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ras, (nv_lds_void *)(st + S::kAS + 256 * (wave % (TM / 64))), 4,
+                                                 (int)d.as, k0 / 16, 0, 0);
     } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (nv_lds_void *)(st + C::kA + 16 * (512 * wave + 64 * i)), 16,
-                                                     (int)d.a[i], 2 * k0, 0, 0);
+        for (int i = 0; i < S::nA; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                d.ra, (nv_lds_void *)(st + S::kA + 16 * (64 * S::nA * wave + 64 * i)), 16, (int)d.a[i], 2 * k0, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (nv_lds_void *)(st + C::kW + 16 * (128 * wave + 64 * i)), 16,
-                                                 (int)d.w[i], k0 / 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rws, (nv_lds_void *)(st + C::kWS + 4 * 64 * wave), 4, (int)d.ws,
-                                             k0 / 16, 0, 0);
+    for (int i = 0; i < S::nW; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            d.rw, (nv_lds_void *)(st + S::kW + 16 * (64 * S::nW * wave + 64 * i)), 16, (int)d.w[i], k0 / 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rws, (nv_lds_void *)(st + S::kWS + 256 * (wave % (TN / 64))), 4,
+                                             (int)d.ws, k0 / 16, 0, 0);
 }
-
-// Four bf16 fragments (steps ks = 0..3) of one packed row: 16 code bytes and the
-// two E4M3 bytes of the lane's K half.
-__device__ __forceinline__ void nv_frags_fp4(const uint8_t *codes, const uint8_t *scl, bf16x8 (&f)[4])
-{
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    const u32x4 c = *reinterpret_cast<const u32x4 *>(codes);
-    const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)*reinterpret_cast<const uint16_t *>(scl), false);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) f[ks] = as_bf16x8(dq8_bf16(c[ks], ks < 2 ? bs[0] : bs[1]));
-}
-
-// Wave layout of the 256 x 256 tile: L = 0 splits it 2 x 2 (128 x 128 per wave),
-// L = 1 splits N four ways (wave w: all 256 rows x columns 64 w .. 64 w + 63), so
-// no two waves widen the same W rows.
-template <int L>
-struct NvWaves {
-    static constexpr int NI = L ? 8 : 4;  // 32-row MFMA tiles per wave
-    static constexpr int NJ = L ? 2 : 4;  // 32-column MFMA tiles per wave
-    __device__ static int row0(int wave) { return L ? 0 : (wave >> 1) * 128; }
-    __device__ static int col0(int wave) { return L ? 64 * wave : (wave & 1) * 128; }
-};
 
 // Per-wave operand state.  A stage's packed rows (16 code bytes and two E4M3
 // scales per lane and row) are read from LDS once; each MFMA step ks widens its
 // fragments from them (bf16 A fragments are read from LDS per step instead).
 // Rows r0 + 32 i + l % 32 share the swizzle terms of l % 32, so every row's LDS
 // offset is a per-lane base plus a constant.
-template <bool A_FP4, int L>
+template <bool A_FP4, int L, int TM, int TN>
 struct NvPipe {
-    static constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
-    static constexpr int NA = A_FP4 ? NI : 1;
+    using S = NvTile<A_FP4, L, TM, TN>;
+    static constexpr int NA = A_FP4 ? S::NI : 1;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
-    u32x4 wc[NJ];
-    f32x2 wsc[NJ];
+    u32x4 wc[S::NJ];
+    f32x2 wsc[S::NJ];
     u32x4 ac[NA];
     f32x2 asc[NA];
     uint32_t wb, wsb;  // W codes / scales of MFMA tile 0
@@ -869,11 +870,12 @@ struct NvPipe {
     uint32_t ak[4];    // W4A16: swizzled 16-byte chunk of step ks in a bf16 A row
 };
 
-template <bool A_FP4, int L>
-__device__ __forceinline__ void nv_pipe_init(NvPipe<A_FP4, L> &p, int wave, int lane)
+template <bool A_FP4, int L, int TM, int TN>
+__device__ __forceinline__ void nv_pipe_init(NvPipe<A_FP4, L, TM, TN> &p, int wave, int lane)
 {
+    using S = NvTile<A_FP4, L, TM, TN>;
     const int half = lane >> 5, l = lane & 31;
-    const int r0 = NvWaves<L>::row0(wave), c0 = NvWaves<L>::col0(wave);
+    const int r0 = S::row0(wave), c0 = S::col0(wave);
     const int hsw = 16 * (half ^ ((l >> 3) & 1));
     p.wb = 32 * (c0 + l) + hsw;
     p.wsb = 4 * (c0 + l) + 2 * half;
@@ -889,71 +891,75 @@ __device__ __forceinline__ void nv_pipe_init(NvPipe<A_FP4, L> &p, int wave, int 
 }
 
 // read the stage's packed rows (codes + scales) into registers
-template <bool A_FP4, int L>
-__device__ __forceinline__ void nv_pipe_raw(NvPipe<A_FP4, L> &p, const uint8_t *st)
+template <bool A_FP4, int L, int TM, int TN>
+__device__ __forceinline__ void nv_pipe_raw(NvPipe<A_FP4, L, TM, TN> &p, const uint8_t *st)
 {
-    using C = NvRing<A_FP4>;
+    using S = NvTile<A_FP4, L, TM, TN>;
 #pragma unroll
-    for (int j = 0; j < NvPipe<A_FP4, L>::NJ; ++j) {
-        p.wc[j] = *reinterpret_cast<const u32x4 *>(st + C::kW + p.wb + 1024 * j);
+    for (int j = 0; j < S::NJ; ++j) {
+        p.wc[j] = *reinterpret_cast<const u32x4 *>(st + S::kW + p.wb + 1024 * j);
         p.wsc[j] = __builtin_amdgcn_cvt_pk_f32_fp8(
-            (int)*reinterpret_cast<const uint16_t *>(st + C::kWS + p.wsb + 128 * j), false);
+            (int)*reinterpret_cast<const uint16_t *>(st + S::kWS + p.wsb + 128 * j), false);
     }
     if constexpr (A_FP4) {
 #pragma unroll
-        for (int i = 0; i < NvPipe<A_FP4, L>::NI; ++i) {
-            p.ac[i] = *reinterpret_cast<const u32x4 *>(st + C::kA + p.ab + 1024 * i);
+        for (int i = 0; i < S::NI; ++i) {
+            p.ac[i] = *reinterpret_cast<const u32x4 *>(st + S::kA + p.ab + 1024 * i);
             p.asc[i] = __builtin_amdgcn_cvt_pk_f32_fp8(
-                (int)*reinterpret_cast<const uint16_t *>(st + C::kAS + p.asb + 128 * i), false);
+                (int)*reinterpret_cast<const uint16_t *>(st + S::kAS + p.asb + 128 * i), false);
         }
     }
 }
 
 // fragments of step ks: lane half h holds K = 32 h + 8 ks + [0, 8) of the stage
-template <bool A_FP4, int L, int KS>
-__device__ __forceinline__ void nv_pipe_frags(const NvPipe<A_FP4, L> &p, const uint8_t *st,
-                                              bf16x8 (&wf)[NvWaves<L>::NJ], bf16x8 (&af)[NvWaves<L>::NI])
+template <bool A_FP4, int L, int TM, int TN, int KS>
+__device__ __forceinline__ void nv_pipe_frags(const NvPipe<A_FP4, L, TM, TN> &p, const uint8_t *st,
+                                              bf16x8 (&wf)[NvTile<A_FP4, L, TM, TN>::NJ],
+                                              bf16x8 (&af)[NvTile<A_FP4, L, TM, TN>::NI])
 {
-    using C = NvRing<A_FP4>;
+    using S = NvTile<A_FP4, L, TM, TN>;
 #pragma unroll
-    for (int j = 0; j < NvWaves<L>::NJ; ++j)
+    for (int j = 0; j < S::NJ; ++j)
         wf[j] = as_bf16x8(dq8_bf16(p.wc[j][KS], KS < 2 ? p.wsc[j][0] : p.wsc[j][1]));
 #pragma unroll
-    for (int i = 0; i < NvWaves<L>::NI; ++i) {
+    for (int i = 0; i < S::NI; ++i) {
         if constexpr (A_FP4)
             af[i] = as_bf16x8(dq8_bf16(p.ac[i][KS], KS < 2 ? p.asc[i][0] : p.asc[i][1]));
         else
-            af[i] = *reinterpret_cast<const bf16x8 *>(st + C::kA + p.ab + p.ak[KS] + 4096 * i);
+            af[i] = *reinterpret_cast<const bf16x8 *>(st + S::kA + p.ab + p.ak[KS] + 4096 * i);
     }
 }
 
-template <int L>
-__device__ __forceinline__ void nv_pipe_mfma(f32x16 (&acc)[NvWaves<L>::NI][NvWaves<L>::NJ],
-                                             const bf16x8 (&wf)[NvWaves<L>::NJ], const bf16x8 (&af)[NvWaves<L>::NI])
+template <int NI, int NJ>
+__device__ __forceinline__ void nv_pipe_mfma(f32x16 (&acc)[NI][NJ], const bf16x8 (&wf)[NJ], const bf16x8 (&af)[NI])
 {
 #pragma unroll
-    for (int i = 0; i < NvWaves<L>::NI; ++i)
+    for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < NvWaves<L>::NJ; ++j)
+        for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
 }
 
-// Spread the 16 MFMAs of a step over the widening (NV VALU) and the reads (ND)
+// Spread the NM MFMAs of a step over the widening (NV VALU) and the reads (ND)
 // of the next step.  NR reads and NB copies (global-to-LDS) go out first, then P
 // MFMAs cover the latency of those reads before any VALU work uses them.
-template <int NV, int ND, int NR = 0, int NB = 0, int P = 0>
+template <int N, int NV, int ND, int T>
+__device__ __forceinline__ void nv_pipe_slot()
+{
+    constexpr int v = NV * (T + 1) / N - NV * T / N, r = ND * (T + 1) / N - ND * T / N;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);  // VALU
+    if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
+    if constexpr (T + 1 < N) nv_pipe_slot<N, NV, ND, T + 1>();
+}
+
+template <int NM, int NV, int ND, int NR = 0, int NB = 0, int P = 0>
 __device__ __forceinline__ void nv_pipe_interleave()
 {
-    constexpr int per = (NV + 15 - P) / (16 - P);
-    if (NR) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS read
-    if (NB) __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // VMEM read
-    if (P) __builtin_amdgcn_sched_group_barrier(0x008, P, 0);    // MFMA
-#pragma unroll
-    for (int t = P; t < 16; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        if (per) __builtin_amdgcn_sched_group_barrier(0x002, per, 0);  // VALU
-        if (ND && t % (16 / ND) == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    }
+    if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS read
+    if constexpr (NB > 0) __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // VMEM read
+    if constexpr (P > 0) __builtin_amdgcn_sched_group_barrier(0x008, P, 0);    // MFMA
+    nv_pipe_slot<NM - P, NV, ND, 0>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -964,70 +970,74 @@ __device__ __forceinline__ void nv_wait_vm()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// One stage t (in `cur`; stage t + 1 in `nxt`).  Entering, f holds step 0's
+// One stage t (in `cur`; stage t + 1 in `nxt`).  Entering, wf / af hold step 0's
 // fragments.  Steps 0-2 multiply while the next step's fragments are formed; then
 // the wave waits until its copies of stage t + 1 landed and its reads of `cur`
 // returned, and a barrier extends both to every wave, so `cur` is free: the copy
 // of stage t + 3 starts into it.  Step 3 multiplies while stage t + 1's packed
 // rows and step-0 fragments are read from `nxt`.  One basic block per stage.
-template <bool A_FP4, int L>
+template <bool A_FP4, int L, int TM, int TN>
 __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, int t, int nk, const NvRingDma &d,
-                                              const NvRingDma &dz, int wave, NvPipe<A_FP4, L> &p,
-                                              f32x16 (&acc)[NvWaves<L>::NI][NvWaves<L>::NJ],
-                                              bf16x8 (&wf)[NvWaves<L>::NJ], bf16x8 (&af)[NvWaves<L>::NI])
+                                              const NvRingDma &dz, int wave, NvPipe<A_FP4, L, TM, TN> &p,
+                                              f32x16 (&acc)[NvTile<A_FP4, L, TM, TN>::NI][NvTile<A_FP4, L, TM, TN>::NJ],
+                                              bf16x8 (&wf)[NvTile<A_FP4, L, TM, TN>::NJ],
+                                              bf16x8 (&af)[NvTile<A_FP4, L, TM, TN>::NI])
 {
-    constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
-    constexpr int NV = 16 * (NJ + (A_FP4 ? NI : 0));      // VALU per step's widening, about
-    constexpr int ND = A_FP4 ? 0 : NI;                     // DS reads per step
+    using S = NvTile<A_FP4, L, TM, TN>;
+    constexpr int NI = S::NI, NJ = S::NJ, NM = NI * NJ;
+    constexpr int NV = 16 * (NJ + (A_FP4 ? NI : 0));  // VALU per step's widening, about
+    constexpr int ND = A_FP4 ? 0 : NI;                // DS reads per step
+    constexpr int P = NM >= 8 ? 4 : 1;
     bf16x8 wf1[NJ], af1[NI];
-    nv_pipe_frags<A_FP4, L, 1>(p, cur, wf1, af1);
-    nv_pipe_mfma<L>(acc, wf, af);
-    nv_pipe_interleave<NV, ND>();
-    nv_pipe_frags<A_FP4, L, 2>(p, cur, wf, af);
-    nv_pipe_mfma<L>(acc, wf1, af1);
-    nv_pipe_interleave<NV, ND>();
-    nv_pipe_frags<A_FP4, L, 3>(p, cur, wf1, af1);
-    nv_pipe_mfma<L>(acc, wf, af);
-    nv_pipe_interleave<NV, ND>();
-    nv_wait_vm<NvRing<A_FP4>::kDma>();
+    nv_pipe_frags<A_FP4, L, TM, TN, 1>(p, cur, wf1, af1);
+    nv_pipe_mfma<NI, NJ>(acc, wf, af);
+    nv_pipe_interleave<NM, NV, ND>();
+    nv_pipe_frags<A_FP4, L, TM, TN, 2>(p, cur, wf, af);
+    nv_pipe_mfma<NI, NJ>(acc, wf1, af1);
+    nv_pipe_interleave<NM, NV, ND>();
+    nv_pipe_frags<A_FP4, L, TM, TN, 3>(p, cur, wf1, af1);
+    nv_pipe_mfma<NI, NJ>(acc, wf, af);
+    nv_pipe_interleave<NM, NV, ND>();
+    nv_wait_vm<S::kDma>();
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    nv_pipe_raw<A_FP4, L>(p, nxt);
-    nv_ring_dma<A_FP4>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
-    nv_pipe_frags<A_FP4, L, 0>(p, nxt, wf, af);
-    nv_pipe_mfma<L>(acc, wf1, af1);
-    nv_pipe_interleave<NV, ND, 2 * (A_FP4 ? NI + NJ : NJ), NvRing<A_FP4>::kDma, 4>();
+    nv_pipe_raw<A_FP4, L, TM, TN>(p, nxt);
+    nv_ring_dma<A_FP4, L, TM, TN>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
+    nv_pipe_frags<A_FP4, L, TM, TN, 0>(p, nxt, wf, af);
+    nv_pipe_mfma<NI, NJ>(acc, wf1, af1);
+    nv_pipe_interleave<NM, NV, ND, 2 * (A_FP4 ? NI + NJ : NJ), S::kDma, P>();
 }
 
 // Epilogue: lane l holds output row r0 + 32 i + l % 32, columns
 // c0 + 32 j + 8 g + 4 (l / 32) + 0..3 in slots 4 g .. 4 g + 3 of acc[i][j].  In
-// round rd, tile rows rd R + [0, R) go through `s0` and rows 128 + rd R + [0, R)
-// through `s1` (rows padded by 16 bytes), then leave as whole-row 16-byte stores.
-template <typename T, bool A_FP4, int L>
-__device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[NvWaves<L>::NI][NvWaves<L>::NJ],
-                                                 uint8_t *s0, uint8_t *s1, const NvGemmArgs &g, int m0, int n0,
-                                                 int wave, int lane, int tid)
+// round rd, tile rows rd R + [0, R) go through `s0` and rows H + rd R + [0, R)
+// through `s1` (H = TM / 2), then leave as whole-row 16-byte stores.
+template <typename T, bool A_FP4, int L, int TM, int TN>
+__device__ __forceinline__ void nv_ring_epilogue(
+    const f32x16 (&acc)[NvTile<A_FP4, L, TM, TN>::NI][NvTile<A_FP4, L, TM, TN>::NJ], uint8_t *s0, uint8_t *s1,
+    const NvGemmArgs &g, int m0, int n0, int wave, int lane, int tid)
 {
-    constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
+    using S = NvTile<A_FP4, L, TM, TN>;
+    constexpr int NI = S::NI, NJ = S::NJ, H = S::H;
     constexpr int es = (int)sizeof(T);
-    constexpr int pitch = 256 * es + 16;
-    constexpr int R = es == 2 ? 64 : 32;      // rows per staging buffer per round
-    constexpr int kPer = 16 / es, kChunks = 256 / kPer;
+    constexpr int pitch = S::epi_pitch(es);
+    constexpr int R = S::epi_rows(es);
+    constexpr int kPer = 16 / es, kChunks = TN / kPer;
+    static_assert(R * pitch <= S::kStage, "epilogue staging");
     const int M = (int)g.M, N = (int)g.N;
     const float wt = g.w_tscale[0];
-    const int r0 = NvWaves<L>::row0(wave), c0 = NvWaves<L>::col0(wave);
+    const int r0 = S::row0(wave), c0 = S::col0(wave);
 #pragma unroll
-    for (int rd = 0; rd < 128 / R; ++rd) {
+    for (int rd = 0; rd < H / R; ++rd) {
 #pragma unroll
         for (int i = 0; i < NI; ++i) {
             // rows of MFMA tile i: r0 + 32 i + [0, 32), one staging buffer, one round
-            const int rr = L ? (32 * i) % 128 : 32 * i;  // row within its half of the tile
+            const int rr = L ? (32 * i) % H : 32 * i;  // row within its half of the tile
             if (rr / R != rd) continue;
-            const int row_t = r0 + 32 * i + (lane & 31);
-            const int m = m0 + row_t;
+            const int m = m0 + r0 + 32 * i + (lane & 31);
             float sc = wt;
             if (A_FP4) sc = (m < M ? g.a_tscale[g.a_per_row ? m : 0] : 0.f) * wt;
-            uint8_t *buf = (L ? 32 * i : r0) >= 128 ? s1 : s0;
+            uint8_t *buf = (L ? 32 * i : r0) >= H ? s1 : s0;
             uint8_t *row = buf + (rr - rd * R + (lane & 31)) * pitch;
 #pragma unroll
             for (int j = 0; j < NJ; ++j) {
@@ -1051,7 +1061,7 @@ __device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[NvWaves<L>:
 #pragma unroll
         for (int half = 0; half < 2; ++half) {
             const uint8_t *st = half ? s1 : s0;
-            const int mrow0 = m0 + 128 * half + rd * R;
+            const int mrow0 = m0 + H * half + rd * R;
             for (int q = tid; q < R * kChunks; q += 256) {
                 const int r = q / kChunks, ch = q % kChunks;
                 const int m = mrow0 + r, n = n0 + ch * kPer;
@@ -1073,21 +1083,21 @@ __device__ __forceinline__ void nv_ring_epilogue(const f32x16 (&acc)[NvWaves<L>:
     }
 }
 
-template <bool A_FP4, int L, typename OutT>
+template <bool A_FP4, int L, typename OutT, int TM, int TN>
 __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 {
-    using C = NvRing<A_FP4>;
-    constexpr int NI = NvWaves<L>::NI, NJ = NvWaves<L>::NJ;
-    __shared__ __align__(16) uint8_t s0[C::kStage];
-    __shared__ __align__(16) uint8_t s1[C::kStage];
-    __shared__ __align__(16) uint8_t s2[C::kStage];
+    using S = NvTile<A_FP4, L, TM, TN>;
+    constexpr int NI = S::NI, NJ = S::NJ;
+    __shared__ __align__(16) uint8_t s0[S::kStage];
+    __shared__ __align__(16) uint8_t s1[S::kStage];
+    __shared__ __align__(16) uint8_t s2[S::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
-    const int tiles_m = (M + BM - 1) / BM, tiles_n = (N + BN - 1) / BN;
+    const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
     int tm, tn;
     tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * BM, n0 = tn * BN;
+    const int m0 = tm * TM, n0 = tn * TN;
     const int nk = K / kRK;
 
     NvRingDma d, dz;
@@ -1097,31 +1107,31 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
         d.ra = nv_rsrc(g.a_codes, (int64_t)M * (K / 2));
         d.ras = nv_rsrc(g.a_scales, (int64_t)M * (K / 16));
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int q = 128 * wave + 64 * i + lane;
+        for (int i = 0; i < S::nA; ++i) {
+            const int q = 64 * S::nA * wave + 64 * i + lane;
             const int r = q >> 1, h = (q & 1) ^ ((r >> 3) & 1);
             d.a[i] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
         }
-        const int qa = 64 * wave + lane;
+        const int qa = (64 * wave + lane) % TM;
         d.as = m0 + qa < M ? (uint32_t)(m0 + qa) * (uint32_t)(K / 16) : kNvOut;
     } else {
         d.ra = nv_rsrc(g.a, ((int64_t)(M - 1) * g.lda + K) * 2);
         d.ras = d.ra;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int q = 512 * wave + 64 * i + lane;
+        for (int i = 0; i < S::nA; ++i) {
+            const int q = 64 * S::nA * wave + 64 * i + lane;
             const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
             d.a[i] = m0 + r < M ? (uint32_t)(((int64_t)(m0 + r) * g.lda + 8 * c) * 2) : kNvOut;
         }
         d.as = kNvOut;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = 128 * wave + 64 * i + lane;
+    for (int i = 0; i < S::nW; ++i) {
+        const int q = 64 * S::nW * wave + 64 * i + lane;
         const int r = q >> 1, h = (q & 1) ^ ((r >> 3) & 1);
         d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
     }
-    const int qw = 64 * wave + lane;
+    const int qw = (64 * wave + lane) % TN;
     d.ws = n0 + qw < N ? (uint32_t)(n0 + qw) * (uint32_t)(K / 16) : kNvOut;
     dz = d;
     dz.ra = nv_rsrc(g.a_codes ? (const void *)g.a_codes : (const void *)g.a, 0);
@@ -1135,25 +1145,25 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
-    NvPipe<A_FP4, L> p;
+    NvPipe<A_FP4, L, TM, TN> p;
     nv_pipe_init(p, wave, lane);
-    nv_ring_dma<A_FP4>(s0, d, 0, wave);
-    nv_ring_dma<A_FP4>(s1, nk > 1 ? d : dz, nk > 1 ? kRK : 0, wave);
-    nv_ring_dma<A_FP4>(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kRK : 0, wave);
-    nv_wait_vm<2 * C::kDma>();
+    nv_ring_dma<A_FP4, L, TM, TN>(s0, d, 0, wave);
+    nv_ring_dma<A_FP4, L, TM, TN>(s1, nk > 1 ? d : dz, nk > 1 ? kRK : 0, wave);
+    nv_ring_dma<A_FP4, L, TM, TN>(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kRK : 0, wave);
+    nv_wait_vm<2 * S::kDma>();
     asm volatile("s_barrier" ::: "memory");
     bf16x8 wf[NJ], af[NI];
-    nv_pipe_raw<A_FP4, L>(p, s0);
-    nv_pipe_frags<A_FP4, L, 0>(p, s0, wf, af);
+    nv_pipe_raw<A_FP4, L, TM, TN>(p, s0);
+    nv_pipe_frags<A_FP4, L, TM, TN, 0>(p, s0, wf, af);
     for (int t = 0; t < nk; t += 3) {
-        nv_pipe_stage<A_FP4, L>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
-        nv_pipe_stage<A_FP4, L>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
-        nv_pipe_stage<A_FP4, L>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<A_FP4, L, TM, TN>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<A_FP4, L, TM, TN>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<A_FP4, L, TM, TN>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    nv_ring_epilogue<OutT, A_FP4, L>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e);
+    nv_ring_epilogue<OutT, A_FP4, L, TM, TN>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e);
 }
 
 constexpr size_t kGemmLds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);  // 128 KiB
@@ -1171,6 +1181,46 @@ static fp4_status launch_prefill(const NvGemmArgs &g, hipStream_t st)
     const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
     hipLaunchKernelGGL((k_nv_gemm<A_FP4, ALIGNED>), dim3(tiles), dim3(256), kGemmLds, st, g);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+template <bool A_FP4, int L, int TM, int TN>
+static void launch_ring(const NvGemmArgs &g, hipStream_t st)
+{
+    const int tiles = (int)(((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN));
+    if (g.c_bf16)
+        hipLaunchKernelGGL((k_nv_gemm_ring<A_FP4, L, __bf16, TM, TN>), dim3(tiles), dim3(256), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_nv_gemm_ring<A_FP4, L, float, TM, TN>), dim3(tiles), dim3(256), 0, st, g);
+}
+
+// 256 x 256 tiles; when the last round of tiles would leave most CUs idle, the
+// tile columns of that round go to a second launch of 128 x 128 tiles, provided
+// they fit in one round (for M = 4096, N = 17408: 1024 large tiles, four full
+// rounds on 256 CUs, then 256 small tiles for the last 1024 columns).
+template <bool A_FP4, int L>
+static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
+{
+    const int64_t cus = device_cu_count();
+    const int64_t tm = (g.M + 255) / 256, tn = (g.N + 255) / 256, tiles = tm * tn;
+    const int64_t rem = tiles % cus;
+    if (tiles > cus && rem != 0 && rem <= cus / 2) {
+        const int64_t cols = tiles / cus * cus / tm;  // 256-wide column blocks kept on large tiles
+        const int64_t n_split = cols * 256;
+        const int64_t small = ((g.M + 127) / 128) * ((g.N - n_split + 127) / 128);
+        if (cols >= 1 && n_split < g.N && small <= cus) {
+            NvGemmArgs big = g;
+            big.N = n_split;
+            launch_ring<A_FP4, L, 256, 256>(big, st);
+            NvGemmArgs rest = g;
+            rest.N = g.N - n_split;
+            rest.w_codes = g.w_codes + n_split * (g.K / 2);
+            rest.w_scales = g.w_scales + n_split * (g.K / 16);
+            rest.c = reinterpret_cast<uint8_t *>(g.c) + n_split * (g.c_bf16 ? 2 : 4);
+            launch_ring<A_FP4, 0, 128, 128>(rest, st);
+            return;
+        }
+    }
+    launch_ring<A_FP4, L, 256, 256>(g, st);
 }
 
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
@@ -1210,14 +1260,8 @@ fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
     const bool ring = aligned && g.M * g.K * 2 < (int64_t(1) << 31) && g.N * (g.K / 2) < (int64_t(1) << 31) &&
                       (g.a_codes || g.M * g.lda * 2 < (int64_t(1) << 31));
     if (ring) {
-        const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
-        if (g.a_codes) {
-            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<true, 0, __bf16>), dim3(tiles), dim3(256), 0, st, g);
-            else hipLaunchKernelGGL((k_nv_gemm_ring<true, 0, float>), dim3(tiles), dim3(256), 0, st, g);
-        } else {
-            if (g.c_bf16) hipLaunchKernelGGL((k_nv_gemm_ring<false, kNvL16, __bf16>), dim3(tiles), dim3(256), 0, st, g);
-            else hipLaunchKernelGGL((k_nv_gemm_ring<false, kNvL16, float>), dim3(tiles), dim3(256), 0, st, g);
-        }
+        if (g.a_codes) launch_ring_split<true, 0>(g, st);
+        else launch_ring_split<false, kNvL16>(g, st);
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
     if (g.a_codes)

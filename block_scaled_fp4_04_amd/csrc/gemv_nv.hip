@@ -294,7 +294,7 @@ static void launch_gemv(const GemvArgs &g, unsigned grid, hipStream_t st)
     hipLaunchKernelGGL((k_nv_gemv_dec<S, D, false, kGvWaves>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
 }
 
-static int cu_count()
+int device_cu_count()
 {
     static int cache[64] = {0};  // per device; benign race: every writer stores the same value
     int dev = 0;
@@ -313,7 +313,7 @@ fp4_status launch_nvfp4_gemv_decode(GemvArgs g, hipStream_t st)
     const int S = (nseg + kGvWaves - 1) / kGvWaves;
     // one workgroup per CU with equal row counts; more workgroups only when a
     // CU's share exceeds kGvMaxT tiles
-    int64_t G = std::min<int64_t>(cu_count(), (g.N + 15) / 16);
+    int64_t G = std::min<int64_t>(device_cu_count(), (g.N + 15) / 16);
     int64_t R = (g.N + G - 1) / G;
     if (R > 16 * kGvMaxT) {
         G = (g.N + 16 * kGvMaxT - 1) / (16 * kGvMaxT);

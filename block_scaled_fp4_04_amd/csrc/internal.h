@@ -53,6 +53,9 @@ struct NvGemmArgs {
 
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st);
 
+// compute units of the current device (cached per device; 256 if unknown)
+int device_cu_count();
+
 // W4A16 decode GEMV over weights in the decode layout (gemv_nv.hip)
 struct GemvArgs {
     const uint16_t *a;        // bf16 [M][lda]

@@ -54,6 +54,8 @@ SHAPES = [
     (257, 1000, 2048),
     # prefill with K a multiple of 64: one to five 64-wide K stages, ragged M and N
     (40, 70, 64), (300, 300, 128), (257, 513, 192), (513, 260, 320),
+    # 258 tiles of 256 x 256: the last 232 columns run as 128 x 128 tiles in a second launch
+    (500, 33000, 128),
 ]
 
 
@@ -72,7 +74,7 @@ def test_w4a16(M, N, K, out):
 
 @pytest.mark.parametrize("M,N,K", [(1, 48, 64), (4, 517, 5120), (16, 300, 1040), (17, 260, 1040),
                                    (300, 520, 5120), (513, 130, 96),
-                                   (40, 70, 64), (257, 513, 192), (513, 260, 320)])
+                                   (40, 70, 64), (257, 513, 192), (513, 260, 320), (500, 33000, 128)])
 @pytest.mark.parametrize("a_mode", ["row", "tensor"])
 def test_w4a4(M, N, K, a_mode):
     log(f"gemm_w4a4 M={M} N={N} K={K} a_mode={a_mode}")
