@@ -770,9 +770,9 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 //  - MFMA computes W_j A_i^T, so each lane ends with 4 consecutive output columns
 //    of one row, which the epilogue stages through LDS into whole-row stores.
 // Stages are three separate LDS objects (the compiler then never waits for a DMA
-// into one before reading another), rotated by unrolling the K loop 3 times;
-// stages past K are copied through size-0 descriptors (zeros, nothing read) and
-// add +0 to the accumulators.
+// into one before reading another), rotated by unrolling the K loop 3 times, with
+// the last K % 3 stages peeled; copies of stages past K go through size-0
+// descriptors (zeros, nothing read).
 constexpr int kRK = 64;  // K elements per stage
 constexpr int kNvL16 = 1;  // wave layout of the W4A16 256 x 256 tile (see NvTile)
 
@@ -1155,11 +1155,15 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
     bf16x8 wf[NJ], af[NI];
     nv_pipe_raw<A_FP4, L, TM, TN>(p, s0);
     nv_pipe_frags<A_FP4, L, TM, TN, 0>(p, s0, wf, af);
-    for (int t = 0; t < nk; t += 3) {
+    const int nfull = nk - nk % 3;
+    for (int t = 0; t < nfull; t += 3) {
         nv_pipe_stage<A_FP4, L, TM, TN>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
         nv_pipe_stage<A_FP4, L, TM, TN>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
         nv_pipe_stage<A_FP4, L, TM, TN>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
     }
+    // the last one or two stages (no copies left to start)
+    if (nk % 3 >= 1) nv_pipe_stage<A_FP4, L, TM, TN>(s0, s1, nfull, nk, d, dz, wave, p, acc, wf, af);
+    if (nk % 3 == 2) nv_pipe_stage<A_FP4, L, TM, TN>(s1, s2, nfull + 1, nk, d, dz, wave, p, acc, wf, af);
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
