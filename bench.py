@@ -149,9 +149,12 @@ def main():
             for M in wl.M}
     outs = {M: torch.empty(M, N, dtype=torch.bfloat16, device=dev) for M in wl.M}
 
+    # every GEMV call reads its own weight copy (12 x 50 MB > the 256 MB Infinity
+    # Cache), as the distinct layers of a decode step would: no call finds its
+    # weights in a cache
     def step(i):
-        for M in wl.M:
-            fp4.gemm_w4a16_decode(acts[M], dcopies[i % R], out=outs[M])
+        for j, M in enumerate(wl.M):
+            fp4.gemm_w4a16_decode(acts[M], dcopies[(len(wl.M) * i + j) % R], out=outs[M])
 
     # ------------------------------------------------------------ the step --
     for i in range(args.warmup):

@@ -65,6 +65,9 @@ def _declare(L):
         "mxfp4_gemm_w4a4_workspace": (sz, [i64, i64]),
         "mxfp4_gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
         "mxfp4_gemm_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
+        "mxfp4_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, p, i32, i64, p]),
+        "mxfp4_pack_decode": (i32, [p, p, i64, i64, p, p, p]),
+        "mxfp4_gemm_w4a16_decode": (i32, [p, i64, i64, i64, p, p, i64, p, i32, i64, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -371,4 +374,57 @@ def mxfp4_gemm_prequant(a: PackedMXFP4, w: PackedMXFP4, dtype=torch.bfloat16,
     _check(L.mxfp4_gemm_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
                                  _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
                                  _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a16(a: torch.Tensor, w: PackedMXFP4, dtype=torch.bfloat16,
+                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """C = A . W^T with bf16 A [M, K] and MXFP4 W [N, K] (K % 128 == 0)."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("mxfp4_gemm_w4a16 takes bfloat16 activations")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    _check(L.mxfp4_gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
+                              _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+@dataclasses.dataclass
+class DecodeMXFP4:
+    """An MXFP4 weight [rows, cols] in the decode layout (see mxfp4_pack_decode):
+    codes [cols/128, rows, 64], scales [cols/128, rows, 4]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+
+
+def mxfp4_pack_decode(w: PackedMXFP4, out: DecodeMXFP4 | None = None) -> DecodeMXFP4:
+    """Rewrite an MXFP4 weight into the decode layout (segment-major)."""
+    L = lib()
+    N, K = w.rows, w.cols
+    if out is None:
+        dev = w.codes.device
+        out = DecodeMXFP4(torch.empty(K // 128, N, 64, dtype=torch.uint8, device=dev),
+                          torch.empty(K // 128, N, 4, dtype=torch.uint8, device=dev), N, K)
+    _check(L.mxfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
+                               _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a16_decode(a: torch.Tensor, w: DecodeMXFP4, dtype=torch.bfloat16,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """Decode GEMV C = A . W^T for bf16 A [M <= 16, K] and an MXFP4 W in the decode layout."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("mxfp4_gemm_w4a16_decode takes bfloat16 activations")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    _check(L.mxfp4_gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
+                                     _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out

@@ -177,7 +177,7 @@ fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
     FP4_TRY(check_packed(codes, scales));
     FP4_TRY(check_packed(codes_p, scales_p));
     FP4_TRY(check_device());
-    return launch_nvfp4_pack_decode(codes, scales, N, K, codes_p, scales_p, stream);
+    return launch_pack_decode(codes, scales, N, K, codes_p, scales_p, false, stream);
 }
 
 fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
@@ -202,7 +202,65 @@ fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, c
     g.c = c;
     g.c_bf16 = ct == FP4_BF16;
     g.ldc = ldc;
-    return launch_nvfp4_gemv_decode(g, stream);
+    return launch_gemv_decode(g, stream);
+}
+
+fp4_status mxfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                             uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream)
+{
+    if (N <= 0 || K <= 0 || K % 128 != 0 || N > INT32_MAX / 2 || K > INT32_MAX / 2) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(codes, scales));
+    FP4_TRY(check_packed(codes_p, scales_p));
+    FP4_TRY(check_device());
+    return launch_pack_decode(codes, scales, N, K, codes_p, scales_p, true, stream);
+}
+
+fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
+                                   const uint8_t *w_scales_p, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                                   hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    if (M > 16 || K > 8192) return FP4_ERR_SHAPE;
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    FP4_TRY(check_packed(w_codes_p, w_scales_p));
+    FP4_TRY(check_device());
+    GemvArgs g{};
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    g.w_codes = w_codes_p;
+    g.w_scales = w_scales_p;
+    g.w_tscale = nullptr;
+    g.M = (int)M;
+    g.N = (int)N;
+    g.K = (int)K;
+    g.mx = 1;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_gemv_decode(g, stream);
+}
+
+fp4_status mxfp4_gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes,
+                            const uint8_t *w_scales, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                            hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    FP4_TRY(check_device());
+    NvGemmArgs g{};
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.w_tscale = nullptr;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_mxfp4_gemm_w4a16(g, stream);
 }
 
 void gemm_w4a4_workspace_offsets(int64_t M, int64_t K, size_t *codes_off, size_t *scales_off,

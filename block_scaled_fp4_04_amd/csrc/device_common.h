@@ -134,6 +134,22 @@ __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v)
     return r;
 }
 
+// ------------------------------------------------ MXFP4 weight dequant -----
+
+// 8 E2M1 codes (nibble i = element i) times a power-of-two block scale -> 8 bf16.
+// `scale` is the fp32 whose exponent field holds the E8M0 byte (byte << 23); the
+// scaled conversion applies exactly that power of two, and E2M1 times a power of
+// two is exact in bf16.
+__device__ __forceinline__ bf16x8 e2m1x8_bf16_pow2(uint32_t codes, float scale)
+{
+    typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+    const bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    const bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    const bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    const bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    return bf16x8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
 
 // E4M3FN byte (sign clear) -> fp32: the byte placed at fp32 bit 20 reads as
 // 2^(e-127) (1 + m/8) (or the denormal m * 2^-129 when e == 0); times 2^120 that

@@ -774,6 +774,9 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 // the last K % 3 stages peeled; copies of stages past K go through size-0
 // descriptors (zeros, nothing read).
 constexpr int kRK = 64;  // K elements per stage
+// Operand formats of the ring kernel (template parameter F): W4A16 with NVFP4
+// weights, W4A4 with NVFP4 on both sides, W4A16 with MXFP4 weights.
+constexpr int kFmtNv16 = 0, kFmtNv44 = 1, kFmtMx16 = 2;
 constexpr int kNvL16 = 1;  // wave layout of the W4A16 256 x 256 tile (see NvTile)
 
 // Tile geometry.  Wave layout L = 0 splits the tile 2 x 2; L = 1 splits N four
@@ -826,10 +829,11 @@ constexpr uint32_t kNvOut = 0x80000000u;  // an offset past every descriptor's s
 // 128 r + 16 (c ^ ((r >> 1) & 7)): conflict-free 16-lane fragment reads.  Scale
 // word of row r at 4 r; with fewer than 256 rows the upper waves repeat the lower
 // waves' rows (same bytes to the same place).
-template <bool A_FP4, int L, int TM, int TN>
+template <int F, int L, int TM, int TN>
 __device__ __forceinline__ void nv_ring_dma(uint8_t *st, const NvRingDma &d, int k0, int wave)
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
+    constexpr bool A_FP4 = F == kFmtNv44;
     if constexpr (A_FP4) {
 #pragma unroll
         for (int i = 0; i < S::nA; ++i)
@@ -847,8 +851,12 @@ __device__ __forceinline__ void nv_ring_dma(uint8_t *st, const NvRingDma &d, int
     for (int i = 0; i < S::nW; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             d.rw, (nv_lds_void *)(st + S::kW + 16 * (64 * S::nW * wave + 64 * i)), 16, (int)d.w[i], k0 / 2, 0, 0);
+    // NVFP4: the row's 4 E4M3 bytes of the stage.  MXFP4: the aligned dword holding
+    // the row's 2 E8M0 bytes of the stage (the two bytes of stage pair t / 2;
+    // K % 128 == 0 keeps it inside the row).
+    const int ks_off = F == kFmtMx16 ? ((k0 / kRK) & ~1) * 2 : k0 / 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rws, (nv_lds_void *)(st + S::kWS + 256 * (wave % (TN / 64))), 4,
-                                             (int)d.ws, k0 / 16, 0, 0);
+                                             (int)d.ws, ks_off, 0, 0);
 }
 
 // Per-wave operand state.  A stage's packed rows (16 code bytes and two E4M3
@@ -856,10 +864,10 @@ __device__ __forceinline__ void nv_ring_dma(uint8_t *st, const NvRingDma &d, int
 // fragments from them (bf16 A fragments are read from LDS per step instead).
 // Rows r0 + 32 i + l % 32 share the swizzle terms of l % 32, so every row's LDS
 // offset is a per-lane base plus a constant.
-template <bool A_FP4, int L, int TM, int TN>
+template <int F, int L, int TM, int TN>
 struct NvPipe {
-    using S = NvTile<A_FP4, L, TM, TN>;
-    static constexpr int NA = A_FP4 ? S::NI : 1;
+    using S = NvTile<F == 1, L, TM, TN>;
+    static constexpr int NA = F == kFmtNv44 ? S::NI : 1;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     u32x4 wc[S::NJ];
     f32x2 wsc[S::NJ];
@@ -870,16 +878,16 @@ struct NvPipe {
     uint32_t ak[4];    // W4A16: swizzled 16-byte chunk of step ks in a bf16 A row
 };
 
-template <bool A_FP4, int L, int TM, int TN>
-__device__ __forceinline__ void nv_pipe_init(NvPipe<A_FP4, L, TM, TN> &p, int wave, int lane)
+template <int F, int L, int TM, int TN>
+__device__ __forceinline__ void nv_pipe_init(NvPipe<F, L, TM, TN> &p, int wave, int lane)
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
     const int half = lane >> 5, l = lane & 31;
     const int r0 = S::row0(wave), c0 = S::col0(wave);
     const int hsw = 16 * (half ^ ((l >> 3) & 1));
     p.wb = 32 * (c0 + l) + hsw;
-    p.wsb = 4 * (c0 + l) + 2 * half;
-    if (A_FP4) {
+    p.wsb = 4 * (c0 + l) + (F == kFmtMx16 ? half : 2 * half);
+    if (F == kFmtNv44) {
         p.ab = 32 * (r0 + l) + hsw;
         p.asb = 4 * (r0 + l) + 2 * half;
     } else {
@@ -891,17 +899,25 @@ __device__ __forceinline__ void nv_pipe_init(NvPipe<A_FP4, L, TM, TN> &p, int wa
 }
 
 // read the stage's packed rows (codes + scales) into registers
-template <bool A_FP4, int L, int TM, int TN>
-__device__ __forceinline__ void nv_pipe_raw(NvPipe<A_FP4, L, TM, TN> &p, const uint8_t *st)
+// (t: the stage's index; MXFP4 picks its E8M0 byte pair by t's parity)
+template <int F, int L, int TM, int TN>
+__device__ __forceinline__ void nv_pipe_raw(NvPipe<F, L, TM, TN> &p, const uint8_t *st, int t)
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
 #pragma unroll
     for (int j = 0; j < S::NJ; ++j) {
         p.wc[j] = *reinterpret_cast<const u32x4 *>(st + S::kW + p.wb + 1024 * j);
-        p.wsc[j] = __builtin_amdgcn_cvt_pk_f32_fp8(
-            (int)*reinterpret_cast<const uint16_t *>(st + S::kWS + p.wsb + 128 * j), false);
+        if constexpr (F == kFmtMx16) {
+            // E8M0 byte e of the lane's 32-element block -> the fp32 2^(e - 127) the
+            // scaled conversion takes its exponent from
+            const uint32_t e = st[S::kWS + p.wsb + 2 * (t & 1) + 128 * j];
+            p.wsc[j][0] = __uint_as_float(e << 23);
+        } else {
+            p.wsc[j] = __builtin_amdgcn_cvt_pk_f32_fp8(
+                (int)*reinterpret_cast<const uint16_t *>(st + S::kWS + p.wsb + 128 * j), false);
+        }
     }
-    if constexpr (A_FP4) {
+    if constexpr (F == kFmtNv44) {
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             p.ac[i] = *reinterpret_cast<const u32x4 *>(st + S::kA + p.ab + 1024 * i);
@@ -912,18 +928,22 @@ __device__ __forceinline__ void nv_pipe_raw(NvPipe<A_FP4, L, TM, TN> &p, const u
 }
 
 // fragments of step ks: lane half h holds K = 32 h + 8 ks + [0, 8) of the stage
-template <bool A_FP4, int L, int TM, int TN, int KS>
-__device__ __forceinline__ void nv_pipe_frags(const NvPipe<A_FP4, L, TM, TN> &p, const uint8_t *st,
-                                              bf16x8 (&wf)[NvTile<A_FP4, L, TM, TN>::NJ],
-                                              bf16x8 (&af)[NvTile<A_FP4, L, TM, TN>::NI])
+template <int F, int L, int TM, int TN, int KS>
+__device__ __forceinline__ void nv_pipe_frags(const NvPipe<F, L, TM, TN> &p, const uint8_t *st,
+                                              bf16x8 (&wf)[NvTile<F == 1, L, TM, TN>::NJ],
+                                              bf16x8 (&af)[NvTile<F == 1, L, TM, TN>::NI])
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
 #pragma unroll
-    for (int j = 0; j < S::NJ; ++j)
-        wf[j] = as_bf16x8(dq8_bf16(p.wc[j][KS], KS < 2 ? p.wsc[j][0] : p.wsc[j][1]));
+    for (int j = 0; j < S::NJ; ++j) {
+        if constexpr (F == kFmtMx16)
+            wf[j] = e2m1x8_bf16_pow2(p.wc[j][KS], p.wsc[j][0]);
+        else
+            wf[j] = as_bf16x8(dq8_bf16(p.wc[j][KS], KS < 2 ? p.wsc[j][0] : p.wsc[j][1]));
+    }
 #pragma unroll
     for (int i = 0; i < S::NI; ++i) {
-        if constexpr (A_FP4)
+        if constexpr (F == kFmtNv44)
             af[i] = as_bf16x8(dq8_bf16(p.ac[i][KS], KS < 2 ? p.asc[i][0] : p.asc[i][1]));
         else
             af[i] = *reinterpret_cast<const bf16x8 *>(st + S::kA + p.ab + p.ak[KS] + 4096 * i);
@@ -976,34 +996,35 @@ __device__ __forceinline__ void nv_wait_vm()
 // returned, and a barrier extends both to every wave, so `cur` is free: the copy
 // of stage t + 3 starts into it.  Step 3 multiplies while stage t + 1's packed
 // rows and step-0 fragments are read from `nxt`.  One basic block per stage.
-template <bool A_FP4, int L, int TM, int TN>
+template <int F, int L, int TM, int TN>
 __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, int t, int nk, const NvRingDma &d,
-                                              const NvRingDma &dz, int wave, NvPipe<A_FP4, L, TM, TN> &p,
-                                              f32x16 (&acc)[NvTile<A_FP4, L, TM, TN>::NI][NvTile<A_FP4, L, TM, TN>::NJ],
-                                              bf16x8 (&wf)[NvTile<A_FP4, L, TM, TN>::NJ],
-                                              bf16x8 (&af)[NvTile<A_FP4, L, TM, TN>::NI])
+                                              const NvRingDma &dz, int wave, NvPipe<F, L, TM, TN> &p,
+                                              f32x16 (&acc)[NvTile<F == 1, L, TM, TN>::NI][NvTile<F == 1, L, TM, TN>::NJ],
+                                              bf16x8 (&wf)[NvTile<F == 1, L, TM, TN>::NJ],
+                                              bf16x8 (&af)[NvTile<F == 1, L, TM, TN>::NI])
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
+    constexpr bool A_FP4 = F == kFmtNv44;
     constexpr int NI = S::NI, NJ = S::NJ, NM = NI * NJ;
-    constexpr int NV = 16 * (NJ + (A_FP4 ? NI : 0));  // VALU per step's widening, about
+    constexpr int NV = (F == kFmtMx16 ? 4 : 16) * (NJ + (A_FP4 ? NI : 0));  // VALU per step's widening, about
     constexpr int ND = A_FP4 ? 0 : NI;                // DS reads per step
     constexpr int P = NM >= 8 ? 4 : 1;
     bf16x8 wf1[NJ], af1[NI];
-    nv_pipe_frags<A_FP4, L, TM, TN, 1>(p, cur, wf1, af1);
+    nv_pipe_frags<F, L, TM, TN, 1>(p, cur, wf1, af1);
     nv_pipe_mfma<NI, NJ>(acc, wf, af);
     nv_pipe_interleave<NM, NV, ND>();
-    nv_pipe_frags<A_FP4, L, TM, TN, 2>(p, cur, wf, af);
+    nv_pipe_frags<F, L, TM, TN, 2>(p, cur, wf, af);
     nv_pipe_mfma<NI, NJ>(acc, wf1, af1);
     nv_pipe_interleave<NM, NV, ND>();
-    nv_pipe_frags<A_FP4, L, TM, TN, 3>(p, cur, wf1, af1);
+    nv_pipe_frags<F, L, TM, TN, 3>(p, cur, wf1, af1);
     nv_pipe_mfma<NI, NJ>(acc, wf, af);
     nv_pipe_interleave<NM, NV, ND>();
     nv_wait_vm<S::kDma>();
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    nv_pipe_raw<A_FP4, L, TM, TN>(p, nxt);
-    nv_ring_dma<A_FP4, L, TM, TN>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
-    nv_pipe_frags<A_FP4, L, TM, TN, 0>(p, nxt, wf, af);
+    nv_pipe_raw<F, L, TM, TN>(p, nxt, t + 1);
+    nv_ring_dma<F, L, TM, TN>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
+    nv_pipe_frags<F, L, TM, TN, 0>(p, nxt, wf, af);
     nv_pipe_mfma<NI, NJ>(acc, wf1, af1);
     nv_pipe_interleave<NM, NV, ND, 2 * (A_FP4 ? NI + NJ : NJ), S::kDma, P>();
 }
@@ -1012,20 +1033,21 @@ __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, 
 // c0 + 32 j + 8 g + 4 (l / 32) + 0..3 in slots 4 g .. 4 g + 3 of acc[i][j].  In
 // round rd, tile rows rd R + [0, R) go through `s0` and rows H + rd R + [0, R)
 // through `s1` (H = TM / 2), then leave as whole-row 16-byte stores.
-template <typename T, bool A_FP4, int L, int TM, int TN>
+template <typename T, int F, int L, int TM, int TN>
 __device__ __forceinline__ void nv_ring_epilogue(
-    const f32x16 (&acc)[NvTile<A_FP4, L, TM, TN>::NI][NvTile<A_FP4, L, TM, TN>::NJ], uint8_t *s0, uint8_t *s1,
+    const f32x16 (&acc)[NvTile<F == 1, L, TM, TN>::NI][NvTile<F == 1, L, TM, TN>::NJ], uint8_t *s0, uint8_t *s1,
     const NvGemmArgs &g, int m0, int n0, int wave, int lane, int tid)
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
     constexpr int NI = S::NI, NJ = S::NJ, H = S::H;
     constexpr int es = (int)sizeof(T);
     constexpr int pitch = S::epi_pitch(es);
     constexpr int R = S::epi_rows(es);
     constexpr int kPer = 16 / es, kChunks = TN / kPer;
     static_assert(R * pitch <= S::kStage, "epilogue staging");
+    constexpr bool A_FP4 = F == kFmtNv44;
     const int M = (int)g.M, N = (int)g.N;
-    const float wt = g.w_tscale[0];
+    const float wt = F == kFmtMx16 ? 1.f : g.w_tscale[0];  // MXFP4 has no tensor scale
     const int r0 = S::row0(wave), c0 = S::col0(wave);
 #pragma unroll
     for (int rd = 0; rd < H / R; ++rd) {
@@ -1083,10 +1105,12 @@ __device__ __forceinline__ void nv_ring_epilogue(
     }
 }
 
-template <bool A_FP4, int L, typename OutT, int TM, int TN>
+template <int F, int L, typename OutT, int TM, int TN>
 __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 {
-    using S = NvTile<A_FP4, L, TM, TN>;
+    using S = NvTile<F == 1, L, TM, TN>;
+    constexpr bool A_FP4 = F == kFmtNv44;
+    constexpr int kWsRow = F == kFmtMx16 ? 32 : 16;  // K elements per weight scale byte
     constexpr int NI = S::NI, NJ = S::NJ;
     __shared__ __align__(16) uint8_t s0[S::kStage];
     __shared__ __align__(16) uint8_t s1[S::kStage];
@@ -1102,7 +1126,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 
     NvRingDma d, dz;
     d.rw = nv_rsrc(g.w_codes, (int64_t)N * (K / 2));
-    d.rws = nv_rsrc(g.w_scales, (int64_t)N * (K / 16));
+    d.rws = nv_rsrc(g.w_scales, (int64_t)N * (K / kWsRow));
     if constexpr (A_FP4) {
         d.ra = nv_rsrc(g.a_codes, (int64_t)M * (K / 2));
         d.ras = nv_rsrc(g.a_scales, (int64_t)M * (K / 16));
@@ -1132,7 +1156,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
         d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
     }
     const int qw = (64 * wave + lane) % TN;
-    d.ws = n0 + qw < N ? (uint32_t)(n0 + qw) * (uint32_t)(K / 16) : kNvOut;
+    d.ws = n0 + qw < N ? (uint32_t)(n0 + qw) * (uint32_t)(K / kWsRow) : kNvOut;
     dz = d;
     dz.ra = nv_rsrc(g.a_codes ? (const void *)g.a_codes : (const void *)g.a, 0);
     dz.ras = dz.ra;
@@ -1145,29 +1169,29 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
-    NvPipe<A_FP4, L, TM, TN> p;
+    NvPipe<F, L, TM, TN> p;
     nv_pipe_init(p, wave, lane);
-    nv_ring_dma<A_FP4, L, TM, TN>(s0, d, 0, wave);
-    nv_ring_dma<A_FP4, L, TM, TN>(s1, nk > 1 ? d : dz, nk > 1 ? kRK : 0, wave);
-    nv_ring_dma<A_FP4, L, TM, TN>(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kRK : 0, wave);
+    nv_ring_dma<F, L, TM, TN>(s0, d, 0, wave);
+    nv_ring_dma<F, L, TM, TN>(s1, nk > 1 ? d : dz, nk > 1 ? kRK : 0, wave);
+    nv_ring_dma<F, L, TM, TN>(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kRK : 0, wave);
     nv_wait_vm<2 * S::kDma>();
     asm volatile("s_barrier" ::: "memory");
     bf16x8 wf[NJ], af[NI];
-    nv_pipe_raw<A_FP4, L, TM, TN>(p, s0);
-    nv_pipe_frags<A_FP4, L, TM, TN, 0>(p, s0, wf, af);
+    nv_pipe_raw<F, L, TM, TN>(p, s0, 0);
+    nv_pipe_frags<F, L, TM, TN, 0>(p, s0, wf, af);
     const int nfull = nk - nk % 3;
     for (int t = 0; t < nfull; t += 3) {
-        nv_pipe_stage<A_FP4, L, TM, TN>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
-        nv_pipe_stage<A_FP4, L, TM, TN>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
-        nv_pipe_stage<A_FP4, L, TM, TN>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<F, L, TM, TN>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<F, L, TM, TN>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<F, L, TM, TN>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
     }
     // the last one or two stages (no copies left to start)
-    if (nk % 3 >= 1) nv_pipe_stage<A_FP4, L, TM, TN>(s0, s1, nfull, nk, d, dz, wave, p, acc, wf, af);
-    if (nk % 3 == 2) nv_pipe_stage<A_FP4, L, TM, TN>(s1, s2, nfull + 1, nk, d, dz, wave, p, acc, wf, af);
+    if (nk % 3 >= 1) nv_pipe_stage<F, L, TM, TN>(s0, s1, nfull, nk, d, dz, wave, p, acc, wf, af);
+    if (nk % 3 == 2) nv_pipe_stage<F, L, TM, TN>(s1, s2, nfull + 1, nk, d, dz, wave, p, acc, wf, af);
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    nv_ring_epilogue<OutT, A_FP4, L, TM, TN>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e);
+    nv_ring_epilogue<OutT, F, L, TM, TN>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e);
 }
 
 constexpr size_t kGemmLds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);  // 128 KiB
@@ -1187,21 +1211,21 @@ static fp4_status launch_prefill(const NvGemmArgs &g, hipStream_t st)
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
-template <bool A_FP4, int L, int TM, int TN>
+template <int F, int L, int TM, int TN>
 static void launch_ring(const NvGemmArgs &g, hipStream_t st)
 {
     const int tiles = (int)(((g.M + TM - 1) / TM) * ((g.N + TN - 1) / TN));
     if (g.c_bf16)
-        hipLaunchKernelGGL((k_nv_gemm_ring<A_FP4, L, __bf16, TM, TN>), dim3(tiles), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((k_nv_gemm_ring<F, L, __bf16, TM, TN>), dim3(tiles), dim3(256), 0, st, g);
     else
-        hipLaunchKernelGGL((k_nv_gemm_ring<A_FP4, L, float, TM, TN>), dim3(tiles), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((k_nv_gemm_ring<F, L, float, TM, TN>), dim3(tiles), dim3(256), 0, st, g);
 }
 
 // 256 x 256 tiles; when the last round of tiles would leave most CUs idle, the
 // tile columns of that round go to a second launch of 128 x 128 tiles, provided
 // they fit in one round (for M = 4096, N = 17408: 1024 large tiles, four full
 // rounds on 256 CUs, then 256 small tiles for the last 1024 columns).
-template <bool A_FP4, int L>
+template <int F, int L>
 static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
 {
     const int64_t cus = device_cu_count();
@@ -1214,17 +1238,26 @@ static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
         if (cols >= 1 && n_split < g.N && small <= cus) {
             NvGemmArgs big = g;
             big.N = n_split;
-            launch_ring<A_FP4, L, 256, 256>(big, st);
+            launch_ring<F, L, 256, 256>(big, st);
             NvGemmArgs rest = g;
             rest.N = g.N - n_split;
             rest.w_codes = g.w_codes + n_split * (g.K / 2);
-            rest.w_scales = g.w_scales + n_split * (g.K / 16);
+            rest.w_scales = g.w_scales + n_split * (g.K / (F == kFmtMx16 ? 32 : 16));
             rest.c = reinterpret_cast<uint8_t *>(g.c) + n_split * (g.c_bf16 ? 2 : 4);
-            launch_ring<A_FP4, 0, 128, 128>(rest, st);
+            launch_ring<F, 0, 128, 128>(rest, st);
             return;
         }
     }
-    launch_ring<A_FP4, L, 256, 256>(g, st);
+    launch_ring<F, L, 256, 256>(g, st);
+}
+
+fp4_status launch_mxfp4_gemm_w4a16(const NvGemmArgs &g, hipStream_t st)
+{
+    // the ring kernel addresses operands with 32-bit byte offsets
+    if (g.K % 128 != 0 || g.M * g.lda * 2 >= (int64_t(1) << 31) || g.N * (g.K / 2) >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    launch_ring_split<kFmtMx16, kNvL16>(g, st);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
@@ -1264,8 +1297,8 @@ fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st)
     const bool ring = aligned && g.M * g.K * 2 < (int64_t(1) << 31) && g.N * (g.K / 2) < (int64_t(1) << 31) &&
                       (g.a_codes || g.M * g.lda * 2 < (int64_t(1) << 31));
     if (ring) {
-        if (g.a_codes) launch_ring_split<true, 0>(g, st);
-        else launch_ring_split<false, kNvL16>(g, st);
+        if (g.a_codes) launch_ring_split<1, 0>(g, st);
+        else launch_ring_split<0, kNvL16>(g, st);
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
     if (g.a_codes)

@@ -29,6 +29,10 @@
 // exactly to E2M1 * E4M3 in bf16 (see dq8_bf16); accumulation is fp32.  The 8
 // waves' partial tiles are added in LDS; the epilogue multiplies by the tensor
 // scale.
+// MXFP4 weights use the same decode layout with 4 E8M0 bytes per segment (one
+// per 32-element block, lane group g's block): scales_p[s][n][4].  Their scales
+// are powers of two, which the scaled E2M1 conversion applies exactly, so the MX
+// variants need no separate scale multiply.
 #include "device_common.h"
 #include "internal.h"
 
@@ -37,8 +41,9 @@ namespace fp4k {
 constexpr int kGvWaves = 8;
 constexpr int kGvMaxT = 8;  // 16-row tiles per workgroup
 
-// thread per (segment, row): 64 code bytes and 8 scale bytes
-__global__ __launch_bounds__(256) void k_nv_pack_decode(const uint8_t *__restrict__ codes,
+// thread per (segment, row): 64 code bytes and 8 scale bytes (NVFP4) or 4 (MXFP4)
+template <int SB>
+__global__ __launch_bounds__(256) void k_pack_decode(const uint8_t *__restrict__ codes,
                                                          const uint8_t *__restrict__ scales, int N, int K,
                                                          uint8_t *__restrict__ cp, uint8_t *__restrict__ sp)
 {
@@ -50,8 +55,11 @@ __global__ __launch_bounds__(256) void k_nv_pack_decode(const uint8_t *__restric
     uint4 *dst = reinterpret_cast<uint4 *>(cp + idx * 64);
 #pragma unroll
     for (int i = 0; i < 4; ++i) dst[i] = src[i];
-    *reinterpret_cast<uint2 *>(sp + idx * 8) =
-        *reinterpret_cast<const uint2 *>(scales + (int64_t)r * (K / 16) + 8 * s);
+    if constexpr (SB == 8)
+        *reinterpret_cast<uint2 *>(sp + idx * 8) = *reinterpret_cast<const uint2 *>(scales + (int64_t)r * (K / 16) + 8 * s);
+    else
+        *reinterpret_cast<uint32_t *>(sp + idx * 4) =
+            *reinterpret_cast<const uint32_t *>(scales + (int64_t)r * (K / 32) + 4 * s);
 }
 
 // Buffer descriptor over `bytes` bytes at `base` (raw, byte-addressed; dword 3
@@ -72,13 +80,14 @@ struct GvTile {
     uint32_t s[S];  // their two E4M3 scale bytes
 };
 
-// E2M1 x 4 (two code bytes, low nibble first) -> bf16 x 4, unscaled (exact).
-__device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half)
+// E2M1 x 4 (two code bytes, low nibble first) -> bf16 x 4, times the power of two
+// in `scale`'s exponent field (1.0: unscaled); exact.
+__device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale = 1.0f)
 {
-    const bf16x2 lo = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 2)
-                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 0);
-    const bf16x2 hi = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 3)
-                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, 1.0f, 1);
+    const bf16x2 lo = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 2)
+                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 0);
+    const bf16x2 hi = half ? __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 3)
+                           : __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, scale, 1);
     return bf16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
@@ -90,7 +99,7 @@ __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half)
 // multiplied by the lane's E4M3 scale, so the scale costs 4 FMAs per 16 codes
 // instead of a multiply per code.  The four K-quarters are summed across lanes
 // at the end of the tile.
-template <int S, int D, bool M4, int W>
+template <int S, int D, bool M4, int W, bool MX>
 __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
 {
     __shared__ f32x4 red[kGvMaxT][W][64];
@@ -108,7 +117,8 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
 
     const __amdgpu_buffer_rsrc_t ra = gv_rsrc(g.a, (uint32_t)((int64_t)(M - 1) * g.lda * 2 + g.K * 2));
     const __amdgpu_buffer_rsrc_t rc = gv_rsrc(g.w_codes, (uint32_t)((int64_t)nseg * N * 64));
-    const __amdgpu_buffer_rsrc_t rs = gv_rsrc(g.w_scales, (uint32_t)((int64_t)nseg * N * 8));
+    constexpr int SB = MX ? 4 : 8;  // scale bytes per row and segment
+    const __amdgpu_buffer_rsrc_t rs = gv_rsrc(g.w_scales, (uint32_t)((int64_t)nseg * N * SB));
 
     // byte offsets of this lane's codes / scales at tile 0, segment seg0 (kGvOut where skipped)
     uint32_t oc[S], os[S];
@@ -116,12 +126,15 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
     for (int s = 0; s < S; ++s) {
         const int64_t e = (int64_t)(seg0 + s) * N + r_lo + n;
         oc[s] = s < ns ? (uint32_t)(e * 64 + 16 * grp) : kGvOut;
-        os[s] = s < ns ? (uint32_t)(e * 8 + 2 * grp) : kGvOut;
+        os[s] = s < ns ? (uint32_t)(e * SB + (MX ? 1 : 2) * grp) : kGvOut;
     }
     auto issue_seg = [&](int t, int s, GvTile<S> &b) {
         const bool ok = r_lo + 16 * t + n < r_hi;
         b.c[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(ok ? oc[s] + 1024 * t : kGvOut), 0, 0);
-        b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? os[s] + 128 * t : kGvOut), 0, 0);
+        if constexpr (MX)
+            b.s[s] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? os[s] + 16 * SB * t : kGvOut), 0, 0);
+        else
+            b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? os[s] + 16 * SB * t : kGvOut), 0, 0);
     };
 
     // activation fragments: A row n (M4: row l % 4; zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8)
@@ -203,7 +216,30 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
             for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(part[blk][i], bs[blk], acc[i]);
     };
     // one segment of a tile, 16x16x32 variant (two accumulator chains)
+    // MXFP4, M <= 4: the lane's 32 codes are one MX block, whose power-of-two scale
+    // the conversion applies exactly; two accumulator chains, no scale multiply
+    auto seg4mx = [&](int s, const GvTile<S> &b, f32x4 &acc0, f32x4 &acc1) {
+        const float sc = __uint_as_float(b.s[s] << 23);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int blk = 0; blk < 2; ++blk) {
+                const int q = 4 * blk + st;
+                const bf16x8 a8 = af[s][q >> 1];
+                const bf16x4 a4 = (q & 1) ? bf16x4{a8[4], a8[5], a8[6], a8[7]} : bf16x4{a8[0], a8[1], a8[2], a8[3]};
+                f32x4 &acc = blk ? acc1 : acc0;
+                acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(b.c[s][q >> 1], q & 1, sc), acc, 0, 0, 0);
+            }
+    };
     auto seg16 = [&](int s, const GvTile<S> &b, f32x4 &acc0, f32x4 &acc1) {
+        if constexpr (MX) {
+            const float sc = __uint_as_float(b.s[s] << 23);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][0], e2m1x8_bf16_pow2(b.c[s][0], sc), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][1], e2m1x8_bf16_pow2(b.c[s][1], sc), acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][2], e2m1x8_bf16_pow2(b.c[s][2], sc), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][3], e2m1x8_bf16_pow2(b.c[s][3], sc), acc1, 0, 0, 0);
+            return;
+        }
         // the two E4M3 block scales of the lane's 32 codes (OCP E4M3FN conversion)
         const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)b.s[s], false);
         acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][0], as_bf16x8(dq8_bf16(b.c[s][0], bs[0])), acc0, 0, 0, 0);
@@ -225,13 +261,16 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
             for (int s = 0; s < S; ++s) {
                 if (t + D - 1 < kGvMaxT) issue_seg(t + D - 1, s, buf[(t + D - 1) % D]);
                 __builtin_amdgcn_sched_barrier(0);
-                if (M4)
+                if (M4 && MX)
+                    seg4mx(s, buf[t % D], acc0, acc1);
+                else if (M4)
                     seg4(s, buf[t % D], acc0);
                 else
                     seg16(s, buf[t % D], acc0, acc1);
                 __builtin_amdgcn_sched_barrier(0);
             }
             if (M4) {
+                if (MX) acc0 += acc1;
                 // sum the four K-quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
@@ -252,7 +291,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
         f32x4 sum = red[wave][0][lane];
 #pragma unroll
         for (int w = 1; w < W; ++w) sum += red[wave][w][lane];
-        const float ts = *g.w_tscale;
+        const float ts = MX ? 1.f : *g.w_tscale;  // MXFP4 has no tensor scale
         const int col = r_lo + 16 * wave + n;
         if (col < r_hi) {
 #pragma unroll
@@ -270,28 +309,38 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
     }
 }
 
-fp4_status launch_nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                                    uint8_t *codes_p, uint8_t *scales_p, hipStream_t st)
+fp4_status launch_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                              uint8_t *codes_p, uint8_t *scales_p, bool mx, hipStream_t st)
 {
     const int64_t threads = N * (K / 128);
     if (threads == 0) return FP4_OK;
-    hipLaunchKernelGGL(k_nv_pack_decode, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, st, codes, scales,
-                       (int)N, (int)K, codes_p, scales_p);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    if (mx)
+        hipLaunchKernelGGL(k_pack_decode<4>, grid, dim3(256), 0, st, codes, scales, (int)N, (int)K, codes_p, scales_p);
+    else
+        hipLaunchKernelGGL(k_pack_decode<8>, grid, dim3(256), 0, st, codes, scales, (int)N, (int)K, codes_p, scales_p);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
-template <int S>
+template <int S, bool MX>
 static void launch_gemv(const GemvArgs &g, unsigned grid, hipStream_t st)
 {
     constexpr int D = S <= 5 ? 3 : 2;  // tiles in flight, bounded by registers
     // the M <= 4 variant's extra registers do not fit beside 8 segments' fragments
     if constexpr (S < 8) {
         if (g.M <= 4) {
-            hipLaunchKernelGGL((k_nv_gemv_dec<S, D, true, kGvWaves>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+            hipLaunchKernelGGL((k_nv_gemv_dec<S, D, true, kGvWaves, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
             return;
         }
     }
-    hipLaunchKernelGGL((k_nv_gemv_dec<S, D, false, kGvWaves>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    hipLaunchKernelGGL((k_nv_gemv_dec<S, D, false, kGvWaves, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+}
+
+template <int S>
+static void launch_gemv_fmt(const GemvArgs &g, unsigned grid, hipStream_t st)
+{
+    if (g.mx) launch_gemv<S, true>(g, grid, st);
+    else launch_gemv<S, false>(g, grid, st);
 }
 
 int device_cu_count()
@@ -307,7 +356,7 @@ int device_cu_count()
     return cache[dev];
 }
 
-fp4_status launch_nvfp4_gemv_decode(GemvArgs g, hipStream_t st)
+fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st)
 {
     const int nseg = g.K / 128;
     const int S = (nseg + kGvWaves - 1) / kGvWaves;
@@ -322,14 +371,14 @@ fp4_status launch_nvfp4_gemv_decode(GemvArgs g, hipStream_t st)
     G = (g.N + R - 1) / R;
     g.rows_per_wg = (int)R;
     switch (S) {
-    case 1: launch_gemv<1>(g, (unsigned)G, st); break;
-    case 2: launch_gemv<2>(g, (unsigned)G, st); break;
-    case 3: launch_gemv<3>(g, (unsigned)G, st); break;
-    case 4: launch_gemv<4>(g, (unsigned)G, st); break;
-    case 5: launch_gemv<5>(g, (unsigned)G, st); break;
-    case 6: launch_gemv<6>(g, (unsigned)G, st); break;
-    case 7: launch_gemv<7>(g, (unsigned)G, st); break;
-    case 8: launch_gemv<8>(g, (unsigned)G, st); break;
+    case 1: launch_gemv_fmt<1>(g, (unsigned)G, st); break;
+    case 2: launch_gemv_fmt<2>(g, (unsigned)G, st); break;
+    case 3: launch_gemv_fmt<3>(g, (unsigned)G, st); break;
+    case 4: launch_gemv_fmt<4>(g, (unsigned)G, st); break;
+    case 5: launch_gemv_fmt<5>(g, (unsigned)G, st); break;
+    case 6: launch_gemv_fmt<6>(g, (unsigned)G, st); break;
+    case 7: launch_gemv_fmt<7>(g, (unsigned)G, st); break;
+    case 8: launch_gemv_fmt<8>(g, (unsigned)G, st); break;
     default: return FP4_ERR_SHAPE;
     }
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;

@@ -61,18 +61,22 @@ struct GemvArgs {
     const uint16_t *a;        // bf16 [M][lda]
     int64_t lda;
     const uint8_t *w_codes;   // [K/128][N][64]
-    const uint8_t *w_scales;  // [K/128][N][8]
-    const float *w_tscale;    // [1]
+    const uint8_t *w_scales;  // NVFP4 [K/128][N][8] E4M3; MXFP4 [K/128][N][4] E8M0
+    const float *w_tscale;    // [1] (NVFP4; unused for MXFP4)
     int M, N, K;
+    int mx;                   // weights are MXFP4
     int rows_per_wg;          // set by the launcher
     void *c;
     int c_bf16;
     int64_t ldc;
 };
 
-fp4_status launch_nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
-                                    uint8_t *codes_p, uint8_t *scales_p, hipStream_t st);
-fp4_status launch_nvfp4_gemv_decode(GemvArgs g, hipStream_t st);
+fp4_status launch_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                              uint8_t *codes_p, uint8_t *scales_p, bool mx, hipStream_t st);
+fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st);
+
+// W4A16 prefill GEMM with MXFP4 weights (gemm_nv.hip; K % 128 == 0)
+fp4_status launch_mxfp4_gemm_w4a16(const NvGemmArgs &g, hipStream_t st);
 
 struct MxGemmArgs {
     const uint8_t *a_codes;  // [M][K/2]

@@ -206,6 +206,33 @@ fp4_status mxfp4_gemm_prequant(const uint8_t *a_codes, const uint8_t *a_scales, 
                                int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
                                int64_t N, void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream);
 
+/* MXFP4 W4A16 GEMM (eefocus.com edge-FP4 article, "FP4 as the next core
+ * standard": MXFP4 blocks of 32 elements with an E8M0 power-of-two scale; aixq.cc
+ * article, "Core difference: W4A4 vs W4A16": 16-bit activations): C = A . W^T
+ * with A bf16 [M][lda] and W MXFP4 row-major, codes [N][K/2], E8M0 scales
+ * [N][K/32].  Each weight is widened exactly to bf16 (E2M1 times a power of two),
+ * fp32 accumulation; no tensor scale.  K % 128 == 0 (FP4_ERR_SHAPE otherwise, and
+ * for operands past 2 GiB).  Tolerance as gemm_w4a16. */
+fp4_status mxfp4_gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes,
+                            const uint8_t *w_scales, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                            hipStream_t stream);
+
+/* Decode layout of an MXFP4 weight: codes as for nvfp4_pack_decode,
+ *   codes_p  uint8 [K/128][N][64]: byte (s*N + n)*64 + b = codes[n][64*s + b]
+ *   scales_p uint8 [K/128][N][4]:  byte (s*N + n)*4 + b  = scales[n][4*s + b]
+ * (the 4 E8M0 bytes of segment s).  Same bytes and count as the row-major form
+ * (4.25 bits a value).  K % 128 == 0; outputs of N*K/2 and N*K/32 bytes, not
+ * overlapping the inputs. */
+fp4_status mxfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                             uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream);
+
+/* MXFP4 W4A16 decode GEMV on a weight in the MXFP4 decode layout: C = A . W^T for
+ * 1 <= M <= 16, K % 128 == 0, K <= 8192.  Arithmetic and tolerance as
+ * mxfp4_gemm_w4a16. */
+fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
+                                   const uint8_t *w_scales_p, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                                   hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -275,6 +275,14 @@ def gemm_w4a4_ref(a_bf16: np.ndarray, w_codes, w_scales, w_tscale, a_per_row=Tru
     return gemm_f64(a, w)
 
 
+def mxfp4_gemm_w4a16_ref(a_bf16: np.ndarray, w_codes, w_scales, rows=None):
+    """fp64 reference of C = A . W^T with bf16 A and W dequantized exactly (MXFP4:
+    E2M1 times the block's E8M0 power of two; no tensor scale).  Returns (C_ref, T)."""
+    a = bf16_bits_to_f64(a_bf16 if rows is None else a_bf16[rows])
+    w = mxfp4_to_f64(w_codes, w_scales)
+    return gemm_f64(a, w)
+
+
 def mxfp4_gemm_w4a4_ref(a_bf16: np.ndarray, w_codes, w_scales, rule=MX_OCP_FLOOR, rows=None):
     """fp64 reference of the MXFP4 W4A4 GEMM (A quantized by this oracle)."""
     src = a_bf16 if rows is None else a_bf16[rows]

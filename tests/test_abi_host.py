@@ -203,6 +203,39 @@ def test_mxfp4_validation(L):
         assert q() == NO_DEVICE and g() == NO_DEVICE
 
 
+def test_mxfp4_w4a16_validation(L):
+    import torch
+
+    def g(**kw):
+        a = dict(a=FAKE, M=8, K=256, lda=256, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=1, ldc=16, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a16(*a.values())
+
+    assert g(a=None) == NULL
+    assert g(K=96, lda=96) == SHAPE                  # K % 128 == 0
+    assert g(lda=128) == LAYOUT
+    assert g(ct=5) == DTYPE
+
+    def pk(**kw):
+        a = dict(codes=FAKE, scales=FAKE, N=32, K=256, cp=FAKE, sp=FAKE, stream=None)
+        a.update(kw)
+        return L.mxfp4_pack_decode(*a.values())
+
+    assert pk(scales=None) == NULL
+    assert pk(K=160) == SHAPE
+
+    def gd(**kw):
+        a = dict(a=FAKE, M=4, K=256, lda=256, wc=FAKE, ws=FAKE, N=32, c=FAKE, ct=1, ldc=32, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a16_decode(*a.values())
+
+    assert gd(M=17) == SHAPE
+    assert gd(K=8320, lda=8320) == SHAPE
+    assert gd(c=None) == NULL
+    if not torch.cuda.is_available():
+        assert g() == NO_DEVICE and pk() == NO_DEVICE and gd() == NO_DEVICE
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import block_scaled_fp4_04_amd as fp4
 

@@ -144,3 +144,28 @@ def test_mxfp4_plain_fp4_matmul_when_scales_are_one(oracle_mod):
     assert np.all(ws == 127)
     c, _ = oracle_mod.mxfp4_gemm_w4a4_ref(to_bf16_bits(av.astype(np.float32)), wc, ws)
     assert np.array_equal(c, av @ wv.T)
+
+
+def test_mxfp4_w4a16_ref_brute_force(oracle_mod):
+    # independent pin: a triple loop over E2M1 grid values times 2^(byte - 127),
+    # written here from the MXFP4 definition, against the oracle's W4A16 reference
+    rng = np.random.default_rng(11)
+    M, N, K = 3, 5, 64
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(110, 140, size=(N, K // 32), dtype=np.uint8)
+    a = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    w = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            nib = (int(codes[n, k // 2]) >> (4 * (k % 2))) & 15
+            v = grid[nib & 7] * (-1.0 if nib & 8 else 1.0)
+            w[n, k] = v * 2.0 ** (int(scales[n, k // 32]) - 127)
+    av = (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ref = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            ref[m, n] = sum(av[m, k] * w[n, k] for k in range(K))
+    got, tol = oracle_mod.mxfp4_gemm_w4a16_ref(a, codes, scales)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
+    assert np.all(tol >= np.abs(got) - 1e-300)
