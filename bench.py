@@ -10,8 +10,8 @@ held in R rotating copies (R * 50.1 MB > 2 x the 256 MB Infinity Cache) so
 every call reads it from HBM.
 
 The same run also times the other kernels of the path on their own workloads
-(weight quantize, dequantize, prefill W4A16 and W4A4 at M = 4096, MXFP4 vs
-NVFP4 W4A4 at M = 8192) with HIP events on the stream they run on, and times the
+(weight quantize, dequantize, prefill W4A16 and W4A4 at M = 4096, MXFP4-weight
+W4A16 decode and prefill, MXFP4 vs NVFP4 W4A4 at M = 8192) with HIP events on the stream they run on, and times the
 CPU oracle on a bounded sample of the decode step as a reported baseline.
 
 Prints one JSON line.  `--gpus N` with N > 1 exits: this path runs on one GPU.
@@ -271,6 +271,32 @@ def components(args, torch, fp4, T, dev, w32, wq):
         "gemm_us": t_g * 1e6, "gemm_TFLOP/s": fl / t_g / 1e12, "gemm_frac_bf16_mfma": fl / t_g / BF16_PEAK,
         "total_us": t_all * 1e6, "total_TFLOP/s": fl / t_all / 1e12}
     del a, c
+
+    # MXFP4 weights with bf16 activations (W4A16): decode GEMV at M = 1, 4, 16 on
+    # the MXFP4 decode layout (12 rotating copies, as the NVFP4 step) and the
+    # prefill GEMM at M = 4096
+    wmx = fp4.mxfp4_quantize(w32)
+    mcopies = [fp4.mxfp4_pack_decode(fp4.PackedMXFP4(wmx.codes.clone(), wmx.scales.clone(), N, K))
+               for _ in range(12)]
+    wl2 = WORKLOADS["decode_gemv_k5120_n17408"]
+    mxd = {}
+    for M in wl2.M:
+        am = torch.from_numpy(wl2.activations_bf16(M).view(np.int16)).view(torch.bfloat16).to(dev)
+        om = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+        t = T.per_launch(lambda i, am=am, om=om: fp4.mxfp4_gemm_w4a16_decode(am, mcopies[i % 12], out=om),
+                         max(it, 30), warmup=5)
+        b = M * K * 2 + N * K // 2 + N * K // 32 + M * N * 2
+        mxd[str(M)] = {"us": round(t * 1e6, 4), "GB/s": round(b / t / 1e9, 1), "frac_hbm": round(b / t / HBM_PEAK, 4),
+                       "bytes": b}
+    out["mxfp4_w4a16_decode_k5120_n17408"] = mxd
+    del mcopies
+    a = torch.from_numpy(wl3.activations_bf16(4096).view(np.int16)).view(torch.bfloat16).to(dev)
+    c = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
+    fl = 2.0 * 4096 * N * K
+    t = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a16(a, wmx, out=c), it)
+    out["mxfp4_w4a16_prefill_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
+                                        "flop": fl, "mfma": "bf16 32x32x16 (MXFP4 widened exactly to bf16)"}
+    del a, c, wmx
 
     # MXFP4 vs NVFP4 W4A4 at M = 8192 on identical bf16 inputs
     wl5 = WORKLOADS["mx_vs_nv_w4a4_m8192"]
