@@ -68,6 +68,10 @@ def _declare(L):
         "mxfp4_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, p, i32, i64, p]),
         "mxfp4_pack_decode": (i32, [p, p, i64, i64, p, p, p]),
         "mxfp4_gemm_w4a16_decode": (i32, [p, i64, i64, i64, p, p, i64, p, i32, i64, p]),
+        "mxfp8_quantize": (i32, [p, i32, i64, i64, i64, p, p, i32, p, p]),
+        "mxfp4_gemm_w4a8_workspace": (sz, [i64, i64]),
+        "mxfp4_gemm_w4a8": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
+        "mxfp4_gemm_w4a8_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -427,4 +431,67 @@ def mxfp4_gemm_w4a16_decode(a: torch.Tensor, w: DecodeMXFP4, dtype=torch.bfloat1
         out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
     _check(L.mxfp4_gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
                                      _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+@dataclasses.dataclass
+class PackedMXFP8:
+    """An MXFP8 tensor [rows, cols]: E4M3FN codes [rows, cols], E8M0 scales [rows, cols/32]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    rows: int
+    cols: int
+
+
+def mxfp8_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None = None,
+                   out: PackedMXFP8 | None = None) -> PackedMXFP8:
+    """MXFP8 (E4M3FN elements, E8M0 per 32) of an fp32 or bf16 [rows, cols] tensor."""
+    L = lib()
+    _need_cuda(x)
+    rows, cols = x.shape
+    if out is None:
+        out = PackedMXFP8(torch.empty(rows, cols, dtype=torch.uint8, device=x.device),
+                          torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device), rows, cols)
+    _check(L.mxfp8_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
+                            _rule(rule), _ptr(nonfinite), _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a8_workspace(M: int, K: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib().mxfp4_gemm_w4a8_workspace(M, K), dtype=torch.uint8, device=device)
+
+
+def mxfp8_packed_a(ws: torch.Tensor, M: int, K: int) -> PackedMXFP8:
+    """A's MXFP8 form inside a mxfp4_gemm_w4a8 workspace."""
+    cb = (M * K + 255) // 256 * 256
+    return PackedMXFP8(ws[:M * K].view(M, K), ws[cb:cb + M * K // 32].view(M, K // 32), M, K)
+
+
+def mxfp4_gemm_w4a8(a: torch.Tensor, w: PackedMXFP4, rule="ocp", dtype=torch.bfloat16,
+                    out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8: bf16 A [M, K] quantized to MXFP8 on the device, MXFP4 W [N, K]."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("mxfp4_gemm_w4a8 takes bfloat16 activations")
+    M, K = a.shape
+    if workspace is None:
+        workspace = mxfp4_gemm_w4a8_workspace(M, K, a.device)
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    _check(L.mxfp4_gemm_w4a8(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
+                             _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                             _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a8_prequant(a: PackedMXFP8, w: PackedMXFP4, dtype=torch.bfloat16,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """The GEMM half of mxfp4_gemm_w4a8 on an MXFP8 A."""
+    L = lib()
+    if out is None:
+        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.mxfp4_gemm_w4a8_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
+                                      _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
+                                      _stream()))
     return out

@@ -437,4 +437,64 @@ fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4
     return launch_mxfp4_gemm(g, stream);
 }
 
+// ------------------------------------------------------------------- W4A8 --
+
+fp4_status mxfp8_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *codes, uint8_t *scales, fp4_mx_rule rule, int32_t *nonfinite,
+                          hipStream_t stream)
+{
+    if (!valid_dtype(xt) || (rule != FP4_MX_OCP_FLOOR && rule != FP4_MX_CEIL)) return FP4_ERR_DTYPE;
+    FP4_TRY(check_matrix(x, rows, cols, ldx, dsize(xt)));
+    if (cols % 32 != 0) return FP4_ERR_SHAPE;
+    if (rows * cols > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(codes, scales));
+    FP4_TRY(check_device());
+    return launch_mxfp8_quantize(x, xt, rows, cols, ldx, codes, scales, rule, nonfinite, stream);
+}
+
+size_t mxfp4_gemm_w4a8_workspace(int64_t M, int64_t K)
+{
+    if (M <= 0 || K <= 0) return 0;
+    return align256((size_t)M * (size_t)K) + align256((size_t)M * (size_t)(K / 32));
+}
+
+fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                    const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                                    fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    FP4_TRY(check_packed(a_codes, a_scales));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    FP4_TRY(check_device());
+    MxGemmArgs g{};
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_mxfp4_gemm_w4a8(g, stream);
+}
+
+fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                           const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                           fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (rule != FP4_MX_OCP_FLOOR && rule != FP4_MX_CEIL) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!ws || !aligned16(ws) || ws_bytes < mxfp4_gemm_w4a8_workspace(M, K)) return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
+    uint8_t *as = ac + align256((size_t)M * (size_t)K);
+    FP4_TRY(launch_mxfp8_quantize(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
+    return mxfp4_gemm_w4a8_prequant(ac, as, M, K, w_codes, w_scales, N, c, ct, ldc, stream);
+}
+
 }  // extern "C"

@@ -583,6 +583,275 @@ static fp4_status launch_mx(const MxGemmArgs &g, hipStream_t st)
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
+// ---- W4A8: MXFP8 activations x MXFP4 weights (K % 128 == 0) -------------
+//
+// W4A8 (edge-FP4 article, eefocus.com: an NPU with native W4A8, weights in FP4
+// and activations in FP8), with both operands in OCP MX form: A E4M3FN bytes
+// and W E2M1 nibbles, each with an E8M0 byte per 32 K-elements.  gfx950's
+// v_mfma_scale_f32_32x32x64_f8f6f4 takes the two formats side by side (source 0
+// FP4, source 1 FP8).  Of the instruction's 64 K-values, lane half h (lanes
+// 32 h ..) supplies, for its row, the FP4 values 32 h .. 32 h + 31 as 16 bytes,
+// but the FP8 values 16 h .. 16 h + 15 and 32 + 16 h .. 32 + 16 h + 15 as its two
+// 16-byte halves; the E8M0 byte a lane half gives applies to K-block h of
+// either operand.  Products are exact, the accumulation fp32.
+//
+// 256 x 256 tiles, waves 2 x 2 of 128 x 128, acc[i][j] = W_j A_i^T as in the
+// MXFP4 kernel.  Three LDS stages of 128 K-elements, each its own LDS object,
+// fed by buffer-to-LDS DMA: A [256][128 B] (16-byte chunk c of row r at slot
+// 8 r + (c ^ ((r >> 1) & 7))), W [256][64 B] (chunk c at 4 r + (c ^ ((r >> 2) & 3))),
+// and each operand's 4 E8M0 bytes per row.  Those swizzles make the 16 lanes of
+// each fragment read hit 16 different 16-byte bank groups.  A stage is two MFMA
+// steps of 64 K; step 1's fragments are read under step 0's MFMAs, and after the
+// barrier that frees the stage (inside step 1) the next stage's step 0 is read
+// and the copy of the stage three ahead starts.
+constexpr int kA8K = 128;                  // K elements per stage
+constexpr int kA8A = 0;                    // A fp8 [256][128]
+constexpr int kA8W = 256 * 128;            // W fp4 [256][64]
+constexpr int kA8SA = kA8W + 256 * 64;     // A scales [256][4]
+constexpr int kA8SW = kA8SA + 1024;        // W scales [256][4]
+constexpr int kA8Stage = kA8SW + 1024;     // 51,200 bytes
+constexpr int kA8Dma = 8 + 4 + 1 + 1;      // copies per wave per stage
+constexpr uint32_t kA8Out = 0x80000000u;   // an offset past every descriptor's size
+constexpr int kA8EpiPitch16 = 256 * 2 + 16, kA8EpiPitch32 = 256 * 4 + 16;
+static_assert(64 * kA8EpiPitch16 <= kA8Stage && 32 * kA8EpiPitch32 <= kA8Stage, "epilogue staging");
+
+struct A8Dma {
+    __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
+    uint32_t a[8], w[4], sa, sw;
+};
+
+__device__ __forceinline__ void a8_dma(uint8_t *st, const A8Dma &d, int k0, int wave)
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + kA8A + 16 * (512 * wave + 64 * i)), 16,
+                                                 (int)d.a[i], k0, 0, 0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kA8W + 16 * (256 * wave + 64 * i)), 16,
+                                                 (int)d.w[i], k0 / 2, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (mx_lds_void *)(st + kA8SA + 256 * wave), 4, (int)d.sa, k0 / 32,
+                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsw, (mx_lds_void *)(st + kA8SW + 256 * wave), 4, (int)d.sw, k0 / 32,
+                                             0, 0);
+}
+
+// per-lane LDS offsets: A row wm 128 + l, W row wn 128 + l (l = lane % 32, half
+// h = lane / 32); fragment i / j adds 32 rows (4096 / 2048 bytes)
+struct A8Lds {
+    uint32_t a[2][2];  // [step][16-byte half p] A chunk 4 ks + 2 p + h
+    uint32_t w[2];     // [step] W chunk 2 ks + h
+    uint32_t sa, sw;   // the row's 4 scale bytes
+    uint32_t hsh;      // 8 h: this lane's scale bytes are bits hsh.. and 16 + hsh..
+};
+
+struct A8Frag {
+    i32x8 a[4];
+    i32x4 w[4];
+};
+
+template <int KS>
+__device__ __forceinline__ void a8_frags(const uint8_t *st, const A8Lds &o, A8Frag &f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const i32x4 lo = *reinterpret_cast<const i32x4 *>(st + o.a[KS][0] + 4096 * i);
+        const i32x4 hi = *reinterpret_cast<const i32x4 *>(st + o.a[KS][1] + 4096 * i);
+        f.a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+        f.w[i] = *reinterpret_cast<const i32x4 *>(st + o.w[KS] + 2048 * i);
+    }
+}
+
+// the lane's E8M0 bytes of the stage: byte 0 = step 0's block, byte 2 = step 1's
+__device__ __forceinline__ void a8_scales(const uint8_t *st, const A8Lds &o, uint32_t (&sa)[4], uint32_t (&sw)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sa[i] = (*reinterpret_cast<const uint32_t *>(st + o.sa + 128 * i) >> o.hsh) & 0x00FF00FFu;
+        sw[i] = (*reinterpret_cast<const uint32_t *>(st + o.sw + 128 * i) >> o.hsh) & 0x00FF00FFu;
+    }
+}
+
+template <int KS>
+__device__ __forceinline__ void a8_mfma(f32x16 (&acc)[4][4], const A8Frag &f, const uint32_t (&sa)[4],
+                                        const uint32_t (&sw)[4])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx2_wide(f.w[j]), f.a[i], acc[i][j], 4, 0,
+                                                                        2 * KS, (int)sw[j], 2 * KS, (int)sa[i]);
+}
+
+template <int NR>
+__device__ __forceinline__ void a8_interleave()
+{
+#pragma unroll
+    for (int t = 0; t < NR; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 16 / NR > 0 ? 16 / NR : 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // DS read
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// One stage t (in `cur`, stage t + 1 in `nxt`); f0 / sa / sw hold step 0 of t.
+__device__ __forceinline__ void a8_stage(uint8_t *cur, const uint8_t *nxt, int t, int nk, const A8Dma &d,
+                                         const A8Dma &dz, const A8Lds &o, int wave, f32x16 (&acc)[4][4], A8Frag &f0,
+                                         A8Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[4])
+{
+    a8_frags<1>(cur, o, f1);
+    a8_mfma<0>(acc, f0, sa, sw);
+    a8_interleave<12>();
+    __builtin_amdgcn_s_waitcnt((kA8Dma & 15) | ((kA8Dma >> 4) << 14) | (7 << 4) | (15 << 8));  // stage t + 1 landed
+    __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));                                // lgkmcnt(0)
+    asm volatile("s_barrier" ::: "memory");
+    uint32_t na[4], nw[4];
+    a8_scales(nxt, o, na, nw);
+    a8_frags<0>(nxt, o, f0);
+    a8_dma(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kA8K, wave);
+    a8_mfma<1>(acc, f1, sa, sw);
+    __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);  // DS read: next stage's scales and step 0
+    __builtin_amdgcn_sched_group_barrier(0x020, kA8Dma, 0);  // VMEM: the copies
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        sa[i] = na[i];
+        sw[i] = nw[i];
+    }
+}
+
+// Epilogue: rounds of R rows per wave pair (wm = 0 rows through s0, wm = 1 through
+// s1, rows padded by 16 bytes), then whole-row 16-byte stores.
+template <typename T>
+__device__ __forceinline__ void a8_epilogue(const f32x16 (&acc)[4][4], uint8_t *s0, uint8_t *s1,
+                                            const MxGemmArgs &g, int m0, int n0, int wm, int wn, int lane, int tid)
+{
+    constexpr int es = (int)sizeof(T);
+    constexpr int pitch = es == 2 ? kA8EpiPitch16 : kA8EpiPitch32;
+    constexpr int R = es == 2 ? 64 : 32;
+    constexpr int kPer = 16 / es, kChunks = 256 / kPer;
+    uint8_t *mine = wm ? s1 : s0;
+#pragma unroll
+    for (int rd = 0; rd < 128 / R; ++rd) {
+#pragma unroll
+        for (int i = rd * R / 32; i < (rd + 1) * R / 32; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    mx2_put<T>(mine + (i * 32 - rd * R + (lane & 31)) * pitch,
+                               wn * 128 + j * 32 + 8 * gq + 4 * (lane >> 5), acc[i][j], gq);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        __syncthreads();
+        mx2_flush<T>(s0, pitch, R, g, m0 + rd * R, n0, tid);
+        mx2_flush<T>(s1, pitch, R, g, m0 + 128 + rd * R, n0, tid);
+        __syncthreads();
+    }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(256) void k_mx_gemm_w4a8(MxGemmArgs g)
+{
+    __shared__ __align__(16) uint8_t s0[kA8Stage];
+    __shared__ __align__(16) uint8_t s1[kA8Stage];
+    __shared__ __align__(16) uint8_t s2[kA8Stage];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1;
+    const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+    const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + MBN - 1) / MBN;
+    int tm, tn;
+    mx_tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * MBM, n0 = tn * MBN;
+    const int nk = K / kA8K;
+
+    A8Dma d, dz;
+    d.ra = mx2_rsrc(g.a_codes, g.M * g.K);
+    d.rw = mx2_rsrc(g.w_codes, g.N * (g.K / 2));
+    d.rsa = mx2_rsrc(g.a_scales, g.M * (g.K / 32));
+    d.rsw = mx2_rsrc(g.w_scales, g.N * (g.K / 32));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int q = 512 * wave + 64 * i + lane;
+        const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
+        d.a[i] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)K + 16 * c : kA8Out;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int q = 256 * wave + 64 * i + lane;
+        const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
+        d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * c : kA8Out;
+    }
+    const int qs = 64 * wave + lane;
+    d.sa = m0 + qs < M ? (uint32_t)(m0 + qs) * (uint32_t)(K / 32) : kA8Out;
+    d.sw = n0 + qs < N ? (uint32_t)(n0 + qs) * (uint32_t)(K / 32) : kA8Out;
+    dz = d;
+    dz.ra = mx2_rsrc(g.a_codes, 0);
+    dz.rw = mx2_rsrc(g.w_codes, 0);
+    dz.rsa = mx2_rsrc(g.a_scales, 0);
+    dz.rsw = mx2_rsrc(g.w_scales, 0);
+
+    A8Lds o;
+    {
+        const int h = lane >> 5, l = lane & 31;
+        const int ra = wm * 128 + l, rw = wn * 128 + l;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+#pragma unroll
+            for (int p = 0; p < 2; ++p) o.a[ks][p] = kA8A + 128 * ra + 16 * ((4 * ks + 2 * p + h) ^ ((ra >> 1) & 7));
+            o.w[ks] = kA8W + 64 * rw + 16 * ((2 * ks + h) ^ ((rw >> 2) & 3));
+        }
+        o.sa = kA8SA + 4 * ra;
+        o.sw = kA8SW + 4 * rw;
+        o.hsh = 8 * h;
+    }
+
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+
+    a8_dma(s0, d, 0, wave);
+    a8_dma(s1, nk > 1 ? d : dz, nk > 1 ? kA8K : 0, wave);
+    a8_dma(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kA8K : 0, wave);
+    __builtin_amdgcn_s_waitcnt(((2 * kA8Dma) & 15) | (((2 * kA8Dma) >> 4) << 14) | (7 << 4) | (15 << 8));
+    asm volatile("s_barrier" ::: "memory");
+    A8Frag f0, f1;
+    uint32_t sa[4], sw[4];
+    a8_scales(s0, o, sa, sw);
+    a8_frags<0>(s0, o, f0);
+    const int nfull = nk - nk % 3;
+    for (int t = 0; t < nfull; t += 3) {
+        a8_stage(s0, s1, t, nk, d, dz, o, wave, acc, f0, f1, sa, sw);
+        a8_stage(s1, s2, t + 1, nk, d, dz, o, wave, acc, f0, f1, sa, sw);
+        a8_stage(s2, s0, t + 2, nk, d, dz, o, wave, acc, f0, f1, sa, sw);
+    }
+    if (nk % 3 >= 1) a8_stage(s0, s1, nfull, nk, d, dz, o, wave, acc, f0, f1, sa, sw);
+    if (nk % 3 == 2) a8_stage(s1, s2, nfull + 1, nk, d, dz, o, wave, acc, f0, f1, sa, sw);
+
+    __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
+    __syncthreads();
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    a8_epilogue<OutT>(acc, s0, s1, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
+}
+
+fp4_status launch_mxfp4_gemm_w4a8(const MxGemmArgs &g, hipStream_t st)
+{
+    // 32-bit byte offsets into A (M K bytes) and W
+    if (g.K % kA8K != 0 || g.M * g.K >= (int64_t(1) << 31) || g.N * (g.K / 2) >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
+    if (g.c_bf16)
+        hipLaunchKernelGGL((k_mx_gemm_w4a8<__bf16>), dim3(tiles), dim3(256), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_mx_gemm_w4a8<float>), dim3(tiles), dim3(256), 0, st, g);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)
 {
     // the staged kernel addresses a matrix with 32-bit byte offsets

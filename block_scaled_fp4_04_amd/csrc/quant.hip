@@ -262,6 +262,53 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, ui
     if (bad && nonfinite) *nonfinite = 1;
 }
 
+// --------------------------------------------------------- MXFP8 quantize --
+//
+// The FP8 activations of W4A8 (edge-FP4 article, eefocus.com: an NPU with native
+// W4A8, weights in FP4 and activations in FP8), read as OCP MX: 32-element blocks
+// with an E8M0 scale 2^k, E4M3FN elements.  Rule 0 (OCP): k = floor(log2 amax) - 8
+// (E4M3's largest exponent is 8), so the block maximum may saturate to 448;
+// rule 1: the smallest k with 448 2^k >= amax.  Elements: sign | E4M3 RNE with
+// saturation of |x| 2^-k (exact scaling).  Lanes (4i .. 4i+3) hold one block.
+template <typename T>
+__global__ __launch_bounds__(256) void k_mxfp8_quant(const T *__restrict__ x, uint32_t units,
+                                                     FastDiv cv, int64_t ldx, int64_t cols,
+                                                     int rule, uint8_t *__restrict__ codes,
+                                                     uint8_t *__restrict__ scales,
+                                                     int32_t *__restrict__ nonfinite)
+{
+    int bad = 0;
+    for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
+        float v[8];
+        Vec8<T>::load(x + (int64_t)r * ldx + (int64_t)c8 * 8, v);
+        float bm = amax8(v, bad);
+        bm = fmaxf(bm, xor1(bm));
+        bm = fmaxf(bm, xor2(bm));
+        int k = 0;
+        uint32_t byte = 0;
+        if (bm != 0.0f) {
+            const int E = __builtin_amdgcn_frexp_expf(bm) - 1;        // floor(log2 bm), exact
+            k = E - 8;
+            if (rule == 1 && __builtin_amdgcn_frexp_mantf(bm) > 0.875f) k = E - 7;  // 448*2^(E-8) < bm
+            k = k < -127 ? -127 : (k > 127 ? 127 : k);
+            byte = (uint32_t)(k + 127);
+        }
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const uint32_t sign = (__float_as_uint(v[i]) >> 24) & 0x80u;
+            const uint32_t mag = bm == 0.0f ? 0u : e4m3_code_sat(__builtin_amdgcn_ldexpf(__builtin_fabsf(v[i]), -k));
+            if (i < 4) lo |= (sign | mag) << (8 * i);
+            else hi |= (sign | mag) << (8 * (i - 4));
+        }
+        *reinterpret_cast<uint2 *>(codes + (int64_t)r * cols + (int64_t)c8 * 8) = make_uint2(lo, hi);
+        if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
+    }
+    if (bad && nonfinite) *nonfinite = 1;
+}
+
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_mxfp4_dequant(const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ scales,
@@ -367,6 +414,22 @@ fp4_status launch_mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int6
                            units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
     else
         hipLaunchKernelGGL(k_mxfp4_quant<float>, dim3(g), dim3(256), 0, st, (const float *)x,
+                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_mxfp8_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                 int64_t ldx, uint8_t *codes, uint8_t *scales, fp4_mx_rule rule,
+                                 int32_t *nonfinite, hipStream_t st)
+{
+    const uint32_t units = (uint32_t)(rows * (cols / 8));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const unsigned g = grid_for(units, 16384);
+    if (xt == FP4_BF16)
+        hipLaunchKernelGGL(k_mxfp8_quant<uint16_t>, dim3(g), dim3(256), 0, st, (const uint16_t *)x,
+                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
+    else
+        hipLaunchKernelGGL(k_mxfp8_quant<float>, dim3(g), dim3(256), 0, st, (const float *)x,
                            units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }

@@ -233,6 +233,39 @@ fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t 
                                    const uint8_t *w_scales_p, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
                                    hipStream_t stream);
 
+/* ---- W4A8: FP4 weights x FP8 activations (eefocus.com edge-FP4 article: an NPU
+ * with native W4A8, weights quantized to FP4 and activations to FP8).  Both
+ * operands take the OCP MX form: MXFP4 weights, MXFP8 activations. ---- */
+
+/* MXFP8 quantize: x [rows][ldx] (fp32 or bf16) -> codes uint8 [rows][cols]
+ * (E4M3FN, sign kept), scales uint8 [rows][cols/32] (E8M0).  Per 32-element
+ * block: rule FP4_MX_OCP_FLOOR: 2^k with k = floor(log2 amax) - 8 (the block
+ * maximum may saturate at 448); FP4_MX_CEIL: the smallest 2^k with 448 2^k >=
+ * amax.  Elements: E4M3 round-to-nearest-even with saturation of |x| / 2^k; a
+ * zero block gets scale byte 0.  cols % 32 == 0. */
+fp4_status mxfp8_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,
+                          uint8_t *codes, uint8_t *scales, fp4_mx_rule rule, int32_t *nonfinite,
+                          hipStream_t stream);
+
+/* Workspace bytes mxfp4_gemm_w4a8 needs: A's MXFP8 codes | scales, each at a
+ * 256-byte boundary. */
+size_t mxfp4_gemm_w4a8_workspace(int64_t M, int64_t K);
+
+/* W4A8 GEMM: the bf16 A is quantized to MXFP8 with `rule` into `ws`, then
+ * C = A_q . W^T on gfx950's block-scaled matrix instruction with FP8 and FP4
+ * operands (exact products, fp32 accumulation).  W MXFP4 [N][K].  K % 128 == 0
+ * (FP4_ERR_SHAPE otherwise).  Tolerance as the other GEMMs, against fp64 over
+ * the dequantized operands. */
+fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                           const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                           fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The GEMM half of mxfp4_gemm_w4a8 on an already-quantized MXFP8 A (codes
+ * [M][K], scales [M][K/32]). */
+fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                    const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                                    fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

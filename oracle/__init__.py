@@ -84,6 +84,8 @@ def lib():
         L.fp4o_mxfp4_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, ctypes.c_int]
         L.fp4o_mxfp4_dequantize.argtypes = [p, p, i64, i64, p]
         L.fp4o_mxfp4_to_f64.argtypes = [p, p, i64, i64, p]
+        L.fp4o_mxfp8_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, ctypes.c_int]
+        L.fp4o_mxfp8_to_f64.argtypes = [p, p, i64, i64, p]
         L.fp4o_gemm_f64.argtypes = [p, p, i64, i64, i64, p, p]
         L.fp4o_num_threads.restype = ctypes.c_int
         L.fp4o_num_threads.argtypes = []
@@ -228,6 +230,28 @@ def mxfp4_to_f64(codes, scales) -> np.ndarray:
     return y
 
 
+def mxfp8_quantize(x: np.ndarray, rule: int = MX_OCP_FLOOR):
+    """MXFP8 (E4M3FN elements, E8M0 per 32): x [rows, cols] fp32 or bf16 bits,
+    cols % 32 == 0.  Returns (codes uint8 [rows, cols], scales uint8 [rows, cols/32])."""
+    x, dt = _input(x)
+    rows, cols = x.shape
+    if cols % 32:
+        raise ValueError("MXFP8 needs whole 32-element blocks along the last axis")
+    codes = np.empty((rows, cols), np.uint8)
+    scales = np.empty((rows, cols // 32), np.uint8)
+    lib().fp4o_mxfp8_quantize(_ptr(x), dt, rows, cols, cols, _ptr(codes), _ptr(scales), int(rule))
+    return codes, scales
+
+
+def mxfp8_to_f64(codes, scales) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, np.uint8)
+    scales = np.ascontiguousarray(scales, np.uint8)
+    rows, cols = codes.shape
+    y = np.empty((rows, cols), np.float64)
+    lib().fp4o_mxfp8_to_f64(_ptr(codes), _ptr(scales), rows, cols, _ptr(y))
+    return y
+
+
 # -------------------------------------------------------------------- GEMM --
 
 def gemm_f64_loop(a: np.ndarray, w: np.ndarray):
@@ -279,6 +303,16 @@ def mxfp4_gemm_w4a16_ref(a_bf16: np.ndarray, w_codes, w_scales, rows=None):
     """fp64 reference of C = A . W^T with bf16 A and W dequantized exactly (MXFP4:
     E2M1 times the block's E8M0 power of two; no tensor scale).  Returns (C_ref, T)."""
     a = bf16_bits_to_f64(a_bf16 if rows is None else a_bf16[rows])
+    w = mxfp4_to_f64(w_codes, w_scales)
+    return gemm_f64(a, w)
+
+
+def mxfp4_gemm_w4a8_ref(a_bf16: np.ndarray, w_codes, w_scales, rule=MX_OCP_FLOOR, rows=None):
+    """fp64 reference of the W4A8 GEMM: A quantized to MXFP8 by this oracle, W
+    MXFP4, both dequantized exactly, then an fp64 product.  Returns (C_ref, T)."""
+    src = a_bf16 if rows is None else a_bf16[rows]
+    ac, asc = mxfp8_quantize(src, rule)
+    a = mxfp8_to_f64(ac, asc)
     w = mxfp4_to_f64(w_codes, w_scales)
     return gemm_f64(a, w)
 

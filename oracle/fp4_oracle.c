@@ -341,6 +341,60 @@ void fp4o_mxfp4_to_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows
         }
 }
 
+/* MXFP8 quantize (the FP8 activations of W4A8; edge-FP4 article, section on
+ * W4A8 in the NPU paragraph: weights FP4, activations FP8).  Reading: OCP MX
+ * blocks of 32 elements with an E8M0 scale, E4M3FN elements.
+ * rule 0: k = floor(log2 amax_b) - 8 (E4M3's largest exponent is 8);
+ * rule 1: the smallest k with 448 * 2^k >= amax_b.
+ * k is clamped to [-127, 127], byte = k + 127; each element is |x| * 2^-k
+ * (exact) rounded to E4M3 with saturation at 448, sign kept (a negative value
+ * that rounds to 0 is 0x80).  A zero block gets byte 0 and signed zeros. */
+void fp4o_mxfp8_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx,
+                         uint8_t *codes, uint8_t *scales, int rule)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t j = 0; j < cols / 32; ++j) {
+            float xv[32];
+            float amax_b = 0.0f;
+            for (int i = 0; i < 32; ++i) {
+                xv[i] = load_x(x, dtype, r * ldx + j * 32 + i);
+                float a = fabsf(xv[i]);
+                if (a > amax_b) amax_b = a;
+            }
+            int k = 0;
+            uint8_t byte = 0;
+            int zero = (amax_b == 0.0f);
+            if (!zero) {
+                int e;
+                (void)frexp((double)amax_b, &e);
+                int E = e - 1;                         /* floor(log2 amax_b), exact */
+                if (rule == 0) k = E - 8;
+                else k = ((double)amax_b <= ldexp(1.75, E)) ? E - 8 : E - 7;
+                if (k < -127) k = -127;
+                if (k > 127) k = 127;
+                byte = (uint8_t)(k + 127);
+            }
+            scales[r * (cols / 32) + j] = byte;
+            for (int i = 0; i < 32; ++i) {
+                uint8_t sign = signbit(xv[i]) ? 0x80 : 0x00;
+                uint8_t mag = zero ? 0 : fp4o_e4m3_encode_sat((float)ldexp(fabs((double)xv[i]), -k));
+                codes[r * cols + j * 32 + i] = (uint8_t)(sign | mag);
+            }
+        }
+    }
+}
+
+/* MXFP8 dequantize to fp64: E4M3(c) * 2^(byte-127), exact. */
+void fp4o_mxfp8_to_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows, int64_t cols,
+                       double *y)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t k = 0; k < cols; ++k)
+            y[r * cols + k] = fp4o_e4m3_decode(codes[r * cols + k]) * fp4o_e8m0_decode(scales[r * (cols / 32) + k / 32]);
+}
+
 /* -------------------------------------------------------------- GEMM ------ */
 
 /* C[m][n] = sum_k a[m][k] * w[n][k] in fp64, and T[m][n] = sum_k |a w|

@@ -236,6 +236,42 @@ def test_mxfp4_w4a16_validation(L):
         assert g() == NO_DEVICE and pk() == NO_DEVICE and gd() == NO_DEVICE
 
 
+def test_w4a8_validation(L):
+    import torch
+
+    def q(**kw):
+        a = dict(x=FAKE, xt=1, rows=2, cols=64, ldx=64, codes=FAKE, scales=FAKE, rule=0,
+                 nonfinite=None, stream=None)
+        a.update(kw)
+        return L.mxfp8_quantize(*a.values())
+
+    assert q(cols=48, ldx=48) == SHAPE
+    assert q(rule=3) == DTYPE
+    assert q(codes=None) == NULL
+    assert L.mxfp4_gemm_w4a8_workspace(4, 256) == 1024 + 256
+    assert L.mxfp4_gemm_w4a8_workspace(0, 256) == 0
+
+    def g(**kw):
+        a = dict(a=FAKE, M=8, K=256, lda=256, rule=0, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=0, ldc=16,
+                 work=FAKE, work_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a8(*a.values())
+
+    assert g(K=96, lda=96) == SHAPE                   # K % 128 == 0
+    assert g(work_bytes=100) == WORKSPACE
+    assert g(rule=7) == DTYPE
+
+    def gp(**kw):
+        a = dict(ac=FAKE, asc=FAKE, M=8, K=256, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=0, ldc=16, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a8_prequant(*a.values())
+
+    assert gp(ac=None) == NULL
+    assert gp(K=160) == SHAPE
+    if not torch.cuda.is_available():
+        assert q() == NO_DEVICE and g() == NO_DEVICE and gp() == NO_DEVICE
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import block_scaled_fp4_04_amd as fp4
 

@@ -169,3 +169,33 @@ def test_mxfp4_w4a16_ref_brute_force(oracle_mod):
     got, tol = oracle_mod.mxfp4_gemm_w4a16_ref(a, codes, scales)
     assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
     assert np.all(tol >= np.abs(got) - 1e-300)
+
+
+def test_mxfp4_w4a8_ref_brute_force(oracle_mod):
+    # independent pin: A quantized by the oracle's MXFP8 (pinned on its own), both
+    # operands decoded here from the E4M3 / E2M1 / E8M0 definitions, triple loop
+    rng = np.random.default_rng(13)
+    M, N, K = 3, 4, 64
+    a = to_bf16_bits(rng.standard_normal((M, K)).astype(np.float32))
+    ac, asc = oracle_mod.mxfp8_quantize(a)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(120, 135, size=(N, K // 32), dtype=np.uint8)
+    grid = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+    def e4m3(b):
+        s, e, m = b >> 7, (b >> 3) & 15, b & 7
+        v = m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7)
+        return -v if s else v
+
+    ref = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            t = 0.0
+            for k in range(K):
+                av = e4m3(int(ac[m, k])) * 2.0 ** (int(asc[m, k // 32]) - 127)
+                nib = (int(codes[n, k // 2]) >> (4 * (k % 2))) & 15
+                wv = grid[nib & 7] * (-1.0 if nib & 8 else 1.0) * 2.0 ** (int(scales[n, k // 32]) - 127)
+                t += av * wv
+            ref[m, n] = t
+    got, _ = oracle_mod.mxfp4_gemm_w4a8_ref(a, codes, scales)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
