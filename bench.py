@@ -34,6 +34,7 @@ METRIC = "NVFP4 GEMM TFLOP/s (prefill) + decode GEMV HBM GB/s, % of roofline"
 HBM_PEAK = 8.0e12          # MI355X HBM3E, bytes/s
 BF16_PEAK = 2.5e15         # dense bf16 MFMA, FLOP/s
 FP4_PEAK = 10.1e15         # dense fp4 MFMA, FLOP/s
+FP8_PEAK = 5.0e15          # dense fp8 MFMA (also an fp8 x fp4 product), FLOP/s
 N, K = 17408, 5120
 
 
@@ -317,6 +318,13 @@ def components(args, torch, fp4, T, dev, w32, wq):
     wsn = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     t_nall = T.per_launch(lambda i: fp4.gemm_w4a4(a, wnv, a_mode="row", out=c, workspace=wsn), it)
     c_nv = c.clone()
+    # W4A8: the same MXFP4 weights, activations as MXFP8
+    ws8 = fp4.mxfp4_gemm_w4a8_workspace(M, K, dev)
+    pa8 = fp4.mxfp8_packed_a(ws8, M, K)
+    t_8q = T.per_launch(lambda i: fp4.mxfp8_quantize(a, out=pa8), it)
+    t_8g = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_prequant(pa8, wmx, out=c), it)
+    t_8all = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8(a, wmx, out=c, workspace=ws8), it)
+    c_a8 = c.clone()
     torch.cuda.synchronize()
     # quantization error against the unquantized bf16 product, on sampled rows
     rows = np.random.default_rng(0).choice(M, 64, replace=False)
@@ -325,7 +333,7 @@ def components(args, torch, fp4, T, dev, w32, wq):
     ref = a64 @ w64.T
     rt = torch.from_numpy(rows).to(dev)
     err = {}
-    for name, cc in (("mxfp4", c_mx), ("nvfp4", c_nv)):
+    for name, cc in (("mxfp4", c_mx), ("nvfp4", c_nv), ("w4a8_mxfp8_mxfp4", c_a8)):
         got = cc[rt].float().cpu().numpy().astype(np.float64)
         err[name] = {"rel_fro": float(np.linalg.norm(got - ref) / np.linalg.norm(ref)),
                      "max_abs_over_max_ref": float(np.abs(got - ref).max() / np.abs(ref).max())}
@@ -335,6 +343,9 @@ def components(args, torch, fp4, T, dev, w32, wq):
         "mxfp4_total_us": t_mall * 1e6, "mxfp4_total_TFLOP/s": fl / t_mall / 1e12,
         "nvfp4_total_us": t_nall * 1e6, "nvfp4_total_TFLOP/s": fl / t_nall / 1e12,
         "nvfp4_frac_bf16_mfma": fl / t_nall / BF16_PEAK,
+        "w4a8_quant_us": t_8q * 1e6, "w4a8_gemm_us": t_8g * 1e6,
+        "w4a8_gemm_TFLOP/s": fl / t_8g / 1e12, "w4a8_gemm_frac_fp8_mfma": fl / t_8g / FP8_PEAK,
+        "w4a8_total_us": t_8all * 1e6, "w4a8_total_TFLOP/s": fl / t_8all / 1e12,
         "error_vs_bf16_product_64_rows": err}
     return {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
             for k, v in out.items()}
