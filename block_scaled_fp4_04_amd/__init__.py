@@ -72,6 +72,13 @@ def _declare(L):
         "mxfp4_gemm_w4a8_workspace": (sz, [i64, i64]),
         "mxfp4_gemm_w4a8": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
         "mxfp4_gemm_w4a8_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
+        "nvfp4_grouped_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, i64, p, p, p, i64, p, i32, i64, p]),
+        "mxfp4_grouped_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, i64, p, p, i64, p, i32, i64, p]),
+        "nvfp4_grouped_gemm_w4a4_workspace": (sz, [i64, i64]),
+        "nvfp4_grouped_gemm_w4a4": (i32, [p, i64, i64, i64, p, p, i64, i64, p, p, p, i64, p, i32, i64, p, sz,
+                                          p]),
+        "nvfp4_grouped_gemm_w4a4_prequant": (i32, [p, p, p, i64, i64, p, p, i64, i64, p, p, p, i64, p, i32,
+                                                   i64, p]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)
@@ -494,4 +501,130 @@ def mxfp4_gemm_w4a8_prequant(a: PackedMXFP8, w: PackedMXFP4, dtype=torch.bfloat1
     _check(L.mxfp4_gemm_w4a8_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
                                       _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
                                       _stream()))
+    return out
+
+
+# ------------------------------------------------------- grouped (MoE) -----
+
+@dataclasses.dataclass
+class ExpertsNVFP4:
+    """E NVFP4 expert weights [E, N, K]: codes uint8 [E, N, K/2], scales uint8
+    [E, N, K/16], one float32 tensor scale per expert [E]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    tscale: torch.Tensor
+    experts: int
+    rows: int
+    cols: int
+
+
+@dataclasses.dataclass
+class ExpertsMXFP4:
+    """E MXFP4 expert weights [E, N, K]: codes uint8 [E, N, K/2], scales uint8 [E, N, K/32]."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    experts: int
+    rows: int
+    cols: int
+
+
+def nvfp4_quantize_experts(w: torch.Tensor) -> ExpertsNVFP4:
+    """Each expert of w [E, N, K] quantized as its own NVFP4 tensor (its own tensor scale)."""
+    E, N, K = w.shape
+    dev = w.device
+    out = ExpertsNVFP4(torch.empty(E, N, K // 2, dtype=torch.uint8, device=dev),
+                       torch.empty(E, N, K // 16, dtype=torch.uint8, device=dev),
+                       torch.empty(E, dtype=torch.float32, device=dev), E, N, K)
+    ws = torch.empty(max(1, lib().nvfp4_quantize_workspace(N, K, PER_TENSOR)), dtype=torch.uint8, device=dev)
+    for e in range(E):
+        nvfp4_quantize(w[e], out=PackedNVFP4(out.codes[e], out.scales[e], out.tscale[e:e + 1], N, K),
+                       workspace=ws)
+    return out
+
+
+def mxfp4_quantize_experts(w: torch.Tensor, rule="ocp") -> ExpertsMXFP4:
+    """MXFP4 of expert weights w [E, N, K] (blocks along K; no tensor scale)."""
+    E, N, K = w.shape
+    p = mxfp4_quantize(w.reshape(E * N, K), rule=rule)
+    return ExpertsMXFP4(p.codes.view(E, N, K // 2), p.scales.view(E, N, K // 32), E, N, K)
+
+
+def _grouped_common(a_rows, group_offs, row_index):
+    _need_cuda(group_offs, row_index)
+    if group_offs.dtype != torch.int32 or not group_offs.is_contiguous():
+        raise TypeError("group_offs must be a contiguous int32 device tensor [groups + 1]")
+    if row_index is not None and (row_index.dtype != torch.int32 or not row_index.is_contiguous()):
+        raise TypeError("row_index must be a contiguous int32 device tensor [rows]")
+    rows = row_index.numel() if row_index is not None else a_rows
+    return rows, group_offs.numel() - 1
+
+
+def nvfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch.Tensor,
+                             row_index: torch.Tensor | None = None, dtype=torch.bfloat16,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """C[t] = A[row_index[t]] . W_e^T for the grouped rows t of group e (bf16 A, NVFP4 experts)."""
+    L = lib()
+    _need_cuda(a)
+    rows, groups = _grouped_common(a.shape[0], group_offs, row_index)
+    if out is None:
+        out = torch.empty(rows, w.rows, dtype=dtype, device=a.device)
+    _check(L.nvfp4_grouped_gemm_w4a16(_ptr(a), a.shape[0], a.shape[1], _ld(a), _ptr(row_index), _ptr(group_offs),
+                                      groups, rows, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                                      _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+def mxfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsMXFP4, group_offs: torch.Tensor,
+                             row_index: torch.Tensor | None = None, dtype=torch.bfloat16,
+                             out: torch.Tensor | None = None) -> torch.Tensor:
+    """As nvfp4_grouped_gemm_w4a16 with MXFP4 experts."""
+    L = lib()
+    _need_cuda(a)
+    rows, groups = _grouped_common(a.shape[0], group_offs, row_index)
+    if out is None:
+        out = torch.empty(rows, w.rows, dtype=dtype, device=a.device)
+    _check(L.mxfp4_grouped_gemm_w4a16(_ptr(a), a.shape[0], a.shape[1], _ld(a), _ptr(row_index), _ptr(group_offs),
+                                      groups, rows, _ptr(w.codes), _ptr(w.scales), w.rows, _ptr(out),
+                                      _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+def nvfp4_grouped_gemm_w4a4_workspace(a_rows: int, K: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib().nvfp4_grouped_gemm_w4a4_workspace(a_rows, K), dtype=torch.uint8, device=device)
+
+
+def nvfp4_grouped_gemm_w4a4(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch.Tensor,
+                            row_index: torch.Tensor | None = None, dtype=torch.bfloat16,
+                            out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """NVFP4 W4A4 grouped GEMM: every A row quantized once per row, then gathered per group."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("nvfp4_grouped_gemm_w4a4 takes bfloat16 activations")
+    rows, groups = _grouped_common(a.shape[0], group_offs, row_index)
+    if workspace is None:
+        workspace = nvfp4_grouped_gemm_w4a4_workspace(a.shape[0], a.shape[1], a.device)
+    if out is None:
+        out = torch.empty(rows, w.rows, dtype=dtype, device=a.device)
+    _check(L.nvfp4_grouped_gemm_w4a4(_ptr(a), a.shape[0], a.shape[1], _ld(a), _ptr(row_index), _ptr(group_offs),
+                                     groups, rows, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                                     _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                                     _stream()))
+    return out
+
+
+def nvfp4_grouped_gemm_w4a4_prequant(a: PackedNVFP4, w: ExpertsNVFP4, group_offs: torch.Tensor,
+                                     row_index: torch.Tensor | None = None, dtype=torch.bfloat16,
+                                     out: torch.Tensor | None = None) -> torch.Tensor:
+    """The GEMM half of nvfp4_grouped_gemm_w4a4 on a per-row NVFP4 A."""
+    L = lib()
+    if not a.per_row:
+        raise ValueError("the grouped W4A4 GEMM takes a per-row NVFP4 A")
+    rows, groups = _grouped_common(a.rows, group_offs, row_index)
+    if out is None:
+        out = torch.empty(rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.nvfp4_grouped_gemm_w4a4_prequant(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale), a.rows, a.cols,
+                                              _ptr(row_index), _ptr(group_offs), groups, rows, _ptr(w.codes),
+                                              _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
+                                              _out_dt(out.dtype), _ld(out), _stream()))
     return out

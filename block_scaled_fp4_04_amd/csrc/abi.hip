@@ -497,4 +497,146 @@ fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4
     return mxfp4_gemm_w4a8_prequant(ac, as, M, K, w_codes, w_scales, N, c, ct, ldc, stream);
 }
 
+// ------------------------------------------------------- grouped (MoE) --
+
+namespace {
+
+constexpr int64_t kMaxGroups = 1 << 16;
+
+// Arguments every grouped GEMM shares.  rows == 0 (no routed rows) is valid: once
+// the sizes and group arguments check out, *empty is set and the caller returns
+// FP4_OK without touching A, W or C (which may then be empty, even null).
+fp4_status check_grouped(int64_t a_rows, int64_t K, const int32_t *row_index, const int32_t *group_offs,
+                         int64_t groups, int64_t rows, int64_t N, int kblock, const void *c, fp4_dtype ct,
+                         int64_t ldc, bool *empty)
+{
+    if (rows < 0) return FP4_ERR_SHAPE;
+    if (groups <= 0 || groups > kMaxGroups) return FP4_ERR_SHAPE;
+    if (!group_offs) return FP4_ERR_NULL;
+    *empty = rows == 0;
+    if (*empty) {
+        if (!valid_dtype(ct)) return FP4_ERR_DTYPE;
+        return N > 0 && K > 0 && K % kblock == 0 ? FP4_OK : FP4_ERR_SHAPE;
+    }
+    FP4_TRY(check_gemm_common(rows, K, N, kblock, c, ct, ldc));
+    if (a_rows <= 0 || a_rows > INT32_MAX / 2) return FP4_ERR_SHAPE;
+    if (!row_index && a_rows < rows) return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
+NvGemmArgs grouped_args(int64_t a_rows, int64_t K, const int32_t *row_index, const int32_t *group_offs,
+                        int64_t groups, int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales,
+                        const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc)
+{
+    NvGemmArgs g{};
+    g.w_codes = w_codes;
+    g.w_scales = w_scales;
+    g.w_tscale = w_tscale;
+    g.M = rows;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    g.groups = (int)groups;
+    g.group_offs = group_offs;
+    g.row_index = row_index;
+    g.a_rows = a_rows;
+    return g;
+}
+
+}  // namespace
+
+fp4_status nvfp4_grouped_gemm_w4a16(const void *a, int64_t a_rows, int64_t K, int64_t lda,
+                                    const int32_t *row_index, const int32_t *group_offs, int64_t groups,
+                                    int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales,
+                                    const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                                    hipStream_t stream)
+{
+    bool empty = false;
+    FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 64, c, ct, ldc, &empty));
+    if (empty) return FP4_OK;
+    FP4_TRY(check_matrix(a, a_rows, K, lda, 2));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!w_tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_device());
+    NvGemmArgs g = grouped_args(a_rows, K, row_index, group_offs, groups, rows, w_codes, w_scales, w_tscale, N, c,
+                                ct, ldc);
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    return launch_grouped_gemm(g, 0, stream);
+}
+
+fp4_status mxfp4_grouped_gemm_w4a16(const void *a, int64_t a_rows, int64_t K, int64_t lda,
+                                    const int32_t *row_index, const int32_t *group_offs, int64_t groups,
+                                    int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales, int64_t N,
+                                    void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    bool empty = false;
+    FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 128, c, ct, ldc, &empty));
+    if (empty) return FP4_OK;
+    FP4_TRY(check_matrix(a, a_rows, K, lda, 2));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    FP4_TRY(check_device());
+    NvGemmArgs g = grouped_args(a_rows, K, row_index, group_offs, groups, rows, w_codes, w_scales, nullptr, N, c,
+                                ct, ldc);
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    return launch_grouped_gemm(g, 2, stream);
+}
+
+fp4_status nvfp4_grouped_gemm_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales,
+                                            const float *a_tscale, int64_t a_rows, int64_t K,
+                                            const int32_t *row_index, const int32_t *group_offs,
+                                            int64_t groups, int64_t rows, const uint8_t *w_codes,
+                                            const uint8_t *w_scales, const float *w_tscale, int64_t N,
+                                            void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    bool empty = false;
+    FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 64, c, ct, ldc, &empty));
+    if (empty) return FP4_OK;
+    FP4_TRY(check_packed(a_codes, a_scales));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!a_tscale || !w_tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_device());
+    NvGemmArgs g = grouped_args(a_rows, K, row_index, group_offs, groups, rows, w_codes, w_scales, w_tscale, N, c,
+                                ct, ldc);
+    g.a_codes = a_codes;
+    g.a_scales = a_scales;
+    g.a_tscale = a_tscale;
+    g.a_per_row = 1;
+    return launch_grouped_gemm(g, 1, stream);
+}
+
+size_t nvfp4_grouped_gemm_w4a4_workspace(int64_t a_rows, int64_t K)
+{
+    return gemm_w4a4_workspace(a_rows, K, FP4_SCALE_PER_ROW);
+}
+
+fp4_status nvfp4_grouped_gemm_w4a4(const void *a, int64_t a_rows, int64_t K, int64_t lda,
+                                   const int32_t *row_index, const int32_t *group_offs, int64_t groups,
+                                   int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales,
+                                   const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws,
+                                   size_t ws_bytes, hipStream_t stream)
+{
+    bool empty = false;
+    FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 64, c, ct, ldc, &empty));
+    if (empty) return FP4_OK;
+    FP4_TRY(check_matrix(a, a_rows, K, lda, 2));
+    if (a_rows * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!w_tscale) return FP4_ERR_NULL;
+    if (!ws || !aligned16(ws) || ws_bytes < nvfp4_grouped_gemm_w4a4_workspace(a_rows, K))
+        return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    size_t co, so, to;
+    gemm_w4a4_workspace_offsets(a_rows, K, &co, &so, &to);
+    uint8_t *base = reinterpret_cast<uint8_t *>(ws);
+    float *at = reinterpret_cast<float *>(base + to);
+    FP4_TRY(launch_nvfp4_quantize(a, FP4_BF16, a_rows, K, lda, base + co, base + so, at, FP4_SCALE_PER_ROW,
+                                  nullptr, nullptr, stream));
+    return nvfp4_grouped_gemm_w4a4_prequant(base + co, base + so, at, a_rows, K, row_index, group_offs, groups,
+                                            rows, w_codes, w_scales, w_tscale, N, c, ct, ldc, stream);
+}
+
 }  // extern "C"

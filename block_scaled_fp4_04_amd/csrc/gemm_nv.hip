@@ -1036,7 +1036,8 @@ __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, 
 template <typename T, int F, int L, int TM, int TN>
 __device__ __forceinline__ void nv_ring_epilogue(
     const f32x16 (&acc)[NvTile<F == 1, L, TM, TN>::NI][NvTile<F == 1, L, TM, TN>::NJ], uint8_t *s0, uint8_t *s1,
-    const NvGemmArgs &g, int m0, int n0, int wave, int lane, int tid)
+    const NvGemmArgs &g, int m0, int n0, int wave, int lane, int tid, const int32_t *ridx = nullptr,
+    int a_rows = 0)
 {
     using S = NvTile<F == 1, L, TM, TN>;
     constexpr int NI = S::NI, NJ = S::NJ, H = S::H;
@@ -1058,7 +1059,11 @@ __device__ __forceinline__ void nv_ring_epilogue(
             if (rr / R != rd) continue;
             const int m = m0 + r0 + 32 * i + (lane & 31);
             float sc = wt;
-            if (A_FP4) sc = (m < M ? g.a_tscale[g.a_per_row ? m : 0] : 0.f) * wt;
+            if (A_FP4) {
+                int am = m < M ? m : -1;  // the row's A row, for its per-row scale
+                if (ridx && am >= 0) am = (uint32_t)ridx[m] < (uint32_t)a_rows ? ridx[m] : -1;
+                sc = (am >= 0 ? g.a_tscale[g.a_per_row ? am : 0] : 0.f) * wt;
+            }
             uint8_t *buf = (L ? 32 * i : r0) >= H ? s1 : s0;
             uint8_t *row = buf + (rr - rd * R + (lane & 31)) * pitch;
 #pragma unroll
@@ -1105,7 +1110,70 @@ __device__ __forceinline__ void nv_ring_epilogue(
     }
 }
 
-template <int F, int L, typename OutT, int TM, int TN>
+__device__ __forceinline__ int nv_wave_incl_scan(int v, int lane)
+{
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        const int t = __shfl_up(v, d);
+        if (lane >= d) v += t;
+    }
+    return v;
+}
+
+// Grouped (MoE) launches.  Group e owns grouped rows [offs[e], offs[e + 1])
+// (each clamped to [0, M]) and needs ceil(rows / TM) * tiles_n tiles.  Every
+// wave scans the offsets 64 groups at a time: the total tile count first (blocks
+// at or past it leave), then the group that holds this block's tile.  Block b
+// takes logical tile L in the XCD-aware order of tile_of; within a group the tile
+// rows vary fastest, so the tiles that share a weight panel sit together.
+template <int TM, int TN>
+__device__ __forceinline__ bool nv_group_tile(const NvGemmArgs &g, int b, int &e, int &tm, int &tn, int &row0,
+                                              int &rows)
+{
+    const int T = (int)g.M, E = g.groups, tiles_n = ((int)g.N + TN - 1) / TN;
+    const int lane = threadIdx.x & 63, passes = (E + 63) / 64;
+    auto group = [&](int c, int &lo, int &hi) -> int {  // tiles of group 64 c + lane
+        const int i = 64 * c + lane;
+        lo = hi = 0;
+        if (i >= E) return 0;
+        lo = min(max(g.group_offs[i], 0), T);
+        hi = min(max(g.group_offs[i + 1], 0), T);
+        return hi > lo ? ((hi - lo + TM - 1) / TM) * tiles_n : 0;
+    };
+    int total = 0;
+    for (int c = 0; c < passes; ++c) {
+        int lo, hi;
+        total += __shfl(nv_wave_incl_scan(group(c, lo, hi), lane), 63);
+    }
+    total = __builtin_amdgcn_readfirstlane(total);
+    if (b >= total) return false;
+    const int per = (total + 7) / 8, xcd = b % 8, idx = b / 8, full = total % 8;
+    const int L = full == 0 || xcd < full ? xcd * per + idx : full * per + (xcd - full) * (per - 1) + idx;
+    int before = 0;
+    for (int c = 0; c < passes; ++c) {
+        int lo, hi;
+        const int n = group(c, lo, hi);
+        const int incl = nv_wave_incl_scan(n, lane);
+        const int sum = __builtin_amdgcn_readfirstlane(__shfl(incl, 63));
+        if (L < before + sum) {
+            const int j = (int)__builtin_ctzll(__ballot(before + incl > L));
+            e = 64 * c + j;
+            const int start = before + __builtin_amdgcn_readfirstlane(__shfl(incl - n, j));
+            row0 = __builtin_amdgcn_readfirstlane(__shfl(lo, j));
+            rows = __builtin_amdgcn_readfirstlane(__shfl(hi, j)) - row0;
+            const int tiles_me = (rows + TM - 1) / TM, li = L - start;
+            tm = li % tiles_me;
+            tn = li / tiles_me;
+            return true;
+        }
+        before += sum;
+    }
+    return false;
+}
+
+// GR: the grouped form (one weight per group, rows by group offsets, optional
+// row gather from A; see NvGemmArgs)
+template <int F, int L, typename OutT, int TM, int TN, bool GR = false>
 __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
 {
     using S = NvTile<F == 1, L, TM, TN>;
@@ -1117,35 +1185,75 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
     __shared__ __align__(16) uint8_t s2[S::kStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
-    const int tiles_m = (M + TM - 1) / TM, tiles_n = (N + TN - 1) / TN;
+    const int N = (int)g.N, K = (int)g.K;
+    const int tiles_n = (N + TN - 1) / TN;
     int tm, tn;
-    tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int32_t *ridx = nullptr;  // grouped row -> A row (gathered groups)
+    int a_rows = (int)g.M;          // rows the A descriptors cover
+    if constexpr (GR) {
+        int e, row0, rows;
+        if (!nv_group_tile<TM, TN>(g, blockIdx.x, e, tm, tn, row0, rows)) return;
+        g.w_codes += (int64_t)e * N * (K / 2);
+        g.w_scales += (int64_t)e * N * (K / kWsRow);
+        if constexpr (F != kFmtMx16) g.w_tscale += e;
+        g.c = reinterpret_cast<uint8_t *>(g.c) + (int64_t)row0 * g.ldc * (int64_t)sizeof(OutT);
+        g.M = rows;
+        if (g.row_index) {
+            ridx = g.row_index + row0;
+            a_rows = (int)g.a_rows;
+        } else {
+            a_rows = rows;
+            if constexpr (A_FP4) {
+                g.a_codes += (int64_t)row0 * (K / 2);
+                g.a_scales += (int64_t)row0 * (K / 16);
+                if (g.a_per_row) g.a_tscale += row0;
+            } else {
+                g.a += (int64_t)row0 * g.lda;
+            }
+        }
+    } else {
+        tile_of(blockIdx.x, gridDim.x, ((int)g.M + TM - 1) / TM, tiles_n, tm, tn);
+    }
+    const int M = (int)g.M;
     const int m0 = tm * TM, n0 = tn * TN;
     const int nk = K / kRK;
+    // A row of tile row m (-1: none; a gathered index outside A counts as none)
+    auto arow = [&](int m) -> int {
+        if (m >= M) return -1;
+        if constexpr (GR) {
+            if (ridx) {
+                const int v = ridx[m];
+                return (uint32_t)v < (uint32_t)a_rows ? v : -1;
+            }
+        }
+        return m;
+    };
 
     NvRingDma d, dz;
     d.rw = nv_rsrc(g.w_codes, (int64_t)N * (K / 2));
     d.rws = nv_rsrc(g.w_scales, (int64_t)N * (K / kWsRow));
     if constexpr (A_FP4) {
-        d.ra = nv_rsrc(g.a_codes, (int64_t)M * (K / 2));
-        d.ras = nv_rsrc(g.a_scales, (int64_t)M * (K / 16));
+        d.ra = nv_rsrc(g.a_codes, (int64_t)a_rows * (K / 2));
+        d.ras = nv_rsrc(g.a_scales, (int64_t)a_rows * (K / 16));
 #pragma unroll
         for (int i = 0; i < S::nA; ++i) {
             const int q = 64 * S::nA * wave + 64 * i + lane;
             const int r = q >> 1, h = (q & 1) ^ ((r >> 3) & 1);
-            d.a[i] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
+            const int ar = arow(m0 + r);
+            d.a[i] = ar >= 0 ? (uint32_t)ar * (uint32_t)(K / 2) + 16 * h : kNvOut;
         }
         const int qa = (64 * wave + lane) % TM;
-        d.as = m0 + qa < M ? (uint32_t)(m0 + qa) * (uint32_t)(K / 16) : kNvOut;
+        const int ara = arow(m0 + qa);
+        d.as = ara >= 0 ? (uint32_t)ara * (uint32_t)(K / 16) : kNvOut;
     } else {
-        d.ra = nv_rsrc(g.a, ((int64_t)(M - 1) * g.lda + K) * 2);
+        d.ra = nv_rsrc(g.a, ((int64_t)(a_rows - 1) * g.lda + K) * 2);
         d.ras = d.ra;
 #pragma unroll
         for (int i = 0; i < S::nA; ++i) {
             const int q = 64 * S::nA * wave + 64 * i + lane;
             const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
-            d.a[i] = m0 + r < M ? (uint32_t)(((int64_t)(m0 + r) * g.lda + 8 * c) * 2) : kNvOut;
+            const int ar = arow(m0 + r);
+            d.a[i] = ar >= 0 ? (uint32_t)(((int64_t)ar * g.lda + 8 * c) * 2) : kNvOut;
         }
         d.as = kNvOut;
     }
@@ -1191,7 +1299,7 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    nv_ring_epilogue<OutT, F, L, TM, TN>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e);
+    nv_ring_epilogue<OutT, F, L, TM, TN>(acc, s0, s1, g, m0, n0, wave, lane_e, 64 * wave + lane_e, ridx, a_rows);
 }
 
 constexpr size_t kGemmLds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);  // 128 KiB
@@ -1249,6 +1357,44 @@ static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
         }
     }
     launch_ring<F, L, 256, 256>(g, st);
+}
+
+// Grouped launches: the grid is an upper bound of the tile count (sum over groups
+// of ceil(rows / TM) <= ceil(M / TM) + groups); blocks past the real count leave
+// at once.  TM = 128 unless groups average 512 rows or more (the last tile of a
+// group is on average half empty).
+template <int F, int L, int TM>
+static void launch_ring_grouped(const NvGemmArgs &g, hipStream_t st)
+{
+    const int64_t grid = ((g.M + TM - 1) / TM + g.groups) * ((g.N + 255) / 256);
+    if (g.c_bf16)
+        hipLaunchKernelGGL((k_nv_gemm_ring<F, L, __bf16, TM, 256, true>), dim3((unsigned)grid), dim3(256), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_nv_gemm_ring<F, L, float, TM, 256, true>), dim3((unsigned)grid), dim3(256), 0, st, g);
+}
+
+fp4_status launch_grouped_gemm(const NvGemmArgs &g, int fmt, hipStream_t st)
+{
+    const bool a_fp4 = fmt == kFmtNv44;
+    // 32-bit byte offsets into A and into one group's weight
+    const int64_t a_bytes = a_fp4 ? g.a_rows * (g.K / 2) : g.a_rows * g.lda * 2;
+    if (g.K % (fmt == kFmtMx16 ? 128 : kRK) != 0 || a_bytes >= (int64_t(1) << 31) ||
+        g.N * (g.K / 2) >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    if (((g.M + 127) / 128 + g.groups) * ((g.N + 255) / 256) >= (int64_t(1) << 31)) return FP4_ERR_SHAPE;
+    const bool big = g.M >= 512 * (int64_t)g.groups;
+    switch (fmt) {
+    case kFmtNv16:
+        big ? launch_ring_grouped<kFmtNv16, kNvL16, 256>(g, st) : launch_ring_grouped<kFmtNv16, kNvL16, 128>(g, st);
+        break;
+    case kFmtNv44:
+        big ? launch_ring_grouped<kFmtNv44, 0, 256>(g, st) : launch_ring_grouped<kFmtNv44, 0, 128>(g, st);
+        break;
+    default:
+        big ? launch_ring_grouped<kFmtMx16, kNvL16, 256>(g, st) : launch_ring_grouped<kFmtMx16, kNvL16, 128>(g, st);
+        break;
+    }
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
 fp4_status launch_mxfp4_gemm_w4a16(const NvGemmArgs &g, hipStream_t st)

@@ -52,9 +52,20 @@ struct NvGemmArgs {
     void *c;
     int c_bf16;
     int64_t ldc;
+    // grouped (MoE) form, groups > 0: M is the number of grouped rows (rows of C),
+    // group e owns rows group_offs[e] .. group_offs[e + 1] - 1 and multiplies them by
+    // weight e (w_codes / w_scales advance by one [N][K] weight per group, w_tscale
+    // by one float); grouped row t reads A row row_index[t] (of a_rows rows), or row
+    // t when row_index is null
+    int groups;
+    const int32_t *group_offs;
+    const int32_t *row_index;
+    int64_t a_rows;
 };
 
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st);
+// grouped GEMM on the ring kernel: F = 0 NVFP4 W4A16, 1 NVFP4 W4A4, 2 MXFP4 W4A16
+fp4_status launch_grouped_gemm(const NvGemmArgs &g, int fmt, hipStream_t st);
 
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();

@@ -266,6 +266,68 @@ fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_sca
                                     const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
                                     fp4_dtype ct, int64_t ldc, hipStream_t stream);
 
+/* ---------------------------------------------------- grouped (MoE) ------ */
+
+/* Grouped GEMMs for mixture-of-experts layers (eefocus.com edge-FP4 article, "FP4
+ * as the next core standard": MoE expert weights stored as MXFP4; aixq.cc article
+ * on Unsloth's Dynamic NVFP4, throughput section: a mixture-of-experts model run
+ * with NVFP4 weights, and all-W4A4 in its "Fast" form).
+ *
+ * One weight per group (expert), stacked: codes [groups][N][K/2], scales
+ * [groups][N][K/16] (NVFP4, E4M3) or [groups][N][K/32] (MXFP4, E8M0), NVFP4
+ * tensor scales [groups] floats.  The `rows` grouped rows are the rows of C
+ * [rows][ldc]; group e owns rows group_offs[e] .. group_offs[e+1]-1 and
+ *   C[t] = A[row_index[t]] . W_e^T      (A[t] when row_index is null),
+ * so a router's permutation is applied while A is loaded and C comes out in
+ * grouped order.  A has a_rows rows; without row_index a_rows >= rows.
+ *
+ * group_offs (device, int32 [groups+1]) must be nondecreasing from 0 to rows,
+ * and row_index (device, int32 [rows]) entries must lie in [0, a_rows).  Other
+ * values give unspecified C but no access outside the buffers: offsets are
+ * clamped to [0, rows], and a row index outside A reads as a zero row.  Empty
+ * groups are allowed.  rows == 0 returns FP4_OK once groups, group_offs, K, N
+ * and the output dtype check out, touching nothing (A, W, C may be null then).
+ * groups <= 65536.
+ * Errors (checked on the host, nothing launched): FP4_ERR_SHAPE for K not a
+ * multiple of 64 (NVFP4) or 128 (MXFP4), A past 2 GiB or one group's weight
+ * codes past 2 GiB; FP4_ERR_NULL, FP4_ERR_LAYOUT as the other GEMMs.
+ * Tolerance as the ungrouped GEMMs, row by row. */
+
+/* NVFP4 weights, bf16 A [a_rows][lda]: each weight widened exactly to bf16,
+ * fp32 accumulation, times the group's tensor scale. */
+fp4_status nvfp4_grouped_gemm_w4a16(const void *a, int64_t a_rows, int64_t K, int64_t lda,
+                                    const int32_t *row_index, const int32_t *group_offs, int64_t groups,
+                                    int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales,
+                                    const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                                    hipStream_t stream);
+
+/* MXFP4 weights, bf16 A: weights widened exactly (E2M1 times a power of two). */
+fp4_status mxfp4_grouped_gemm_w4a16(const void *a, int64_t a_rows, int64_t K, int64_t lda,
+                                    const int32_t *row_index, const int32_t *group_offs, int64_t groups,
+                                    int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales, int64_t N,
+                                    void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
+/* Workspace bytes of nvfp4_grouped_gemm_w4a4: A's per-row NVFP4 form, laid out
+ * as gemm_w4a4's per-row workspace for a_rows x K. */
+size_t nvfp4_grouped_gemm_w4a4_workspace(int64_t a_rows, int64_t K);
+
+/* NVFP4 W4A4: every A row (token) is quantized once, per row, into `ws`; the
+ * grouped GEMM then reads the packed rows through row_index. */
+fp4_status nvfp4_grouped_gemm_w4a4(const void *a, int64_t a_rows, int64_t K, int64_t lda,
+                                   const int32_t *row_index, const int32_t *group_offs, int64_t groups,
+                                   int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales,
+                                   const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws,
+                                   size_t ws_bytes, hipStream_t stream);
+
+/* The GEMM half of nvfp4_grouped_gemm_w4a4 on a per-row NVFP4 A (codes
+ * [a_rows][K/2], scales [a_rows][K/16], a_tscale [a_rows]). */
+fp4_status nvfp4_grouped_gemm_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales,
+                                            const float *a_tscale, int64_t a_rows, int64_t K,
+                                            const int32_t *row_index, const int32_t *group_offs,
+                                            int64_t groups, int64_t rows, const uint8_t *w_codes,
+                                            const uint8_t *w_scales, const float *w_tscale, int64_t N,
+                                            void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -324,3 +324,50 @@ def mxfp4_gemm_w4a4_ref(a_bf16: np.ndarray, w_codes, w_scales, rule=MX_OCP_FLOOR
     a = mxfp4_to_f64(ac, asc)
     w = mxfp4_to_f64(w_codes, w_scales)
     return gemm_f64(a, w)
+
+
+# ------------------------------------------------------- grouped (MoE) --
+#
+# Mixture-of-experts layers (edge-FP4 article, eefocus.com, "FP4 as the next core
+# standard": expert weights in MXFP4; Unsloth Dynamic NVFP4 article, aixq.cc,
+# throughput section: a mixture-of-experts model with NVFP4 weights, W4A16 and
+# all-W4A4).  Grouped row t of group e (group_offs[e] <= t < group_offs[e + 1])
+# is C[t] = A[row_index[t]] . W_e^T, over exactly dequantized operands in fp64.
+
+def _grouped_ref(a_f64, w_f64_of, group_offs, row_index, rows):
+    offs = np.asarray(group_offs, np.int64)
+    sel = np.arange(int(offs[-1])) if rows is None else np.asarray(rows, np.int64)
+    grp = np.searchsorted(offs, sel, side="right") - 1     # last group starting at or before t
+    arow = sel if row_index is None else np.asarray(row_index, np.int64)[sel]
+    out_c = out_t = None
+    for e in np.unique(grp):
+        m = grp == e
+        c, t = gemm_f64(a_f64[arow[m]], w_f64_of(int(e)))
+        if out_c is None:
+            out_c = np.zeros((len(sel), c.shape[1]))
+            out_t = np.zeros((len(sel), c.shape[1]))
+        out_c[m], out_t[m] = c, t
+    return out_c, out_t
+
+
+def nvfp4_grouped_gemm_w4a16_ref(a_bf16, w_codes, w_scales, w_tscale, group_offs, row_index=None, rows=None):
+    """fp64 grouped W4A16 with NVFP4 experts (codes [E, N, K/2], scales [E, N, K/16],
+    tensor scales [E]); ``rows`` restricts it to those grouped rows.  Returns (C_ref, T)."""
+    a = bf16_bits_to_f64(a_bf16)
+    return _grouped_ref(a, lambda e: nvfp4_to_f64(w_codes[e], w_scales[e], np.asarray(w_tscale)[e:e + 1]),
+                        group_offs, row_index, rows)
+
+
+def mxfp4_grouped_gemm_w4a16_ref(a_bf16, w_codes, w_scales, group_offs, row_index=None, rows=None):
+    """fp64 grouped W4A16 with MXFP4 experts (codes [E, N, K/2], scales [E, N, K/32])."""
+    a = bf16_bits_to_f64(a_bf16)
+    return _grouped_ref(a, lambda e: mxfp4_to_f64(w_codes[e], w_scales[e]), group_offs, row_index, rows)
+
+
+def nvfp4_grouped_gemm_w4a4_ref(a_bf16, w_codes, w_scales, w_tscale, group_offs, row_index=None, rows=None):
+    """fp64 grouped NVFP4 W4A4: every A row quantized per row by this oracle, then
+    dequantized exactly, gathered per group and multiplied by the expert."""
+    ac, asc, ats = nvfp4_quantize(a_bf16, per_row=True)
+    a = nvfp4_to_f64(ac, asc, ats, per_row=True)
+    return _grouped_ref(a, lambda e: nvfp4_to_f64(w_codes[e], w_scales[e], np.asarray(w_tscale)[e:e + 1]),
+                        group_offs, row_index, rows)

@@ -28,8 +28,12 @@ __all__ = [
     "activations_f32",
     "to_bf16_bits",
     "bf16_bits_to_f32",
+    "moe_routing",
+    "group_by_expert",
     "Workload",
+    "MoeWorkload",
     "WORKLOADS",
+    "MOE_WORKLOADS",
 ]
 
 
@@ -68,6 +72,39 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """bfloat16 bit patterns -> fp32 (exact widening)."""
     return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def moe_routing(tokens: int, experts: int, top_k: int, skew: float = 1.0, dead: int = 0,
+                seed: int = 2) -> np.ndarray:
+    """Top-k expert ids [tokens, top_k] (int32, distinct per token, best first).
+
+    Router logits are N(0, 1) per (token, expert) plus a per-expert bias
+    ``skew * N(0, 1)``, so expert loads are uneven; the last ``dead`` experts get
+    no tokens at all."""
+    rng = np.random.default_rng(seed)
+    bias = rng.standard_normal(experts).astype(np.float32) * np.float32(skew)
+    logits = rng.standard_normal((tokens, experts), dtype=np.float32) + bias
+    if dead:
+        logits[:, experts - dead:] = -np.inf
+    top = np.argsort(-logits, axis=1, kind="stable")[:, :top_k]
+    return top.astype(np.int32)
+
+
+def group_by_expert(topk: np.ndarray, experts: int):
+    """The grouped row layout of a routing: (group_offs int32 [experts + 1],
+    row_index int32 [tokens * top_k] = the token of each grouped row, slot_row
+    int32 [tokens, top_k] = the grouped row of each (token, slot)).  Rows of one
+    expert keep token order (a stable sort of the flattened (token, slot) list)."""
+    T, k = topk.shape
+    flat = topk.reshape(-1).astype(np.int64)
+    order = np.argsort(flat, kind="stable")
+    counts = np.bincount(flat, minlength=experts)
+    offs = np.zeros(experts + 1, np.int64)
+    np.cumsum(counts, out=offs[1:])
+    row_index = (order // k).astype(np.int32)
+    slot_row = np.empty(T * k, np.int64)
+    slot_row[order] = np.arange(T * k)
+    return offs.astype(np.int32), row_index, slot_row.reshape(T, k).astype(np.int32)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -112,4 +149,53 @@ WORKLOADS = {
     # MXFP4 vs NVFP4 W4A4 at M=8192 on identical bf16 inputs
     "mx_vs_nv_w4a4_m8192": Workload("mx_vs_nv_w4a4_m8192", (8192,), 5120, 17408, 0.02, 0.001,
                                     20.0, 0.005, 30.0),
+}
+
+
+@dataclasses.dataclass(frozen=True)
+class MoeWorkload:
+    """A mixture-of-experts layer: `tokens` bf16 rows of width K, each routed to
+    `top_k` of `experts` weights [N, K] (drawn like the dense weights, one
+    generator for all experts, expert e = rows e N .. e N + N - 1)."""
+    name: str
+    tokens: int
+    experts: int
+    top_k: int
+    K: int
+    N: int
+    w_sigma: float
+    w_outlier_p: float
+    w_outlier_factor: float
+    a_channel_p: float = 0.0
+    a_channel_factor: float = 1.0
+    skew: float = 1.0
+    dead: int = 0
+    w_seed: int = 0
+    a_seed: int = 1
+    r_seed: int = 2
+
+    def expert_weights(self) -> np.ndarray:
+        w = weights(self.experts * self.N, self.K, self.w_sigma, self.w_outlier_p, self.w_outlier_factor,
+                    self.w_seed)
+        return w.reshape(self.experts, self.N, self.K)
+
+    def activations_bf16(self) -> np.ndarray:
+        return to_bf16_bits(activations_f32(self.tokens, self.K, self.a_channel_p, self.a_channel_factor,
+                                            self.a_seed))
+
+    def routing(self):
+        """(topk, group_offs, row_index, slot_row) of the workload's router."""
+        top = moe_routing(self.tokens, self.experts, self.top_k, self.skew, self.dead, self.r_seed)
+        return (top,) + group_by_expert(top, self.experts)
+
+
+# Mixture-of-experts workloads (the pages name MoE models and MXFP4 expert weights
+# but print no layer sizes; these sizes are chosen here: 128 experts, 8 per token,
+# hidden 2048, expert output 1536 (gate and up projections side by side)).
+MOE_WORKLOADS = {
+    # prefill-sized batch: 4096 tokens -> 32768 grouped rows, mean 256 per expert;
+    # router bias skew 0.3 gives loads from 0 to 794 rows (median 229), and the
+    # last 4 experts get none
+    "moe_e128_top8_t4096_k2048_n1536": MoeWorkload("moe_e128_top8_t4096_k2048_n1536", 4096, 128, 8, 2048, 1536,
+                                                   0.02, 0.001, 20.0, 0.005, 30.0, skew=0.3, dead=4),
 }

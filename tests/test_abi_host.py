@@ -272,6 +272,55 @@ def test_w4a8_validation(L):
         assert q() == NO_DEVICE and g() == NO_DEVICE and gp() == NO_DEVICE
 
 
+def test_grouped_validation(L):
+    import torch
+
+    def g(fn="nvfp4_grouped_gemm_w4a16", **kw):
+        a = dict(a=FAKE, a_rows=64, K=256, lda=256, ridx=FAKE, offs=FAKE, groups=4, rows=128, wc=FAKE,
+                 ws=FAKE, wt=FAKE, N=16, c=FAKE, ct=0, ldc=16, stream=None)
+        if fn == "mxfp4_grouped_gemm_w4a16":
+            del a["wt"]
+        a.update(kw)
+        return getattr(L, fn)(*a.values())
+
+    for fn in ("nvfp4_grouped_gemm_w4a16", "mxfp4_grouped_gemm_w4a16"):
+        assert g(fn, groups=0) == SHAPE
+        assert g(fn, groups=(1 << 16) + 1) == SHAPE
+        assert g(fn, offs=None) == NULL
+        assert g(fn, rows=-1) == SHAPE
+        assert g(fn, ridx=None) == SHAPE            # without a gather A needs >= rows rows
+        assert g(fn, a_rows=0) == SHAPE
+        assert g(fn, K=96, lda=96) == SHAPE
+        assert g(fn, ldc=8) == LAYOUT
+        assert g(fn, a=None) == NULL
+    assert g(K=320, lda=320) != SHAPE                 # NVFP4: K % 64
+    assert g("mxfp4_grouped_gemm_w4a16", K=320, lda=320) == SHAPE   # MXFP4: K % 128
+    assert g(wt=None) == NULL
+    assert L.nvfp4_grouped_gemm_w4a4_workspace(64, 256) == L.gemm_w4a4_workspace(64, 256, 1)
+
+    def q(**kw):
+        a = dict(a=FAKE, a_rows=64, K=256, lda=256, ridx=FAKE, offs=FAKE, groups=4, rows=128, wc=FAKE,
+                 ws=FAKE, wt=FAKE, N=16, c=FAKE, ct=0, ldc=16, work=FAKE, work_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return L.nvfp4_grouped_gemm_w4a4(*a.values())
+
+    assert q(work_bytes=100) == WORKSPACE
+    assert q(groups=0) == SHAPE
+
+    def qp(**kw):
+        a = dict(ac=FAKE, asc=FAKE, at=FAKE, a_rows=64, K=256, ridx=FAKE, offs=FAKE, groups=4, rows=128,
+                 wc=FAKE, ws=FAKE, wt=FAKE, N=16, c=FAKE, ct=0, ldc=16, stream=None)
+        a.update(kw)
+        return L.nvfp4_grouped_gemm_w4a4_prequant(*a.values())
+
+    assert qp(at=None) == NULL
+    assert qp(K=40) == SHAPE
+    if not torch.cuda.is_available():
+        assert g() == NO_DEVICE and q() == NO_DEVICE and qp() == NO_DEVICE
+    assert g(rows=0, a=None, c=None, wc=None, ws=None, wt=None, ridx=None, a_rows=0) == 0   # empty: no-op
+    assert g(rows=0, K=40) == SHAPE and g(rows=0, offs=None) == NULL
+
+
 def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     import block_scaled_fp4_04_amd as fp4
 
