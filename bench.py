@@ -54,6 +54,7 @@ def parse():
     ap.add_argument("--only-decode", action="store_true", help="decode step only (profiling runs)")
     ap.add_argument("--only-components", action="store_true",
                     help="quantize / dequantize / prefill GEMM components only (profiling runs)")
+    ap.add_argument("--only-moe", action="store_true", help="grouped (MoE) GEMM components only (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -129,6 +130,12 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_bytes": src.numel()}))
+        return
+
+    if args.only_moe:
+        print(json.dumps({"components": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                                                for kk, vv in v.items()}
+                                         for k, v in moe_components(args, torch, fp4, T, dev).items()}}))
         return
 
     wl = WORKLOADS["decode_gemv_k5120_n17408"]
@@ -347,8 +354,45 @@ def components(args, torch, fp4, T, dev, w32, wq):
         "w4a8_gemm_TFLOP/s": fl / t_8g / 1e12, "w4a8_gemm_frac_fp8_mfma": fl / t_8g / FP8_PEAK,
         "w4a8_total_us": t_8all * 1e6, "w4a8_total_TFLOP/s": fl / t_8all / 1e12,
         "error_vs_bf16_product_64_rows": err}
+    del a, c, c_mx, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8
+    out.update(moe_components(args, torch, fp4, T, dev))
     return {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
             for k, v in out.items()}
+
+
+def moe_components(args, torch, fp4, T, dev):
+    """Grouped (MoE) GEMMs: 4096 tokens routed top-8 over 128 experts [1536, 2048];
+    the router's permutation is applied inside the kernel (row_index)."""
+    from synthetic import MOE_WORKLOADS
+
+    it = args.comp_iters
+    out = {}
+    wlm = MOE_WORKLOADS["moe_e128_top8_t4096_k2048_n1536"]
+    _, offs, ridx, _ = wlm.routing()
+    rows = int(offs[-1])
+    a = torch.from_numpy(wlm.activations_bf16().view(np.int16)).view(torch.bfloat16).to(dev)
+    wexp = torch.from_numpy(wlm.expert_weights()).to(dev)
+    env = fp4.nvfp4_quantize_experts(wexp)
+    emx = fp4.mxfp4_quantize_experts(wexp)
+    del wexp
+    go = torch.from_numpy(offs).to(dev)
+    ri = torch.from_numpy(ridx).to(dev)
+    c = torch.empty(rows, wlm.N, dtype=torch.bfloat16, device=dev)
+    wsg = fp4.nvfp4_grouped_gemm_w4a4_workspace(wlm.tokens, wlm.K, dev)
+    fl = 2.0 * rows * wlm.N * wlm.K
+    t_gnv = T.per_launch(lambda i: fp4.nvfp4_grouped_gemm_w4a16(a, env, go, ri, out=c), it)
+    t_gmx = T.per_launch(lambda i: fp4.mxfp4_grouped_gemm_w4a16(a, emx, go, ri, out=c), it)
+    t_g44 = T.per_launch(lambda i: fp4.nvfp4_grouped_gemm_w4a4(a, env, go, ri, out=c, workspace=wsg), it)
+    loads = np.diff(offs)
+    out["moe_grouped_" + wlm.name] = {
+        "rows": rows, "experts": wlm.experts, "empty_experts": int((loads == 0).sum()),
+        "max_rows_per_expert": int(loads.max()), "flop": fl,
+        "nvfp4_w4a16_us": t_gnv * 1e6, "nvfp4_w4a16_TFLOP/s": fl / t_gnv / 1e12,
+        "nvfp4_w4a16_frac_bf16_mfma": fl / t_gnv / BF16_PEAK,
+        "mxfp4_w4a16_us": t_gmx * 1e6, "mxfp4_w4a16_TFLOP/s": fl / t_gmx / 1e12,
+        "mxfp4_w4a16_frac_bf16_mfma": fl / t_gmx / BF16_PEAK,
+        "nvfp4_w4a4_total_us": t_g44 * 1e6, "nvfp4_w4a4_total_TFLOP/s": fl / t_g44 / 1e12}
+    return out
 
 
 def cpu_baseline(wl, wq):
