@@ -86,6 +86,7 @@ def lib():
         L.fp4o_mxfp4_to_f64.argtypes = [p, p, i64, i64, p]
         L.fp4o_mxfp8_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, p, p, ctypes.c_int]
         L.fp4o_mxfp8_to_f64.argtypes = [p, p, i64, i64, p]
+        L.fp4o_int4_quantize.argtypes = [p, ctypes.c_int, i64, i64, i64, ctypes.c_int, ctypes.c_int, p, p, p]
         L.fp4o_gemm_f64.argtypes = [p, p, i64, i64, i64, p, p]
         L.fp4o_num_threads.restype = ctypes.c_int
         L.fp4o_num_threads.argtypes = []
@@ -250,6 +251,35 @@ def mxfp8_to_f64(codes, scales) -> np.ndarray:
     y = np.empty((rows, cols), np.float64)
     lib().fp4o_mxfp8_to_f64(_ptr(codes), _ptr(scales), rows, cols, _ptr(y))
     return y
+
+
+# -------------------------------------------------------------------- INT4 --
+#
+# The integer baseline (edge-FP4 article, section on why FP4 suits compression;
+# NVFP4 wiki, competition section).  Symmetric levels -7..7, one step per block;
+# the step's container is one of the INT4_* kinds (see fp4o_int4_quantize).
+
+INT4_F32, INT4_BF16, INT4_E4M3_TENSOR, INT4_E8M0 = 0, 1, 2, 3
+
+
+def int4_quantize(x: np.ndarray, block: int, kind: int):
+    """x [rows, cols] fp32 or bf16 bits, cols % block == 0.  Returns (codes int8
+    [rows, cols], step float64 [rows, cols / block], tensor scale float32 (kind 2))."""
+    x, dt = _input(x)
+    rows, cols = x.shape
+    if cols % block:
+        raise ValueError("INT4 needs whole blocks along the last axis")
+    codes = np.empty((rows, cols), np.int8)
+    step = np.empty((rows, cols // block), np.float64)
+    ts = np.zeros(1, np.float32)
+    lib().fp4o_int4_quantize(_ptr(x), dt, rows, cols, cols, int(block), int(kind), _ptr(codes), _ptr(step), _ptr(ts))
+    return codes, step, ts[0]
+
+
+def int4_to_f64(codes, step) -> np.ndarray:
+    """codes x step, exactly, in fp64."""
+    block = codes.shape[1] // step.shape[1]
+    return codes.astype(np.float64) * np.repeat(np.asarray(step, np.float64), block, axis=1)
 
 
 # -------------------------------------------------------------------- GEMM --

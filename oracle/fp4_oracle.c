@@ -395,6 +395,75 @@ void fp4o_mxfp8_to_f64(const uint8_t *codes, const uint8_t *scales, int64_t rows
             y[r * cols + k] = fp4o_e4m3_decode(codes[r * cols + k]) * fp4o_e8m0_decode(scales[r * (cols / 32) + k / 32]);
 }
 
+/* ------------------------------------------------------------- INT4 ------- */
+
+/* INT4 linear quantization, the integer baseline FP4 is compared with (edge-FP4
+ * article, section on why FP4 suits compression: INT4's evenly spaced levels
+ * lack a floating-point dynamic range; NVFP4 wiki, competition section: INT4
+ * versions lose more accuracy than FP4 on some tasks).  The pages fix no INT4
+ * layout; this one is symmetric: levels -7..7, one step d per block of `block`
+ * elements along a row, element = round-half-even(x / d) saturated at +-7.  The
+ * step d comes from the block's amax_b in one of four containers:
+ *   kind 0: d = fl32(amax_b / 7)                        (fp32 per block)
+ *   kind 1: d = bf16_rne(fl32(amax_b / 7))               (bf16 per block)
+ *   kind 2: d = E4M3(b) * s, s = fl32(amax_tensor / (448 * 7)),
+ *           b = E4M3_rne_sat(fl32(amax_b / fl32(7 s)))   (NVFP4's container)
+ *   kind 3: d = 2^k, the smallest k with 7 * 2^k >= amax_b (MXFP4's container)
+ * A zero block has d = 0 and codes 0.  codes [rows][cols] int8; dstep
+ * [rows][cols / block] the decoded steps; *tensor_scale gets s (kind 2). */
+void fp4o_int4_quantize(const void *x, int dtype, int64_t rows, int64_t cols, int64_t ldx, int block,
+                        int kind, int8_t *codes, double *dstep, float *tensor_scale)
+{
+    float s = 0.0f;
+    if (kind == 2) {
+        float amax = 0.0f;
+        for (int64_t r = 0; r < rows; ++r) {
+            float a = amax_rows(x, dtype, r, r + 1, cols, ldx);
+            if (a > amax) amax = a;
+        }
+        s = amax / (448.0f * 7.0f);
+        if (tensor_scale) *tensor_scale = s;
+    }
+    const int64_t nb = cols / block;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        for (int64_t j = 0; j < nb; ++j) {
+            float amax_b = 0.0f;
+            for (int i = 0; i < block; ++i) {
+                float a = fabsf(load_x(x, dtype, r * ldx + j * block + i));
+                if (a > amax_b) amax_b = a;
+            }
+            double d = 0.0;
+            if (amax_b > 0.0f) {
+                if (kind == 0) {
+                    d = (double)(amax_b / 7.0f);
+                } else if (kind == 1) {
+                    d = (double)bf16_to_f32(fp4o_f32_to_bf16(amax_b / 7.0f));
+                } else if (kind == 2) {
+                    d = fp4o_e4m3_decode(fp4o_e4m3_encode_sat(amax_b / (7.0f * s))) * (double)s;
+                } else {
+                    int e;
+                    (void)frexp((double)amax_b / 7.0, &e);   /* amax/7 in [2^(e-1), 2^e) */
+                    int k = e;
+                    if (ldexp(7.0, k - 1) >= (double)amax_b) k -= 1;   /* exact power-of-two case */
+                    d = ldexp(1.0, k);
+                }
+            }
+            dstep[r * nb + j] = d;
+            for (int i = 0; i < block; ++i) {
+                int8_t q = 0;
+                if (d > 0.0) {
+                    double v = nearbyint((double)load_x(x, dtype, r * ldx + j * block + i) / d);
+                    if (v > 7.0) v = 7.0;
+                    if (v < -7.0) v = -7.0;
+                    q = (int8_t)v;
+                }
+                codes[r * cols + j * block + i] = q;
+            }
+        }
+    }
+}
+
 /* -------------------------------------------------------------- GEMM ------ */
 
 /* C[m][n] = sum_k a[m][k] * w[n][k] in fp64, and T[m][n] = sum_k |a w|

@@ -28,6 +28,7 @@ __all__ = [
     "activations_f32",
     "to_bf16_bits",
     "bf16_bits_to_f32",
+    "heavy_tailed",
     "moe_routing",
     "group_by_expert",
     "Workload",
@@ -59,6 +60,25 @@ def activations_f32(rows: int, cols: int, channel_p: float = 0.0,
         cmask = rng.random(cols) < channel_p
         a[:, cmask] *= np.float32(channel_factor)
     return a
+
+
+def heavy_tailed(rows: int, cols: int, kind: str, seed: int = 0) -> np.ndarray:
+    """fp32 [rows, cols] from a named distribution: "gaussian" N(0, 1),
+    "gaussian_outliers" N(0, 1) with 0.1% of entries x20, "student_t3" Student's t
+    with 3 degrees of freedom, "laplace" Laplace(0, 1), "channel_outliers" N(0, 1)
+    with 0.5% of the columns x30 (the activation recipe)."""
+    rng = np.random.default_rng(seed)
+    if kind == "gaussian":
+        return rng.standard_normal((rows, cols), dtype=np.float32)
+    if kind == "gaussian_outliers":
+        return weights(rows, cols, 1.0, 0.001, 20.0, seed)
+    if kind == "student_t3":
+        return rng.standard_t(3.0, (rows, cols)).astype(np.float32)
+    if kind == "laplace":
+        return rng.laplace(0.0, 1.0, (rows, cols)).astype(np.float32)
+    if kind == "channel_outliers":
+        return activations_f32(rows, cols, 0.005, 30.0, seed)
+    raise ValueError(kind)
 
 
 def to_bf16_bits(x: np.ndarray) -> np.ndarray:
