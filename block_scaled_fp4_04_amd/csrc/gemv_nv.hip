@@ -17,8 +17,8 @@
 // row offset works (a workgroup's row range needs no alignment).  The bytes and
 // their count are those of the row-major form: only their order changes.
 //
-// GEMV.  One workgroup of 8 waves per CU owns ceil(N / G) consecutive rows
-// (G workgroups), so every CU streams the same weight bytes.  Wave w owns the K
+// GEMV.  A workgroup of 8 waves owns a run of consecutive rows, a whole number
+// of 16-row tiles, with at most one workgroup per CU.  Wave w owns the K
 // segments [S w, S w + S): its activation fragments are loaded once and stay in
 // registers, and it walks the workgroup's 16-row tiles with loads for D - 1
 // tiles in flight.  Lane (n, g) = (l % 16, l / 16) loads, per tile and segment,
@@ -360,15 +360,16 @@ fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st)
 {
     const int nseg = g.K / 128;
     const int S = (nseg + kGvWaves - 1) / kGvWaves;
-    // one workgroup per CU with equal row counts; more workgroups only when a
-    // CU's share exceeds kGvMaxT tiles
-    int64_t G = std::min<int64_t>(device_cu_count(), (g.N + 15) / 16);
-    int64_t R = (g.N + G - 1) / G;
-    if (R > 16 * kGvMaxT) {
-        G = (g.N + 16 * kGvMaxT - 1) / (16 * kGvMaxT);
-        R = (g.N + G - 1) / G;
-    }
-    G = (g.N + R - 1) / R;
+    // whole 16-row tiles per workgroup, all workgroups in one round (at most one
+    // per CU): a workgroup's last tile is multiplied in full whether or not its
+    // rows exist, and that math is not hidden under the loads, so fewer, full
+    // workgroups beat one per CU with a partial last tile (N = 17408: 218
+    // workgroups of 80 rows run faster than 256 of 68).  More workgroups than
+    // CUs only when a CU's share would exceed kGvMaxT tiles.
+    const int64_t tiles = (g.N + 15) / 16, cus = device_cu_count();
+    const int64_t per = std::min<int64_t>((tiles + cus - 1) / cus, kGvMaxT);
+    const int64_t R = 16 * per;
+    const int64_t G = (g.N + R - 1) / R;
     g.rows_per_wg = (int)R;
     switch (S) {
     case 1: launch_gemv_fmt<1>(g, (unsigned)G, st); break;
