@@ -19,9 +19,8 @@
 //
 // GEMV.  A workgroup of 8 waves owns a run of consecutive rows, a whole number
 // of 16-row tiles, with at most one workgroup per CU.  Wave w owns the K
-// segments [S w, S w + S): its activation fragments are loaded once and stay in
-// registers, and it walks the workgroup's 16-row tiles with loads for D - 1
-// tiles in flight.  Lane (n, g) = (l % 16, l / 16) loads, per tile and segment,
+// segments [S w, S w + S) of all the workgroup's tiles (the walk is described
+// above k_nv_gemv_dec).  Lane (n, g) = (l % 16, l / 16) loads, per tile and segment,
 // the 32 codes of row n at K 32 g .. 32 g + 31 and their 2 scale bytes; the
 // codes feed four 16x16x32 bf16 MFMAs, MFMA j contracting K values
 // 32 g + 8 j + [0, 8) of every lane group g (a permutation of K that the
@@ -74,12 +73,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, uint
 
 constexpr uint32_t kGvOut = 0x80000000u;  // an offset past every descriptor's size
 
-template <int S>
-struct GvTile {
-    u32x4 c[S];     // 32 codes of row n, K 32 grp .. 32 grp + 31 of each segment
-    uint32_t s[S];  // their two E4M3 scale bytes
-};
-
 // E2M1 x 4 (two code bytes, low nibble first) -> bf16 x 4, times the power of two
 // in `scale`'s exponent field (1.0: unscaled); exact.
 __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale = 1.0f)
@@ -91,6 +84,15 @@ __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale 
     return bf16x4{lo[0], lo[1], hi[0], hi[1]};
 }
 
+// Work order.  A wave owns the K segments seg0 .. seg0 + S - 1 and the
+// workgroup's NT tiles; it walks them segment-major, (s, t) = (0, 0), (0, 1),
+// ..., (1, 0), ..., with one accumulator set per tile, so it needs one segment's
+// activation fragments at a time (the next segment's are fetched while the
+// current one is used) and the 16 x 16 variant's 160 KiB of activations per CU
+// arrive spread over the kernel instead of all before the first product.  The
+// weight loads run D units (tile and segment) ahead.  S and NT are compile-time,
+// so every buffer index is fixed and the whole walk is one basic block per unit.
+//
 // M4: M <= 4 variant.  Sixteen 4x4x4 bf16 MFMA blocks: block b = l / 4 multiplies
 // activation rows 0..3 (lane 4 b + i supplies row i) by W rows 4 (b % 4) + j
 // (lane 4 b + j, so lane l still owns W row l % 16) over K-quarter b / 4 of the
@@ -98,11 +100,14 @@ __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale 
 // in bf16); each NVFP4 block's four steps accumulate from zero and the partial is
 // multiplied by the lane's E4M3 scale, so the scale costs 4 FMAs per 16 codes
 // instead of a multiply per code.  The four K-quarters are summed across lanes
-// at the end of the tile.
-template <int S, int D, bool M4, int W, bool MX>
-__global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
+// at the end.  The activation rows (4 x K bf16) are staged in LDS once per
+// workgroup: the lanes 4 p + i of a wave all need row i.
+template <int S, int NT, bool M4, bool MX>
+__global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
 {
-    __shared__ f32x4 red[kGvMaxT][W][64];
+    constexpr int W = kGvWaves;
+    constexpr int D = M4 ? 8 : 5;  // units (tile, segment) of weight loads in flight
+    __shared__ f32x4 red[NT][W][64];
     __shared__ __align__(16) uint16_t alds[M4 ? 4 * 1024 * S : 8];  // M4: A rows 0..3, K <= 1024 S
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -113,174 +118,149 @@ __global__ __launch_bounds__(64 * W, 1) void k_nv_gemv_dec(GemvArgs g)
     const int ns = max(0, min(S, nseg - seg0));  // this wave's segments
     const int r_lo = blockIdx.x * g.rows_per_wg;
     const int r_hi = min(r_lo + g.rows_per_wg, N);
-    const int nt = (r_hi - r_lo + 15) >> 4;
+    const int nt = (r_hi - r_lo + 15) >> 4;      // <= NT
 
     const __amdgpu_buffer_rsrc_t ra = gv_rsrc(g.a, (uint32_t)((int64_t)(M - 1) * g.lda * 2 + g.K * 2));
     const __amdgpu_buffer_rsrc_t rc = gv_rsrc(g.w_codes, (uint32_t)((int64_t)nseg * N * 64));
     constexpr int SB = MX ? 4 : 8;  // scale bytes per row and segment
     const __amdgpu_buffer_rsrc_t rs = gv_rsrc(g.w_scales, (uint32_t)((int64_t)nseg * N * SB));
 
-    // byte offsets of this lane's codes / scales at tile 0, segment seg0 (kGvOut where skipped)
-    uint32_t oc[S], os[S];
-#pragma unroll
-    for (int s = 0; s < S; ++s) {
-        const int64_t e = (int64_t)(seg0 + s) * N + r_lo + n;
-        oc[s] = s < ns ? (uint32_t)(e * 64 + 16 * grp) : kGvOut;
-        os[s] = s < ns ? (uint32_t)(e * SB + (MX ? 1 : 2) * grp) : kGvOut;
-    }
-    auto issue_seg = [&](int t, int s, GvTile<S> &b) {
-        const bool ok = r_lo + 16 * t + n < r_hi;
-        b.c[s] = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(ok ? oc[s] + 1024 * t : kGvOut), 0, 0);
+    // unit u = (segment u / NT, tile u % NT): the lane's 32 codes (row n, K 32 grp ..)
+    // and their scale byte(s); rows past the workgroup's range and segments the
+    // wave does not own read nothing
+    auto issue = [&](int u, u32x4 &c, uint32_t &sc) {
+        const int s = u / NT, t = u % NT;
+        const bool ok = s < ns && r_lo + 16 * t + n < r_hi;
+        const int64_t e = (int64_t)(seg0 + s) * N + r_lo + 16 * t + n;
+        c = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(ok ? (uint32_t)(e * 64 + 16 * grp) : kGvOut), 0, 0);
         if constexpr (MX)
-            b.s[s] = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? os[s] + 16 * SB * t : kGvOut), 0, 0);
+            sc = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? (uint32_t)(e * SB + grp) : kGvOut), 0, 0);
         else
-            b.s[s] = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? os[s] + 16 * SB * t : kGvOut), 0, 0);
+            sc = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? (uint32_t)(e * SB + 2 * grp) : kGvOut), 0, 0);
+    };
+    // activation fragments of segment s: A row arow (zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8)
+    const int arow = M4 ? (lane & 3) : n;
+    auto frags = [&](int s, bf16x8 (&dst)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (M4) {
+                bf16x8 v = {};
+                if (s < ns) v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * (seg0 + s) + 32 * grp + 8 * j);
+                dst[j] = v;
+            } else {
+                const uint32_t off = (s < ns && arow < M)
+                    ? (uint32_t)(((int64_t)arow * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j) * 2) : kGvOut;
+                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
+                __builtin_memcpy(&dst[j], &v, 16);
+            }
+        }
     };
 
-    // activation fragments: A row n (M4: row l % 4; zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8)
-    const int arow = M4 ? (lane & 3) : n;
-    bf16x8 af[S][4];
-    GvTile<S> buf[D];
+    u32x4 bc[D];
+    uint32_t bsc[D];
     if constexpr (M4) {
-        // M <= 4: lanes 4 p + i (p = 0..3) need the same activation bytes, so the
-        // workgroup stages A ([4][K] bf16, rows past M zero) in LDS once and every
-        // wave reads its fragments from there.  The A loads go out first, then
-        // the first tiles' weight loads, so waiting for A does not wait for them.
-        constexpr int kAChunks = S;  // 16-byte chunks per thread: 4 * K / 8 <= 4 * 1024 S / 8 = 512 S
-        const int cpr = g.K >> 3;    // chunks per row
-        u32x4 ach[kAChunks];
+        // the A loads go out first, then the first units' weight loads, so waiting
+        // for A does not wait for them
+        const int cpr = g.K >> 3;  // 16-byte chunks per row; 4 cpr <= 512 S = 64 W S / 8 chunks
+        u32x4 ach[S];
 #pragma unroll
-        for (int c = 0; c < kAChunks; ++c) {
+        for (int c = 0; c < S; ++c) {
             const int idx = (int)threadIdx.x + 64 * W * c;
             const int row = idx / cpr, col = idx - row * cpr;
             const uint32_t off = (row < M && row < 4) ? (uint32_t)(((int64_t)row * g.lda + 8 * col) * 2) : kGvOut;
             ach[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < D - 1; ++k)
+        for (int k = 0; k < D - 1; ++k) issue(k, bc[k], bsc[k]);
 #pragma unroll
-            for (int s = 0; s < S; ++s) issue_seg(k, s, buf[k]);
-#pragma unroll
-        for (int c = 0; c < kAChunks; ++c) {
+        for (int c = 0; c < S; ++c) {
             const int idx = (int)threadIdx.x + 64 * W * c;
             if (idx < 4 * cpr) *reinterpret_cast<u32x4 *>(alds + 8 * idx) = ach[c];
         }
         __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0): this wave's A stores done
         asm volatile("s_barrier" ::: "memory");
+    }
+    bf16x8 af[2][4];
+    frags(0, af[0]);
+    if constexpr (!M4) {
 #pragma unroll
-        for (int s = 0; s < S; ++s)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                bf16x8 v = {};
-                if (s < ns) v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * (seg0 + s) + 32 * grp + 8 * j);
-                af[s][j] = v;
-            }
-    } else {
-        // loaded segment by segment between tile 0's weight loads so the first
-        // math waits only for its own segment
-#pragma unroll
-        for (int s = 0; s < S; ++s) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t off = (s < ns && arow < M)
-                    ? (uint32_t)(((int64_t)arow * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j) * 2) : kGvOut;
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-                __builtin_memcpy(&af[s][j], &v, 16);
-            }
-            issue_seg(0, s, buf[0]);
-        }
-#pragma unroll
-        for (int k = 1; k < D - 1; ++k)
-#pragma unroll
-            for (int s = 0; s < S; ++s) issue_seg(k, s, buf[k]);
+        for (int k = 0; k < D - 1; ++k) issue(k, bc[k], bsc[k]);
     }
 
     typedef float f32x2 __attribute__((ext_vector_type(2)));
-    // one segment of a tile, M <= 4 variant
-    auto seg4 = [&](int s, const GvTile<S> &b, f32x4 &acc) {
-        const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)b.s[s], false);
-        // the two NVFP4 blocks' MFMA chains interleaved, so each hides the other's latency
-        f32x4 part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+    f32x4 acc[NT][2];
 #pragma unroll
-        for (int st = 0; st < 4; ++st)
+    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // one unit: the lane's 32 codes c with scale byte(s) sc against fragments a
+    auto unit = [&](const bf16x8 (&a)[4], const u32x4 &c, uint32_t sc, f32x4 &acc0, f32x4 &acc1) {
+        if constexpr (M4) {
+            const float msc = MX ? __uint_as_float(sc << 23) : 1.0f;  // MXFP4: the block's power of two
+            f32x4 part[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            // the two accumulation chains interleaved, so each hides the other's latency
 #pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int q = 4 * blk + st;  // K values 4 q .. 4 q + 3 of the lane's 32
-                const bf16x8 a8 = af[s][q >> 1];
-                const bf16x4 a4 = (q & 1) ? bf16x4{a8[4], a8[5], a8[6], a8[7]} : bf16x4{a8[0], a8[1], a8[2], a8[3]};
-                part[blk] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(b.c[s][q >> 1], q & 1), part[blk], 0, 0, 0);
+            for (int st = 0; st < 4; ++st)
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk) {
+                    const int q = 4 * blk + st;  // K values 4 q .. 4 q + 3 of the lane's 32
+                    const bf16x8 a8 = a[q >> 1];
+                    const bf16x4 a4 = (q & 1) ? bf16x4{a8[4], a8[5], a8[6], a8[7]} : bf16x4{a8[0], a8[1], a8[2], a8[3]};
+                    f32x4 &dst = MX ? (blk ? acc1 : acc0) : part[blk];
+                    dst = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(c[q >> 1], q & 1, msc), dst, 0, 0, 0);
+                }
+            if constexpr (!MX) {
+                // each NVFP4 block's partial times its E4M3 scale
+                const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc, false);
+#pragma unroll
+                for (int blk = 0; blk < 2; ++blk)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) acc0[i] = __builtin_fmaf(part[blk][i], bs[blk], acc0[i]);
             }
-#pragma unroll
-        for (int blk = 0; blk < 2; ++blk)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(part[blk][i], bs[blk], acc[i]);
-    };
-    // one segment of a tile, 16x16x32 variant (two accumulator chains)
-    // MXFP4, M <= 4: the lane's 32 codes are one MX block, whose power-of-two scale
-    // the conversion applies exactly; two accumulator chains, no scale multiply
-    auto seg4mx = [&](int s, const GvTile<S> &b, f32x4 &acc0, f32x4 &acc1) {
-        const float sc = __uint_as_float(b.s[s] << 23);
-#pragma unroll
-        for (int st = 0; st < 4; ++st)
-#pragma unroll
-            for (int blk = 0; blk < 2; ++blk) {
-                const int q = 4 * blk + st;
-                const bf16x8 a8 = af[s][q >> 1];
-                const bf16x4 a4 = (q & 1) ? bf16x4{a8[4], a8[5], a8[6], a8[7]} : bf16x4{a8[0], a8[1], a8[2], a8[3]};
-                f32x4 &acc = blk ? acc1 : acc0;
-                acc = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(a4, e2m1x4_bf16(b.c[s][q >> 1], q & 1, sc), acc, 0, 0, 0);
-            }
-    };
-    auto seg16 = [&](int s, const GvTile<S> &b, f32x4 &acc0, f32x4 &acc1) {
-        if constexpr (MX) {
-            const float sc = __uint_as_float(b.s[s] << 23);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][0], e2m1x8_bf16_pow2(b.c[s][0], sc), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][1], e2m1x8_bf16_pow2(b.c[s][1], sc), acc1, 0, 0, 0);
-            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][2], e2m1x8_bf16_pow2(b.c[s][2], sc), acc0, 0, 0, 0);
-            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][3], e2m1x8_bf16_pow2(b.c[s][3], sc), acc1, 0, 0, 0);
-            return;
+        } else if constexpr (MX) {
+            const float msc = __uint_as_float(sc << 23);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], e2m1x8_bf16_pow2(c[0], msc), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], e2m1x8_bf16_pow2(c[1], msc), acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], e2m1x8_bf16_pow2(c[2], msc), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], e2m1x8_bf16_pow2(c[3], msc), acc1, 0, 0, 0);
+        } else {
+            // the two E4M3 block scales of the lane's 32 codes (OCP E4M3FN conversion)
+            const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)sc, false);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[0], as_bf16x8(dq8_bf16(c[0], bs[0])), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[1], as_bf16x8(dq8_bf16(c[1], bs[0])), acc1, 0, 0, 0);
+            acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[2], as_bf16x8(dq8_bf16(c[2], bs[1])), acc0, 0, 0, 0);
+            acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[3], as_bf16x8(dq8_bf16(c[3], bs[1])), acc1, 0, 0, 0);
         }
-        // the two E4M3 block scales of the lane's 32 codes (OCP E4M3FN conversion)
-        const f32x2 bs = __builtin_amdgcn_cvt_pk_f32_fp8((int)b.s[s], false);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][0], as_bf16x8(dq8_bf16(b.c[s][0], bs[0])), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][1], as_bf16x8(dq8_bf16(b.c[s][1], bs[0])), acc1, 0, 0, 0);
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][2], as_bf16x8(dq8_bf16(b.c[s][2], bs[1])), acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[s][3], as_bf16x8(dq8_bf16(b.c[s][3], bs[1])), acc1, 0, 0, 0);
     };
 
-    // D tiles in flight.  The tile loop is unrolled completely, so every buffer is
-    // a fixed register set and no load in flight crosses a loop back edge.  The
-    // loads of tile t + D - 1 are spread over tile t's segments, one segment's
-    // loads before each segment's math, so the wave keeps loads in flight while it
-    // computes; loads for tiles at or past nt read nothing.
+    // the walk: fully unrolled, so every buffer is a fixed register set and no
+    // load in flight crosses a loop back edge; units of tiles at or past nt are
+    // neither loaded (their rows lie past the range) nor multiplied
 #pragma unroll
-    for (int t = 0; t < kGvMaxT; ++t) {
+    for (int s = 0; s < S; ++s) {
+        if (s + 1 < S) frags(s + 1, af[(s + 1) & 1]);
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int u = s * NT + t;
+            if (u + D - 1 < S * NT) issue(u + D - 1, bc[(u + D - 1) % D], bsc[(u + D - 1) % D]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (t < nt) unit(af[s & 1], bc[u % D], bsc[u % D], acc[t][0], acc[t][1]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
         if (t < nt) {
-            f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = acc0;
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
-                if (t + D - 1 < kGvMaxT) issue_seg(t + D - 1, s, buf[(t + D - 1) % D]);
-                __builtin_amdgcn_sched_barrier(0);
-                if (M4 && MX)
-                    seg4mx(s, buf[t % D], acc0, acc1);
-                else if (M4)
-                    seg4(s, buf[t % D], acc0);
-                else
-                    seg16(s, buf[t % D], acc0, acc1);
-                __builtin_amdgcn_sched_barrier(0);
-            }
-            if (M4) {
-                if (MX) acc0 += acc1;
+            f32x4 v = M4 && !MX ? acc[t][0] : acc[t][0] + acc[t][1];
+            if constexpr (M4) {
                 // sum the four K-quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    acc0[i] += __shfl_xor(acc0[i], 16);
-                    acc0[i] += __shfl_xor(acc0[i], 32);
+                    v[i] += __shfl_xor(v[i], 16);
+                    v[i] += __shfl_xor(v[i], 32);
                 }
-                red[t][wave][lane] = acc0;
-            } else {
-                red[t][wave][lane] = acc0 + acc1;
             }
+            red[t][wave][lane] = v;
         }
     }
     __syncthreads();
@@ -322,25 +302,35 @@ fp4_status launch_pack_decode(const uint8_t *codes, const uint8_t *scales, int64
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
-template <int S, bool MX>
+template <int S, int NT, bool MX>
 static void launch_gemv(const GemvArgs &g, unsigned grid, hipStream_t st)
 {
-    constexpr int D = S <= 5 ? 3 : 2;  // tiles in flight, bounded by registers
-    // the M <= 4 variant's extra registers do not fit beside 8 segments' fragments
-    if constexpr (S < 8) {
-        if (g.M <= 4) {
-            hipLaunchKernelGGL((k_nv_gemv_dec<S, D, true, kGvWaves, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
-            return;
-        }
-    }
-    hipLaunchKernelGGL((k_nv_gemv_dec<S, D, false, kGvWaves, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    if (g.M <= 4)
+        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, false, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+}
+
+template <int S, int NT>
+static void launch_gemv_fmt(const GemvArgs &g, unsigned grid, hipStream_t st)
+{
+    if (g.mx) launch_gemv<S, NT, true>(g, grid, st);
+    else launch_gemv<S, NT, false>(g, grid, st);
 }
 
 template <int S>
-static void launch_gemv_fmt(const GemvArgs &g, unsigned grid, hipStream_t st)
+static void launch_gemv_nt(const GemvArgs &g, int nt, unsigned grid, hipStream_t st)
 {
-    if (g.mx) launch_gemv<S, true>(g, grid, st);
-    else launch_gemv<S, false>(g, grid, st);
+    switch (nt) {
+    case 1: launch_gemv_fmt<S, 1>(g, grid, st); break;
+    case 2: launch_gemv_fmt<S, 2>(g, grid, st); break;
+    case 3: launch_gemv_fmt<S, 3>(g, grid, st); break;
+    case 4: launch_gemv_fmt<S, 4>(g, grid, st); break;
+    case 5: launch_gemv_fmt<S, 5>(g, grid, st); break;
+    case 6: launch_gemv_fmt<S, 6>(g, grid, st); break;
+    case 7: launch_gemv_fmt<S, 7>(g, grid, st); break;
+    default: launch_gemv_fmt<S, 8>(g, grid, st); break;
+    }
 }
 
 int device_cu_count()
@@ -371,15 +361,16 @@ fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st)
     const int64_t R = 16 * per;
     const int64_t G = (g.N + R - 1) / R;
     g.rows_per_wg = (int)R;
+    const int nt = (int)per;
     switch (S) {
-    case 1: launch_gemv_fmt<1>(g, (unsigned)G, st); break;
-    case 2: launch_gemv_fmt<2>(g, (unsigned)G, st); break;
-    case 3: launch_gemv_fmt<3>(g, (unsigned)G, st); break;
-    case 4: launch_gemv_fmt<4>(g, (unsigned)G, st); break;
-    case 5: launch_gemv_fmt<5>(g, (unsigned)G, st); break;
-    case 6: launch_gemv_fmt<6>(g, (unsigned)G, st); break;
-    case 7: launch_gemv_fmt<7>(g, (unsigned)G, st); break;
-    case 8: launch_gemv_fmt<8>(g, (unsigned)G, st); break;
+    case 1: launch_gemv_nt<1>(g, nt, (unsigned)G, st); break;
+    case 2: launch_gemv_nt<2>(g, nt, (unsigned)G, st); break;
+    case 3: launch_gemv_nt<3>(g, nt, (unsigned)G, st); break;
+    case 4: launch_gemv_nt<4>(g, nt, (unsigned)G, st); break;
+    case 5: launch_gemv_nt<5>(g, nt, (unsigned)G, st); break;
+    case 6: launch_gemv_nt<6>(g, nt, (unsigned)G, st); break;
+    case 7: launch_gemv_nt<7>(g, nt, (unsigned)G, st); break;
+    case 8: launch_gemv_nt<8>(g, nt, (unsigned)G, st); break;
     default: return FP4_ERR_SHAPE;
     }
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
