@@ -73,6 +73,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t gv_rsrc(const void *base, uint
 
 constexpr uint32_t kGvOut = 0x80000000u;  // an offset past every descriptor's size
 
+// s_waitcnt vmcnt(N): wait until at most N vector-memory operations of this wave are outstanding
+template <int N>
+__device__ __forceinline__ void nv_wait_vm_gv()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // E2M1 x 4 (two code bytes, low nibble first) -> bf16 x 4, times the power of two
 // in `scale`'s exponent field (1.0: unscaled); exact.
 __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale = 1.0f)
@@ -109,6 +117,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     constexpr int D = M4 ? 8 : 5;  // units (tile, segment) of weight loads in flight
     __shared__ f32x4 red[NT][W][64];
     __shared__ __align__(16) uint16_t alds[M4 ? 4 * 1024 * S : 8];  // M4: A rows 0..3, K <= 1024 S
+    __shared__ __align__(16) uint8_t a16[M4 ? 16 : W * 2 * 4096];    // M > 4: per wave, two segments of A
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, grp = lane >> 4;
@@ -138,22 +147,38 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         else
             sc = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? (uint32_t)(e * SB + 2 * grp) : kGvOut), 0, 0);
     };
-    // activation fragments of segment s: A row arow (zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8)
+    // activation fragments of segment s: A row arow (zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8).
+    // M <= 4 reads them from the workgroup's staged rows.  M > 4 copies each
+    // segment's 16 rows x 128 K (4 KiB) into one of the wave's two LDS buffers by
+    // DMA first: copy i covers rows 4 i .. 4 i + 3 as whole 256-byte row pieces
+    // (lane L lands in row 4 i + L / 16, slot L % 16 and fetches the row's 16-byte
+    // chunk slot ^ row), 8 cache lines per copy where a fragment load straight from
+    // memory touches 32; the chunk swizzle lets each 16-lane group of a fragment
+    // read hit 16 different bank groups.
     const int arow = M4 ? (lane & 3) : n;
     auto frags = [&](int s, bf16x8 (&dst)[4]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            if constexpr (M4) {
-                bf16x8 v = {};
-                if (s < ns) v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * (seg0 + s) + 32 * grp + 8 * j);
-                dst[j] = v;
-            } else {
-                const uint32_t off = (s < ns && arow < M)
-                    ? (uint32_t)(((int64_t)arow * g.lda + 128 * (seg0 + s) + 32 * grp + 8 * j) * 2) : kGvOut;
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
-                __builtin_memcpy(&dst[j], &v, 16);
-            }
+            bf16x8 v = {};
+            if (s < ns) v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * (seg0 + s) + 32 * grp + 8 * j);
+            dst[j] = v;
         }
+    };
+    typedef __attribute__((address_space(3))) void gv_lds_void;
+    auto a_dma = [&](int s, int b) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int r = 4 * i + (lane >> 4), slot = lane & 15, ch = slot ^ r;
+            const uint32_t off =
+                (s < ns && r < M) ? (uint32_t)(((int64_t)r * g.lda + 128 * (seg0 + s)) * 2 + 16 * ch) : kGvOut;
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (gv_lds_void *)(a16 + 8192 * wave + 4096 * b + 1024 * i), 16,
+                                                     (int)off, 0, 0, 0);
+        }
+    };
+    auto frags16 = [&](int b, bf16x8 (&dst)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            dst[j] = *reinterpret_cast<const bf16x8 *>(a16 + 8192 * wave + 4096 * b + 256 * n + 16 * ((4 * grp + j) ^ n));
     };
 
     u32x4 bc[D];
@@ -181,10 +206,14 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         asm volatile("s_barrier" ::: "memory");
     }
     bf16x8 af[2][4];
-    frags(0, af[0]);
-    if constexpr (!M4) {
+    if constexpr (M4) {
+        frags(0, af[0]);
+    } else {
+        a_dma(0, 0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int k = 0; k < D - 1; ++k) issue(k, bc[k], bsc[k]);
+        __builtin_amdgcn_sched_barrier(0);
     }
 
     typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -237,11 +266,23 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     // neither loaded (their rows lie past the range) nor multiplied
 #pragma unroll
     for (int s = 0; s < S; ++s) {
-        if (s + 1 < S) frags(s + 1, af[(s + 1) & 1]);
+        if constexpr (M4) {
+            if (s + 1 < S) frags(s + 1, af[(s + 1) & 1]);
+        } else {
+            // segment s's copy is older than every load issued after it: the 2 (D - 1)
+            // of the first units before segment 0, then 2 NT per segment (each unit
+            // issues its two loads, past the end too, where they read nothing)
+            if (s == 0) nv_wait_vm_gv<2 * (D - 1)>();
+            else nv_wait_vm_gv<2 * NT>();
+            __builtin_amdgcn_sched_barrier(0);
+            frags16(s & 1, af[s & 1]);
+            if (s + 1 < S) a_dma(s + 1, (s + 1) & 1);
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int u = s * NT + t;
-            if (u + D - 1 < S * NT) issue(u + D - 1, bc[(u + D - 1) % D], bsc[(u + D - 1) % D]);
+            if (!M4 || u + D - 1 < S * NT) issue(u + D - 1, bc[(u + D - 1) % D], bsc[(u + D - 1) % D]);
             __builtin_amdgcn_sched_barrier(0);
             if (t < nt) unit(af[s & 1], bc[u % D], bsc[u % D], acc[t][0], acc[t][1]);
             __builtin_amdgcn_sched_barrier(0);
