@@ -36,6 +36,8 @@ BF16_PEAK = 2.5e15         # dense bf16 MFMA, FLOP/s
 FP4_PEAK = 10.1e15         # dense fp4 MFMA, FLOP/s
 FP8_PEAK = 5.0e15          # dense fp8 MFMA (also an fp8 x fp4 product), FLOP/s
 N, K = 17408, 5120
+# component groups of --only-components / --only
+COMPONENT_GROUPS = ["quant", "prefill_m4096", "mxfp4_w4a16", "m8192", "moe"]
 
 
 def log(msg):
@@ -55,6 +57,8 @@ def parse():
     ap.add_argument("--only-components", action="store_true",
                     help="quantize / dequantize / prefill GEMM components only (profiling runs)")
     ap.add_argument("--only-moe", action="store_true", help="grouped (MoE) GEMM components only (profiling runs)")
+    ap.add_argument("--only", choices=COMPONENT_GROUPS, default=None,
+                    help="with --only-components: one group of components (profiling runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -237,6 +241,25 @@ def components(args, torch, fp4, T, dev, w32, wq):
 
     it = args.comp_iters
     out = {}
+    want = lambda grp: args.only in (None, grp)  # noqa: E731
+    wl3 = WORKLOADS["prefill_w4a16_m4096"]
+
+    if want("quant"):
+        quant_components(fp4, T, dev, w32, wq, it, out)
+    if want("prefill_m4096"):
+        prefill_components(torch, fp4, T, dev, wq, wl3, it, out)
+    if want("mxfp4_w4a16"):
+        mx16_components(torch, fp4, T, dev, w32, wl3, it, out)
+    if want("m8192"):
+        m8192_components(torch, fp4, T, dev, w32, it, out)
+    if want("moe"):
+        out.update(moe_components(args, torch, fp4, T, dev))
+    return {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
+            for k, v in out.items()}
+
+
+def quant_components(fp4, T, dev, w32, wq, it, out):
+    import torch
 
     # weight quantize (fp32 -> NVFP4, per tensor: amax pass + quantize pass)
     w32b = w32.clone()   # two fp32 copies (712 MB) exceed the Infinity Cache
@@ -258,8 +281,9 @@ def components(args, torch, fp4, T, dev, w32, wq):
                                          "frac_hbm": b / t / HBM_PEAK, "bytes": b}
     del y
 
+
+def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     # prefill W4A16 and W4A4 at M = 4096
-    wl3 = WORKLOADS["prefill_w4a16_m4096"]
     M = 4096
     a = torch.from_numpy(wl3.activations_bf16(M).view(np.int16)).view(torch.bfloat16).to(dev)
     c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
@@ -279,6 +303,10 @@ def components(args, torch, fp4, T, dev, w32, wq):
         "gemm_us": t_g * 1e6, "gemm_TFLOP/s": fl / t_g / 1e12, "gemm_frac_bf16_mfma": fl / t_g / BF16_PEAK,
         "total_us": t_all * 1e6, "total_TFLOP/s": fl / t_all / 1e12}
     del a, c
+
+
+def mx16_components(torch, fp4, T, dev, w32, wl3, it, out):
+    from synthetic import WORKLOADS
 
     # MXFP4 weights with bf16 activations (W4A16): decode GEMV at M = 1, 4, 16 on
     # the MXFP4 decode layout (12 rotating copies, as the NVFP4 step) and the
@@ -305,6 +333,10 @@ def components(args, torch, fp4, T, dev, w32, wq):
     out["mxfp4_w4a16_prefill_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
                                         "flop": fl, "mfma": "bf16 32x32x16 (MXFP4 widened exactly to bf16)"}
     del a, c, wmx
+
+
+def m8192_components(torch, fp4, T, dev, w32, it, out):
+    from synthetic import WORKLOADS
 
     # MXFP4 vs NVFP4 W4A4 at M = 8192 on identical bf16 inputs
     wl5 = WORKLOADS["mx_vs_nv_w4a4_m8192"]
@@ -355,9 +387,6 @@ def components(args, torch, fp4, T, dev, w32, wq):
         "w4a8_total_us": t_8all * 1e6, "w4a8_total_TFLOP/s": fl / t_8all / 1e12,
         "error_vs_bf16_product_64_rows": err}
     del a, c, c_mx, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8
-    out.update(moe_components(args, torch, fp4, T, dev))
-    return {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv) for kk, vv in v.items()}
-            for k, v in out.items()}
 
 
 def moe_components(args, torch, fp4, T, dev):
