@@ -61,6 +61,8 @@ def test_pack_decode_layout(N, K):
 SHAPES = [
     (1, 16, 128), (1, 100, 1024), (2, 33, 5120), (4, 517, 5120), (16, 300, 1024), (5, 40, 384),
     (3, 1000, 8192), (1, 4097, 2048), (16, 1, 128), (7, 40000, 256), (16, 2000, 1152),
+    # 3, 4, 6 and 7 16-row tiles per workgroup on a 256-CU part
+    (16, 9600, 256), (1, 14400, 256), (5, 22400, 128), (4, 27200, 384),
 ]
 
 
