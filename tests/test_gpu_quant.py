@@ -69,7 +69,8 @@ def test_prefill_activations_per_row_full_size():
 
 # ------------------------------------------------------------ ragged ------
 
-@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (17, 80), (33, 1040), (130, 5120), (257, 272)])
+@pytest.mark.parametrize("rows,cols", [(1, 16), (3, 48), (17, 80), (33, 1040), (130, 5120), (257, 272),
+                                       (5, 8192), (3, 8208), (2, 16384)])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("mode", ["tensor", "row"])
 def test_ragged_shapes(rows, cols, dtype, mode):
@@ -79,16 +80,18 @@ def test_ragged_shapes(rows, cols, dtype, mode):
     _nv_check(x, mode, f"ragged {rows}x{cols}")
 
 
-def test_strided_input():
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_strided_input(mode):
     x = weights(40, 160, 1.0, 0.01, 10.0, seed=77)
     big = torch.zeros(40, 256, dtype=torch.float32, device=dev())
     big[:, :160] = f32_to_dev(x)
     view = big[:, :160]
-    p = fp4().nvfp4_quantize(view)
+    p = fp4().nvfp4_quantize(view, mode=mode)
     torch.cuda.synchronize()
-    oc, os_, ot = oracle.nvfp4_quantize(x)
+    oc, os_, ot = oracle.nvfp4_quantize(x, per_row=mode == "row")
     assert_bytes_equal(p.codes, oc, "strided codes")
     assert_bytes_equal(p.scales, os_, "strided scales")
+    assert np.array_equal(p.tscale.cpu().numpy(), ot), "strided tensor scale(s)"
 
 
 # ------------------------------------------------------- adversarial ------
