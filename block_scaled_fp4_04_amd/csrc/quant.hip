@@ -63,13 +63,16 @@ __device__ __forceinline__ float amax8(const float v[8], int &bad)
 // Codes of 8 values under divisor d (d == 0: signed zeros), nibble i = value i.
 __device__ __forceinline__ uint32_t nvfp4_codes8(const float v[8], float d)
 {
-    uint32_t w = 0;
+    if (d == 0.0f) {
+        uint32_t w = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const uint32_t c = d == 0.0f ? ((__float_as_uint(v[i]) >> 28) & 8u) : e2m1_code(v[i] / d);
-        w |= c << (4 * i);
+        for (int i = 0; i < 8; ++i) w |= ((__float_as_uint(v[i]) >> 28) & 8u) << (4 * i);
+        return w;
     }
-    return w;
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = v[i] / d;  // correctly rounded
+    return e2m1x8_code(q);
 }
 
 // ------------------------------------------------------------------ amax --
@@ -253,8 +256,10 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, ui
             if (rule == 1 && __builtin_amdgcn_frexp_mantf(bm) > 0.75f) k = E - 1;  // 6*2^(E-2) < bm
             k = k < -127 ? -127 : (k > 127 ? 127 : k);
             byte = (uint32_t)(k + 127);
+            float q[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) w |= e2m1_code(__builtin_amdgcn_ldexpf(v[i], -k)) << (4 * i);
+            for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_ldexpf(v[i], -k);  // exact
+            w = e2m1x8_code(q);
         }
         *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
         if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
