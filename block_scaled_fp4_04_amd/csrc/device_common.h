@@ -72,6 +72,19 @@ __device__ __forceinline__ uint32_t e4m3_code_sat(float q)
     return code > 0x7Eu ? 0x7Eu : code;
 }
 
+// E4M3FN bytes of four non-negative values (byte i = q_i), round to nearest even,
+// saturating at 448: gfx950's scaled FP8 conversion with scale 1 on min(q, 448).
+// That gives exactly e4m3_code_sat's byte for every non-negative fp32 input up to
+// +inf (checked over all those bit patterns on the device; without the clamp the
+// conversion returns NaN past the top of the range).
+__device__ __forceinline__ uint32_t e4m3x4_code_sat(float q0, float q1, float q2, float q3)
+{
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    v2i16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2i16{0, 0}, fminf(q0, 448.0f), fminf(q1, 448.0f), 1.0f, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(q2, 448.0f), fminf(q3, 448.0f), 1.0f, true);
+    return (uint32_t)(uint16_t)r[0] | ((uint32_t)(uint16_t)r[1] << 16);
+}
+
 // E4M3FN byte -> fp32 (sign honoured; 0x7F/0xFF are never produced by the quantizer).
 __device__ __forceinline__ float e4m3_value(uint32_t b)
 {

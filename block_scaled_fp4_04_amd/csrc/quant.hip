@@ -123,7 +123,7 @@ __device__ __forceinline__ void nvfp4_unit(const float v[8], float s, float six_
     int dummy = 0;
     float bm = amax8(v, dummy);
     bm = fmaxf(bm, xor1(bm));
-    const uint32_t b = bm == 0.0f ? 0u : e4m3_code_sat(bm / six_s);
+    const uint32_t b = bm == 0.0f ? 0u : e4m3x4_code_sat(bm / six_s, 0.0f, 0.0f, 0.0f) & 0xFFu;
     const float d = e4m3_value(b) * s;
     *code_word = nvfp4_codes8(v, d);
     if (even) *scale_byte = (uint8_t)b;
@@ -300,14 +300,18 @@ __global__ __launch_bounds__(256) void k_mxfp8_quant(const T *__restrict__ x, ui
             k = k < -127 ? -127 : (k > 127 ? 127 : k);
             byte = (uint32_t)(k + 127);
         }
-        uint32_t lo = 0, hi = 0;
+        float a[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t sign = (__float_as_uint(v[i]) >> 24) & 0x80u;
-            const uint32_t mag = bm == 0.0f ? 0u : e4m3_code_sat(__builtin_amdgcn_ldexpf(__builtin_fabsf(v[i]), -k));
-            if (i < 4) lo |= (sign | mag) << (8 * i);
-            else hi |= (sign | mag) << (8 * (i - 4));
-        }
+        for (int i = 0; i < 8; ++i) a[i] = bm == 0.0f ? 0.0f : __builtin_amdgcn_ldexpf(__builtin_fabsf(v[i]), -k);  // exact
+        // the sign bits: bit 7 of each code byte (the top byte of each value)
+        const uint32_t s_lo = __builtin_amdgcn_perm(__builtin_amdgcn_perm(__float_as_uint(v[3]), __float_as_uint(v[2]), 0x0c0c0703u),
+                                                    __builtin_amdgcn_perm(__float_as_uint(v[1]), __float_as_uint(v[0]), 0x0c0c0703u),
+                                                    0x05040100u) & 0x80808080u;
+        const uint32_t s_hi = __builtin_amdgcn_perm(__builtin_amdgcn_perm(__float_as_uint(v[7]), __float_as_uint(v[6]), 0x0c0c0703u),
+                                                    __builtin_amdgcn_perm(__float_as_uint(v[5]), __float_as_uint(v[4]), 0x0c0c0703u),
+                                                    0x05040100u) & 0x80808080u;
+        const uint32_t lo = e4m3x4_code_sat(a[0], a[1], a[2], a[3]) | s_lo;
+        const uint32_t hi = e4m3x4_code_sat(a[4], a[5], a[6], a[7]) | s_hi;
         *reinterpret_cast<uint2 *>(codes + (int64_t)r * cols + (int64_t)c8 * 8) = make_uint2(lo, hi);
         if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
     }
