@@ -194,6 +194,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_rows(const T *__restrict__ 
 
 // ------------------------------------------------------- NVFP4 dequantize --
 
+// One thread per 16-block: 8 code bytes, one E4M3 byte, 16 outputs (two or four
+// 16-byte stores).  E2M1 -> fp32 by the scaled FP4 conversion with scale 1
+// (exact), then fl32(fl32(E2M1 * E4M3) * s), the first product exact; bf16 by
+// round to nearest even.
 template <bool OUT_BF16>
 __global__ __launch_bounds__(256) void k_nvfp4_dequant(const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ scales,
@@ -202,27 +206,44 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant(const uint8_t *__restrict
                                                        int64_t cols, void *__restrict__ y,
                                                        int64_t ldy)
 {
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
     for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
         const uint32_t r = fdiv(u, cv);
-        const uint32_t c8 = u - r * cv.d;
-        const uint32_t w = *reinterpret_cast<const uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
-        const float bs = e4m3_value(scales[(int64_t)r * (cols / 16) + (c8 >> 1)]);
+        const uint32_t b = u - r * cv.d;  // block within the row
+        const uint2 w = *reinterpret_cast<const uint2 *>(codes + (int64_t)r * (cols / 2) + (int64_t)b * 8);
+        const float bs = e4m3_value(scales[(int64_t)r * (cols / 16) + b]);
         const float s = tscale[per_row ? r : 0];
-        float o[8];
+        float o[16];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = (e2m1_value(w >> (4 * i)) * bs) * s;  // first product exact
-        const int64_t off = (int64_t)r * ldy + (int64_t)c8 * 8;
+        for (int q = 0; q < 8; ++q) {
+            const uint32_t word = q < 4 ? w.x : w.y;
+            f32x2 p;
+            switch (q & 3) {
+            case 0: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 0); break;
+            case 1: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 1); break;
+            case 2: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 2); break;
+            default: p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(word, 1.0f, 3); break;
+            }
+            o[2 * q] = (p[0] * bs) * s;
+            o[2 * q + 1] = (p[1] * bs) * s;
+        }
+        const int64_t off = (int64_t)r * ldy + (int64_t)b * 16;
         if (OUT_BF16) {
-            uint4 p;
-            p.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);
-            p.y = f32_to_bf16_rne(o[2]) | (f32_to_bf16_rne(o[3]) << 16);
-            p.z = f32_to_bf16_rne(o[4]) | (f32_to_bf16_rne(o[5]) << 16);
-            p.w = f32_to_bf16_rne(o[6]) | (f32_to_bf16_rne(o[7]) << 16);
-            *reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(y) + off) = p;
+            uint4 pk[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                pk[h].x = f32_to_bf16_rne(o[8 * h + 0]) | (f32_to_bf16_rne(o[8 * h + 1]) << 16);
+                pk[h].y = f32_to_bf16_rne(o[8 * h + 2]) | (f32_to_bf16_rne(o[8 * h + 3]) << 16);
+                pk[h].z = f32_to_bf16_rne(o[8 * h + 4]) | (f32_to_bf16_rne(o[8 * h + 5]) << 16);
+                pk[h].w = f32_to_bf16_rne(o[8 * h + 6]) | (f32_to_bf16_rne(o[8 * h + 7]) << 16);
+            }
+            uint4 *yp = reinterpret_cast<uint4 *>(reinterpret_cast<uint16_t *>(y) + off);
+            yp[0] = pk[0];
+            yp[1] = pk[1];
         } else {
-            float *yp = reinterpret_cast<float *>(y) + off;
-            *reinterpret_cast<float4 *>(yp) = make_float4(o[0], o[1], o[2], o[3]);
-            *reinterpret_cast<float4 *>(yp + 4) = make_float4(o[4], o[5], o[6], o[7]);
+            float4 *yp = reinterpret_cast<float4 *>(reinterpret_cast<float *>(y) + off);
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yp[q] = make_float4(o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]);
         }
     }
 }
@@ -398,8 +419,8 @@ fp4_status launch_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, 
                                    fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
                                    fp4_dtype yt, int64_t ldy, hipStream_t st)
 {
-    const uint32_t units = (uint32_t)(rows * (cols / 8));
-    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const uint32_t units = (uint32_t)(rows * (cols / 16));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 16));
     const unsigned g = grid_for(units, 16384);
     const int pr = mode == FP4_SCALE_PER_ROW;
     if (yt == FP4_BF16)
