@@ -95,10 +95,18 @@ class Timer:
     def __init__(self, torch):
         self.torch = torch
 
-    def per_launch(self, fn, iters, warmup=3):
+    def per_launch(self, fn, iters, warmup=3, warm_s=0.05):
+        """Seconds per launch over `iters` launches, after `warmup` launches and at
+        least `warm_s` seconds of them (so heavy kernels are timed at the clock they
+        sustain, not while it ramps up)."""
         torch = self.torch
-        for i in range(warmup):
+        t0 = time.perf_counter()
+        i = 0
+        while i < warmup or (time.perf_counter() - t0 < warm_s and i < 1000):
             fn(i)
+            if i >= warmup:
+                torch.cuda.synchronize()
+            i += 1
         torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)

@@ -50,18 +50,26 @@ def flags():
     ]
 
 
+def _compile(src: str, verbose: bool) -> tuple[str, subprocess.CompletedProcess]:
+    obj = os.path.join(LIBDIR, src.replace(".hip", ".o"))
+    cmd = [HIPCC, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd.remove("-shared")
+    if verbose:
+        print(" ".join(cmd), file=sys.stderr)
+    return obj, subprocess.run(cmd, capture_output=True, text=True)
+
+
 def build(verbose: bool = False) -> str:
-    """Compile every HIP source into LIB; always recompiles."""
+    """Compile every HIP source into LIB (the sources in parallel); always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+
     os.makedirs(LIBDIR, exist_ok=True)
     tlib = _torch_libdir()
+    jobs = max(1, min(len(SOURCES), int(os.environ.get("MAX_JOBS", os.cpu_count() or 1))))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        results = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
     objs = []
-    for src in SOURCES:
-        obj = os.path.join(LIBDIR, src.replace(".hip", ".o"))
-        cmd = [HIPCC, *flags(), "-c", os.path.join(CSRC, src), "-o", obj]
-        cmd.remove("-shared")
-        if verbose:
-            print(" ".join(cmd), file=sys.stderr)
-        r = subprocess.run(cmd, capture_output=True, text=True)
+    for src, (obj, r) in zip(SOURCES, results):
         if r.returncode != 0:
             sys.stderr.write(r.stdout + r.stderr)
             raise RuntimeError(f"hipcc failed on {src}")

@@ -8,11 +8,11 @@
 // for those 32 K-elements.  Products of two E2M1 values times two powers of two
 // are exact; the matrix core accumulates in fp32.
 //
-// Tiling: 256 x 256 output tile per workgroup, 4 waves of 128 x 128 (4 x 4
-// MFMA tiles of 32 x 32).  Packed codes and scale bytes are staged in LDS
-// unchanged.  K % 256 == 0 takes the staged kernel (two 256-element LDS stages
-// filled by global-to-LDS DMA); other K take a register-prefetch kernel with
-// 128-element steps that masks the K tail.
+// Tiling: 256 x 256 output tile per workgroup.  Packed codes and scale bytes are
+// staged in LDS unchanged.  K % 256 == 0 takes the staged kernel (8 waves of
+// 128 x 64, two 256-element LDS stages filled by global-to-LDS DMA); other K
+// take a register-prefetch kernel (4 waves of 128 x 128) with 128-element steps
+// that masks the K tail.
 #include "device_common.h"
 #include "internal.h"
 
@@ -105,7 +105,10 @@ __device__ __forceinline__ void mx_store_block(const f32x16 (&acc)[4][4], uint8_
 
 // ---- main path (K % 256 == 0): two LDS stages of 256 K-elements fed by DMA ----
 //
-// Each stage holds, for both operands, 256 tile rows x 128 code bytes (16-byte
+// 8 waves, two per SIMD, as 2 (M) x 4 (N) blocks of 128 x 64 outputs (4 x 2 MFMA
+// tiles of 32 x 32): while one wave of a SIMD waits on LDS or the barrier the
+// other keeps the matrix core busy, and 8 waves read LDS at almost twice the rate
+// 4 waves reach.  Each stage holds, for both operands, 256 tile rows x 128 code bytes (16-byte
 // chunk c of row r at slot 8 r + (c ^ ((r >> 1) & 7)), so the 16 lanes of an MFMA
 // fragment read hit 16 different bank groups) and 256 rows x 8 E8M0 bytes.  The
 // two stages are separate LDS objects: the compiler can then tell a DMA into one
@@ -120,11 +123,11 @@ constexpr int kSScl = MBM * (kSK / 32);           // 2 KiB of scale bytes per op
 constexpr int kSStage = 2 * kSTile + 2 * kSScl;   // 69,632 bytes
 static_assert(2 * kMxStageRows * kMxStagePitch <= kSStage, "two waves' output staging must fit a stage");
 
-// Per-lane byte offsets (from the matrix base at k0 = 0) of the 20 DMA transfers a
-// wave issues per stage: 8 x 16 bytes of A codes, 8 of W codes, 2 x 4 bytes of
-// scales per operand.  Code slot q = 512 wave + 64 i + lane is row q / 8, chunk
-// (q % 8) ^ ((row >> 1) & 7); scale dword q = 128 wave + 64 i + lane is row q / 2,
-// bytes 4 (q % 2) .. +3.  Rows past the matrix edge re-read the last row: their
+// Per-lane byte offsets (from the matrix base at k0 = 0) of the 10 DMA transfers a
+// wave issues per stage: 4 x 16 bytes of A codes, 4 of W codes, one 4-byte scale
+// dword per operand.  Code slot q = 256 wave + 64 i + lane is row q / 8, chunk
+// (q % 8) ^ ((row >> 1) & 7); scale dword q = 64 wave + lane is row q / 2, bytes
+// 4 (q % 2) .. +3.  Rows past the matrix edge re-read the last row: their
 // products land only in outputs that are never stored.  The copies are buffer
 // loads into LDS: a 32-bit per-lane offset, the stage's K offset as the scalar
 // offset, and a descriptor per matrix whose size bound makes the hardware return
@@ -133,7 +136,7 @@ static_assert(2 * kMxStageRows * kMxStagePitch <= kSStage, "two waves' output st
 // nothing, so every stage runs the same code.
 struct Mx2Dma {
     __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
-    uint32_t a[8], w[8], as[2], ws[2];
+    uint32_t a[4], w[4], as, ws;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t mx2_rsrc(const uint8_t *base, int64_t bytes)
@@ -146,53 +149,51 @@ __device__ __forceinline__ void mx2_dma(uint8_t *st, const Mx2Dma &d, int k0, in
 {
     // d's descriptors are chosen by the caller (matrix or empty)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + 16 * (512 * wave + 64 * i)), 16,
+    for (int i = 0; i < 4; ++i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + 16 * (256 * wave + 64 * i)), 16,
                                                  (int)d.a[i], k0 / 2, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kSTile + 16 * (512 * wave + 64 * i)), 16,
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kSTile + 16 * (256 * wave + 64 * i)), 16,
                                                  (int)d.w[i], k0 / 2, 0, 0);
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (mx_lds_void *)(st + 2 * kSTile + 4 * (128 * wave + 64 * i)), 4,
-                                                 (int)d.as[i], k0 / 32, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsw,
-                                                 (mx_lds_void *)(st + 2 * kSTile + kSScl + 4 * (128 * wave + 64 * i)), 4,
-                                                 (int)d.ws[i], k0 / 32, 0, 0);
-    }
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (mx_lds_void *)(st + 2 * kSTile + 4 * (64 * wave)), 4, (int)d.as,
+                                             k0 / 32, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsw, (mx_lds_void *)(st + 2 * kSTile + kSScl + 4 * (64 * wave)), 4,
+                                             (int)d.ws, k0 / 32, 0, 0);
 }
 
 // LDS offsets one lane reads within a stage: fragment (i, ks) of A is at
-// la[ks] + 4096 i, of W at lw[ks] + 4096 j; the 8 scale bytes of A row i at
-// lsa + 256 i, of W row j at lsw + 256 j.
+// la[ks] + 4096 i (i < 4), of W at lw[ks] + 4096 j (j < 2); the 8 scale bytes of
+// A row i at lsa + 256 i, of W row j at lsw + 256 j.
 struct Mx2Lds {
     uint32_t la[4], lw[4], lsa, lsw, sel;
 };
 
 struct Mx2Frag {
-    i32x4 a[4], w[4];
+    i32x4 a[4], w[2];
 };
 
 __device__ __forceinline__ void mx2_frags(const uint8_t *st, uint32_t la, uint32_t lw, Mx2Frag &f)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        f.a[i] = *reinterpret_cast<const i32x4 *>(st + la + 4096 * i);
-        f.w[i] = *reinterpret_cast<const i32x4 *>(st + lw + 4096 * i);
-    }
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(st + la + 4096 * i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.w[j] = *reinterpret_cast<const i32x4 *>(st + lw + 4096 * j);
 }
 
 // The lane's MFMA scale operand for step ks is byte ks of one dword: lanes 0..31
 // supply blocks 0, 2, 4, 6 of the row's 8 blocks in the stage, lanes 32..63
 // blocks 1, 3, 5, 7 (the K-half of the 32 x 32 x 64 instruction each half covers).
-__device__ __forceinline__ void mx2_scales(const uint8_t *st, const Mx2Lds &o, uint32_t (&sa)[4], uint32_t (&sw)[4])
+__device__ __forceinline__ void mx2_scales(const uint8_t *st, const Mx2Lds &o, uint32_t (&sa)[4], uint32_t (&sw)[2])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const uint2 va = *reinterpret_cast<const uint2 *>(st + o.lsa + 256 * i);
-        const uint2 vw = *reinterpret_cast<const uint2 *>(st + o.lsw + 256 * i);
         sa[i] = __builtin_amdgcn_perm(va.y, va.x, o.sel);
-        sw[i] = __builtin_amdgcn_perm(vw.y, vw.x, o.sel);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+        const uint2 vw = *reinterpret_cast<const uint2 *>(st + o.lsw + 256 * j);
+        sw[j] = __builtin_amdgcn_perm(vw.y, vw.x, o.sel);
     }
 }
 
@@ -203,27 +204,26 @@ __device__ __forceinline__ i32x8 mx2_wide(i32x4 v) { return __builtin_shufflevec
 // + 0..3 in slots 4 g .. 4 g + 3, which the epilogue writes as one 8- or 16-byte
 // piece.
 template <int KS, int I0, int I1>
-__device__ __forceinline__ void mx2_mfma(f32x16 (&acc)[4][4], const Mx2Frag &f, const uint32_t (&sa)[4],
-                                         const uint32_t (&sw)[4])
+__device__ __forceinline__ void mx2_mfma(f32x16 (&acc)[4][2], const Mx2Frag &f, const uint32_t (&sa)[4],
+                                         const uint32_t (&sw)[2])
 {
 #pragma unroll
     for (int i = I0; i < I1; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx2_wide(f.w[j]), mx2_wide(f.a[i]), acc[i][j],
                                                                         4, 4, KS, (int)sw[j], KS, (int)sa[i]);
 }
 
-// Interleave the LDS reads of the next step with the MFMAs of this one: pairs of
-// MFMAs alternate with single reads, so neither the reads' latency nor their
+// Interleave the 6 LDS reads of the next step with the 8 MFMAs of this one, one
+// read after each of the first 6 MFMAs, so neither the reads' latency nor their
 // registers pile up.
-template <int N_READ, int N_MFMA>
 __device__ __forceinline__ void mx2_interleave()
 {
 #pragma unroll
-    for (int t = 0; t < N_READ; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, N_MFMA / N_READ, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                // DS read
+    for (int t = 0; t < 6; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
     __builtin_amdgcn_sched_barrier(0);
 }
@@ -235,34 +235,33 @@ __device__ __forceinline__ void mx2_interleave()
 // `oth` fetch stale bytes that are never used.  The stage is one basic block
 // whose instruction order the scheduling groups fix.
 __device__ __forceinline__ void mx2_stage(uint8_t *cur, uint8_t *oth, int k_next2, const Mx2Dma &dn,
-                                          const Mx2Lds &o, int wave, f32x16 (&acc)[4][4], Mx2Frag &f0,
-                                          Mx2Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[4])
+                                          const Mx2Lds &o, int wave, f32x16 (&acc)[4][2], Mx2Frag &f0,
+                                          Mx2Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[2])
 {
     mx2_frags(cur, o.la[1], o.lw[1], f1);
     mx2_mfma<0, 0, 4>(acc, f0, sa, sw);
-    mx2_interleave<8, 16>();
+    mx2_interleave();
     mx2_frags(cur, o.la[2], o.lw[2], f0);
     mx2_mfma<1, 0, 4>(acc, f1, sa, sw);
-    mx2_interleave<8, 16>();
+    mx2_interleave();
     mx2_frags(cur, o.la[3], o.lw[3], f1);
     mx2_mfma<2, 0, 4>(acc, f0, sa, sw);
-    mx2_interleave<8, 16>();
+    mx2_interleave();
     mx2_mfma<3, 0, 2>(acc, f1, sa, sw);
     __builtin_amdgcn_sched_barrier(0);
     // this wave's copy into `oth` has landed and its reads of `cur` returned; after
     // the barrier the same holds for every wave
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    uint32_t na[4], nw[4];
+    uint32_t na[4], nw[2];
     mx2_scales(oth, o, na, nw);
     mx2_frags(oth, o.la[0], o.lw[0], f0);
     mx2_dma(cur, dn, k_next2, wave);
     mx2_mfma<3, 2, 4>(acc, f1, sa, sw);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sa[i] = na[i];
-        sw[i] = nw[i];
-    }
+    for (int i = 0; i < 4; ++i) sa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sw[j] = nw[j];
     __builtin_amdgcn_sched_barrier(0);
 }
 
@@ -270,7 +269,7 @@ __device__ __forceinline__ void mx2_stage(uint8_t *cur, uint8_t *oth, int k_next
 // every store instruction writes whole 512-byte (bf16) or 1 KiB (fp32) row
 // runs.  Rows are padded by 16 bytes.  bf16: waves with wm = 0 stage tile rows
 // 0..127 in s0 and waves with wm = 1 rows 128..255 in s1, in one round; fp32: the
-// same split, 64 rows per wave pair per round, two rounds.
+// same split, 64 rows per wave row per round, two rounds.
 template <typename T>
 __device__ __forceinline__ void mx2_put(uint8_t *row, int col, const f32x16 &a, int g)
 {
@@ -284,15 +283,16 @@ __device__ __forceinline__ void mx2_put(uint8_t *row, int col, const f32x16 &a, 
 }
 
 // Store `rows` staged rows of width 256 elements (pitch bytes apart in `st`) to
-// output rows m_first.. and columns n0..; threads take 16-byte chunks in order.
-template <typename T>
+// output rows m_first.. and columns n0..; the NT threads take 16-byte chunks in
+// order.
+template <typename T, int NT = 256>
 __device__ __forceinline__ void mx2_flush(const uint8_t *st, int pitch, int rows, const MxGemmArgs &g, int m_first,
                                           int n0, int tid)
 {
     constexpr int kPer = 16 / (int)sizeof(T);              // elements per chunk
     constexpr int kChunks = 256 / kPer;                    // chunks per row
     const int M = (int)g.M, N = (int)g.N;
-    for (int q = tid; q < rows * kChunks; q += 256) {
+    for (int q = tid; q < rows * kChunks; q += NT) {
         const int r = q / kChunks, ch = q % kChunks;
         const int m = m_first + r, n = n0 + ch * kPer;
         if (m >= M || n >= N) continue;
@@ -311,12 +311,12 @@ __device__ __forceinline__ void mx2_flush(const uint8_t *st, int pitch, int rows
 }
 
 template <typename T>
-__device__ __forceinline__ void mx2_epilogue(const f32x16 (&acc)[4][4], uint8_t *s0, uint8_t *s1, const MxGemmArgs &g,
+__device__ __forceinline__ void mx2_epilogue(const f32x16 (&acc)[4][2], uint8_t *s0, uint8_t *s1, const MxGemmArgs &g,
                                              int m0, int n0, int wm, int wn, int lane, int tid)
 {
     constexpr int pitch = 256 * (int)sizeof(T) + 16;
     constexpr int rounds = sizeof(T) == 2 ? 1 : 2;
-    constexpr int rows = 128 / rounds;                     // staged rows per wave pair per round
+    constexpr int rows = 128 / rounds;                     // staged rows per wave row per round
     static_assert(rows * pitch <= kSStage, "a staged half tile must fit one stage buffer");
     uint8_t *mine = wm ? s1 : s0;
 #pragma unroll
@@ -324,28 +324,28 @@ __device__ __forceinline__ void mx2_epilogue(const f32x16 (&acc)[4][4], uint8_t 
 #pragma unroll
         for (int i = rd * (4 / rounds); i < (rd + 1) * (4 / rounds); ++i)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+            for (int j = 0; j < 2; ++j) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq)
                     mx2_put<T>(mine + (i * 32 - rd * rows + (lane & 31)) * pitch,
-                               wn * 128 + j * 32 + 8 * gq + 4 * (lane >> 5), acc[i][j], gq);
+                               wn * 64 + j * 32 + 8 * gq + 4 * (lane >> 5), acc[i][j], gq);
                 __builtin_amdgcn_sched_barrier(0);  // convert block by block: few live VGPRs
             }
         __syncthreads();
-        mx2_flush<T>(s0, pitch, rows, g, m0 + rd * rows, n0, tid);
-        mx2_flush<T>(s1, pitch, rows, g, m0 + 128 + rd * rows, n0, tid);
+        mx2_flush<T, 512>(s0, pitch, rows, g, m0 + rd * rows, n0, tid);
+        mx2_flush<T, 512>(s1, pitch, rows, g, m0 + 128 + rd * rows, n0, tid);
         if (rd + 1 < rounds) __syncthreads();
     }
 }
 
 template <typename OutT>
-__global__ __launch_bounds__(256) void k_mx_gemm_2s(MxGemmArgs g)
+__global__ __launch_bounds__(512) void k_mx_gemm_2s(MxGemmArgs g)
 {
     __shared__ __align__(16) uint8_t s0[kSStage];
     __shared__ __align__(16) uint8_t s1[kSStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
     const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + MBN - 1) / MBN;
     int tm, tn;
@@ -359,28 +359,27 @@ __global__ __launch_bounds__(256) void k_mx_gemm_2s(MxGemmArgs g)
     d.rsa = mx2_rsrc(g.a_scales, g.M * (g.K / 32));
     d.rsw = mx2_rsrc(g.w_scales, g.N * (g.K / 32));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = 512 * wave + 64 * i + lane;
+    for (int i = 0; i < 4; ++i) {
+        const int q = 256 * wave + 64 * i + lane;
         const int r = q >> 3;
         const int c = (q & 7) ^ ((r >> 1) & 7);
         d.a[i] = (uint32_t)min(m0 + r, M - 1) * (uint32_t)(K / 2) + 16 * c;
         d.w[i] = (uint32_t)min(n0 + r, N - 1) * (uint32_t)(K / 2) + 16 * c;
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-        const int q = 128 * wave + 64 * i + lane;
-        d.as[i] = (uint32_t)min(m0 + (q >> 1), M - 1) * (uint32_t)(K / 32) + 4 * (q & 1);
-        d.ws[i] = (uint32_t)min(n0 + (q >> 1), N - 1) * (uint32_t)(K / 32) + 4 * (q & 1);
+    {
+        const int q = 64 * wave + lane;
+        d.as = (uint32_t)min(m0 + (q >> 1), M - 1) * (uint32_t)(K / 32) + 4 * (q & 1);
+        d.ws = (uint32_t)min(n0 + (q >> 1), N - 1) * (uint32_t)(K / 32) + 4 * (q & 1);
     }
     Mx2Lds o;
     const int half = lane >> 5, x = ((lane & 31) >> 1) & 7;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         o.la[ks] = 128 * (wm * 128 + (lane & 31)) + 16 * ((2 * ks + half) ^ x);
-        o.lw[ks] = kSTile + 128 * (wn * 128 + (lane & 31)) + 16 * ((2 * ks + half) ^ x);
+        o.lw[ks] = kSTile + 128 * (wn * 64 + (lane & 31)) + 16 * ((2 * ks + half) ^ x);
     }
     o.lsa = 2 * kSTile + 8 * (wm * 128 + (lane & 31));
-    o.lsw = 2 * kSTile + kSScl + 8 * (wn * 128 + (lane & 31));
+    o.lsw = 2 * kSTile + kSScl + 8 * (wn * 64 + (lane & 31));
     o.sel = half ? 0x07050301u : 0x06040200u;
     dz = d;
     dz.ra = mx2_rsrc(g.a_codes, 0);
@@ -388,11 +387,11 @@ __global__ __launch_bounds__(256) void k_mx_gemm_2s(MxGemmArgs g)
     dz.rsa = mx2_rsrc(g.a_scales, 0);
     dz.rsw = mx2_rsrc(g.w_scales, 0);
 
-    f32x16 acc[4][4];
+    f32x16 acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
 
     // Stages t = 0 .. T-1 with T = nk rounded up to even: with nk odd, stage 0 is
     // an all-zero stage (its products add +0 to accumulators that start at +0)
@@ -405,7 +404,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm_2s(MxGemmArgs g)
     __syncthreads();
     mx2_dma(s1, stage_d(1), stage_k(1), wave);
     Mx2Frag f0, f1;
-    uint32_t sa[4], sw[4];
+    uint32_t sa[4], sw[2];
     mx2_scales(s0, o, sa, sw);
     mx2_frags(s0, o.la[0], o.lw[0], f0);
     for (int t = 0; t < T; t += 2) {
@@ -858,9 +857,9 @@ fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)
     if (g.K % kSK == 0 && g.M * (g.K / 2) < (int64_t(1) << 32) && g.N * (g.K / 2) < (int64_t(1) << 32)) {
         const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
         if (g.c_bf16)
-            hipLaunchKernelGGL(k_mx_gemm_2s<__bf16>, dim3(tiles), dim3(256), 0, st, g);
+            hipLaunchKernelGGL(k_mx_gemm_2s<__bf16>, dim3(tiles), dim3(512), 0, st, g);
         else
-            hipLaunchKernelGGL(k_mx_gemm_2s<float>, dim3(tiles), dim3(256), 0, st, g);
+            hipLaunchKernelGGL(k_mx_gemm_2s<float>, dim3(tiles), dim3(512), 0, st, g);
         return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     }
     return launch_mx<false>(g, st);
