@@ -594,8 +594,9 @@ static fp4_status launch_mx(const MxGemmArgs &g, hipStream_t st)
 // 16-byte halves; the E8M0 byte a lane half gives applies to K-block h of
 // either operand.  Products are exact, the accumulation fp32.
 //
-// 256 x 256 tiles, waves 2 x 2 of 128 x 128, acc[i][j] = W_j A_i^T as in the
-// MXFP4 kernel.  Three LDS stages of 128 K-elements, each its own LDS object,
+// 256 x 256 tiles, 8 waves (two per SIMD) as 4 (M) x 2 (N) blocks of 64 x 128
+// (the 32-byte FP8 fragments make the A side the expensive one to hold and read),
+// acc[i][j] = W_j A_i^T as in the MXFP4 kernel.  Three LDS stages of 128 K-elements, each its own LDS object,
 // fed by buffer-to-LDS DMA: A [256][128 B] (16-byte chunk c of row r at slot
 // 8 r + (c ^ ((r >> 1) & 7))), W [256][64 B] (chunk c at 4 r + (c ^ ((r >> 2) & 3))),
 // and each operand's 4 E8M0 bytes per row.  Those swizzles make the 16 lanes of
@@ -609,33 +610,35 @@ constexpr int kA8W = 256 * 128;            // W fp4 [256][64]
 constexpr int kA8SA = kA8W + 256 * 64;     // A scales [256][4]
 constexpr int kA8SW = kA8SA + 1024;        // W scales [256][4]
 constexpr int kA8Stage = kA8SW + 1024;     // 51,200 bytes
-constexpr int kA8Dma = 8 + 4 + 1 + 1;      // copies per wave per stage
+constexpr int kA8Dma = 4 + 2 + 1;          // copies per wave per stage
 constexpr uint32_t kA8Out = 0x80000000u;   // an offset past every descriptor's size
 constexpr int kA8EpiPitch16 = 256 * 2 + 16, kA8EpiPitch32 = 256 * 4 + 16;
 static_assert(64 * kA8EpiPitch16 <= kA8Stage && 32 * kA8EpiPitch32 <= kA8Stage, "epilogue staging");
 
+// Per-lane source offsets of a wave's copies: A code slot q = 256 wave + 64 i +
+// lane (row q / 8), W code slot q = 128 wave + 64 i + lane (row q / 4), and one
+// scale dword: waves 0..3 copy A's rows 64 wave + lane, waves 4..7 W's rows
+// 64 (wave - 4) + lane, into bytes kA8SA + 256 wave + 4 lane of the stage.
 struct A8Dma {
-    __amdgpu_buffer_rsrc_t ra, rw, rsa, rsw;
-    uint32_t a[8], w[4], sa, sw;
+    __amdgpu_buffer_rsrc_t ra, rw, rs;
+    uint32_t a[4], w[2], s;
 };
 
 __device__ __forceinline__ void a8_dma(uint8_t *st, const A8Dma &d, int k0, int wave)
 {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + kA8A + 16 * (512 * wave + 64 * i)), 16,
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + kA8A + 16 * (256 * wave + 64 * i)), 16,
                                                  (int)d.a[i], k0, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kA8W + 16 * (256 * wave + 64 * i)), 16,
+    for (int i = 0; i < 2; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kA8W + 16 * (128 * wave + 64 * i)), 16,
                                                  (int)d.w[i], k0 / 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsa, (mx_lds_void *)(st + kA8SA + 256 * wave), 4, (int)d.sa, k0 / 32,
-                                             0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rsw, (mx_lds_void *)(st + kA8SW + 256 * wave), 4, (int)d.sw, k0 / 32,
-                                             0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (mx_lds_void *)(st + kA8SA + 256 * wave), 4, (int)d.s, k0 / 32, 0,
+                                             0);
 }
 
-// per-lane LDS offsets: A row wm 128 + l, W row wn 128 + l (l = lane % 32, half
+// per-lane LDS offsets: A row wm 64 + l, W row wn 128 + l (l = lane % 32, half
 // h = lane / 32); fragment i / j adds 32 rows (4096 / 2048 bytes)
 struct A8Lds {
     uint32_t a[2][2];  // [step][16-byte half p] A chunk 4 ks + 2 p + h
@@ -645,7 +648,7 @@ struct A8Lds {
 };
 
 struct A8Frag {
-    i32x8 a[4];
+    i32x8 a[2];
     i32x4 w[4];
 };
 
@@ -653,106 +656,112 @@ template <int KS>
 __device__ __forceinline__ void a8_frags(const uint8_t *st, const A8Lds &o, A8Frag &f)
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i) {
         const i32x4 lo = *reinterpret_cast<const i32x4 *>(st + o.a[KS][0] + 4096 * i);
         const i32x4 hi = *reinterpret_cast<const i32x4 *>(st + o.a[KS][1] + 4096 * i);
         f.a[i] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        f.w[i] = *reinterpret_cast<const i32x4 *>(st + o.w[KS] + 2048 * i);
     }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f.w[j] = *reinterpret_cast<const i32x4 *>(st + o.w[KS] + 2048 * j);
 }
 
 // the lane's E8M0 bytes of the stage: byte 0 = step 0's block, byte 2 = step 1's
-__device__ __forceinline__ void a8_scales(const uint8_t *st, const A8Lds &o, uint32_t (&sa)[4], uint32_t (&sw)[4])
+__device__ __forceinline__ void a8_scales(const uint8_t *st, const A8Lds &o, uint32_t (&sa)[2], uint32_t (&sw)[4])
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 2; ++i)
         sa[i] = (*reinterpret_cast<const uint32_t *>(st + o.sa + 128 * i) >> o.hsh) & 0x00FF00FFu;
-        sw[i] = (*reinterpret_cast<const uint32_t *>(st + o.sw + 128 * i) >> o.hsh) & 0x00FF00FFu;
-    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+        sw[j] = (*reinterpret_cast<const uint32_t *>(st + o.sw + 128 * j) >> o.hsh) & 0x00FF00FFu;
 }
 
 template <int KS>
-__device__ __forceinline__ void a8_mfma(f32x16 (&acc)[4][4], const A8Frag &f, const uint32_t (&sa)[4],
+__device__ __forceinline__ void a8_mfma(f32x16 (&acc)[2][4], const A8Frag &f, const uint32_t (&sa)[2],
                                         const uint32_t (&sw)[4])
 {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx2_wide(f.w[j]), f.a[i], acc[i][j], 4, 0,
                                                                         2 * KS, (int)sw[j], 2 * KS, (int)sa[i]);
 }
 
-template <int NR>
+// the 8 fragment reads of step 1 under the 8 MFMAs of step 0, one after each
 __device__ __forceinline__ void a8_interleave()
 {
 #pragma unroll
-    for (int t = 0; t < NR; ++t) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 16 / NR > 0 ? 16 / NR : 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                          // DS read
+    for (int t = 0; t < 8; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
     }
     __builtin_amdgcn_sched_barrier(0);
 }
 
 // One stage t (in `cur`, stage t + 1 in `nxt`); f0 / sa / sw hold step 0 of t.
 __device__ __forceinline__ void a8_stage(uint8_t *cur, const uint8_t *nxt, int t, int nk, const A8Dma &d,
-                                         const A8Dma &dz, const A8Lds &o, int wave, f32x16 (&acc)[4][4], A8Frag &f0,
-                                         A8Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[4])
+                                         const A8Dma &dz, const A8Lds &o, int wave, f32x16 (&acc)[2][4], A8Frag &f0,
+                                         A8Frag &f1, uint32_t (&sa)[2], uint32_t (&sw)[4])
 {
     a8_frags<1>(cur, o, f1);
     a8_mfma<0>(acc, f0, sa, sw);
-    a8_interleave<12>();
+    a8_interleave();
     __builtin_amdgcn_s_waitcnt((kA8Dma & 15) | ((kA8Dma >> 4) << 14) | (7 << 4) | (15 << 8));  // stage t + 1 landed
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));                                // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    uint32_t na[4], nw[4];
+    uint32_t na[2], nw[4];
     a8_scales(nxt, o, na, nw);
     a8_frags<0>(nxt, o, f0);
     a8_dma(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kA8K, wave);
     a8_mfma<1>(acc, f1, sa, sw);
-    __builtin_amdgcn_sched_group_barrier(0x100, 20, 0);  // DS read: next stage's scales and step 0
+    __builtin_amdgcn_sched_group_barrier(0x100, 14, 0);  // DS read: next stage's scales and step 0
     __builtin_amdgcn_sched_group_barrier(0x020, kA8Dma, 0);  // VMEM: the copies
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);  // MFMA
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        sa[i] = na[i];
-        sw[i] = nw[i];
-    }
+    for (int i = 0; i < 2; ++i) sa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sw[j] = nw[j];
 }
 
-// Epilogue: rounds of R rows per wave pair (wm = 0 rows through s0, wm = 1 through
-// s1, rows padded by 16 bytes), then whole-row 16-byte stores.
+// Epilogue: tile rows 0..127 (waves wm = 0, 1) pass through s0, rows 128..255
+// (wm = 2, 3) through s1, in rounds of R rows (rows padded by 16 bytes), each
+// round then stored as whole-row 16-byte pieces.
 template <typename T>
-__device__ __forceinline__ void a8_epilogue(const f32x16 (&acc)[4][4], uint8_t *s0, uint8_t *s1,
+__device__ __forceinline__ void a8_epilogue(const f32x16 (&acc)[2][4], uint8_t *s0, uint8_t *s1,
                                             const MxGemmArgs &g, int m0, int n0, int wm, int wn, int lane, int tid)
 {
     constexpr int es = (int)sizeof(T);
     constexpr int pitch = es == 2 ? kA8EpiPitch16 : kA8EpiPitch32;
     constexpr int R = es == 2 ? 64 : 32;
-    constexpr int kPer = 16 / es, kChunks = 256 / kPer;
-    uint8_t *mine = wm ? s1 : s0;
+    uint8_t *mine = wm >= 2 ? s1 : s0;
+    const int half_row0 = 64 * (wm & 1);  // the wave's first row within its 128-row half
 #pragma unroll
     for (int rd = 0; rd < 128 / R; ++rd) {
 #pragma unroll
-        for (int i = rd * R / 32; i < (rd + 1) * R / 32; ++i)
+        for (int i = 0; i < 2; ++i) {
+            const int r = half_row0 + 32 * i - rd * R;  // wave-uniform
+            if (r >= 0 && r < R) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
+                for (int j = 0; j < 4; ++j) {
 #pragma unroll
-                for (int gq = 0; gq < 4; ++gq)
-                    mx2_put<T>(mine + (i * 32 - rd * R + (lane & 31)) * pitch,
-                               wn * 128 + j * 32 + 8 * gq + 4 * (lane >> 5), acc[i][j], gq);
-                __builtin_amdgcn_sched_barrier(0);
+                    for (int gq = 0; gq < 4; ++gq)
+                        mx2_put<T>(mine + (r + (lane & 31)) * pitch, wn * 128 + j * 32 + 8 * gq + 4 * (lane >> 5),
+                                   acc[i][j], gq);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
             }
+        }
         __syncthreads();
-        mx2_flush<T>(s0, pitch, R, g, m0 + rd * R, n0, tid);
-        mx2_flush<T>(s1, pitch, R, g, m0 + 128 + rd * R, n0, tid);
+        mx2_flush<T, 512>(s0, pitch, R, g, m0 + rd * R, n0, tid);
+        mx2_flush<T, 512>(s1, pitch, R, g, m0 + 128 + rd * R, n0, tid);
         __syncthreads();
     }
 }
 
 template <typename OutT>
-__global__ __launch_bounds__(256) void k_mx_gemm_w4a8(MxGemmArgs g)
+__global__ __launch_bounds__(512) void k_mx_gemm_w4a8(MxGemmArgs g)
 {
     __shared__ __align__(16) uint8_t s0[kA8Stage];
     __shared__ __align__(16) uint8_t s1[kA8Stage];
@@ -770,33 +779,33 @@ __global__ __launch_bounds__(256) void k_mx_gemm_w4a8(MxGemmArgs g)
     A8Dma d, dz;
     d.ra = mx2_rsrc(g.a_codes, g.M * g.K);
     d.rw = mx2_rsrc(g.w_codes, g.N * (g.K / 2));
-    d.rsa = mx2_rsrc(g.a_scales, g.M * (g.K / 32));
-    d.rsw = mx2_rsrc(g.w_scales, g.N * (g.K / 32));
+    d.rs = wave < 4 ? mx2_rsrc(g.a_scales, g.M * (g.K / 32)) : mx2_rsrc(g.w_scales, g.N * (g.K / 32));
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        const int q = 512 * wave + 64 * i + lane;
+    for (int i = 0; i < 4; ++i) {
+        const int q = 256 * wave + 64 * i + lane;
         const int r = q >> 3, c = (q & 7) ^ ((r >> 1) & 7);
         d.a[i] = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)K + 16 * c : kA8Out;
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int q = 256 * wave + 64 * i + lane;
+    for (int i = 0; i < 2; ++i) {
+        const int q = 128 * wave + 64 * i + lane;
         const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
         d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * c : kA8Out;
     }
-    const int qs = 64 * wave + lane;
-    d.sa = m0 + qs < M ? (uint32_t)(m0 + qs) * (uint32_t)(K / 32) : kA8Out;
-    d.sw = n0 + qs < N ? (uint32_t)(n0 + qs) * (uint32_t)(K / 32) : kA8Out;
+    {
+        const int r = 64 * (wave & 3) + lane;
+        if (wave < 4) d.s = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(K / 32) : kA8Out;
+        else d.s = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 32) : kA8Out;
+    }
     dz = d;
     dz.ra = mx2_rsrc(g.a_codes, 0);
     dz.rw = mx2_rsrc(g.w_codes, 0);
-    dz.rsa = mx2_rsrc(g.a_scales, 0);
-    dz.rsw = mx2_rsrc(g.w_scales, 0);
+    dz.rs = mx2_rsrc(g.a_scales, 0);
 
     A8Lds o;
     {
         const int h = lane >> 5, l = lane & 31;
-        const int ra = wm * 128 + l, rw = wn * 128 + l;
+        const int ra = wm * 64 + l, rw = wn * 128 + l;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
 #pragma unroll
@@ -808,9 +817,9 @@ __global__ __launch_bounds__(256) void k_mx_gemm_w4a8(MxGemmArgs g)
         o.hsh = 8 * h;
     }
 
-    f32x16 acc[4][4];
+    f32x16 acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = f32x16{};
 
@@ -820,7 +829,7 @@ __global__ __launch_bounds__(256) void k_mx_gemm_w4a8(MxGemmArgs g)
     __builtin_amdgcn_s_waitcnt(((2 * kA8Dma) & 15) | (((2 * kA8Dma) >> 4) << 14) | (7 << 4) | (15 << 8));
     asm volatile("s_barrier" ::: "memory");
     A8Frag f0, f1;
-    uint32_t sa[4], sw[4];
+    uint32_t sa[2], sw[4];
     a8_scales(s0, o, sa, sw);
     a8_frags<0>(s0, o, f0);
     const int nfull = nk - nk % 3;
@@ -845,9 +854,9 @@ fp4_status launch_mxfp4_gemm_w4a8(const MxGemmArgs &g, hipStream_t st)
         return FP4_ERR_SHAPE;
     const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
     if (g.c_bf16)
-        hipLaunchKernelGGL((k_mx_gemm_w4a8<__bf16>), dim3(tiles), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((k_mx_gemm_w4a8<__bf16>), dim3(tiles), dim3(512), 0, st, g);
     else
-        hipLaunchKernelGGL((k_mx_gemm_w4a8<float>), dim3(tiles), dim3(256), 0, st, g);
+        hipLaunchKernelGGL((k_mx_gemm_w4a8<float>), dim3(tiles), dim3(512), 0, st, g);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
