@@ -65,6 +65,9 @@ def _declare(L):
         "mxfp4_gemm_w4a4_workspace": (sz, [i64, i64]),
         "mxfp4_gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
         "mxfp4_gemm_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
+        "mxfp4_gemm_w4a4_seg_workspace": (sz, [i64, i64]),
+        "mxfp4_gemm_w4a4_seg": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
+        "mxfp4_gemm_prequant_seg": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
         "mxfp4_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, p, i32, i64, p]),
         "mxfp4_pack_decode": (i32, [p, p, i64, i64, p, p, p]),
         "mxfp4_gemm_w4a16_decode": (i32, [p, i64, i64, i64, p, p, i64, p, i32, i64, p]),
@@ -423,6 +426,46 @@ def mxfp4_pack_decode(w: PackedMXFP4, out: DecodeMXFP4 | None = None) -> DecodeM
                           torch.empty(K // 128, N, 4, dtype=torch.uint8, device=dev), N, K)
     _check(L.mxfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
                                _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a4_seg_workspace(M: int, K: int, device="cuda") -> torch.Tensor:
+    return torch.empty(lib().mxfp4_gemm_w4a4_seg_workspace(M, K), dtype=torch.uint8, device=device)
+
+
+def mxfp4_seg_packed_a(ws: torch.Tensor, M: int, K: int) -> DecodeMXFP4:
+    """Views of A's segment-major MXFP4 form inside an mxfp4_gemm_w4a4_seg workspace."""
+    cb = (M * (K // 2) + 255) // 256 * 256
+    return DecodeMXFP4(ws[:M * K // 2].view(K // 128, M, 64), ws[cb:cb + M * K // 32].view(K // 128, M, 4), M, K)
+
+
+def mxfp4_gemm_w4a4_seg(a: torch.Tensor, w: DecodeMXFP4, rule="ocp", dtype=torch.bfloat16,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """MXFP4 W4A4 GEMM with W in the decode (segment-major) layout; A is quantized
+    into the workspace in that layout.  The same result as mxfp4_gemm_w4a4."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("mxfp4_gemm_w4a4_seg takes bfloat16 activations")
+    M, K = a.shape
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    if workspace is None:
+        workspace = mxfp4_gemm_w4a4_seg_workspace(M, K, a.device)
+    _check(L.mxfp4_gemm_w4a4_seg(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
+                                 _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                                 _stream()))
+    return out
+
+
+def mxfp4_gemm_prequant_seg(a: DecodeMXFP4, w: DecodeMXFP4, dtype=torch.bfloat16,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """The GEMM half of mxfp4_gemm_w4a4_seg: A and W both in the segment-major layout."""
+    L = lib()
+    if out is None:
+        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.mxfp4_gemm_prequant_seg(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
+                                     _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
 
 

@@ -437,6 +437,63 @@ fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4
     return launch_mxfp4_gemm(g, stream);
 }
 
+// ------------------------------------------- MXFP4 W4A4, segment-major ----
+
+size_t mxfp4_gemm_w4a4_seg_workspace(int64_t M, int64_t K)
+{
+    return mxfp4_gemm_w4a4_workspace(M, K);  // the same bytes, in the other order
+}
+
+fp4_status mxfp4_gemm_prequant_seg(const uint8_t *a_codes_p, const uint8_t *a_scales_p, int64_t M, int64_t K,
+                                   const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                                   fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    FP4_TRY(check_packed(a_codes_p, a_scales_p));
+    FP4_TRY(check_packed(w_codes_p, w_scales_p));
+    FP4_TRY(check_device());
+    MxGemmArgs g{};
+    g.a_codes = a_codes_p;
+    g.a_scales = a_scales_p;
+    g.w_codes = w_codes_p;
+    g.w_scales = w_scales_p;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_mxfp4_gemm_seg(g, stream);
+}
+
+fp4_status mxfp4_gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                               const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                               fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    if (rule != FP4_MX_OCP_FLOOR && rule != FP4_MX_CEIL) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(w_codes_p, w_scales_p));
+    if (!ws || !aligned16(ws) || ws_bytes < mxfp4_gemm_w4a4_seg_workspace(M, K)) return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
+    uint8_t *as = ac + align256((size_t)M * (size_t)(K / 2));
+    FP4_TRY(launch_mxfp4_quantize_seg(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
+    MxGemmArgs g{};
+    g.a_codes = ac;
+    g.a_scales = as;
+    g.w_codes = w_codes_p;
+    g.w_scales = w_scales_p;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    return launch_mxfp4_gemm_seg(g, stream);
+}
+
 // ------------------------------------------------------------------- W4A8 --
 
 fp4_status mxfp8_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,

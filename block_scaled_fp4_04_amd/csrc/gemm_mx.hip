@@ -860,6 +860,283 @@ fp4_status launch_mxfp4_gemm_w4a8(const MxGemmArgs &g, hipStream_t st)
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
+// ---- segment-major operands: a ring of four LDS slots of 128 K-elements ----
+//
+// Both operands in the segment-major layout (the MXFP4 decode layout): for each
+// 128-element K segment s, every row's 64 code bytes at (s rows + r) 64 and its
+// 4 E8M0 bytes at (s rows + r) 4.  One segment of a 256-row panel is then 16 KiB
+// of contiguous bytes, so a slot of 128 K costs whole cache lines; in the
+// row-major layout the same slot is 64-byte halves of lines, which the memory
+// system moves at three quarters of the rate (a copy-only kernel with the GEMM's
+// pattern: 239 us against 178 us).  With 34 KiB slots four fit in LDS: while
+// slot s is multiplied, slots s + 1 and s + 2 are landing and slot s + 3 is being
+// copied, its 5 copies per wave spread among slot s's MFMAs; a copy issued in a
+// burst holds back the MFMAs behind it in the wave's instruction stream.
+//
+// 8 waves as in k_mx_gemm_2s (2 x 4 blocks of 128 x 64).  Slot layout: codes
+// [256][64] per operand (16-byte chunk c of row r at slot c ^ ((r >> 2) & 3)),
+// then each operand's [256][4] scale bytes.  Rows past the matrix read the last
+// row (their products land only in outputs that are never stored); slots past
+// the end are filled through size-0 descriptors (zeros).  Slot count T is nk
+// rounded up to a multiple of 4, the first T - nk slots being such zero slots.
+constexpr int kQK = 128;                         // K elements per slot
+constexpr int kQTile = 256 * 64;                 // 16 KiB of codes per operand
+constexpr int kQScl = 256 * 4;                   // 1 KiB of scale bytes per operand
+constexpr int kQSlot = 2 * kQTile + 2 * kQScl;   // 34,816 bytes
+constexpr int kQDma = 5;                         // copies per wave per slot
+
+// per-lane source offsets within a segment: A / W code slot q = 128 wave + 64 i +
+// lane (row q / 4); one scale dword, waves 0..3 for A rows 64 wave + lane, waves
+// 4..7 for W rows 64 (wave - 4) + lane.  A segment's bytes start at s * seg_a /
+// seg_w / seg_s (the scalar offset of each copy).
+struct MqDma {
+    __amdgpu_buffer_rsrc_t ra, rw, rs;
+    uint32_t a[2], w[2], s;
+    uint32_t seg_a, seg_w, seg_s;
+};
+
+template <int P>
+__device__ __forceinline__ void mq_dma(uint8_t *st, const MqDma &d, int seg, int wave)
+{
+    if constexpr (P < 2)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + 16 * (128 * wave + 64 * P)), 16,
+                                                 (int)d.a[P], seg * (int)d.seg_a, 0, 0);
+    else if constexpr (P < 4)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kQTile + 16 * (128 * wave + 64 * (P - 2))),
+                                                 16, (int)d.w[P - 2], seg * (int)d.seg_w, 0, 0);
+    else
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (mx_lds_void *)(st + 2 * kQTile + 256 * wave), 4, (int)d.s,
+                                                 seg * (int)d.seg_s, 0, 0);
+}
+
+__device__ __forceinline__ void mq_dma_all(uint8_t *st, const MqDma &d, int seg, int wave)
+{
+    mq_dma<0>(st, d, seg, wave);
+    mq_dma<1>(st, d, seg, wave);
+    mq_dma<2>(st, d, seg, wave);
+    mq_dma<3>(st, d, seg, wave);
+    mq_dma<4>(st, d, seg, wave);
+}
+
+// LDS offsets one lane reads within a slot: A fragment (i, ks) at la[ks] + 2048 i,
+// W fragment (j, ks) at lw[ks] + 2048 j; scale dwords at lsa + 128 i, lsw + 128 j
+struct MqLds {
+    uint32_t la[2], lw[2], lsa, lsw, hsh;
+};
+
+__device__ __forceinline__ void mq_frags(const uint8_t *st, uint32_t la, uint32_t lw, Mx2Frag &f)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(st + la + 2048 * i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.w[j] = *reinterpret_cast<const i32x4 *>(st + lw + 2048 * j);
+}
+
+// the lane's E8M0 bytes of the slot: byte 0 = step 0's block (2 * 0 + h), byte 2 =
+// step 1's (2 + h), h the lane half
+__device__ __forceinline__ void mq_scales(const uint8_t *st, const MqLds &o, uint32_t (&sa)[4], uint32_t (&sw)[2])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = (*reinterpret_cast<const uint32_t *>(st + o.lsa + 128 * i) >> o.hsh) & 0x00FF00FFu;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sw[j] = (*reinterpret_cast<const uint32_t *>(st + o.lsw + 128 * j) >> o.hsh) & 0x00FF00FFu;
+}
+
+template <int KS, int I0, int I1>
+__device__ __forceinline__ void mq_mfma(f32x16 (&acc)[4][2], const Mx2Frag &f, const uint32_t (&sa)[4],
+                                        const uint32_t (&sw)[2])
+{
+#pragma unroll
+    for (int i = I0; i < I1; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx2_wide(f.w[j]), mx2_wide(f.a[i]), acc[i][j],
+                                                                        4, 4, 2 * KS, (int)sw[j], 2 * KS, (int)sa[i]);
+}
+
+// Slot s: multiply `cur` (f0 / sa / sw hold its step 0); copy segment `seg` (slot
+// s + 3) into `dst`, which the previous barrier freed, spread among the MFMAs; at
+// the barrier slot s + 1 (`nxt`) must have landed, while the 10 copies of slots
+// s + 2 and s + 3 may still be in flight.  One basic block.
+__device__ __forceinline__ void mq_slot(const uint8_t *cur, const uint8_t *nxt, uint8_t *dst, const MqDma &d,
+                                        int seg, const MqLds &o, int wave, f32x16 (&acc)[4][2], Mx2Frag &f0,
+                                        Mx2Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[2])
+{
+    // step 0: 8 MFMAs, the 6 reads of step 1's fragments, 3 copies
+    mq_frags(cur, o.la[1], o.lw[1], f1);
+    mq_mfma<0, 0, 4>(acc, f0, sa, sw);
+    mq_dma<0>(dst, d, seg, wave);
+    mq_dma<1>(dst, d, seg, wave);
+    mq_dma<2>(dst, d, seg, wave);
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
+        if (t < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
+        if (t == 1 || t == 4 || t == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // step 1, first half: 4 MFMAs, 2 copies
+    mq_mfma<1, 0, 2>(acc, f1, sa, sw);
+    mq_dma<3>(dst, d, seg, wave);
+    mq_dma<4>(dst, d, seg, wave);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (t == 0 || t == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    // slot s + 1 has landed (vmcnt 10) and this wave's reads of `cur` returned; the
+    // barrier extends both to every wave
+    __builtin_amdgcn_s_waitcnt(((2 * kQDma) & 15) | (7 << 4));
+    asm volatile("s_barrier" ::: "memory");
+    uint32_t na[4], nw[2];
+    mq_scales(nxt, o, na, nw);
+    mq_frags(nxt, o.la[0], o.lw[0], f0);
+    mq_mfma<1, 2, 4>(acc, f1, sa, sw);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sa[i] = na[i];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) sw[j] = nw[j];
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// Epilogue through the four slots: bf16 stages 64 tile rows per slot (slots 0, 1
+// rows 0..127 from the waves with wm = 0, slots 2, 3 rows 128..255), one round;
+// fp32 32 rows per slot, two rounds.
+template <typename T>
+__device__ __forceinline__ void mq_epilogue(const f32x16 (&acc)[4][2], uint8_t *q0, uint8_t *q1, uint8_t *q2,
+                                            uint8_t *q3, const MxGemmArgs &g, int m0, int n0, int wm, int wn,
+                                            int lane, int tid)
+{
+    constexpr int pitch = 256 * (int)sizeof(T) + 16;
+    constexpr int rows = sizeof(T) == 2 ? 64 : 32;  // rows per slot per round
+    constexpr int rounds = sizeof(T) == 2 ? 1 : 2;
+    static_assert(rows * pitch <= kQSlot, "a slot holds a round's rows");
+#pragma unroll
+    for (int rd = 0; rd < rounds; ++rd) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            if (sizeof(T) == 4 && i / 2 != rd) continue;
+            const int rr = sizeof(T) == 2 ? 32 * i : 32 * i - 64 * rd;  // row within the round's two slots
+            const int sub = rr / rows;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                uint8_t *slot = wm ? (sub ? q3 : q2) : (sub ? q1 : q0);
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq)
+                    mx2_put<T>(slot + (rr % rows + (lane & 31)) * pitch, wn * 64 + j * 32 + 8 * gq + 4 * (lane >> 5),
+                               acc[i][j], gq);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        __syncthreads();
+        const int mr = m0 + (sizeof(T) == 4 ? 64 * rd : 0);
+        mx2_flush<T, 512>(q0, pitch, rows, g, mr, n0, tid);
+        mx2_flush<T, 512>(q1, pitch, rows, g, mr + rows, n0, tid);
+        mx2_flush<T, 512>(q2, pitch, rows, g, mr + 128, n0, tid);
+        mx2_flush<T, 512>(q3, pitch, rows, g, mr + 128 + rows, n0, tid);
+        if (rd + 1 < rounds) __syncthreads();
+    }
+}
+
+template <typename OutT>
+__global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
+{
+    __shared__ __align__(16) uint8_t q0[kQSlot];
+    __shared__ __align__(16) uint8_t q1[kQSlot];
+    __shared__ __align__(16) uint8_t q2[kQSlot];
+    __shared__ __align__(16) uint8_t q3[kQSlot];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
+    const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + MBN - 1) / MBN;
+    int tm, tn;
+    mx_tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+    const int m0 = tm * MBM, n0 = tn * MBN;
+    const int nk = K / kQK;
+
+    MqDma d, dz;
+    d.ra = mx2_rsrc(g.a_codes, g.M * (g.K / 2));
+    d.rw = mx2_rsrc(g.w_codes, g.N * (g.K / 2));
+    d.rs = wave < 4 ? mx2_rsrc(g.a_scales, g.M * (g.K / 32)) : mx2_rsrc(g.w_scales, g.N * (g.K / 32));
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+        const int q = 128 * wave + 64 * i + lane;
+        const int r = q >> 2;
+        const int c = (q & 3) ^ ((r >> 2) & 3);
+        d.a[i] = (uint32_t)min(m0 + r, M - 1) * 64u + 16 * c;
+        d.w[i] = (uint32_t)min(n0 + r, N - 1) * 64u + 16 * c;
+    }
+    {
+        const int r = 64 * (wave & 3) + lane;
+        d.s = (uint32_t)(wave < 4 ? min(m0 + r, M - 1) : min(n0 + r, N - 1)) * 4u;
+    }
+    d.seg_a = (uint32_t)M * 64u;
+    d.seg_w = (uint32_t)N * 64u;
+    d.seg_s = (uint32_t)(wave < 4 ? M : N) * 4u;
+    dz = d;
+    dz.ra = mx2_rsrc(g.a_codes, 0);
+    dz.rw = mx2_rsrc(g.w_codes, 0);
+    dz.rs = mx2_rsrc(g.a_scales, 0);
+
+    MqLds o;
+    {
+        const int h = lane >> 5, l = lane & 31;
+        const int ra = wm * 128 + l, rw = wn * 64 + l;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            o.la[ks] = 64 * ra + 16 * ((2 * ks + h) ^ ((ra >> 2) & 3));
+            o.lw[ks] = kQTile + 64 * rw + 16 * ((2 * ks + h) ^ ((rw >> 2) & 3));
+        }
+        o.lsa = 2 * kQTile + 4 * ra;
+        o.lsw = 2 * kQTile + kQScl + 4 * rw;
+        o.hsh = 8 * h;
+    }
+
+    f32x16 acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+
+    const int T = (nk + 3) & ~3, ph = T - nk;
+    auto seg_of = [&](int t) { return max(t - ph, 0); };
+    auto slot_d = [&](int t) -> const MqDma & { return (t >= ph && t < T) ? d : dz; };
+    mq_dma_all(q0, slot_d(0), seg_of(0), wave);
+    mq_dma_all(q1, slot_d(1), seg_of(1), wave);
+    mq_dma_all(q2, slot_d(2), seg_of(2), wave);
+    __builtin_amdgcn_s_waitcnt(((2 * kQDma) & 15) | (7 << 4));  // slot 0 landed
+    asm volatile("s_barrier" ::: "memory");
+    Mx2Frag f0, f1;
+    uint32_t sa[4], sw[2];
+    mq_scales(q0, o, sa, sw);
+    mq_frags(q0, o.la[0], o.lw[0], f0);
+    for (int t = 0; t < T; t += 4) {
+        mq_slot(q0, q1, q3, slot_d(t + 3), seg_of(t + 3), o, wave, acc, f0, f1, sa, sw);
+        mq_slot(q1, q2, q0, slot_d(t + 4), seg_of(t + 4), o, wave, acc, f0, f1, sa, sw);
+        mq_slot(q2, q3, q1, slot_d(t + 5), seg_of(t + 5), o, wave, acc, f0, f1, sa, sw);
+        mq_slot(q3, q0, q2, slot_d(t + 6), seg_of(t + 6), o, wave, acc, f0, f1, sa, sw);
+    }
+    __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
+    __syncthreads();
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    mq_epilogue<OutT>(acc, q0, q1, q2, q3, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
+}
+
+fp4_status launch_mxfp4_gemm_seg(const MxGemmArgs &g, hipStream_t st)
+{
+    // 32-bit byte offsets and descriptor sizes
+    if (g.K % kQK != 0 || g.M * (g.K / 2) >= (int64_t(1) << 31) || g.N * (g.K / 2) >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
+    if (g.c_bf16)
+        hipLaunchKernelGGL(k_mx_gemm_seg<__bf16>, dim3(tiles), dim3(512), 0, st, g);
+    else
+        hipLaunchKernelGGL(k_mx_gemm_seg<float>, dim3(tiles), dim3(512), 0, st, g);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)
 {
     // the staged kernel addresses a matrix with 32-bit byte offsets

@@ -30,6 +30,10 @@ fp4_status launch_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, 
 fp4_status launch_mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                                  int64_t ldx, uint8_t *codes, uint8_t *scales, fp4_mx_rule rule,
                                  int32_t *nonfinite, hipStream_t st);
+// the same quantizer writing the segment-major layout (cols % 128 == 0)
+fp4_status launch_mxfp4_quantize_seg(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                     int64_t ldx, uint8_t *codes_p, uint8_t *scales_p, fp4_mx_rule rule,
+                                     int32_t *nonfinite, hipStream_t st);
 fp4_status launch_mxfp8_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                                  int64_t ldx, uint8_t *codes, uint8_t *scales, fp4_mx_rule rule,
                                  int32_t *nonfinite, hipStream_t st);
@@ -104,6 +108,9 @@ struct MxGemmArgs {
 };
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st);
+// Both operands segment-major (codes [K/128][rows][64], scales [K/128][rows][4]);
+// K % 128 == 0
+fp4_status launch_mxfp4_gemm_seg(const MxGemmArgs &g, hipStream_t st);
 // W4A8: A MXFP8 (E4M3 bytes [M][K], E8M0 [M][K/32]), W MXFP4; K % 128 == 0
 fp4_status launch_mxfp4_gemm_w4a8(const MxGemmArgs &g, hipStream_t st);
 

@@ -250,13 +250,15 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant(const uint8_t *__restrict
 
 // --------------------------------------------------------- MXFP4 quantize --
 
-// Lanes (4i .. 4i+3) hold one 32-block.
-template <typename T>
+// Lanes (4i .. 4i+3) hold one 32-block.  SEG writes the segment-major layout
+// instead of row-major: the 64 code bytes and 4 scale bytes of row r's 128-element
+// segment s at (s rows + r) * 64 and (s rows + r) * 4 (cols % 128 == 0).
+template <typename T, bool SEG = false>
 __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, uint32_t units,
                                                      FastDiv cv, int64_t ldx, int64_t cols,
                                                      int rule, uint8_t *__restrict__ codes,
                                                      uint8_t *__restrict__ scales,
-                                                     int32_t *__restrict__ nonfinite)
+                                                     int32_t *__restrict__ nonfinite, int64_t rows = 0)
 {
     int bad = 0;
     for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
@@ -282,8 +284,14 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, ui
             for (int i = 0; i < 8; ++i) q[i] = __builtin_amdgcn_ldexpf(v[i], -k);  // exact
             w = e2m1x8_code(q);
         }
-        *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
-        if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
+        if (SEG) {
+            const int64_t piece = (int64_t)(c8 >> 4) * rows + r;  // (segment, row)
+            *reinterpret_cast<uint32_t *>(codes + piece * 64 + (c8 & 15u) * 4) = w;
+            if ((c8 & 3u) == 0u) scales[piece * 4 + ((c8 >> 2) & 3u)] = (uint8_t)byte;
+        } else {
+            *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
+            if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
+        }
     }
     if (bad && nonfinite) *nonfinite = 1;
 }
@@ -441,10 +449,26 @@ fp4_status launch_mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int6
     const unsigned g = grid_for(units, 16384);
     if (xt == FP4_BF16)
         hipLaunchKernelGGL(k_mxfp4_quant<uint16_t>, dim3(g), dim3(256), 0, st, (const uint16_t *)x,
-                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
+                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite, rows);
     else
         hipLaunchKernelGGL(k_mxfp4_quant<float>, dim3(g), dim3(256), 0, st, (const float *)x,
-                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite);
+                           units, cv, ldx, cols, (int)rule, codes, scales, nonfinite, rows);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_mxfp4_quantize_seg(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
+                                     int64_t ldx, uint8_t *codes_p, uint8_t *scales_p, fp4_mx_rule rule,
+                                     int32_t *nonfinite, hipStream_t st)
+{
+    const uint32_t units = (uint32_t)(rows * (cols / 8));
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
+    const unsigned g = grid_for(units, 16384);
+    if (xt == FP4_BF16)
+        hipLaunchKernelGGL((k_mxfp4_quant<uint16_t, true>), dim3(g), dim3(256), 0, st, (const uint16_t *)x,
+                           units, cv, ldx, cols, (int)rule, codes_p, scales_p, nonfinite, rows);
+    else
+        hipLaunchKernelGGL((k_mxfp4_quant<float, true>), dim3(g), dim3(256), 0, st, (const float *)x,
+                           units, cv, ldx, cols, (int)rule, codes_p, scales_p, nonfinite, rows);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 

@@ -233,6 +233,27 @@ fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t 
                                    const uint8_t *w_scales_p, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
                                    hipStream_t stream);
 
+/* MXFP4 W4A4 GEMM on segment-major operands (eefocus.com edge-FP4 article, "FP4
+ * as the next core standard": MXFP4, 32-element blocks with an E8M0 scale).  The
+ * same product as mxfp4_gemm_w4a4, bit for bit, with W in the MXFP4 decode layout
+ * (mxfp4_pack_decode) instead of row-major: a 256-row panel's 128-element K
+ * segment is then contiguous, which is how the kernel reads it.  A (bf16
+ * [M][lda]) is quantized with `rule` into `ws` in the same layout (codes
+ * [K/128][M][64] at ws, E8M0 [K/128][M][4] at the next 256-byte boundary).
+ * K % 128 == 0, M * K / 2 and N * K / 2 below 2^31 (FP4_ERR_SHAPE otherwise);
+ * FP4_ERR_WORKSPACE for a null, unaligned or short ws.  C [M][ldc] fp32 or bf16
+ * is written; nothing is allocated. */
+size_t mxfp4_gemm_w4a4_seg_workspace(int64_t M, int64_t K);
+fp4_status mxfp4_gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                               const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                               fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The GEMM half of mxfp4_gemm_w4a4_seg: A and W both MXFP4 in the segment-major
+ * (decode) layout, codes [K/128][rows][64], scales [K/128][rows][4]. */
+fp4_status mxfp4_gemm_prequant_seg(const uint8_t *a_codes_p, const uint8_t *a_scales_p, int64_t M, int64_t K,
+                                   const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                                   fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
 /* ---- W4A8: FP4 weights x FP8 activations (eefocus.com edge-FP4 article: an NPU
  * with native W4A8, weights quantized to FP4 and activations to FP8).  Both
  * operands take the OCP MX form: MXFP4 weights, MXFP8 activations. ---- */

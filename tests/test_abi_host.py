@@ -236,6 +236,39 @@ def test_mxfp4_w4a16_validation(L):
         assert g() == NO_DEVICE and pk() == NO_DEVICE and gd() == NO_DEVICE
 
 
+def test_mxfp4_segment_major_gemm_validation(L):
+    import torch
+
+    assert L.mxfp4_gemm_w4a4_seg_workspace(4096, 5120) == L.mxfp4_gemm_w4a4_workspace(4096, 5120)
+    assert L.mxfp4_gemm_w4a4_seg_workspace(0, 128) == 0
+
+    def g(**kw):
+        a = dict(a=FAKE, M=8, K=256, lda=256, rule=0, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=0, ldc=16,
+                 work=FAKE, work_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a4_seg(*a.values())
+
+    assert g(K=96, lda=96) == SHAPE                  # whole 128-element segments
+    assert g(lda=128) == LAYOUT
+    assert g(rule=3) == DTYPE
+    assert g(wc=None) == NULL
+    assert g(work_bytes=100) == WORKSPACE
+    assert g(work=FAKE + 4) == WORKSPACE             # 16-byte aligned
+    assert g(ldc=8) == LAYOUT
+
+    def p(**kw):
+        a = dict(ac=FAKE, asc=FAKE, M=8, K=256, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=1, ldc=16, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_prequant_seg(*a.values())
+
+    assert p(K=160) == SHAPE
+    assert p(asc=None) == NULL
+    assert p(M=0) == SHAPE
+    assert p(ct=4) == DTYPE
+    if not torch.cuda.is_available():
+        assert g() == NO_DEVICE and p() == NO_DEVICE
+
+
 def test_w4a8_validation(L):
     import torch
 
