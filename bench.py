@@ -362,6 +362,15 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
     t_mg = T.per_launch(lambda i: fp4.mxfp4_gemm_prequant(pam, wmx, out=c), it)
     t_mall = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a4(a, wmx, out=c, workspace=wsm), it)
     c_mx = c.clone()
+    # the same GEMM with W in the decode (segment-major) layout and A quantized into it
+    wmd = fp4.mxfp4_pack_decode(wmx)
+    wss = fp4.mxfp4_gemm_w4a4_seg_workspace(M, K, dev)
+    pas = fp4.mxfp4_seg_packed_a(wss, M, K)
+    fp4.mxfp4_gemm_w4a4_seg(a, wmd, out=c, workspace=wss)
+    t_sg = T.per_launch(lambda i: fp4.mxfp4_gemm_prequant_seg(pas, wmd, out=c), it)
+    t_sall = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a4_seg(a, wmd, out=c, workspace=wss), it)
+    torch.cuda.synchronize()
+    seg_equal = bool(torch.equal(c.view(torch.int16), c_mx.view(torch.int16)))
     wsn = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     t_nall = T.per_launch(lambda i: fp4.gemm_w4a4(a, wnv, a_mode="row", out=c, workspace=wsn), it)
     c_nv = c.clone()
@@ -372,6 +381,10 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
     t_8g = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_prequant(pa8, wmx, out=c), it)
     t_8all = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8(a, wmx, out=c, workspace=ws8), it)
     c_a8 = c.clone()
+    t_8sg = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_prequant_seg(pa8, wmd, out=c), it)
+    t_8sall = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_seg(a, wmd, out=c, workspace=ws8), it)
+    torch.cuda.synchronize()
+    w4a8_seg_equal = bool(torch.equal(c.view(torch.int16), c_a8.view(torch.int16)))
     torch.cuda.synchronize()
     # quantization error against the unquantized bf16 product, on sampled rows
     rows = np.random.default_rng(0).choice(M, 64, replace=False)
@@ -388,13 +401,19 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
         "mxfp4_quant_us": t_mq * 1e6, "mxfp4_gemm_us": t_mg * 1e6,
         "mxfp4_gemm_TFLOP/s": fl / t_mg / 1e12, "mxfp4_gemm_frac_fp4_mfma": fl / t_mg / FP4_PEAK,
         "mxfp4_total_us": t_mall * 1e6, "mxfp4_total_TFLOP/s": fl / t_mall / 1e12,
+        "mxfp4_seg_gemm_us": t_sg * 1e6, "mxfp4_seg_gemm_TFLOP/s": fl / t_sg / 1e12,
+        "mxfp4_seg_gemm_frac_fp4_mfma": fl / t_sg / FP4_PEAK, "mxfp4_seg_total_us": t_sall * 1e6,
+        "mxfp4_seg_equals_row_major": seg_equal,
         "nvfp4_total_us": t_nall * 1e6, "nvfp4_total_TFLOP/s": fl / t_nall / 1e12,
         "nvfp4_frac_bf16_mfma": fl / t_nall / BF16_PEAK,
         "w4a8_quant_us": t_8q * 1e6, "w4a8_gemm_us": t_8g * 1e6,
         "w4a8_gemm_TFLOP/s": fl / t_8g / 1e12, "w4a8_gemm_frac_fp8_mfma": fl / t_8g / FP8_PEAK,
         "w4a8_total_us": t_8all * 1e6, "w4a8_total_TFLOP/s": fl / t_8all / 1e12,
+        "w4a8_seg_gemm_us": t_8sg * 1e6, "w4a8_seg_gemm_TFLOP/s": fl / t_8sg / 1e12,
+        "w4a8_seg_gemm_frac_fp8_mfma": fl / t_8sg / FP8_PEAK, "w4a8_seg_total_us": t_8sall * 1e6,
+        "w4a8_seg_equals_row_major": w4a8_seg_equal,
         "error_vs_bf16_product_64_rows": err}
-    del a, c, c_mx, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8
+    del a, c, c_mx, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8, wmd, wss
 
 
 def moe_components(args, torch, fp4, T, dev):

@@ -75,6 +75,8 @@ def _declare(L):
         "mxfp4_gemm_w4a8_workspace": (sz, [i64, i64]),
         "mxfp4_gemm_w4a8": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
         "mxfp4_gemm_w4a8_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
+        "mxfp4_gemm_w4a8_seg": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
+        "mxfp4_gemm_w4a8_prequant_seg": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
         "nvfp4_grouped_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, i64, p, p, p, i64, p, i32, i64, p]),
         "mxfp4_grouped_gemm_w4a16": (i32, [p, i64, i64, i64, p, p, i64, i64, p, p, i64, p, i32, i64, p]),
         "nvfp4_grouped_gemm_w4a4_workspace": (sz, [i64, i64]),
@@ -544,6 +546,36 @@ def mxfp4_gemm_w4a8_prequant(a: PackedMXFP8, w: PackedMXFP4, dtype=torch.bfloat1
     _check(L.mxfp4_gemm_w4a8_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
                                       _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
                                       _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a8_seg(a: torch.Tensor, w: DecodeMXFP4, rule="ocp", dtype=torch.bfloat16,
+                        out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """W4A8 with the MXFP4 W in the decode (segment-major) layout; the same result as mxfp4_gemm_w4a8."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("mxfp4_gemm_w4a8_seg takes bfloat16 activations")
+    M, K = a.shape
+    if workspace is None:
+        workspace = mxfp4_gemm_w4a8_workspace(M, K, a.device)
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    _check(L.mxfp4_gemm_w4a8_seg(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
+                                 _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                                 _stream()))
+    return out
+
+
+def mxfp4_gemm_w4a8_prequant_seg(a: PackedMXFP8, w: DecodeMXFP4, dtype=torch.bfloat16,
+                                 out: torch.Tensor | None = None) -> torch.Tensor:
+    """The GEMM half of mxfp4_gemm_w4a8_seg on an MXFP8 A."""
+    L = lib()
+    if out is None:
+        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.mxfp4_gemm_w4a8_prequant_seg(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
+                                          _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
+                                          _stream()))
     return out
 
 

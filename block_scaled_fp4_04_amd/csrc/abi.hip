@@ -515,9 +515,12 @@ size_t mxfp4_gemm_w4a8_workspace(int64_t M, int64_t K)
     return align256((size_t)M * (size_t)K) + align256((size_t)M * (size_t)(K / 32));
 }
 
-fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
-                                    const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
-                                    fp4_dtype ct, int64_t ldc, hipStream_t stream)
+namespace {
+
+// the GEMM half of both W4A8 forms (w_seg: W segment-major)
+fp4_status w4a8_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K, const uint8_t *w_codes,
+                     const uint8_t *w_scales, int64_t N, void *c, fp4_dtype ct, int64_t ldc, bool w_seg,
+                     hipStream_t stream)
 {
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
     FP4_TRY(check_packed(a_codes, a_scales));
@@ -534,12 +537,13 @@ fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_sca
     g.c = c;
     g.c_bf16 = ct == FP4_BF16;
     g.ldc = ldc;
+    g.w_seg = w_seg ? 1 : 0;
     return launch_mxfp4_gemm_w4a8(g, stream);
 }
 
-fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
-                           const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
-                           fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+fp4_status w4a8_full(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule, const uint8_t *w_codes,
+                     const uint8_t *w_scales, int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws,
+                     size_t ws_bytes, bool w_seg, hipStream_t stream)
 {
     if (rule != FP4_MX_OCP_FLOOR && rule != FP4_MX_CEIL) return FP4_ERR_DTYPE;
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
@@ -551,7 +555,37 @@ fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4
     uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
     uint8_t *as = ac + align256((size_t)M * (size_t)K);
     FP4_TRY(launch_mxfp8_quantize(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
-    return mxfp4_gemm_w4a8_prequant(ac, as, M, K, w_codes, w_scales, N, c, ct, ldc, stream);
+    return w4a8_gemm(ac, as, M, K, w_codes, w_scales, N, c, ct, ldc, w_seg, stream);
+}
+
+}  // namespace
+
+fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                    const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                                    fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    return w4a8_gemm(a_codes, a_scales, M, K, w_codes, w_scales, N, c, ct, ldc, false, stream);
+}
+
+fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                           const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
+                           fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return w4a8_full(a, M, K, lda, rule, w_codes, w_scales, N, c, ct, ldc, ws, ws_bytes, false, stream);
+}
+
+fp4_status mxfp4_gemm_w4a8_prequant_seg(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                        const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                                        fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    return w4a8_gemm(a_codes, a_scales, M, K, w_codes_p, w_scales_p, N, c, ct, ldc, true, stream);
+}
+
+fp4_status mxfp4_gemm_w4a8_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                               const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                               fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return w4a8_full(a, M, K, lda, rule, w_codes_p, w_scales_p, N, c, ct, ldc, ws, ws_bytes, true, stream);
 }
 
 // ------------------------------------------------------- grouped (MoE) --

@@ -618,10 +618,14 @@ static_assert(64 * kA8EpiPitch16 <= kA8Stage && 32 * kA8EpiPitch32 <= kA8Stage, 
 // Per-lane source offsets of a wave's copies: A code slot q = 256 wave + 64 i +
 // lane (row q / 8), W code slot q = 128 wave + 64 i + lane (row q / 4), and one
 // scale dword: waves 0..3 copy A's rows 64 wave + lane, waves 4..7 W's rows
-// 64 (wave - 4) + lane, into bytes kA8SA + 256 wave + 4 lane of the stage.
+// 64 (wave - 4) + lane, into bytes kA8SA + 256 wave + 4 lane of the stage.  Stage
+// t's bytes start t * w_step past a W offset and t * s_step past this wave's
+// scale offset: 64 and 4 for row-major W, N * 64 and N * 4 for segment-major W
+// (whose 128-element segments are contiguous panels; A stays row-major).
 struct A8Dma {
     __amdgpu_buffer_rsrc_t ra, rw, rs;
     uint32_t a[4], w[2], s;
+    uint32_t w_step, s_step;
 };
 
 __device__ __forceinline__ void a8_dma(uint8_t *st, const A8Dma &d, int k0, int wave)
@@ -630,12 +634,13 @@ __device__ __forceinline__ void a8_dma(uint8_t *st, const A8Dma &d, int k0, int 
     for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.ra, (mx_lds_void *)(st + kA8A + 16 * (256 * wave + 64 * i)), 16,
                                                  (int)d.a[i], k0, 0, 0);
+    const int t = k0 / kA8K;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rw, (mx_lds_void *)(st + kA8W + 16 * (128 * wave + 64 * i)), 16,
-                                                 (int)d.w[i], k0 / 2, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (mx_lds_void *)(st + kA8SA + 256 * wave), 4, (int)d.s, k0 / 32, 0,
-                                             0);
+                                                 (int)d.w[i], t * (int)d.w_step, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rs, (mx_lds_void *)(st + kA8SA + 256 * wave), 4, (int)d.s,
+                                             t * (int)d.s_step, 0, 0);
 }
 
 // per-lane LDS offsets: A row wm 64 + l, W row wn 128 + l (l = lane % 32, half
@@ -790,13 +795,15 @@ __global__ __launch_bounds__(512) void k_mx_gemm_w4a8(MxGemmArgs g)
     for (int i = 0; i < 2; ++i) {
         const int q = 128 * wave + 64 * i + lane;
         const int r = q >> 2, c = (q & 3) ^ ((r >> 2) & 3);
-        d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * c : kA8Out;
+        d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(g.w_seg ? 64 : K / 2) + 16 * c : kA8Out;
     }
     {
         const int r = 64 * (wave & 3) + lane;
         if (wave < 4) d.s = m0 + r < M ? (uint32_t)(m0 + r) * (uint32_t)(K / 32) : kA8Out;
-        else d.s = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 32) : kA8Out;
+        else d.s = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(g.w_seg ? 4 : K / 32) : kA8Out;
     }
+    d.w_step = g.w_seg ? (uint32_t)N * 64u : 64u;
+    d.s_step = g.w_seg && wave >= 4 ? (uint32_t)N * 4u : 4u;
     dz = d;
     dz.ra = mx2_rsrc(g.a_codes, 0);
     dz.rw = mx2_rsrc(g.w_codes, 0);

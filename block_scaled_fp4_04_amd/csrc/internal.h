@@ -105,6 +105,7 @@ struct MxGemmArgs {
     void *c;
     int c_bf16;
     int64_t ldc;
+    int w_seg;  // W4A8: W in the segment-major layout ([K/128][N][64], [K/128][N][4])
 };
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st);

@@ -287,6 +287,18 @@ fp4_status mxfp4_gemm_w4a8_prequant(const uint8_t *a_codes, const uint8_t *a_sca
                                     const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
                                     fp4_dtype ct, int64_t ldc, hipStream_t stream);
 
+/* W4A8 with W in the MXFP4 decode layout (mxfp4_pack_decode: codes [K/128][N][64],
+ * scales [K/128][N][4]); A as in mxfp4_gemm_w4a8.  The same result as
+ * mxfp4_gemm_w4a8 / _prequant on the row-major W, bit for bit; the weight's
+ * 128-element segments are then contiguous panels, which the kernel copies whole.
+ * Arguments, workspace and errors as those two. */
+fp4_status mxfp4_gemm_w4a8_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
+                               const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                               fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);
+fp4_status mxfp4_gemm_w4a8_prequant_seg(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M, int64_t K,
+                                        const uint8_t *w_codes_p, const uint8_t *w_scales_p, int64_t N, void *c,
+                                        fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
 /* ---------------------------------------------------- grouped (MoE) ------ */
 
 /* Grouped GEMMs for mixture-of-experts layers (eefocus.com edge-FP4 article, "FP4

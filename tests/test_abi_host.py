@@ -269,6 +269,32 @@ def test_mxfp4_segment_major_gemm_validation(L):
         assert g() == NO_DEVICE and p() == NO_DEVICE
 
 
+def test_w4a8_segment_major_validation(L):
+    import torch
+
+    def g(**kw):
+        a = dict(a=FAKE, M=8, K=256, lda=256, rule=0, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=0, ldc=16,
+                 work=FAKE, work_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a8_seg(*a.values())
+
+    assert g(K=192, lda=192) == SHAPE
+    assert g(rule=7) == DTYPE
+    assert g(work_bytes=16) == WORKSPACE
+    assert g(wc=None) == NULL
+
+    def p(**kw):
+        a = dict(ac=FAKE, asc=FAKE, M=8, K=256, wc=FAKE, ws=FAKE, N=16, c=FAKE, ct=1, ldc=16, stream=None)
+        a.update(kw)
+        return L.mxfp4_gemm_w4a8_prequant_seg(*a.values())
+
+    assert p(K=64) == SHAPE
+    assert p(ws=None) == NULL
+    assert p(ldc=15) == LAYOUT
+    if not torch.cuda.is_available():
+        assert g() == NO_DEVICE and p() == NO_DEVICE
+
+
 def test_w4a8_validation(L):
     import torch
 

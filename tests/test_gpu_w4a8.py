@@ -83,14 +83,19 @@ def test_w4a8_gemm(M, N, K, rule):
     a, wc, wsc = _case(M, N, K, seed=5 * M + 3 * N + K)
     r = oracle.MX_OCP_FLOOR if rule == "ocp" else oracle.MX_CEIL
     ws = fp4().mxfp4_gemm_w4a8_workspace(M, K, dev())
-    c = fp4().mxfp4_gemm_w4a8(bf16bits_to_dev(a), _packed_mx(wc, wsc), rule=rule, dtype=torch.float32,
-                              workspace=ws)
+    wp = _packed_mx(wc, wsc)
+    c = fp4().mxfp4_gemm_w4a8(bf16bits_to_dev(a), wp, rule=rule, dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
     pa = fp4().mxfp8_packed_a(ws, M, K)
     ac, asc = oracle.mxfp8_quantize(a, r)
     assert np.array_equal(pa.codes.cpu().numpy(), ac) and np.array_equal(pa.scales.cpu().numpy(), asc)
     ref, tol = oracle.mxfp4_gemm_w4a8_ref(a, wc, wsc, r)
     assert_gemm_close(c, ref, tol, f"w4a8 {M}x{N}x{K}")
+    # W in the decode (segment-major) layout: the same kernel arithmetic, bit for bit
+    cs = fp4().mxfp4_gemm_w4a8_seg(bf16bits_to_dev(a), fp4().mxfp4_pack_decode(wp), rule=rule,
+                                   dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(cs, c), "segment-major W differs from row-major W"
 
 
 @pytest.mark.parametrize("M,N,K", [(40, 300, 256), (300, 260, 1024)])
@@ -100,6 +105,24 @@ def test_w4a8_bf16_output(M, N, K):
     torch.cuda.synchronize()
     ref, tol = oracle.mxfp4_gemm_w4a8_ref(a, wc, wsc)
     assert_gemm_close(c, ref, tol, f"w4a8 bf16 {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("M,N,K", [(33, 300, 384), (300, 260, 1024)])
+def test_w4a8_prequant_seg_guard_band(M, N, K):
+    log(f"mxfp4_gemm_w4a8_prequant_seg M={M} N={N} K={K}")
+    a, wc, wsc = _case(M, N, K, seed=2 * M + N)
+    ac, asc = oracle.mxfp8_quantize(a)
+    pa = fp4().PackedMXFP8(torch.from_numpy(ac).to(dev()), torch.from_numpy(asc).to(dev()), M, K)
+    wp = _packed_mx(wc, wsc)
+    big = torch.full((M + 3, N + 40), -5.0, dtype=torch.bfloat16, device=dev())
+    view = big[:M, :N]
+    fp4().mxfp4_gemm_w4a8_prequant_seg(pa, fp4().mxfp4_pack_decode(wp), out=view)
+    rm = fp4().mxfp4_gemm_w4a8_prequant(pa, wp, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.all(big[:M, N:] == -5.0) and torch.all(big[M:, :] == -5.0)
+    assert torch.equal(view.view(torch.int16), rm.view(torch.int16))
+    ref, tol = oracle.mxfp4_gemm_w4a8_ref(a, wc, wsc)
+    assert_gemm_close(view, ref, tol, f"w4a8 prequant seg {M}x{N}x{K}")
 
 
 def _grid_vals(rng, shape):
@@ -133,8 +156,12 @@ def test_w4a8_full_size_sampled():
     w = WORKLOADS["decode_gemv_k5120_n17408"].weights()
     wc, wsc = oracle.mxfp4_quantize(to_bf16_bits(w))
     a = wl.activations_bf16(8192)
-    c = fp4().mxfp4_gemm_w4a8(bf16bits_to_dev(a), _packed_mx(wc, wsc), dtype=torch.bfloat16)
+    wp = _packed_mx(wc, wsc)
+    ad = bf16bits_to_dev(a)
+    c = fp4().mxfp4_gemm_w4a8(ad, wp, dtype=torch.bfloat16)
+    cs = fp4().mxfp4_gemm_w4a8_seg(ad, fp4().mxfp4_pack_decode(wp), dtype=torch.bfloat16)
     torch.cuda.synchronize()
+    assert torch.equal(cs.view(torch.int16), c.view(torch.int16))
     rng = np.random.default_rng(4)
     rows = np.unique(np.concatenate([[0, 8191], rng.choice(8192, 48, replace=False)]))
     ref, tol = oracle.mxfp4_gemm_w4a8_ref(a, wc, wsc, rows=rows)
