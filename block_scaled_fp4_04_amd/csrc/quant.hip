@@ -252,9 +252,7 @@ __global__ __launch_bounds__(256) void k_nvfp4_dequant(const uint8_t *__restrict
 
 // Lanes (4i .. 4i+3) hold one 32-block.  SEG writes the segment-major layout
 // instead of row-major: the 64 code bytes and 4 scale bytes of row r's 128-element
-// segment s at (s rows + r) * 64 and (s rows + r) * 4 (cols % 128 == 0); its units
-// run segment-major too (16 per row piece, then the next row), so a wave writes
-// 256 contiguous code bytes.
+// segment s at (s rows + r) * 64 and (s rows + r) * 4 (cols % 128 == 0).
 template <typename T, bool SEG = false>
 __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, uint32_t units,
                                                      FastDiv cv, int64_t ldx, int64_t cols,
@@ -264,16 +262,8 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, ui
 {
     int bad = 0;
     for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
-        uint32_t r, c8;
-        if (SEG) {
-            const uint32_t piece = u >> 4;            // (segment, row) = s rows + r
-            const uint32_t sg = fdiv(piece, cv);      // cv divides by rows here
-            r = piece - sg * cv.d;
-            c8 = 16 * sg + (u & 15u);
-        } else {
-            r = fdiv(u, cv);
-            c8 = u - r * cv.d;
-        }
+        const uint32_t r = fdiv(u, cv);
+        const uint32_t c8 = u - r * cv.d;
         float v[8];
         Vec8<T>::load(x + (int64_t)r * ldx + (int64_t)c8 * 8, v);
         float bm = amax8(v, bad);
@@ -471,7 +461,7 @@ fp4_status launch_mxfp4_quantize_seg(const void *x, fp4_dtype xt, int64_t rows, 
                                      int32_t *nonfinite, hipStream_t st)
 {
     const uint32_t units = (uint32_t)(rows * (cols / 8));
-    const FastDiv cv = make_fastdiv((uint32_t)rows);  // units are (segment, row, 8-group)
+    const FastDiv cv = make_fastdiv((uint32_t)(cols / 8));
     const unsigned g = grid_for(units, 16384);
     if (xt == FP4_BF16)
         hipLaunchKernelGGL((k_mxfp4_quant<uint16_t, true>), dim3(g), dim3(256), 0, st, (const uint16_t *)x,
