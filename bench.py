@@ -297,8 +297,14 @@ def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     fl = 2.0 * M * N * K
     t = T.per_launch(lambda i: fp4.gemm_w4a16(a, wq, out=c), it)
+    # the same GEMM on the weight in the decode layout (one packed weight for decode and prefill)
+    wd = fp4.nvfp4_pack_decode(wq)
+    t_d = T.per_launch(lambda i: fp4.gemm_w4a16_decode(a, wd, out=c), it)
     out["prefill_w4a16_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
+                                  "decode_layout_us": t_d * 1e6, "decode_layout_TFLOP/s": fl / t_d / 1e12,
+                                  "decode_layout_frac_bf16_mfma": fl / t_d / BF16_PEAK,
                                   "flop": fl, "mfma": "bf16 32x32x16 (NVFP4 widened exactly to bf16)"}
+    del wd
     # activation quantization alone (per row) and the fused W4A4 call
     wsa = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     pa = fp4.w4a4_packed_a(wsa, M, K, "row")
@@ -333,14 +339,17 @@ def mx16_components(torch, fp4, T, dev, w32, wl3, it, out):
         mxd[str(M)] = {"us": round(t * 1e6, 4), "GB/s": round(b / t / 1e9, 1), "frac_hbm": round(b / t / HBM_PEAK, 4),
                        "bytes": b}
     out["mxfp4_w4a16_decode_k5120_n17408"] = mxd
+    md0 = mcopies[0]
     del mcopies
     a = torch.from_numpy(wl3.activations_bf16(4096).view(np.int16)).view(torch.bfloat16).to(dev)
     c = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
     fl = 2.0 * 4096 * N * K
     t = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a16(a, wmx, out=c), it)
+    t_d = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a16_decode(a, md0, out=c), it)
     out["mxfp4_w4a16_prefill_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
+                                        "decode_layout_us": t_d * 1e6, "decode_layout_TFLOP/s": fl / t_d / 1e12,
                                         "flop": fl, "mfma": "bf16 32x32x16 (MXFP4 widened exactly to bf16)"}
-    del a, c, wmx
+    del a, c, wmx, md0
 
 
 def m8192_components(torch, fp4, T, dev, w32, it, out):

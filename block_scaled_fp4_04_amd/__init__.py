@@ -274,7 +274,8 @@ def nvfp4_pack_decode(w: PackedNVFP4, out: DecodeNVFP4 | None = None) -> DecodeN
 
 def gemm_w4a16_decode(a: torch.Tensor, w: DecodeNVFP4, dtype=torch.bfloat16,
                       out: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode GEMV C = A . W^T for bf16 A [M <= 16, K] and W in the decode layout."""
+    """C = A . W^T for bf16 A [M, K] and W in the decode layout: the decode GEMV for M <= 16,
+    the prefill GEMM on the same layout for larger M."""
     L = lib()
     _need_cuda(a)
     if a.dtype != torch.bfloat16:
@@ -473,7 +474,8 @@ def mxfp4_gemm_prequant_seg(a: DecodeMXFP4, w: DecodeMXFP4, dtype=torch.bfloat16
 
 def mxfp4_gemm_w4a16_decode(a: torch.Tensor, w: DecodeMXFP4, dtype=torch.bfloat16,
                             out: torch.Tensor | None = None) -> torch.Tensor:
-    """Decode GEMV C = A . W^T for bf16 A [M <= 16, K] and an MXFP4 W in the decode layout."""
+    """C = A . W^T for bf16 A [M, K] and an MXFP4 W in the decode layout (GEMV for M <= 16,
+    the prefill GEMM on the same layout for larger M)."""
     L = lib()
     _need_cuda(a)
     if a.dtype != torch.bfloat16:

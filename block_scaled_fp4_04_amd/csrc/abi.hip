@@ -180,16 +180,44 @@ fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
     return launch_pack_decode(codes, scales, N, K, codes_p, scales_p, false, stream);
 }
 
+namespace {
+
+// M > 16 on a decode-layout weight: the prefill ring kernel reading that layout
+fp4_status w4a16_seg_prefill(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
+                             const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
+                             int64_t ldc, bool mx, hipStream_t stream)
+{
+    NvGemmArgs g{};
+    g.a = reinterpret_cast<const uint16_t *>(a);
+    g.lda = lda;
+    g.w_codes = w_codes_p;
+    g.w_scales = w_scales_p;
+    g.w_tscale = w_tscale;
+    g.M = M;
+    g.N = N;
+    g.K = K;
+    g.c = c;
+    g.c_bf16 = ct == FP4_BF16;
+    g.ldc = ldc;
+    g.w_seg = 1;
+    g.w_rows = N;
+    g.w_row0 = 0;
+    return launch_gemm_w4a16_seg(g, mx, stream);
+}
+
+}  // namespace
+
 fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
                              const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
                              fp4_dtype ct, int64_t ldc, hipStream_t stream)
 {
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
-    if (M > 16 || K > 8192) return FP4_ERR_SHAPE;
+    if (M <= 16 && K > 8192) return FP4_ERR_SHAPE;
     FP4_TRY(check_matrix(a, M, K, lda, 2));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
     if (!w_tscale) return FP4_ERR_NULL;
     FP4_TRY(check_device());
+    if (M > 16) return w4a16_seg_prefill(a, M, K, lda, w_codes_p, w_scales_p, w_tscale, N, c, ct, ldc, false, stream);
     GemvArgs g{};
     g.a = reinterpret_cast<const uint16_t *>(a);
     g.lda = lda;
@@ -220,10 +248,11 @@ fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t 
                                    hipStream_t stream)
 {
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
-    if (M > 16 || K > 8192) return FP4_ERR_SHAPE;
+    if (M <= 16 && K > 8192) return FP4_ERR_SHAPE;
     FP4_TRY(check_matrix(a, M, K, lda, 2));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
     FP4_TRY(check_device());
+    if (M > 16) return w4a16_seg_prefill(a, M, K, lda, w_codes_p, w_scales_p, nullptr, N, c, ct, ldc, true, stream);
     GemvArgs g{};
     g.a = reinterpret_cast<const uint16_t *>(a);
     g.lda = lda;

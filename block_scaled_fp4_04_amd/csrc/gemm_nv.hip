@@ -762,6 +762,9 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 //    A tiles (W4A16) or packed codes + E4M3 bytes (W4A4 A, and W always).  LDS
 //    holds W at 4.5 bits a value, not widened, so a 256 x 256 stage is 41 KiB
 //    (W4A16) or 18 KiB (W4A4) and three stages are in flight.
+//  - W may also come in the decode layout (segment-major, see nvfp4_pack_decode):
+//    a stage's W panel is then one half of each row's 64-byte segment piece, 256
+//    rows 64 bytes apart, instead of 32-byte pieces of 256 separate rows.
 //  - Each wave widens the W (and W4A4 A) fragments it multiplies straight from
 //    LDS into registers (exact E2M1 x E4M3 in bf16), between MFMAs.
 //  - The K order inside a 64-element stage is permuted the same way for both
@@ -814,6 +817,11 @@ struct NvTile {
 struct NvRingDma {
     __amdgpu_buffer_rsrc_t ra, ras, rw, rws;
     uint32_t a[8], as, w[2], ws;
+    // W in the decode layout: a 128-element segment's codes and scale bytes of all
+    // weight rows are seg_w and seg_s bytes; stage k0 is half (k0 / 64) % 2 of
+    // segment k0 / 128
+    int seg;
+    uint32_t seg_w, seg_s;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t nv_rsrc(const void *base, int64_t bytes)
@@ -850,11 +858,13 @@ __device__ __forceinline__ void nv_ring_dma(uint8_t *st, const NvRingDma &d, int
 #pragma unroll
     for (int i = 0; i < S::nW; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            d.rw, (nv_lds_void *)(st + S::kW + 16 * (64 * S::nW * wave + 64 * i)), 16, (int)d.w[i], k0 / 2, 0, 0);
+            d.rw, (nv_lds_void *)(st + S::kW + 16 * (64 * S::nW * wave + 64 * i)), 16, (int)d.w[i],
+            d.seg ? (int)((k0 >> 7) * d.seg_w + ((k0 >> 6) & 1) * 32) : k0 / 2, 0, 0);
     // NVFP4: the row's 4 E4M3 bytes of the stage.  MXFP4: the aligned dword holding
     // the row's 2 E8M0 bytes of the stage (the two bytes of stage pair t / 2;
     // K % 128 == 0 keeps it inside the row).
-    const int ks_off = F == kFmtMx16 ? ((k0 / kRK) & ~1) * 2 : k0 / 16;
+    const int ks_off = d.seg ? (int)((k0 >> 7) * d.seg_s + (F == kFmtMx16 ? 0 : ((k0 >> 6) & 1) * 4))
+                             : F == kFmtMx16 ? ((k0 / kRK) & ~1) * 2 : k0 / 16;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(d.rws, (nv_lds_void *)(st + S::kWS + 256 * (wave % (TN / 64))), 4,
                                              (int)d.ws, ks_off, 0, 0);
 }
@@ -1230,8 +1240,12 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
     };
 
     NvRingDma d, dz;
-    d.rw = nv_rsrc(g.w_codes, (int64_t)N * (K / 2));
-    d.rws = nv_rsrc(g.w_scales, (int64_t)N * (K / kWsRow));
+    const int64_t w_rows = g.w_seg ? g.w_rows : N;  // rows the W descriptors cover
+    d.rw = nv_rsrc(g.w_codes, w_rows * (K / 2));
+    d.rws = nv_rsrc(g.w_scales, w_rows * (K / kWsRow));
+    d.seg = g.w_seg;
+    d.seg_w = (uint32_t)w_rows * 64u;
+    d.seg_s = (uint32_t)w_rows * (F == kFmtMx16 ? 4u : 8u);
     if constexpr (A_FP4) {
         d.ra = nv_rsrc(g.a_codes, (int64_t)a_rows * (K / 2));
         d.ras = nv_rsrc(g.a_scales, (int64_t)a_rows * (K / 16));
@@ -1261,10 +1275,13 @@ __global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
     for (int i = 0; i < S::nW; ++i) {
         const int q = 64 * S::nW * wave + 64 * i + lane;
         const int r = q >> 1, h = (q & 1) ^ ((r >> 3) & 1);
-        d.w[i] = n0 + r < N ? (uint32_t)(n0 + r) * (uint32_t)(K / 2) + 16 * h : kNvOut;
+        const uint32_t wr = g.w_seg ? (uint32_t)(g.w_row0 + n0 + r) * 64u : (uint32_t)(n0 + r) * (uint32_t)(K / 2);
+        d.w[i] = n0 + r < N ? wr + 16 * h : kNvOut;
     }
     const int qw = (64 * wave + lane) % TN;
-    d.ws = n0 + qw < N ? (uint32_t)(n0 + qw) * (uint32_t)(K / kWsRow) : kNvOut;
+    const uint32_t wsr = g.w_seg ? (uint32_t)(g.w_row0 + n0 + qw) * (F == kFmtMx16 ? 4u : 8u)
+                                 : (uint32_t)(n0 + qw) * (uint32_t)(K / kWsRow);
+    d.ws = n0 + qw < N ? wsr : kNvOut;
     dz = d;
     dz.ra = nv_rsrc(g.a_codes ? (const void *)g.a_codes : (const void *)g.a, 0);
     dz.ras = dz.ra;
@@ -1349,8 +1366,12 @@ static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
             launch_ring<F, L, 256, 256>(big, st);
             NvGemmArgs rest = g;
             rest.N = g.N - n_split;
-            rest.w_codes = g.w_codes + n_split * (g.K / 2);
-            rest.w_scales = g.w_scales + n_split * (g.K / (F == kFmtMx16 ? 32 : 16));
+            if (g.w_seg) {
+                rest.w_row0 = g.w_row0 + n_split;  // the decode layout interleaves rows per segment
+            } else {
+                rest.w_codes = g.w_codes + n_split * (g.K / 2);
+                rest.w_scales = g.w_scales + n_split * (g.K / (F == kFmtMx16 ? 32 : 16));
+            }
             rest.c = reinterpret_cast<uint8_t *>(g.c) + n_split * (g.c_bf16 ? 2 : 4);
             launch_ring<F, 0, 128, 128>(rest, st);
             return;
@@ -1394,6 +1415,16 @@ fp4_status launch_grouped_gemm(const NvGemmArgs &g, int fmt, hipStream_t st)
         big ? launch_ring_grouped<kFmtMx16, kNvL16, 256>(g, st) : launch_ring_grouped<kFmtMx16, kNvL16, 128>(g, st);
         break;
     }
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_gemm_w4a16_seg(const NvGemmArgs &g, bool mx, hipStream_t st)
+{
+    // the ring kernel addresses operands with 32-bit byte offsets
+    if (g.K % 128 != 0 || g.M * g.lda * 2 >= (int64_t(1) << 31) || g.w_rows * (g.K / 2) >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    if (mx) launch_ring_split<kFmtMx16, kNvL16>(g, st);
+    else launch_ring_split<kFmtNv16, kNvL16>(g, st);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 

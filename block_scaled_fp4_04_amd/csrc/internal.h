@@ -65,9 +65,15 @@ struct NvGemmArgs {
     const int32_t *group_offs;
     const int32_t *row_index;
     int64_t a_rows;
+    // W in the decode (segment-major) layout of w_rows rows, this launch's weight
+    // rows starting at row w_row0 (ring kernel, not grouped)
+    int w_seg;
+    int64_t w_rows, w_row0;
 };
 
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st);
+// W4A16 prefill on a weight in the decode layout (NVFP4, or MXFP4 when mx)
+fp4_status launch_gemm_w4a16_seg(const NvGemmArgs &g, bool mx, hipStream_t st);
 // grouped GEMM on the ring kernel: F = 0 NVFP4 W4A16, 1 NVFP4 W4A4, 2 MXFP4 W4A16
 fp4_status launch_grouped_gemm(const NvGemmArgs &g, int fmt, hipStream_t st);
 

@@ -142,10 +142,13 @@ fp4_status gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, const ui
 fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
                              uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream);
 
-/* W4A16 decode GEMV (aixq.cc article, "Core difference: W4A4 vs W4A16") on a
- * weight in the decode layout: C = A . W^T for 1 <= M <= 16, K % 128 == 0,
- * K <= 8192.  Same arithmetic and tolerance as gemm_w4a16 (each weight widened
- * exactly to E2M1 * E4M3 in bfloat16, fp32 accumulation, times w_tscale). */
+/* W4A16 (aixq.cc article, "Core difference: W4A4 vs W4A16") on a weight in the
+ * decode layout: C = A . W^T, K % 128 == 0.  1 <= M <= 16 (K <= 8192) runs the
+ * decode GEMV; larger M the prefill GEMM reading the same layout (the result
+ * gemm_w4a16 gives on the row-major weight, bit for bit), so one packed weight
+ * serves both.  Same arithmetic and tolerance as gemm_w4a16 (each weight widened
+ * exactly to E2M1 * E4M3 in bfloat16, fp32 accumulation, times w_tscale).
+ * FP4_ERR_SHAPE for M * lda or N * K / 2 bytes of 2 GiB or more when M > 16. */
 fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
                              const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
                              fp4_dtype ct, int64_t ldc, hipStream_t stream);
@@ -226,9 +229,10 @@ fp4_status mxfp4_gemm_w4a16(const void *a, int64_t M, int64_t K, int64_t lda, co
 fp4_status mxfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
                              uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream);
 
-/* MXFP4 W4A16 decode GEMV on a weight in the MXFP4 decode layout: C = A . W^T for
- * 1 <= M <= 16, K % 128 == 0, K <= 8192.  Arithmetic and tolerance as
- * mxfp4_gemm_w4a16. */
+/* MXFP4 W4A16 on a weight in the MXFP4 decode layout: C = A . W^T, K % 128 == 0;
+ * the decode GEMV for 1 <= M <= 16 (K <= 8192), the prefill GEMM on the same
+ * layout for larger M (mxfp4_gemm_w4a16's result, bit for bit).  Arithmetic and
+ * tolerance as mxfp4_gemm_w4a16. */
 fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
                                    const uint8_t *w_scales_p, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
                                    hipStream_t stream);

@@ -168,14 +168,15 @@ def test_decode_layout_validation(L):
 
     assert gd(a=None) == NULL
     assert gd(wt=None) == NULL
-    assert gd(M=17) == SHAPE           # decode takes at most 16 rows
     assert gd(K=192, lda=192) == SHAPE
-    assert gd(K=8320, lda=8320) == SHAPE
+    assert gd(K=8320, lda=8320) == SHAPE   # the GEMV (M <= 16) takes K <= 8192
+    assert gd(M=17, K=192, lda=192) == SHAPE
     assert gd(lda=128) == LAYOUT
     assert gd(ws=FAKE + 4) == LAYOUT
     assert gd(ct=9) == DTYPE
     if not torch.cuda.is_available():
-        assert gd() == NO_DEVICE
+        # M > 16 is the prefill GEMM on the same layout, with no K <= 8192 limit
+        assert gd() == NO_DEVICE and gd(M=17) == NO_DEVICE and gd(M=4096, K=8320, lda=8320) == NO_DEVICE
 
 
 def test_mxfp4_validation(L):
@@ -229,11 +230,12 @@ def test_mxfp4_w4a16_validation(L):
         a.update(kw)
         return L.mxfp4_gemm_w4a16_decode(*a.values())
 
-    assert gd(M=17) == SHAPE
     assert gd(K=8320, lda=8320) == SHAPE
+    assert gd(M=40, K=96, lda=96) == SHAPE
     assert gd(c=None) == NULL
     if not torch.cuda.is_available():
         assert g() == NO_DEVICE and pk() == NO_DEVICE and gd() == NO_DEVICE
+        assert gd(M=17) == NO_DEVICE and gd(M=300, K=8320, lda=8320) == NO_DEVICE
 
 
 def test_mxfp4_segment_major_gemm_validation(L):

@@ -107,7 +107,53 @@ def test_decode_exact_when_operands_are_grid_values(M, N, K):
     assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
 
 
+# M > 16 on the decode layout: the prefill GEMM reading it, ragged tiles, K of one
+# to forty segments, and a grid whose last round of columns runs as a second
+# launch of 128 x 128 tiles (500 x 33000: its weight rows start at row 32768)
+PREFILL = [(17, 260, 1024), (40, 70, 128), (300, 520, 5120), (257, 513, 1280), (513, 260, 640),
+           (500, 33000, 128)]
+
+
+@pytest.mark.parametrize("M,N,K", PREFILL)
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_decode_layout_prefill(M, N, K, out):
+    log(f"gemm_w4a16_decode (prefill, M > 16) M={M} N={N} K={K} out={out}")
+    w = weights(N, K, 0.02, 0.001, 20.0, seed=5 * M + N + K)
+    a = to_bf16_bits(activations_f32(M, K, 0.005, 30.0, seed=M + 3 * N + K))
+    oc, os_, ot = oracle.nvfp4_quantize(w)
+    wp = _packed_nv(oc, os_, ot)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    ad = bf16bits_to_dev(a)
+    c = fp4().gemm_w4a16_decode(ad, fp4().nvfp4_pack_decode(wp), dtype=dt)
+    c_rm = fp4().gemm_w4a16(ad, wp, dtype=dt)
+    torch.cuda.synchronize()
+    ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot)
+    assert_gemm_close(c, ref, tol, f"decode layout prefill {M}x{N}x{K}")
+    bits = torch.int16 if out == "bf16" else torch.int32
+    assert torch.equal(c.view(bits), c_rm.view(bits)), "decode-layout and row-major prefill differ"
+
+
 _cache = {}
+
+
+def test_decode_layout_prefill_full_size():
+    wl = WORKLOADS["prefill_w4a16_m4096"]
+    M = 4096
+    log(f"gemm_w4a16_decode prefill full size M={M} N={wl.N} K={wl.K} (all of C vs row-major, sampled rows vs oracle)")
+    if "nv" not in _cache:
+        _cache["nv"] = oracle.nvfp4_quantize(WORKLOADS["decode_gemv_k5120_n17408"].weights())
+    oc, os_, ot = _cache["nv"]
+    a = wl.activations_bf16(M)
+    wp = _packed_nv(oc, os_, ot)
+    ad = bf16bits_to_dev(a)
+    c = fp4().gemm_w4a16_decode(ad, fp4().nvfp4_pack_decode(wp), dtype=torch.bfloat16)
+    c_rm = fp4().gemm_w4a16(ad, wp, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(c.view(torch.int16), c_rm.view(torch.int16))
+    rng = np.random.default_rng(9)
+    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 48, replace=False)]))
+    ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot, rows=rows)
+    assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, "decode layout prefill sampled")
 
 
 @pytest.mark.parametrize("M", [1, 4, 16])

@@ -137,6 +137,26 @@ def test_mxfp4_decode_exact_with_grid_operands(M, N, K):
     assert np.array_equal(c.cpu().numpy().astype(np.float64), ref)
 
 
+# M > 16 on the MXFP4 decode layout: the prefill GEMM reading it (a second launch
+# of 128 x 128 tiles for the last columns of 500 x 33000)
+@pytest.mark.parametrize("M,N,K", [(17, 260, 1024), (40, 70, 128), (300, 520, 5120), (513, 260, 640),
+                                   (500, 33000, 128)])
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_mxfp4_decode_layout_prefill(M, N, K, out):
+    log(f"mxfp4_gemm_w4a16_decode (prefill, M > 16) M={M} N={N} K={K} out={out}")
+    a, wc, wsc = _case(M, N, K, seed=13 * M + N + K)
+    wp = _packed_mx(wc, wsc)
+    dt = torch.bfloat16 if out == "bf16" else torch.float32
+    ad = bf16bits_to_dev(a)
+    c = fp4().mxfp4_gemm_w4a16_decode(ad, fp4().mxfp4_pack_decode(wp), dtype=dt)
+    c_rm = fp4().mxfp4_gemm_w4a16(ad, wp, dtype=dt)
+    torch.cuda.synchronize()
+    ref, tol = oracle.mxfp4_gemm_w4a16_ref(a, wc, wsc)
+    assert_gemm_close(c, ref, tol, f"mxfp4 decode layout prefill {M}x{N}x{K}")
+    bits = torch.int16 if out == "bf16" else torch.int32
+    assert torch.equal(c.view(bits), c_rm.view(bits)), "decode-layout and row-major prefill differ"
+
+
 _cache = {}
 
 
