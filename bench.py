@@ -297,14 +297,13 @@ def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     fl = 2.0 * M * N * K
     t = T.per_launch(lambda i: fp4.gemm_w4a16(a, wq, out=c), it)
-    # the same GEMM on the weight in the decode layout (one packed weight for decode and prefill)
+    # the same GEMMs on the weight in the decode layout (one packed weight for decode and prefill)
     wd = fp4.nvfp4_pack_decode(wq)
     t_d = T.per_launch(lambda i: fp4.gemm_w4a16_decode(a, wd, out=c), it)
     out["prefill_w4a16_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
                                   "decode_layout_us": t_d * 1e6, "decode_layout_TFLOP/s": fl / t_d / 1e12,
                                   "decode_layout_frac_bf16_mfma": fl / t_d / BF16_PEAK,
                                   "flop": fl, "mfma": "bf16 32x32x16 (NVFP4 widened exactly to bf16)"}
-    del wd
     # activation quantization alone (per row) and the fused W4A4 call
     wsa = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     pa = fp4.w4a4_packed_a(wsa, M, K, "row")
@@ -312,11 +311,15 @@ def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     bq = M * K * 2 + M * K // 2 + M * K // 16 + 4 * M
     t_g = T.per_launch(lambda i: fp4.gemm_nvfp4_prequant(pa, wq, out=c), it)
     t_all = T.per_launch(lambda i: fp4.gemm_w4a4(a, wq, a_mode="row", out=c, workspace=wsa), it)
+    t_gd = T.per_launch(lambda i: fp4.gemm_nvfp4_prequant_seg(pa, wd, out=c), it)
+    t_alld = T.per_launch(lambda i: fp4.gemm_w4a4_seg(a, wd, a_mode="row", out=c, workspace=wsa), it)
     out["prefill_w4a4_m4096"] = {
         "quant_us": t_q * 1e6, "quant_GB/s": bq / t_q / 1e9, "quant_frac_hbm": bq / t_q / HBM_PEAK,
         "gemm_us": t_g * 1e6, "gemm_TFLOP/s": fl / t_g / 1e12, "gemm_frac_bf16_mfma": fl / t_g / BF16_PEAK,
-        "total_us": t_all * 1e6, "total_TFLOP/s": fl / t_all / 1e12}
-    del a, c
+        "total_us": t_all * 1e6, "total_TFLOP/s": fl / t_all / 1e12,
+        "decode_layout_gemm_us": t_gd * 1e6, "decode_layout_gemm_TFLOP/s": fl / t_gd / 1e12,
+        "decode_layout_total_us": t_alld * 1e6}
+    del a, c, wd
 
 
 def mx16_components(torch, fp4, T, dev, w32, wl3, it, out):

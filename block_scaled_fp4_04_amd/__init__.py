@@ -60,6 +60,8 @@ def _declare(L):
         "gemm_w4a4_workspace_offsets": (None, [i64, i64, p, p, p]),
         "gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p, sz, p]),
         "gemm_nvfp4_w4a4_prequant": (i32, [p, p, p, i32, i64, i64, p, p, p, i64, p, i32, i64, p]),
+        "gemm_w4a4_seg": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p, sz, p]),
+        "gemm_nvfp4_w4a4_prequant_seg": (i32, [p, p, p, i32, i64, i64, p, p, p, i64, p, i32, i64, p]),
         "mxfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, i32, p, p]),
         "mxfp4_dequantize": (i32, [p, p, i64, i64, p, i32, i64, p]),
         "mxfp4_gemm_w4a4_workspace": (sz, [i64, i64]),
@@ -333,6 +335,37 @@ def gemm_nvfp4_prequant(a: PackedNVFP4, w: PackedNVFP4, dtype=torch.bfloat16,
                                       PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
                                       _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
                                       _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
+def gemm_w4a4_seg(a: torch.Tensor, w: DecodeNVFP4, a_mode="row", dtype=torch.bfloat16,
+                  out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_w4a4 with W in the decode layout: the same result."""
+    L = lib()
+    _need_cuda(a)
+    if a.dtype != torch.bfloat16:
+        raise TypeError("gemm_w4a4_seg takes bfloat16 activations")
+    M, K = a.shape
+    m = _mode(a_mode)
+    if out is None:
+        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    if workspace is None:
+        workspace = gemm_w4a4_workspace(M, K, m, a.device)
+    _check(L.gemm_w4a4_seg(_ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                           _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(), _stream()))
+    return out
+
+
+def gemm_nvfp4_prequant_seg(a: PackedNVFP4, w: DecodeNVFP4, dtype=torch.bfloat16,
+                            out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_nvfp4_prequant with W in the decode layout."""
+    L = lib()
+    if out is None:
+        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
+    _check(L.gemm_nvfp4_w4a4_prequant_seg(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
+                                          PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
+                                          _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
+                                          _out_dt(out.dtype), _ld(out), _stream()))
     return out
 
 

@@ -313,18 +313,13 @@ size_t gemm_w4a4_workspace(int64_t M, int64_t K, fp4_scale_mode a_mode)
     return t + ts + amax;
 }
 
-fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales,
-                                    const float *a_tscale, fp4_scale_mode a_mode, int64_t M,
-                                    int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
-                                    const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
-                                    int64_t ldc, hipStream_t stream)
+namespace {
+
+// the GEMM half of the NVFP4 W4A4 forms, arguments checked (w_seg: W in the decode layout)
+fp4_status w4a4_launch(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_tscale, fp4_scale_mode a_mode,
+                       int64_t M, int64_t K, const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale,
+                       int64_t N, void *c, fp4_dtype ct, int64_t ldc, bool w_seg, hipStream_t stream)
 {
-    if (a_mode != FP4_SCALE_PER_TENSOR && a_mode != FP4_SCALE_PER_ROW) return FP4_ERR_DTYPE;
-    FP4_TRY(check_gemm_common(M, K, N, 16, c, ct, ldc));
-    FP4_TRY(check_packed(a_codes, a_scales));
-    FP4_TRY(check_packed(w_codes, w_scales));
-    if (!a_tscale || !w_tscale) return FP4_ERR_NULL;
-    FP4_TRY(check_device());
     NvGemmArgs g{};
     g.a_codes = a_codes;
     g.a_scales = a_scales;
@@ -339,16 +334,33 @@ fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_sca
     g.c = c;
     g.c_bf16 = ct == FP4_BF16;
     g.ldc = ldc;
-    return launch_nvfp4_gemm(g, stream);
+    if (!w_seg) return launch_nvfp4_gemm(g, stream);
+    g.w_seg = 1;
+    g.w_rows = N;
+    g.w_row0 = 0;
+    return launch_gemm_w4a4_seg(g, stream);
 }
 
-fp4_status gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
-                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale,
-                     int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
-                     hipStream_t stream)
+fp4_status w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_tscale, fp4_scale_mode a_mode,
+                         int64_t M, int64_t K, const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale,
+                         int64_t N, void *c, fp4_dtype ct, int64_t ldc, bool w_seg, hipStream_t stream)
 {
     if (a_mode != FP4_SCALE_PER_TENSOR && a_mode != FP4_SCALE_PER_ROW) return FP4_ERR_DTYPE;
-    FP4_TRY(check_gemm_common(M, K, N, 16, c, ct, ldc));
+    FP4_TRY(check_gemm_common(M, K, N, w_seg ? 128 : 16, c, ct, ldc));
+    FP4_TRY(check_packed(a_codes, a_scales));
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!a_tscale || !w_tscale) return FP4_ERR_NULL;
+    FP4_TRY(check_device());
+    return w4a4_launch(a_codes, a_scales, a_tscale, a_mode, M, K, w_codes, w_scales, w_tscale, N, c, ct, ldc, w_seg,
+                       stream);
+}
+
+fp4_status w4a4_full(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode, const uint8_t *w_codes,
+                     const uint8_t *w_scales, const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
+                     void *ws, size_t ws_bytes, bool w_seg, hipStream_t stream)
+{
+    if (a_mode != FP4_SCALE_PER_TENSOR && a_mode != FP4_SCALE_PER_ROW) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, w_seg ? 128 : 16, c, ct, ldc));
     FP4_TRY(check_matrix(a, M, K, lda, 2));
     if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
     FP4_TRY(check_packed(w_codes, w_scales));
@@ -365,21 +377,43 @@ fp4_status gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale
     void *amax_ws = base + to + align256((size_t)(a_mode == FP4_SCALE_PER_ROW ? M : 1) * sizeof(float));
     FP4_TRY(launch_nvfp4_quantize(a, FP4_BF16, M, K, lda, ac, as, at, a_mode, amax_ws, nullptr,
                                   stream));
-    NvGemmArgs g{};
-    g.a_codes = ac;
-    g.a_scales = as;
-    g.a_tscale = at;
-    g.a_per_row = a_mode == FP4_SCALE_PER_ROW;
-    g.w_codes = w_codes;
-    g.w_scales = w_scales;
-    g.w_tscale = w_tscale;
-    g.M = M;
-    g.N = N;
-    g.K = K;
-    g.c = c;
-    g.c_bf16 = ct == FP4_BF16;
-    g.ldc = ldc;
-    return launch_nvfp4_gemm(g, stream);
+    return w4a4_launch(ac, as, at, a_mode, M, K, w_codes, w_scales, w_tscale, N, c, ct, ldc, w_seg, stream);
+}
+
+}  // namespace
+
+fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales,
+                                    const float *a_tscale, fp4_scale_mode a_mode, int64_t M,
+                                    int64_t K, const uint8_t *w_codes, const uint8_t *w_scales,
+                                    const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
+                                    int64_t ldc, hipStream_t stream)
+{
+    return w4a4_prequant(a_codes, a_scales, a_tscale, a_mode, M, K, w_codes, w_scales, w_tscale, N, c, ct, ldc, false,
+                         stream);
+}
+
+fp4_status gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                     const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale,
+                     int64_t N, void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
+                     hipStream_t stream)
+{
+    return w4a4_full(a, M, K, lda, a_mode, w_codes, w_scales, w_tscale, N, c, ct, ldc, ws, ws_bytes, false, stream);
+}
+
+fp4_status gemm_nvfp4_w4a4_prequant_seg(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_tscale,
+                                        fp4_scale_mode a_mode, int64_t M, int64_t K, const uint8_t *w_codes_p,
+                                        const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
+                                        fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    return w4a4_prequant(a_codes, a_scales, a_tscale, a_mode, M, K, w_codes_p, w_scales_p, w_tscale, N, c, ct, ldc,
+                         true, stream);
+}
+
+fp4_status gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                         const uint8_t *w_codes_p, const uint8_t *w_scales_p, const float *w_tscale, int64_t N,
+                         void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream)
+{
+    return w4a4_full(a, M, K, lda, a_mode, w_codes_p, w_scales_p, w_tscale, N, c, ct, ldc, ws, ws_bytes, true, stream);
 }
 
 // ------------------------------------------------------------------ MXFP4 --

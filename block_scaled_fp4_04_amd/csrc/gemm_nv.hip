@@ -1428,6 +1428,15 @@ fp4_status launch_gemm_w4a16_seg(const NvGemmArgs &g, bool mx, hipStream_t st)
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
+fp4_status launch_gemm_w4a4_seg(const NvGemmArgs &g, hipStream_t st)
+{
+    // the ring kernel addresses operands with 32-bit byte offsets
+    if (g.K % 128 != 0 || g.M * (g.K / 2) >= (int64_t(1) << 31) || g.w_rows * (g.K / 2) >= (int64_t(1) << 31))
+        return FP4_ERR_SHAPE;
+    launch_ring_split<kFmtNv44, 0>(g, st);
+    return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
 fp4_status launch_mxfp4_gemm_w4a16(const NvGemmArgs &g, hipStream_t st)
 {
     // the ring kernel addresses operands with 32-bit byte offsets

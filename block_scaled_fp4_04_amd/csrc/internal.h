@@ -74,6 +74,8 @@ struct NvGemmArgs {
 fp4_status launch_nvfp4_gemm(const NvGemmArgs &g, hipStream_t st);
 // W4A16 prefill on a weight in the decode layout (NVFP4, or MXFP4 when mx)
 fp4_status launch_gemm_w4a16_seg(const NvGemmArgs &g, bool mx, hipStream_t st);
+// NVFP4 W4A4 on a weight in the decode layout
+fp4_status launch_gemm_w4a4_seg(const NvGemmArgs &g, hipStream_t st);
 // grouped GEMM on the ring kernel: F = 0 NVFP4 W4A16, 1 NVFP4 W4A4, 2 MXFP4 W4A16
 fp4_status launch_grouped_gemm(const NvGemmArgs &g, int fmt, hipStream_t st);
 

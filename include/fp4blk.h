@@ -180,6 +180,19 @@ fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_sca
                                     const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
                                     int64_t ldc, hipStream_t stream);
 
+/* NVFP4 W4A4 with W in the decode layout (nvfp4_pack_decode): the same result as
+ * gemm_w4a4 / gemm_nvfp4_w4a4_prequant on the row-major W, bit for bit; each
+ * 64-element K stage then reads a weight panel whose rows are 64 bytes apart
+ * instead of K/2.  K % 128 == 0; other arguments, workspace and errors as those
+ * two. */
+fp4_status gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                         const uint8_t *w_codes_p, const uint8_t *w_scales_p, const float *w_tscale, int64_t N,
+                         void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);
+fp4_status gemm_nvfp4_w4a4_prequant_seg(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_tscale,
+                                        fp4_scale_mode a_mode, int64_t M, int64_t K, const uint8_t *w_codes_p,
+                                        const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
+                                        fp4_dtype ct, int64_t ldc, hipStream_t stream);
+
 /* ------------------------------------------------------------ MXFP4 ------ */
 
 /* MXFP4 quantize (eefocus.com article, "FP4 as the next core standard").

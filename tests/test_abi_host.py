@@ -143,6 +143,28 @@ def test_gemm_validation(L):
     if not torch.cuda.is_available():
         assert g4() == NO_DEVICE
 
+    def g4s(**kw):
+        a = dict(a=FAKE, M=8, K=256, lda=256, mode=1, wc=FAKE, ws=FAKE, wt=FAKE, N=32, c=FAKE, ct=0,
+                 ldc=32, work=FAKE, work_bytes=1 << 20, stream=None)
+        a.update(kw)
+        return L.gemm_w4a4_seg(*a.values())
+
+    assert g4s(K=64, lda=64) == SHAPE       # whole 128-element segments
+    assert g4s(wt=None) == NULL
+    assert g4s(work_bytes=16) == WORKSPACE
+
+    def p4s(**kw):
+        a = dict(ac=FAKE, asc=FAKE, at=FAKE, mode=1, M=8, K=256, wc=FAKE, ws=FAKE, wt=FAKE, N=32, c=FAKE,
+                 ct=1, ldc=32, stream=None)
+        a.update(kw)
+        return L.gemm_nvfp4_w4a4_prequant_seg(*a.values())
+
+    assert p4s(K=192) == SHAPE
+    assert p4s(at=None) == NULL
+    assert p4s(mode=5) == DTYPE
+    if not torch.cuda.is_available():
+        assert g4s() == NO_DEVICE and p4s() == NO_DEVICE
+
 
 def test_decode_layout_validation(L):
     import torch

@@ -92,6 +92,12 @@ def test_w4a4(M, N, K, a_mode):
     assert np.array_equal(pa.tscale.cpu().numpy(), ats)
     ref, tol = oracle.gemm_w4a4_ref(a, oc, os_, ot, a_per_row=(a_mode == "row"))
     assert_gemm_close(c, ref, tol, f"w4a4 {M}x{N}x{K}")
+    if K % 128 == 0:
+        # W in the decode layout: the same kernel arithmetic, bit for bit
+        cs = fp4().gemm_w4a4_seg(bf16bits_to_dev(a), fp4().nvfp4_pack_decode(_packed_nv(oc, os_, ot)),
+                                 a_mode=a_mode, dtype=torch.float32)
+        torch.cuda.synchronize()
+        assert torch.equal(cs.view(torch.int32), c.view(torch.int32)), "decode-layout W4A4 differs"
 
 
 # K % 256 == 0 takes the two-stage kernel (K / 256 odd adds a leading zero stage);
