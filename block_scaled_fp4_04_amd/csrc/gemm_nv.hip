@@ -971,25 +971,28 @@ __device__ __forceinline__ void nv_pipe_mfma(f32x16 (&acc)[NI][NJ], const bf16x8
 }
 
 // Spread the NM MFMAs of a step over the widening (NV VALU) and the reads (ND)
-// of the next step.  NR reads and NB copies (global-to-LDS) go out first, then P
-// MFMAs cover the latency of those reads before any VALU work uses them.
-template <int N, int NV, int ND, int T>
+// of the next step.  NR reads go out first, then P MFMAs cover their latency
+// before any VALU work uses them; the NB copies (global-to-LDS) are spread one per
+// MFMA slot, since a burst of copies holds back the MFMAs behind it in the wave's
+// instruction stream.
+template <int N, int NV, int ND, int T, int NC = 0>
 __device__ __forceinline__ void nv_pipe_slot()
 {
     constexpr int v = NV * (T + 1) / N - NV * T / N, r = ND * (T + 1) / N - ND * T / N;
+    constexpr int cp = NC * (T + 1) / N - NC * T / N;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    if constexpr (cp > 0) __builtin_amdgcn_sched_group_barrier(0x020, cp, 0);  // copies
     if constexpr (v > 0) __builtin_amdgcn_sched_group_barrier(0x002, v, 0);  // VALU
     if constexpr (r > 0) __builtin_amdgcn_sched_group_barrier(0x100, r, 0);  // DS read
-    if constexpr (T + 1 < N) nv_pipe_slot<N, NV, ND, T + 1>();
+    if constexpr (T + 1 < N) nv_pipe_slot<N, NV, ND, T + 1, NC>();
 }
 
 template <int NM, int NV, int ND, int NR = 0, int NB = 0, int P = 0>
 __device__ __forceinline__ void nv_pipe_interleave()
 {
     if constexpr (NR > 0) __builtin_amdgcn_sched_group_barrier(0x100, NR, 0);  // DS read
-    if constexpr (NB > 0) __builtin_amdgcn_sched_group_barrier(0x020, NB, 0);  // VMEM read
     if constexpr (P > 0) __builtin_amdgcn_sched_group_barrier(0x008, P, 0);    // MFMA
-    nv_pipe_slot<NM - P, NV, ND, 0>();
+    nv_pipe_slot<NM - P, NV, ND, 0, NB>();
     __builtin_amdgcn_sched_barrier(0);
 }
 
