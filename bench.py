@@ -47,8 +47,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    # a step takes about 38 us: 200 warm-up steps (8 ms) bring the clock to the rate
+    # it sustains, and 500 timed steps (19 ms) average over it
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=12, help="weight copies cycled through")
     ap.add_argument("--comp-iters", type=int, default=20, help="timed launches per component")
     ap.add_argument("--skip-components", action="store_true")
