@@ -1,14 +1,20 @@
-"""GPU parity of the row-major NVFP4 GEMMs with an operand past 2 GiB.
+"""GPU parity of the GEMMs with operands at and past their 32-bit offset limits.
 
-W4A16 and W4A4 (aixq.cc article, "Core difference: W4A4 vs W4A16") on the NVFP4
-format (NVFP4 wiki, format section).  The ring kernel addresses its operands
-with 32-bit byte offsets; gemm_w4a16 / gemm_w4a4 send larger operands to the
-tile kernel with 64-bit addressing.  Three cases, K = 5120:
-  - W4A16, A of 209,716 rows (2,147,491,840 bytes of bf16), N = 256;
-  - W4A4 (A quantized per row inside the call), the same A;
-  - W4A16, W of 838,861 rows (2,147,484,160 code bytes), M = 64.
+W4A16 and W4A4 (aixq.cc article, "Core difference: W4A4 vs W4A16") on NVFP4
+(NVFP4 wiki, format section) and MXFP4 (edge-FP4 article, section "FP4 as the
+next core standard"), K = 5120:
+  - NVFP4 W4A16 and W4A4, A of 209,716 rows (2,147,491,840 bytes of bf16); and
+    W4A16 with W of 838,861 rows (2,147,484,160 code bytes).  The ring kernel
+    addresses operands with 32-bit byte offsets, so these take the tile kernel
+    with 64-bit addressing;
+  - MXFP4 W4A4 with A's codes past 2^31 bytes (1,048,576 rows: the staged
+    kernel's unsigned 32-bit offsets) and past 2^32 bytes (1,677,722 rows: the
+    64-bit tile kernel);
+  - the segment-major MXFP4 GEMM and W4A8 just under their 2^31-byte limits
+    (838,860 and 419,430 rows), the former also equal bit for bit to the
+    row-major kernel.
 Operands repeat a seeded base of 679 rows (A: bf16 activation rows; W: the
-oracle's NVFP4 quantization of 679 weight rows, so the tensor scale is that of
+oracle's quantization of 679 weight rows, so an NVFP4 tensor scale is that of
 the whole W), row r being base row r mod 679; 679 does not divide the row
 offsets at which a 32-bit byte offset would wrap, so a wrapped read lands on a
 different row.  C is compared with the oracle's fp64 product on sampled rows
@@ -115,4 +121,76 @@ def test_nvfp4_gemm_w_past_2gib():
     ref, tol = oracle.gemm_w4a16_ref(a, wc[cols % P], wsc[cols % P], wt)
     assert_gemm_close(c[:, torch.from_numpy(cols).to(dev())], ref, tol, "w4a16 W past 2 GiB")
     del codes, scales, c
+    torch.cuda.empty_cache()
+
+
+# ------------------------------------------------------------------ MXFP4 --
+#
+# MXFP4 (edge-FP4 article, section "FP4 as the next core standard": E8M0 scale
+# per 32).  The row-major W4A4 GEMM runs the staged kernel while A's codes stay
+# under 2^32 bytes (unsigned 32-bit offsets) and the 64-bit tile kernel beyond;
+# the segment-major kernel and W4A8 (MXFP8 A, one byte a value) take operands up
+# to just under 2^31 bytes.
+
+def _w_small_mx(N, seed):
+    w = to_bf16_bits(weights(N, K, 0.02, 0.001, 20.0, seed=seed))
+    return oracle.mxfp4_quantize(w)
+
+
+def _mx_rows(M):
+    return np.union1d(_sample(M, K // 2, seed=M % 1000), _sample(M, K * 2, seed=M % 997))
+
+
+@pytest.mark.parametrize("M", [1048576, 1677722])   # A codes past 2^31 (staged kernel), past 2^32 (tile kernel)
+def test_mxfp4_gemm_a_past_2gib_and_4gib(M):
+    N = 256
+    ab = _a_base()
+    log(f"mxfp4_gemm_w4a4 A {M}x{K} bf16 ({M * K // 2} bytes of A codes), N={N}")
+    a = _tile_rows(bf16bits_to_dev(ab), M)
+    wc, wsc = _w_small_mx(N, seed=48)
+    wp = fp4().PackedMXFP4(torch.from_numpy(wc).to(dev()), torch.from_numpy(wsc).to(dev()), N, K)
+    c = fp4().mxfp4_gemm_w4a4(a, wp, dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = _mx_rows(M)
+    ref, tol = oracle.mxfp4_gemm_w4a4_ref(ab[rows % P], wc, wsc)
+    assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, f"mxfp4 w4a4 M={M}")
+    del a, c
+    torch.cuda.empty_cache()
+
+
+def test_mxfp4_seg_gemm_just_under_2gib():
+    M, N = 838860, 256
+    assert M * K // 2 < (1 << 31) <= (M + 1) * K // 2
+    ab = _a_base()
+    log(f"mxfp4_gemm_w4a4_seg A {M}x{K} ({M * K // 2} bytes of A codes), N={N}")
+    a = _tile_rows(bf16bits_to_dev(ab), M)
+    wc, wsc = _w_small_mx(N, seed=49)
+    wp = fp4().PackedMXFP4(torch.from_numpy(wc).to(dev()), torch.from_numpy(wsc).to(dev()), N, K)
+    ws = fp4().mxfp4_gemm_w4a4_seg_workspace(M, K, dev())
+    c = fp4().mxfp4_gemm_w4a4_seg(a, fp4().mxfp4_pack_decode(wp), dtype=torch.float32, workspace=ws)
+    c_rm = fp4().mxfp4_gemm_w4a4(a, wp, dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = _mx_rows(M)
+    ref, tol = oracle.mxfp4_gemm_w4a4_ref(ab[rows % P], wc, wsc)
+    ri = torch.from_numpy(rows).to(dev())
+    assert_gemm_close(c[ri], ref, tol, "mxfp4 seg just under 2 GiB")
+    assert torch.equal(c, c_rm), "segment-major and row-major kernels differ"
+    del a, c, c_rm, ws
+    torch.cuda.empty_cache()
+
+
+def test_w4a8_gemm_just_under_2gib():
+    M, N = 419430, 256
+    assert M * K < (1 << 31) <= (M + 1) * K
+    ab = _a_base()
+    log(f"mxfp4_gemm_w4a8 A {M}x{K} ({M * K} bytes of MXFP8 codes), N={N}")
+    a = _tile_rows(bf16bits_to_dev(ab), M)
+    wc, wsc = _w_small_mx(N, seed=50)
+    wp = fp4().PackedMXFP4(torch.from_numpy(wc).to(dev()), torch.from_numpy(wsc).to(dev()), N, K)
+    c = fp4().mxfp4_gemm_w4a8(a, wp, dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = np.union1d(_sample(M, K, seed=51), _sample(M, K * 2, seed=52))
+    ref, tol = oracle.mxfp4_gemm_w4a8_ref(ab[rows % P], wc, wsc)
+    assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, "w4a8 just under 2 GiB")
+    del a, c
     torch.cuda.empty_cache()
