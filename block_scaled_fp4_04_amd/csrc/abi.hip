@@ -42,6 +42,16 @@ size_t dsize(fp4_dtype t) { return t == FP4_F32 ? 4 : 2; }
 
 bool valid_dtype(int t) { return t == FP4_F32 || t == FP4_BF16; }
 
+// Kernels that address an operand with 32-bit buffer offsets take operands under
+// 2 GiB; the entry points check this on the host, before anything is launched.
+constexpr int64_t k2GiB = int64_t(1) << 31;
+
+// M rows and N rows of row_bytes each both stay under 2 GiB
+bool codes_under_2gib(int64_t M, int64_t N, int64_t row_bytes)
+{
+    return M * row_bytes < k2GiB && N * row_bytes < k2GiB;
+}
+
 // rows x cols input with leading dimension ld (elements of size es): rows stay
 // 16-byte aligned when the base is and ld * es is a multiple of 16.
 fp4_status check_matrix(const void *p, int64_t rows, int64_t cols, int64_t ld, size_t es)
@@ -350,6 +360,7 @@ fp4_status w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_scales, const 
     FP4_TRY(check_packed(a_codes, a_scales));
     FP4_TRY(check_packed(w_codes, w_scales));
     if (!a_tscale || !w_tscale) return FP4_ERR_NULL;
+    if (w_seg && !codes_under_2gib(M, N, K / 2)) return FP4_ERR_SHAPE;
     FP4_TRY(check_device());
     return w4a4_launch(a_codes, a_scales, a_tscale, a_mode, M, K, w_codes, w_scales, w_tscale, N, c, ct, ldc, w_seg,
                        stream);
@@ -367,6 +378,7 @@ fp4_status w4a4_full(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale
     if (!w_tscale) return FP4_ERR_NULL;
     if (!ws || !aligned16(ws) || ws_bytes < gemm_w4a4_workspace(M, K, a_mode))
         return FP4_ERR_WORKSPACE;
+    if (w_seg && !codes_under_2gib(M, N, K / 2)) return FP4_ERR_SHAPE;  // before A is quantized
     FP4_TRY(check_device());
     size_t co, so, to;
     gemm_w4a4_workspace_offsets(M, K, &co, &so, &to);
@@ -514,6 +526,7 @@ fp4_status mxfp4_gemm_prequant_seg(const uint8_t *a_codes_p, const uint8_t *a_sc
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
     FP4_TRY(check_packed(a_codes_p, a_scales_p));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
+    if (!codes_under_2gib(M, N, K / 2)) return FP4_ERR_SHAPE;
     FP4_TRY(check_device());
     MxGemmArgs g{};
     g.a_codes = a_codes_p;
@@ -539,6 +552,7 @@ fp4_status mxfp4_gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda,
     if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
     if (!ws || !aligned16(ws) || ws_bytes < mxfp4_gemm_w4a4_seg_workspace(M, K)) return FP4_ERR_WORKSPACE;
+    if (!codes_under_2gib(M, N, K / 2)) return FP4_ERR_SHAPE;  // before A is quantized
     FP4_TRY(check_device());
     uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
     uint8_t *as = ac + align256((size_t)M * (size_t)(K / 2));
@@ -588,6 +602,7 @@ fp4_status w4a8_gemm(const uint8_t *a_codes, const uint8_t *a_scales, int64_t M,
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
     FP4_TRY(check_packed(a_codes, a_scales));
     FP4_TRY(check_packed(w_codes, w_scales));
+    if (M * K >= k2GiB || !codes_under_2gib(0, N, K / 2)) return FP4_ERR_SHAPE;
     FP4_TRY(check_device());
     MxGemmArgs g{};
     g.a_codes = a_codes;
@@ -614,6 +629,7 @@ fp4_status w4a8_full(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_ru
     if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
     FP4_TRY(check_packed(w_codes, w_scales));
     if (!ws || !aligned16(ws) || ws_bytes < mxfp4_gemm_w4a8_workspace(M, K)) return FP4_ERR_WORKSPACE;
+    if (M * K >= k2GiB || !codes_under_2gib(0, N, K / 2)) return FP4_ERR_SHAPE;  // before A is quantized
     FP4_TRY(check_device());
     uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
     uint8_t *as = ac + align256((size_t)M * (size_t)K);

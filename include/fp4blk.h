@@ -183,8 +183,9 @@ fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_sca
 /* NVFP4 W4A4 with W in the decode layout (nvfp4_pack_decode): the same result as
  * gemm_w4a4 / gemm_nvfp4_w4a4_prequant on the row-major W, bit for bit; each
  * 64-element K stage then reads a weight panel whose rows are 64 bytes apart
- * instead of K/2.  K % 128 == 0; other arguments, workspace and errors as those
- * two. */
+ * instead of K/2.  K % 128 == 0, M * K / 2 and N * K / 2 below 2^31
+ * (FP4_ERR_SHAPE otherwise, checked before A is quantized); other arguments,
+ * workspace and errors as those two. */
 fp4_status gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
                          const uint8_t *w_codes_p, const uint8_t *w_scales_p, const float *w_tscale, int64_t N,
                          void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);
@@ -257,8 +258,8 @@ fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t 
  * segment is then contiguous, which is how the kernel reads it.  A (bf16
  * [M][lda]) is quantized with `rule` into `ws` in the same layout (codes
  * [K/128][M][64] at ws, E8M0 [K/128][M][4] at the next 256-byte boundary).
- * K % 128 == 0, M * K / 2 and N * K / 2 below 2^31 (FP4_ERR_SHAPE otherwise);
- * FP4_ERR_WORKSPACE for a null, unaligned or short ws.  C [M][ldc] fp32 or bf16
+ * K % 128 == 0, M * K / 2 and N * K / 2 below 2^31 (FP4_ERR_SHAPE otherwise,
+ * checked before A is quantized); FP4_ERR_WORKSPACE for a null, unaligned or short ws.  C [M][ldc] fp32 or bf16
  * is written; nothing is allocated. */
 size_t mxfp4_gemm_w4a4_seg_workspace(int64_t M, int64_t K);
 fp4_status mxfp4_gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
@@ -291,9 +292,10 @@ size_t mxfp4_gemm_w4a8_workspace(int64_t M, int64_t K);
 
 /* W4A8 GEMM: the bf16 A is quantized to MXFP8 with `rule` into `ws`, then
  * C = A_q . W^T on gfx950's block-scaled matrix instruction with FP8 and FP4
- * operands (exact products, fp32 accumulation).  W MXFP4 [N][K].  K % 128 == 0
- * (FP4_ERR_SHAPE otherwise).  Tolerance as the other GEMMs, against fp64 over
- * the dequantized operands. */
+ * operands (exact products, fp32 accumulation).  W MXFP4 [N][K].  K % 128 == 0,
+ * M * K (A's MXFP8 bytes) and N * K / 2 below 2^31 (FP4_ERR_SHAPE otherwise,
+ * checked before anything is launched).  Tolerance as the other GEMMs, against
+ * fp64 over the dequantized operands. */
 fp4_status mxfp4_gemm_w4a8(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
                            const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
                            fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);

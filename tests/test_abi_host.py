@@ -162,8 +162,14 @@ def test_gemm_validation(L):
     assert p4s(K=192) == SHAPE
     assert p4s(at=None) == NULL
     assert p4s(mode=5) == DTYPE
+    # A or W codes of 2^31 bytes or more (K = 5120: 838,861 rows) are refused on
+    # the host, before A is quantized
+    big = dict(K=5120, lda=5120, work_bytes=1 << 40)
+    assert g4s(M=838861, ldc=32, **big) == SHAPE and g4s(N=838861, ldc=838861, **big) == SHAPE
+    assert p4s(M=838861, K=5120) == SHAPE and p4s(N=838861, K=5120, ldc=838861) == SHAPE
     if not torch.cuda.is_available():
         assert g4s() == NO_DEVICE and p4s() == NO_DEVICE
+        assert g4s(M=838860, **big) == NO_DEVICE    # just under the limit
 
 
 def test_decode_layout_validation(L):
@@ -289,8 +295,13 @@ def test_mxfp4_segment_major_gemm_validation(L):
     assert p(asc=None) == NULL
     assert p(M=0) == SHAPE
     assert p(ct=4) == DTYPE
+    # codes of 2^31 bytes or more (K = 5120: 838,861 rows), refused before A is quantized
+    big = dict(K=5120, lda=5120, work_bytes=1 << 40)
+    assert g(M=838861, **big) == SHAPE and g(N=838861, ldc=838861, **big) == SHAPE
+    assert p(M=838861, K=5120) == SHAPE and p(N=838861, K=5120, ldc=838861) == SHAPE
     if not torch.cuda.is_available():
         assert g() == NO_DEVICE and p() == NO_DEVICE
+        assert g(M=838860, **big) == NO_DEVICE and p(M=838860, K=5120) == NO_DEVICE
 
 
 def test_w4a8_segment_major_validation(L):
@@ -315,8 +326,14 @@ def test_w4a8_segment_major_validation(L):
     assert p(K=64) == SHAPE
     assert p(ws=None) == NULL
     assert p(ldc=15) == LAYOUT
+    # MXFP8 A of 2^31 bytes or more (K = 5120: 419,431 rows) or W codes past it,
+    # refused before A is quantized
+    big = dict(K=5120, lda=5120, work_bytes=1 << 40)
+    assert g(M=419431, **big) == SHAPE and g(N=838861, ldc=838861, **big) == SHAPE
+    assert p(M=419431, K=5120) == SHAPE
     if not torch.cuda.is_available():
         assert g() == NO_DEVICE and p() == NO_DEVICE
+        assert g(M=419430, **big) == NO_DEVICE and p(M=419430, K=5120) == NO_DEVICE
 
 
 def test_w4a8_validation(L):
