@@ -141,13 +141,78 @@ def _dt(t: torch.Tensor) -> int:
 
 
 def _out_dt(dtype) -> int:
-    return FP4_F32 if dtype == torch.float32 else FP4_BF16
+    if dtype == torch.float32:
+        return FP4_F32
+    if dtype == torch.bfloat16:
+        return FP4_BF16
+    raise TypeError(f"outputs are float32 or bfloat16, got {dtype}")
 
 
 def _need_cuda(*ts):
+    """Every tensor given is a device tensor, and all are on one device."""
+    devs = {t.device for t in ts if t is not None}
     for t in ts:
         if t is not None and not t.is_cuda:
             raise ValueError("libfp4blk takes device tensors")
+    if len(devs) > 1:
+        raise ValueError(f"tensors on several devices: {sorted(str(d) for d in devs)}")
+
+
+# Argument checks.  The C ABI receives bare pointers and sizes, so it cannot see a
+# tensor that is smaller than the sizes passed with it; these checks run before
+# anything is handed to the library (shapes and dtypes first, then devices).
+
+def _shape(t: torch.Tensor, shape, what: str):
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{what} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _u8(t: torch.Tensor, shape, what: str):
+    """A packed byte array: uint8, the given shape, contiguous (the ABI takes no row stride for it)."""
+    if t.dtype != torch.uint8:
+        raise TypeError(f"{what} must be uint8, got {t.dtype}")
+    _shape(t, shape, what)
+    if not t.is_contiguous():
+        raise ValueError(f"{what} must be contiguous")
+
+
+def _f32_vec(t: torch.Tensor, n: int, what: str):
+    if t.dtype != torch.float32 or t.numel() != n or not t.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous float32 tensor of {n} element(s), got {t.dtype} "
+                         f"{tuple(t.shape)}")
+
+
+def _matrix(t: torch.Tensor, shape, dtypes, what: str):
+    if t.dtype not in dtypes:
+        raise TypeError(f"{what} must be {' or '.join(str(d) for d in dtypes)}, got {t.dtype}")
+    _shape(t, shape, what)
+    _ld(t)
+
+
+def _out(out, M: int, N: int, dtype, like: torch.Tensor) -> torch.Tensor:
+    """The GEMM / dequantize output: allocated when None, else checked (shape (M, N),
+    float32 or bfloat16, unit stride along rows)."""
+    if out is None:
+        _out_dt(dtype)
+        return torch.empty(M, N, dtype=dtype, device=like.device)
+    _out_dt(out.dtype)
+    _matrix(out, (M, N), (torch.float32, torch.bfloat16), "out")
+    return out
+
+
+def _workspace(ws, need: int, like: torch.Tensor) -> torch.Tensor:
+    if ws is None:
+        return torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+    if ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, {need} needed")
+    return ws
+
+
+def _k_match(K: int, cols: int):
+    if K != cols:
+        raise ValueError(f"A has K = {K} columns but the weight has {cols}")
 
 
 def _mode(m) -> int:
@@ -167,8 +232,13 @@ def _rule(r) -> int:
 
 
 def _ld(t: torch.Tensor) -> int:
-    if t.dim() != 2 or t.stride(1) != 1:
+    """The row stride (leading dimension) of a 2-D tensor with unit stride along its rows.
+    A single row's stride is never followed, and torch may report any value for it
+    (0 after unsqueeze or expand): it is given as the row length then."""
+    if t.dim() != 2 or (t.stride(1) != 1 and t.shape[1] > 1):
         raise ValueError("expected a 2-D tensor with unit stride along its rows")
+    if t.shape[0] <= 1:
+        return max(t.stride(0), t.shape[1])
     return t.stride(0)
 
 
@@ -186,6 +256,12 @@ class PackedNVFP4:
     def nbytes(self) -> int:
         return self.codes.numel() + self.scales.numel() + 4 * self.tscale.numel()
 
+    def check(self, what="NVFP4 tensor"):
+        _u8(self.codes, (self.rows, self.cols // 2), f"{what} codes")
+        _u8(self.scales, (self.rows, self.cols // 16), f"{what} scales")
+        _f32_vec(self.tscale, self.rows if self.per_row else 1, f"{what} tensor scale")
+        return self
+
 
 @dataclasses.dataclass
 class PackedMXFP4:
@@ -198,6 +274,11 @@ class PackedMXFP4:
     def nbytes(self) -> int:
         return self.codes.numel() + self.scales.numel()
 
+    def check(self, what="MXFP4 tensor"):
+        _u8(self.codes, (self.rows, self.cols // 2), f"{what} codes")
+        _u8(self.scales, (self.rows, self.cols // 32), f"{what} scales")
+        return self
+
 
 # --------------------------------------------------------------- NVFP4 -----
 
@@ -205,18 +286,22 @@ def nvfp4_quantize(x: torch.Tensor, mode="tensor", nonfinite: torch.Tensor | Non
                    out: PackedNVFP4 | None = None, workspace: torch.Tensor | None = None) -> PackedNVFP4:
     """Quantize a 2-D fp32/bf16 device tensor to NVFP4 (blocks along its rows)."""
     L = lib()
-    _need_cuda(x, nonfinite)
+    _dt(x)
     rows, cols = x.shape
     m = _mode(mode)
-    dev = x.device
     if out is None:
-        out = PackedNVFP4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=dev),
-                          torch.empty(rows, cols // 16, dtype=torch.uint8, device=dev),
-                          torch.empty(rows if m == PER_ROW else 1, dtype=torch.float32, device=dev),
+        out = PackedNVFP4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device),
+                          torch.empty(rows, cols // 16, dtype=torch.uint8, device=x.device),
+                          torch.empty(rows if m == PER_ROW else 1, dtype=torch.float32, device=x.device),
                           rows, cols, m == PER_ROW)
+    if (out.rows, out.cols, out.per_row) != (rows, cols, m == PER_ROW):
+        raise ValueError("out does not describe this tensor and scale mode")
+    out.check("out")
+    if nonfinite is not None and (nonfinite.dtype != torch.int32 or nonfinite.numel() < 1):
+        raise ValueError("nonfinite must be an int32 tensor of at least one element")
     wsb = L.nvfp4_quantize_workspace(rows, cols, m)
-    if workspace is None and wsb:
-        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    workspace = _workspace(workspace, wsb, x) if wsb else workspace
+    _need_cuda(x, nonfinite, out.codes, out.scales, out.tscale, workspace)
     _check(L.nvfp4_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
                             _ptr(out.tscale), m, _ptr(workspace), wsb, _ptr(nonfinite), _stream()))
     return out
@@ -224,24 +309,39 @@ def nvfp4_quantize(x: torch.Tensor, mode="tensor", nonfinite: torch.Tensor | Non
 
 def nvfp4_dequantize(p: PackedNVFP4, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
     L = lib()
-    if out is None:
-        out = torch.empty(p.rows, p.cols, dtype=dtype, device=p.codes.device)
+    p.check("p")
+    out = _out(out, p.rows, p.cols, dtype, p.codes)
+    _need_cuda(p.codes, p.scales, p.tscale, out)
     _check(L.nvfp4_dequantize(_ptr(p.codes), _ptr(p.scales), _ptr(p.tscale),
                               PER_ROW if p.per_row else PER_TENSOR, p.rows, p.cols, _ptr(out),
                               _out_dt(out.dtype), _ld(out), _stream()))
     return out
 
 
+def _bf16_a(a: torch.Tensor, fn: str):
+    if a.dtype != torch.bfloat16:
+        raise TypeError(f"{fn} takes bfloat16 activations")
+    if a.dim() != 2:
+        raise ValueError(f"{fn} takes a 2-D activation tensor [M, K]")
+    _ld(a)
+    return a.shape
+
+
+def _weight_nv(w: PackedNVFP4, K: int):
+    if w.per_row:
+        raise ValueError("NVFP4 weights carry one tensor scale (quantize them with mode='tensor')")
+    w.check("w")
+    _k_match(K, w.cols)
+
+
 def gemm_w4a16(a: torch.Tensor, w: PackedNVFP4, dtype=torch.bfloat16,
                out: torch.Tensor | None = None) -> torch.Tensor:
     """C = A . W^T with bf16 A [M, K] and NVFP4 W [N, K] (per-tensor scale)."""
     L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("gemm_w4a16 takes bfloat16 activations")
-    M, K = a.shape
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    M, K = _bf16_a(a, "gemm_w4a16")
+    _weight_nv(w, K)
+    out = _out(out, M, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, w.tscale, out)
     _check(L.gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                         _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
@@ -257,18 +357,29 @@ class DecodeNVFP4:
     rows: int
     cols: int
 
+    def check(self, what="w"):
+        _u8(self.codes, (self.cols // 128, self.rows, 64), f"{what} codes")
+        _u8(self.scales, (self.cols // 128, self.rows, 8), f"{what} scales")
+        _f32_vec(self.tscale, 1, f"{what} tensor scale")
+        return self
+
 
 def nvfp4_pack_decode(w: PackedNVFP4, out: DecodeNVFP4 | None = None) -> DecodeNVFP4:
     """Rewrite a per-tensor NVFP4 weight into the decode layout (segment-major)."""
     L = lib()
     if w.per_row:
         raise ValueError("the decode layout holds weights with a per-tensor scale")
+    w.check("w")
     N, K = w.rows, w.cols
     if out is None:
         dev = w.codes.device
         out = DecodeNVFP4(torch.empty(K // 128, N, 64, dtype=torch.uint8, device=dev),
                           torch.empty(K // 128, N, 8, dtype=torch.uint8, device=dev),
                           w.tscale, N, K)
+    if (out.rows, out.cols) != (N, K):
+        raise ValueError("out does not describe this weight")
+    out.check("out")
+    _need_cuda(w.codes, w.scales, out.codes, out.scales)
     _check(L.nvfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
                                _stream()))
     return out
@@ -279,12 +390,11 @@ def gemm_w4a16_decode(a: torch.Tensor, w: DecodeNVFP4, dtype=torch.bfloat16,
     """C = A . W^T for bf16 A [M, K] and W in the decode layout: the decode GEMV for M <= 16,
     the prefill GEMM on the same layout for larger M."""
     L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("gemm_w4a16_decode takes bfloat16 activations")
-    M, K = a.shape
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    M, K = _bf16_a(a, "gemm_w4a16_decode")
+    w.check("w")
+    _k_match(K, w.cols)
+    out = _out(out, M, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, w.tscale, out)
     _check(L.gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                                _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
@@ -307,66 +417,61 @@ def w4a4_packed_a(ws: torch.Tensor, M: int, K: int, a_mode="row") -> PackedNVFP4
     return PackedNVFP4(codes, scales, tscale, M, K, per_row)
 
 
+def _w4a4(fn_name: str, a, w, a_mode, dtype, out, workspace, w_check):
+    L = lib()
+    M, K = _bf16_a(a, fn_name)
+    w_check(w, K)
+    m = _mode(a_mode)
+    out = _out(out, M, w.rows, dtype, a)
+    workspace = _workspace(workspace, L.gemm_w4a4_workspace(M, K, m), a)
+    _need_cuda(a, w.codes, w.scales, w.tscale, out, workspace)
+    _check(getattr(L, fn_name)(_ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                               _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                               _stream()))
+    return out
+
+
 def gemm_w4a4(a: torch.Tensor, w: PackedNVFP4, a_mode="row", dtype=torch.bfloat16,
               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """NVFP4 W4A4: quantize bf16 A on the device (per row by default), then C = A_q . W^T."""
+    return _w4a4("gemm_w4a4", a, w, a_mode, dtype, out, workspace, _weight_nv)
+
+
+def _prequant_nv(fn_name: str, a: PackedNVFP4, w, dtype, out):
     L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("gemm_w4a4 takes bfloat16 activations")
-    M, K = a.shape
-    m = _mode(a_mode)
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
-    if workspace is None:
-        workspace = gemm_w4a4_workspace(M, K, m, a.device)
-    _check(L.gemm_w4a4(_ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
-                       _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                       _stream()))
+    a.check("a")
+    _k_match(a.cols, w.cols)
+    out = _out(out, a.rows, w.rows, dtype, a.codes)
+    _need_cuda(a.codes, a.scales, a.tscale, w.codes, w.scales, w.tscale, out)
+    _check(getattr(L, fn_name)(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
+                               PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
+                               _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
+                               _out_dt(out.dtype), _ld(out), _stream()))
     return out
 
 
 def gemm_nvfp4_prequant(a: PackedNVFP4, w: PackedNVFP4, dtype=torch.bfloat16,
                         out: torch.Tensor | None = None) -> torch.Tensor:
-    L = lib()
-    if out is None:
-        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
-    _check(L.gemm_nvfp4_w4a4_prequant(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
-                                      PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
-                                      _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
-                                      _out_dt(out.dtype), _ld(out), _stream()))
-    return out
+    _weight_nv(w, a.cols)
+    return _prequant_nv("gemm_nvfp4_w4a4_prequant", a, w, dtype, out)
+
+
+def _weight_nv_dec(w: DecodeNVFP4, K: int):
+    w.check("w")
+    _k_match(K, w.cols)
 
 
 def gemm_w4a4_seg(a: torch.Tensor, w: DecodeNVFP4, a_mode="row", dtype=torch.bfloat16,
                   out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """gemm_w4a4 with W in the decode layout: the same result."""
-    L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("gemm_w4a4_seg takes bfloat16 activations")
-    M, K = a.shape
-    m = _mode(a_mode)
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
-    if workspace is None:
-        workspace = gemm_w4a4_workspace(M, K, m, a.device)
-    _check(L.gemm_w4a4_seg(_ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
-                           _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(), _stream()))
-    return out
+    return _w4a4("gemm_w4a4_seg", a, w, a_mode, dtype, out, workspace, _weight_nv_dec)
 
 
 def gemm_nvfp4_prequant_seg(a: PackedNVFP4, w: DecodeNVFP4, dtype=torch.bfloat16,
                             out: torch.Tensor | None = None) -> torch.Tensor:
     """gemm_nvfp4_prequant with W in the decode layout."""
-    L = lib()
-    if out is None:
-        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
-    _check(L.gemm_nvfp4_w4a4_prequant_seg(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
-                                          PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
-                                          _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
-                                          _out_dt(out.dtype), _ld(out), _stream()))
-    return out
+    _weight_nv_dec(w, a.cols)
+    return _prequant_nv("gemm_nvfp4_w4a4_prequant_seg", a, w, dtype, out)
 
 
 # --------------------------------------------------------------- MXFP4 -----
@@ -374,11 +479,17 @@ def gemm_nvfp4_prequant_seg(a: PackedNVFP4, w: DecodeNVFP4, dtype=torch.bfloat16
 def mxfp4_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None = None,
                    out: PackedMXFP4 | None = None) -> PackedMXFP4:
     L = lib()
-    _need_cuda(x, nonfinite)
+    _dt(x)
     rows, cols = x.shape
     if out is None:
         out = PackedMXFP4(torch.empty(rows, cols // 2, dtype=torch.uint8, device=x.device),
                           torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device), rows, cols)
+    if (out.rows, out.cols) != (rows, cols):
+        raise ValueError("out does not describe this tensor")
+    out.check("out")
+    if nonfinite is not None and (nonfinite.dtype != torch.int32 or nonfinite.numel() < 1):
+        raise ValueError("nonfinite must be an int32 tensor of at least one element")
+    _need_cuda(x, nonfinite, out.codes, out.scales)
     _check(L.mxfp4_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
                             _rule(rule), _ptr(nonfinite), _stream()))
     return out
@@ -386,28 +497,48 @@ def mxfp4_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None =
 
 def mxfp4_dequantize(p: PackedMXFP4, dtype=torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
     L = lib()
-    if out is None:
-        out = torch.empty(p.rows, p.cols, dtype=dtype, device=p.codes.device)
+    p.check("p")
+    out = _out(out, p.rows, p.cols, dtype, p.codes)
+    _need_cuda(p.codes, p.scales, out)
     _check(L.mxfp4_dequantize(_ptr(p.codes), _ptr(p.scales), p.rows, p.cols, _ptr(out),
                               _out_dt(out.dtype), _ld(out), _stream()))
     return out
 
 
+def _weight_mx(w: PackedMXFP4, K: int):
+    w.check("w")
+    _k_match(K, w.cols)
+
+
+def _mx_full(fn_name: str, ws_name: str, a, w, rule, dtype, out, workspace, w_check):
+    """The MXFP4 / W4A8 entry points that quantize bf16 A into a workspace first."""
+    L = lib()
+    M, K = _bf16_a(a, fn_name)
+    w_check(w, K)
+    r = _rule(rule)
+    out = _out(out, M, w.rows, dtype, a)
+    workspace = _workspace(workspace, getattr(L, ws_name)(M, K), a)
+    _need_cuda(a, w.codes, w.scales, out, workspace)
+    _check(getattr(L, fn_name)(_ptr(a), M, K, _ld(a), r, _ptr(w.codes), _ptr(w.scales), w.rows,
+                               _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
+                               _stream()))
+    return out
+
+
+def _mx_prequant(fn_name: str, a, w, dtype, out):
+    L = lib()
+    a.check("a")
+    _k_match(a.cols, w.cols)
+    out = _out(out, a.rows, w.rows, dtype, a.codes)
+    _need_cuda(a.codes, a.scales, w.codes, w.scales, out)
+    _check(getattr(L, fn_name)(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes), _ptr(w.scales),
+                               w.rows, _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    return out
+
+
 def mxfp4_gemm_w4a4(a: torch.Tensor, w: PackedMXFP4, rule="ocp", dtype=torch.bfloat16,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
-    L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("mxfp4_gemm_w4a4 takes bfloat16 activations")
-    M, K = a.shape
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
-    if workspace is None:
-        workspace = torch.empty(L.mxfp4_gemm_w4a4_workspace(M, K), dtype=torch.uint8, device=a.device)
-    _check(L.mxfp4_gemm_w4a4(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
-                             _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                             _stream()))
-    return out
+    return _mx_full("mxfp4_gemm_w4a4", "mxfp4_gemm_w4a4_workspace", a, w, rule, dtype, out, workspace, _weight_mx)
 
 
 def mxfp4_packed_a(ws: torch.Tensor, M: int, K: int) -> PackedMXFP4:
@@ -418,25 +549,18 @@ def mxfp4_packed_a(ws: torch.Tensor, M: int, K: int) -> PackedMXFP4:
 
 def mxfp4_gemm_prequant(a: PackedMXFP4, w: PackedMXFP4, dtype=torch.bfloat16,
                         out: torch.Tensor | None = None) -> torch.Tensor:
-    L = lib()
-    if out is None:
-        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
-    _check(L.mxfp4_gemm_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
-                                 _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
-                                 _stream()))
-    return out
+    w.check("w")
+    return _mx_prequant("mxfp4_gemm_prequant", a, w, dtype, out)
 
 
 def mxfp4_gemm_w4a16(a: torch.Tensor, w: PackedMXFP4, dtype=torch.bfloat16,
                      out: torch.Tensor | None = None) -> torch.Tensor:
     """C = A . W^T with bf16 A [M, K] and MXFP4 W [N, K] (K % 128 == 0)."""
     L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("mxfp4_gemm_w4a16 takes bfloat16 activations")
-    M, K = a.shape
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    M, K = _bf16_a(a, "mxfp4_gemm_w4a16")
+    _weight_mx(w, K)
+    out = _out(out, M, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, out)
     _check(L.mxfp4_gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
                               _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
@@ -451,15 +575,30 @@ class DecodeMXFP4:
     rows: int
     cols: int
 
+    def check(self, what="w"):
+        _u8(self.codes, (self.cols // 128, self.rows, 64), f"{what} codes")
+        _u8(self.scales, (self.cols // 128, self.rows, 4), f"{what} scales")
+        return self
+
+
+def _weight_mx_dec(w: DecodeMXFP4, K: int):
+    w.check("w")
+    _k_match(K, w.cols)
+
 
 def mxfp4_pack_decode(w: PackedMXFP4, out: DecodeMXFP4 | None = None) -> DecodeMXFP4:
     """Rewrite an MXFP4 weight into the decode layout (segment-major)."""
     L = lib()
+    w.check("w")
     N, K = w.rows, w.cols
     if out is None:
         dev = w.codes.device
         out = DecodeMXFP4(torch.empty(K // 128, N, 64, dtype=torch.uint8, device=dev),
                           torch.empty(K // 128, N, 4, dtype=torch.uint8, device=dev), N, K)
+    if (out.rows, out.cols) != (N, K):
+        raise ValueError("out does not describe this weight")
+    out.check("out")
+    _need_cuda(w.codes, w.scales, out.codes, out.scales)
     _check(L.mxfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
                                _stream()))
     return out
@@ -479,30 +618,15 @@ def mxfp4_gemm_w4a4_seg(a: torch.Tensor, w: DecodeMXFP4, rule="ocp", dtype=torch
                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """MXFP4 W4A4 GEMM with W in the decode (segment-major) layout; A is quantized
     into the workspace in that layout.  The same result as mxfp4_gemm_w4a4."""
-    L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("mxfp4_gemm_w4a4_seg takes bfloat16 activations")
-    M, K = a.shape
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
-    if workspace is None:
-        workspace = mxfp4_gemm_w4a4_seg_workspace(M, K, a.device)
-    _check(L.mxfp4_gemm_w4a4_seg(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
-                                 _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                                 _stream()))
-    return out
+    return _mx_full("mxfp4_gemm_w4a4_seg", "mxfp4_gemm_w4a4_seg_workspace", a, w, rule, dtype, out, workspace,
+                    _weight_mx_dec)
 
 
 def mxfp4_gemm_prequant_seg(a: DecodeMXFP4, w: DecodeMXFP4, dtype=torch.bfloat16,
                             out: torch.Tensor | None = None) -> torch.Tensor:
     """The GEMM half of mxfp4_gemm_w4a4_seg: A and W both in the segment-major layout."""
-    L = lib()
-    if out is None:
-        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
-    _check(L.mxfp4_gemm_prequant_seg(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
-                                     _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
-    return out
+    w.check("w")
+    return _mx_prequant("mxfp4_gemm_prequant_seg", a, w, dtype, out)
 
 
 def mxfp4_gemm_w4a16_decode(a: torch.Tensor, w: DecodeMXFP4, dtype=torch.bfloat16,
@@ -510,12 +634,10 @@ def mxfp4_gemm_w4a16_decode(a: torch.Tensor, w: DecodeMXFP4, dtype=torch.bfloat1
     """C = A . W^T for bf16 A [M, K] and an MXFP4 W in the decode layout (GEMV for M <= 16,
     the prefill GEMM on the same layout for larger M)."""
     L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("mxfp4_gemm_w4a16_decode takes bfloat16 activations")
-    M, K = a.shape
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
+    M, K = _bf16_a(a, "mxfp4_gemm_w4a16_decode")
+    _weight_mx_dec(w, K)
+    out = _out(out, M, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, out)
     _check(L.mxfp4_gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
                                      _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
@@ -529,16 +651,27 @@ class PackedMXFP8:
     rows: int
     cols: int
 
+    def check(self, what="MXFP8 tensor"):
+        _u8(self.codes, (self.rows, self.cols), f"{what} codes")
+        _u8(self.scales, (self.rows, self.cols // 32), f"{what} scales")
+        return self
+
 
 def mxfp8_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None = None,
                    out: PackedMXFP8 | None = None) -> PackedMXFP8:
     """MXFP8 (E4M3FN elements, E8M0 per 32) of an fp32 or bf16 [rows, cols] tensor."""
     L = lib()
-    _need_cuda(x)
+    _dt(x)
     rows, cols = x.shape
     if out is None:
         out = PackedMXFP8(torch.empty(rows, cols, dtype=torch.uint8, device=x.device),
                           torch.empty(rows, cols // 32, dtype=torch.uint8, device=x.device), rows, cols)
+    if (out.rows, out.cols) != (rows, cols):
+        raise ValueError("out does not describe this tensor")
+    out.check("out")
+    if nonfinite is not None and (nonfinite.dtype != torch.int32 or nonfinite.numel() < 1):
+        raise ValueError("nonfinite must be an int32 tensor of at least one element")
+    _need_cuda(x, nonfinite, out.codes, out.scales)
     _check(L.mxfp8_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
                             _rule(rule), _ptr(nonfinite), _stream()))
     return out
@@ -557,61 +690,28 @@ def mxfp8_packed_a(ws: torch.Tensor, M: int, K: int) -> PackedMXFP8:
 def mxfp4_gemm_w4a8(a: torch.Tensor, w: PackedMXFP4, rule="ocp", dtype=torch.bfloat16,
                     out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A8: bf16 A [M, K] quantized to MXFP8 on the device, MXFP4 W [N, K]."""
-    L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("mxfp4_gemm_w4a8 takes bfloat16 activations")
-    M, K = a.shape
-    if workspace is None:
-        workspace = mxfp4_gemm_w4a8_workspace(M, K, a.device)
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
-    _check(L.mxfp4_gemm_w4a8(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
-                             _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                             _stream()))
-    return out
+    return _mx_full("mxfp4_gemm_w4a8", "mxfp4_gemm_w4a8_workspace", a, w, rule, dtype, out, workspace, _weight_mx)
 
 
 def mxfp4_gemm_w4a8_prequant(a: PackedMXFP8, w: PackedMXFP4, dtype=torch.bfloat16,
                              out: torch.Tensor | None = None) -> torch.Tensor:
     """The GEMM half of mxfp4_gemm_w4a8 on an MXFP8 A."""
-    L = lib()
-    if out is None:
-        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
-    _check(L.mxfp4_gemm_w4a8_prequant(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
-                                      _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
-                                      _stream()))
-    return out
+    w.check("w")
+    return _mx_prequant("mxfp4_gemm_w4a8_prequant", a, w, dtype, out)
 
 
 def mxfp4_gemm_w4a8_seg(a: torch.Tensor, w: DecodeMXFP4, rule="ocp", dtype=torch.bfloat16,
                         out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """W4A8 with the MXFP4 W in the decode (segment-major) layout; the same result as mxfp4_gemm_w4a8."""
-    L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("mxfp4_gemm_w4a8_seg takes bfloat16 activations")
-    M, K = a.shape
-    if workspace is None:
-        workspace = mxfp4_gemm_w4a8_workspace(M, K, a.device)
-    if out is None:
-        out = torch.empty(M, w.rows, dtype=dtype, device=a.device)
-    _check(L.mxfp4_gemm_w4a8_seg(_ptr(a), M, K, _ld(a), _rule(rule), _ptr(w.codes), _ptr(w.scales), w.rows,
-                                 _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                                 _stream()))
-    return out
+    return _mx_full("mxfp4_gemm_w4a8_seg", "mxfp4_gemm_w4a8_workspace", a, w, rule, dtype, out, workspace,
+                    _weight_mx_dec)
 
 
 def mxfp4_gemm_w4a8_prequant_seg(a: PackedMXFP8, w: DecodeMXFP4, dtype=torch.bfloat16,
                                  out: torch.Tensor | None = None) -> torch.Tensor:
     """The GEMM half of mxfp4_gemm_w4a8_seg on an MXFP8 A."""
-    L = lib()
-    if out is None:
-        out = torch.empty(a.rows, w.rows, dtype=dtype, device=a.codes.device)
-    _check(L.mxfp4_gemm_w4a8_prequant_seg(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes),
-                                          _ptr(w.scales), w.rows, _ptr(out), _out_dt(out.dtype), _ld(out),
-                                          _stream()))
-    return out
+    w.check("w")
+    return _mx_prequant("mxfp4_gemm_w4a8_prequant_seg", a, w, dtype, out)
 
 
 # ------------------------------------------------------- grouped (MoE) -----
@@ -627,6 +727,12 @@ class ExpertsNVFP4:
     rows: int
     cols: int
 
+    def check(self, what="w"):
+        _u8(self.codes, (self.experts, self.rows, self.cols // 2), f"{what} codes")
+        _u8(self.scales, (self.experts, self.rows, self.cols // 16), f"{what} scales")
+        _f32_vec(self.tscale, self.experts, f"{what} tensor scales")
+        return self
+
 
 @dataclasses.dataclass
 class ExpertsMXFP4:
@@ -636,6 +742,11 @@ class ExpertsMXFP4:
     experts: int
     rows: int
     cols: int
+
+    def check(self, what="w"):
+        _u8(self.codes, (self.experts, self.rows, self.cols // 2), f"{what} codes")
+        _u8(self.scales, (self.experts, self.rows, self.cols // 32), f"{what} scales")
+        return self
 
 
 def nvfp4_quantize_experts(w: torch.Tensor) -> ExpertsNVFP4:
@@ -659,14 +770,20 @@ def mxfp4_quantize_experts(w: torch.Tensor, rule="ocp") -> ExpertsMXFP4:
     return ExpertsMXFP4(p.codes.view(E, N, K // 2), p.scales.view(E, N, K // 32), E, N, K)
 
 
-def _grouped_common(a_rows, group_offs, row_index):
-    _need_cuda(group_offs, row_index)
-    if group_offs.dtype != torch.int32 or not group_offs.is_contiguous():
-        raise TypeError("group_offs must be a contiguous int32 device tensor [groups + 1]")
-    if row_index is not None and (row_index.dtype != torch.int32 or not row_index.is_contiguous()):
-        raise TypeError("row_index must be a contiguous int32 device tensor [rows]")
+def _grouped_common(a_rows, K, w, group_offs, row_index):
+    """Checks the grouping and the experts; returns (grouped rows, groups)."""
+    if group_offs.dtype != torch.int32 or group_offs.dim() != 1 or not group_offs.is_contiguous():
+        raise TypeError("group_offs must be a contiguous 1-D int32 device tensor [groups + 1]")
+    if row_index is not None and (row_index.dtype != torch.int32 or row_index.dim() != 1
+                                  or not row_index.is_contiguous()):
+        raise TypeError("row_index must be a contiguous 1-D int32 device tensor [rows]")
+    groups = group_offs.numel() - 1
+    if groups != w.experts:
+        raise ValueError(f"group_offs describes {groups} groups but the weight holds {w.experts} experts")
+    w.check("w")
+    _k_match(K, w.cols)
     rows = row_index.numel() if row_index is not None else a_rows
-    return rows, group_offs.numel() - 1
+    return rows, groups
 
 
 def nvfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch.Tensor,
@@ -674,11 +791,11 @@ def nvfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch
                              out: torch.Tensor | None = None) -> torch.Tensor:
     """C[t] = A[row_index[t]] . W_e^T for the grouped rows t of group e (bf16 A, NVFP4 experts)."""
     L = lib()
-    _need_cuda(a)
-    rows, groups = _grouped_common(a.shape[0], group_offs, row_index)
-    if out is None:
-        out = torch.empty(rows, w.rows, dtype=dtype, device=a.device)
-    _check(L.nvfp4_grouped_gemm_w4a16(_ptr(a), a.shape[0], a.shape[1], _ld(a), _ptr(row_index), _ptr(group_offs),
+    a_rows, K = _bf16_a(a, "nvfp4_grouped_gemm_w4a16")
+    rows, groups = _grouped_common(a_rows, K, w, group_offs, row_index)
+    out = _out(out, rows, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, w.tscale, group_offs, row_index, out)
+    _check(L.nvfp4_grouped_gemm_w4a16(_ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
                                       groups, rows, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                                       _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
     return out
@@ -689,11 +806,11 @@ def mxfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsMXFP4, group_offs: torch
                              out: torch.Tensor | None = None) -> torch.Tensor:
     """As nvfp4_grouped_gemm_w4a16 with MXFP4 experts."""
     L = lib()
-    _need_cuda(a)
-    rows, groups = _grouped_common(a.shape[0], group_offs, row_index)
-    if out is None:
-        out = torch.empty(rows, w.rows, dtype=dtype, device=a.device)
-    _check(L.mxfp4_grouped_gemm_w4a16(_ptr(a), a.shape[0], a.shape[1], _ld(a), _ptr(row_index), _ptr(group_offs),
+    a_rows, K = _bf16_a(a, "mxfp4_grouped_gemm_w4a16")
+    rows, groups = _grouped_common(a_rows, K, w, group_offs, row_index)
+    out = _out(out, rows, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, group_offs, row_index, out)
+    _check(L.mxfp4_grouped_gemm_w4a16(_ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
                                       groups, rows, _ptr(w.codes), _ptr(w.scales), w.rows, _ptr(out),
                                       _out_dt(out.dtype), _ld(out), _stream()))
     return out
@@ -708,15 +825,12 @@ def nvfp4_grouped_gemm_w4a4(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch.
                             out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """NVFP4 W4A4 grouped GEMM: every A row quantized once per row, then gathered per group."""
     L = lib()
-    _need_cuda(a)
-    if a.dtype != torch.bfloat16:
-        raise TypeError("nvfp4_grouped_gemm_w4a4 takes bfloat16 activations")
-    rows, groups = _grouped_common(a.shape[0], group_offs, row_index)
-    if workspace is None:
-        workspace = nvfp4_grouped_gemm_w4a4_workspace(a.shape[0], a.shape[1], a.device)
-    if out is None:
-        out = torch.empty(rows, w.rows, dtype=dtype, device=a.device)
-    _check(L.nvfp4_grouped_gemm_w4a4(_ptr(a), a.shape[0], a.shape[1], _ld(a), _ptr(row_index), _ptr(group_offs),
+    a_rows, K = _bf16_a(a, "nvfp4_grouped_gemm_w4a4")
+    rows, groups = _grouped_common(a_rows, K, w, group_offs, row_index)
+    out = _out(out, rows, w.rows, dtype, a)
+    workspace = _workspace(workspace, L.nvfp4_grouped_gemm_w4a4_workspace(a_rows, K), a)
+    _need_cuda(a, w.codes, w.scales, w.tscale, group_offs, row_index, out, workspace)
+    _check(L.nvfp4_grouped_gemm_w4a4(_ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
                                      groups, rows, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                                      _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
                                      _stream()))
@@ -730,9 +844,10 @@ def nvfp4_grouped_gemm_w4a4_prequant(a: PackedNVFP4, w: ExpertsNVFP4, group_offs
     L = lib()
     if not a.per_row:
         raise ValueError("the grouped W4A4 GEMM takes a per-row NVFP4 A")
-    rows, groups = _grouped_common(a.rows, group_offs, row_index)
-    if out is None:
-        out = torch.empty(rows, w.rows, dtype=dtype, device=a.codes.device)
+    a.check("a")
+    rows, groups = _grouped_common(a.rows, a.cols, w, group_offs, row_index)
+    out = _out(out, rows, w.rows, dtype, a.codes)
+    _need_cuda(a.codes, a.scales, a.tscale, w.codes, w.scales, w.tscale, group_offs, row_index, out)
     _check(L.nvfp4_grouped_gemm_w4a4_prequant(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale), a.rows, a.cols,
                                               _ptr(row_index), _ptr(group_offs), groups, rows, _ptr(w.codes),
                                               _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),

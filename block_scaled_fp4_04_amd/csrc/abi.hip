@@ -192,6 +192,17 @@ fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
 
 namespace {
 
+// Both kernels behind the decode-layout entry points address A and the weight
+// with 32-bit byte offsets (the GEMV's buffer descriptors hold 32-bit sizes, and
+// its out-of-range offset 2^31 must lie past every operand): A's bytes up to its
+// last element and the weight's code bytes stay below 2^31 for every M.
+fp4_status check_decode_limits(int64_t M, int64_t K, int64_t lda, int64_t N)
+{
+    if ((M - 1) * lda * 2 + K * 2 >= k2GiB || M * lda * 2 >= k2GiB) return FP4_ERR_SHAPE;
+    if (N * (K / 2) >= k2GiB) return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
 // M > 16 on a decode-layout weight: the prefill ring kernel reading that layout
 fp4_status w4a16_seg_prefill(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
                              const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c, fp4_dtype ct,
@@ -224,6 +235,7 @@ fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, c
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
     if (M <= 16 && K > 8192) return FP4_ERR_SHAPE;
     FP4_TRY(check_matrix(a, M, K, lda, 2));
+    FP4_TRY(check_decode_limits(M, K, lda, N));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
     if (!w_tscale) return FP4_ERR_NULL;
     FP4_TRY(check_device());
@@ -260,6 +272,7 @@ fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t 
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
     if (M <= 16 && K > 8192) return FP4_ERR_SHAPE;
     FP4_TRY(check_matrix(a, M, K, lda, 2));
+    FP4_TRY(check_decode_limits(M, K, lda, N));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
     FP4_TRY(check_device());
     if (M > 16) return w4a16_seg_prefill(a, M, K, lda, w_codes_p, w_scales_p, nullptr, N, c, ct, ldc, true, stream);
@@ -694,6 +707,19 @@ fp4_status check_grouped(int64_t a_rows, int64_t K, const int32_t *row_index, co
     return FP4_OK;
 }
 
+// The grouped kernel's own limits, checked here so that nothing (not even the
+// W4A4 activation quantizer) is launched for a call the kernel would refuse:
+// 32-bit byte offsets into A (its bf16 rows, or its packed codes for W4A4) and
+// into one group's weight codes, and a grid below 2^31 workgroups.
+fp4_status check_grouped_limits(int64_t a_rows, int64_t K, int64_t lda, bool a_fp4, int64_t groups,
+                                int64_t rows, int64_t N)
+{
+    const int64_t a_bytes = a_fp4 ? a_rows * (K / 2) : a_rows * lda * 2;
+    if (a_bytes >= k2GiB || N * (K / 2) >= k2GiB) return FP4_ERR_SHAPE;
+    if (((rows + 127) / 128 + groups) * ((N + 255) / 256) >= k2GiB) return FP4_ERR_SHAPE;
+    return FP4_OK;
+}
+
 NvGemmArgs grouped_args(int64_t a_rows, int64_t K, const int32_t *row_index, const int32_t *group_offs,
                         int64_t groups, int64_t rows, const uint8_t *w_codes, const uint8_t *w_scales,
                         const float *w_tscale, int64_t N, void *c, fp4_dtype ct, int64_t ldc)
@@ -727,6 +753,7 @@ fp4_status nvfp4_grouped_gemm_w4a16(const void *a, int64_t a_rows, int64_t K, in
     FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 64, c, ct, ldc, &empty));
     if (empty) return FP4_OK;
     FP4_TRY(check_matrix(a, a_rows, K, lda, 2));
+    FP4_TRY(check_grouped_limits(a_rows, K, lda, false, groups, rows, N));
     FP4_TRY(check_packed(w_codes, w_scales));
     if (!w_tscale) return FP4_ERR_NULL;
     FP4_TRY(check_device());
@@ -746,6 +773,7 @@ fp4_status mxfp4_grouped_gemm_w4a16(const void *a, int64_t a_rows, int64_t K, in
     FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 128, c, ct, ldc, &empty));
     if (empty) return FP4_OK;
     FP4_TRY(check_matrix(a, a_rows, K, lda, 2));
+    FP4_TRY(check_grouped_limits(a_rows, K, lda, false, groups, rows, N));
     FP4_TRY(check_packed(w_codes, w_scales));
     FP4_TRY(check_device());
     NvGemmArgs g = grouped_args(a_rows, K, row_index, group_offs, groups, rows, w_codes, w_scales, nullptr, N, c,
@@ -765,6 +793,7 @@ fp4_status nvfp4_grouped_gemm_w4a4_prequant(const uint8_t *a_codes, const uint8_
     bool empty = false;
     FP4_TRY(check_grouped(a_rows, K, row_index, group_offs, groups, rows, N, 64, c, ct, ldc, &empty));
     if (empty) return FP4_OK;
+    FP4_TRY(check_grouped_limits(a_rows, K, K, true, groups, rows, N));
     FP4_TRY(check_packed(a_codes, a_scales));
     FP4_TRY(check_packed(w_codes, w_scales));
     if (!a_tscale || !w_tscale) return FP4_ERR_NULL;
@@ -794,6 +823,7 @@ fp4_status nvfp4_grouped_gemm_w4a4(const void *a, int64_t a_rows, int64_t K, int
     if (empty) return FP4_OK;
     FP4_TRY(check_matrix(a, a_rows, K, lda, 2));
     if (a_rows * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_grouped_limits(a_rows, K, lda, true, groups, rows, N));  // before A is quantized
     FP4_TRY(check_packed(w_codes, w_scales));
     if (!w_tscale) return FP4_ERR_NULL;
     if (!ws || !aligned16(ws) || ws_bytes < nvfp4_grouped_gemm_w4a4_workspace(a_rows, K))

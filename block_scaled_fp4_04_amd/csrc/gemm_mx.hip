@@ -570,13 +570,8 @@ constexpr size_t kMxLds = (size_t)4 * MBM * kRowBytes + (size_t)2 * (MBM + MBN) 
 template <bool ALIGNED>
 static fp4_status launch_mx(const MxGemmArgs &g, hipStream_t st)
 {
-    static bool attr_set = false;  // benign race: every setter writes the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)k_mx_gemm<ALIGNED>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kMxLds) != hipSuccess)
-            return FP4_ERR_HIP;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};  // per device
+    if (!set_max_lds_once((const void *)k_mx_gemm<ALIGNED>, (int)kMxLds, lds_set)) return FP4_ERR_HIP;
     const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
     hipLaunchKernelGGL(k_mx_gemm<ALIGNED>, dim3(tiles), dim3(256), kMxLds, st, g);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;

@@ -532,13 +532,8 @@ template <int S>
 static fp4_status launch_decode_persist(const NvGemmArgs &g, hipStream_t st)
 {
     using C = PersistCfg<S>;
-    static bool attr_set = false;  // benign race: every setter writes the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)k_nv_decode_persist<S>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)C::kLds) != hipSuccess)
-            return FP4_ERR_HIP;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};  // per device
+    if (!set_max_lds_once((const void *)k_nv_decode_persist<S>, (int)C::kLds, lds_set)) return FP4_ERR_HIP;
     // enough workgroups that none owns more than kPersistMaxT tiles, at least one per CU
     int64_t grid = (g.N + 16 * kPersistMaxT - 1) / (16 * kPersistMaxT);
     if (grid < 256) grid = 256;
@@ -1327,13 +1322,8 @@ constexpr size_t kGemmLds = (size_t)2 * (BM + BN) * BK * sizeof(uint16_t);  // 1
 template <bool A_FP4, bool ALIGNED>
 static fp4_status launch_prefill(const NvGemmArgs &g, hipStream_t st)
 {
-    static bool attr_set = false;  // benign race: every setter writes the same value
-    if (!attr_set) {
-        if (hipFuncSetAttribute((const void *)k_nv_gemm<A_FP4, ALIGNED>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)kGemmLds) != hipSuccess)
-            return FP4_ERR_HIP;
-        attr_set = true;
-    }
+    static std::atomic<uint64_t> lds_set{0};  // per device
+    if (!set_max_lds_once((const void *)k_nv_gemm<A_FP4, ALIGNED>, (int)kGemmLds, lds_set)) return FP4_ERR_HIP;
     const int tiles = (int)(((g.M + BM - 1) / BM) * ((g.N + BN - 1) / BN));
     hipLaunchKernelGGL((k_nv_gemm<A_FP4, ALIGNED>), dim3(tiles), dim3(256), kGemmLds, st, g);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;

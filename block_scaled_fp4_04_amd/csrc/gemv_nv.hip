@@ -376,15 +376,15 @@ static void launch_gemv_nt(const GemvArgs &g, int nt, unsigned grid, hipStream_t
 
 int device_cu_count()
 {
-    static int cache[64] = {0};  // per device; benign race: every writer stores the same value
+    static std::atomic<int> cache[64];  // per device; 0 until first asked (zero-initialized: static storage)
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (!cache[dev]) {
-        int n = 0;
+    int n = cache[dev].load(std::memory_order_relaxed);
+    if (!n) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-        cache[dev] = n;
+        cache[dev].store(n, std::memory_order_relaxed);  // every writer stores the same value
     }
-    return cache[dev];
+    return n;
 }
 
 fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st)

@@ -4,6 +4,8 @@
 
 #include <stdint.h>
 
+#include <atomic>
+
 #include "fp4blk.h"
 
 namespace fp4k {
@@ -81,6 +83,21 @@ fp4_status launch_grouped_gemm(const NvGemmArgs &g, int fmt, hipStream_t st);
 
 // compute units of the current device (cached per device; 256 if unknown)
 int device_cu_count();
+
+// Raises kernel `fn`'s dynamic LDS limit to `bytes` on the current device, once
+// per device: `done` holds one bit per device id (0..63).  Two threads making the
+// first call on a device at once may both set the attribute, which is harmless
+// (the same value); the bit is published with release / acquire ordering.
+inline bool set_max_lds_once(const void *fn, int bytes, std::atomic<uint64_t> &done)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return false;
+    const uint64_t bit = uint64_t(1) << dev;
+    if (done.load(std::memory_order_acquire) & bit) return true;
+    if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes) != hipSuccess) return false;
+    done.fetch_or(bit, std::memory_order_release);
+    return true;
+}
 
 // W4A16 decode GEMV over weights in the decode layout (gemv_nv.hip)
 struct GemvArgs {

@@ -60,6 +60,59 @@ __device__ __forceinline__ float amax8(const float v[8], int &bad)
     return m;
 }
 
+// ------------------------------------------- division by a shared divisor --
+//
+// Every value of a 16-block is divided by the same step d = fl32(E4M3(b) s), and
+// every block byte of a row or tensor by the same 6 s.  gfx950's correctly
+// rounded fp32 division (as the compiler emits it for a / b) is: pre-scale both
+// operands (div_scale), y = rcp(b) refined by one Newton step, q0 = a y, then two
+// remainder corrections q <- q + (a - b q) y by FMA, and a final special-value
+// fix-up (div_fixup).  Only the product and the corrections depend on a, so
+// rcp_refined() computes y once per divisor and div_refined() repeats the rest
+// per value: a product and four FMAs in place of about eleven instructions.
+// The pre-scaling is the identity (and the fix-up returns its input) when b and
+// 1/b are normal, a is zero or not tiny (|a| >= 2^-103) and a / b is neither
+// denormal nor within 2^96 of overflow.  nv_fast_scale(s) admits tensor scales
+// s in [2^-50, 2^50]; every divisor is then in [2^-59, 2^59], and every quotient
+// that can decide an E2M1 code or an E4M3 byte (a / b >= 2^-11) has a normal
+// numerator, so it is formed exactly as by the division.  Smaller quotients
+// land on code 0 / byte 0 either way.  Other scales take the IEEE division.
+
+__device__ __forceinline__ bool nv_fast_scale(float s) { return s >= 0x1p-50f && s <= 0x1p50f; }
+
+__device__ __forceinline__ float rcp_refined(float b)
+{
+    const float y0 = __builtin_amdgcn_rcpf(b);
+    return __builtin_fmaf(__builtin_fmaf(-b, y0, 1.0f), y0, y0);
+}
+
+__device__ __forceinline__ float div_refined(float a, float b, float y)
+{
+    const float q0 = a * y;
+    const float q1 = __builtin_fmaf(__builtin_fmaf(-b, q0, a), y, q0);
+    return __builtin_fmaf(__builtin_fmaf(-b, q1, a), y, q1);
+}
+
+// The E4M3 block byte and the codes of one 8-element unit (lanes 2i, 2i + 1 hold
+// one 16-block) on the fast path: bm8 = max|v| over the unit, y6 = rcp_refined(6 s).
+// A block whose byte is 0 divides by s 2^20 instead of 0: its quotients are then
+// below 2^-27 and every code is the sign alone, as the definition asks.
+__device__ __forceinline__ uint32_t nvfp4_unit_fast(const float v[8], float bm8, float s, float six_s, float y6,
+                                                    uint32_t &code_word)
+{
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    const float bm = fmaxf(bm8, xor1(bm8));
+    const uint32_t b = e4m3x4_code_sat(div_refined(bm, six_s, y6), 0.0f, 0.0f, 0.0f) & 0xFFu;
+    const f32x2 bv = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+    const float d = b ? bv[0] * s : s * 0x1p20f;
+    const float y = rcp_refined(d);
+    float q[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = __builtin_copysignf(div_refined(__builtin_fabsf(v[i]), d, y), v[i]);
+    code_word = e2m1x8_code(q);
+    return b;
+}
+
 // Codes of 8 values under divisor d (d == 0: signed zeros), nibble i = value i.
 __device__ __forceinline__ uint32_t nvfp4_codes8(const float v[8], float d)
 {
@@ -140,6 +193,8 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_tensor(const T *__restrict_
 {
     const float s = tscale[0];
     const float six_s = 6.0f * s;
+    const bool fast = nv_fast_scale(s);
+    const float y6 = rcp_refined(six_s);
     for (uint32_t u = blockIdx.x * 256u + threadIdx.x; u < units; u += gridDim.x * 256u) {
         const uint32_t r = fdiv(u, cv);
         const uint32_t c8 = u - r * cv.d;
@@ -147,7 +202,13 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_tensor(const T *__restrict_
         Vec8<T>::load(x + (int64_t)r * ldx + (int64_t)c8 * 8, v);
         uint32_t w;
         uint8_t *sp = scales + (int64_t)r * (cols / 16) + (c8 >> 1);
-        nvfp4_unit(v, s, six_s, &w, sp, (c8 & 1u) == 0u);
+        if (fast) {
+            int dummy = 0;
+            const uint32_t b = nvfp4_unit_fast(v, amax8(v, dummy), s, six_s, y6, w);
+            if ((c8 & 1u) == 0u) *sp = (uint8_t)b;
+        } else {
+            nvfp4_unit(v, s, six_s, &w, sp, (c8 & 1u) == 0u);
+        }
         *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
     }
 }
@@ -188,6 +249,110 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_rows(const T *__restrict__ 
             uint32_t w;
             nvfp4_unit(v, s, six_s, &w, scales + r * (cols / 16) + (u >> 1), (u & 1) == 0);
             *reinterpret_cast<uint32_t *>(codes + r * (cols / 2) + u * 4) = w;
+        }
+    }
+}
+
+// Per-row mode for rows of at most 512 U elements: one wave per row, four rows per
+// workgroup.  Lane l owns the 8-element units l, l + 64, ..., l + 64 (U - 1) of
+// its row; all U loads go out at once (a buffer descriptor over the row returns
+// zeros past its end), the row maximum is a wave reduction, and the row is
+// quantized from registers: it is read from memory once and no barrier is
+// needed.  bf16 rows keep their packed bits (maxima on the 16-bit magnitudes,
+// which order like the values; 0x7F80 and above is Inf or NaN).
+template <typename T, int U>
+__global__ __launch_bounds__(256) void k_nvfp4_quant_rows_w(const T *__restrict__ x, int64_t rows, int cols,
+                                                            int64_t ldx, uint8_t *__restrict__ codes,
+                                                            uint8_t *__restrict__ scales, float *__restrict__ tscale,
+                                                            int32_t *__restrict__ nonfinite)
+{
+    constexpr bool BF = sizeof(T) == 2;
+    constexpr int WPU = BF ? 1 : 2;  // 16-byte loads per unit
+    const int lane = threadIdx.x & 63;
+    const int64_t r = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    if (r >= rows) return;  // whole waves
+    const int units = cols >> 3;
+    const __amdgpu_buffer_rsrc_t rx =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(x + r * ldx), (short)0, cols * (int)sizeof(T), 0x00020000);
+    u32x4 raw[U][WPU];
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+#pragma unroll
+        for (int h = 0; h < WPU; ++h)
+            raw[i][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, (lane + 64 * i) * 16 * WPU + 16 * h, 0, 0);
+
+    float um[U];  // max |v| of each unit
+    float m = 0.0f;
+    int bad = 0;
+#pragma unroll
+    for (int i = 0; i < U; ++i) {
+        if constexpr (BF) {
+            typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+            u16x2 h[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const uint32_t mag = raw[i][0][k] & 0x7FFF7FFFu;
+                __builtin_memcpy(&h[k], &mag, 4);
+            }
+            const u16x2 t = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
+                                                      __builtin_elementwise_max(h[2], h[3]));
+            const uint32_t mb = t[0] > t[1] ? t[0] : t[1];
+            bad |= mb >= 0x7F80u;
+            um[i] = __uint_as_float(mb << 16);
+        } else {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[k] = __uint_as_float(raw[i][0][k]);
+                v[4 + k] = __uint_as_float(raw[i][1][k]);
+            }
+            um[i] = amax8(v, bad);
+        }
+        m = fmaxf(m, um[i]);
+    }
+    if (bad && nonfinite) *nonfinite = 1;
+    m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(m))));  // every lane holds it
+    const float s = m / 2688.0f;
+    const float six_s = 6.0f * s;
+    if (lane == 0) tscale[r] = s;
+    uint8_t *cr = codes + r * (cols / 2);
+    uint8_t *sr = scales + r * (cols / 16);
+    auto unpack = [&](int i, float (&v)[8]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            if constexpr (BF) {
+                v[2 * k] = __uint_as_float(raw[i][0][k] << 16);
+                v[2 * k + 1] = __uint_as_float(raw[i][0][k] & 0xFFFF0000u);
+            } else {
+                v[k] = __uint_as_float(raw[i][0][k]);
+                v[4 + k] = __uint_as_float(raw[i][1][k]);
+            }
+        }
+    };
+    auto store = [&](int u, uint32_t w, uint32_t b) {
+        if (u < units) {
+            *reinterpret_cast<uint32_t *>(cr + u * 4) = w;
+            if ((u & 1) == 0) sr[u >> 1] = (uint8_t)b;
+        }
+    };
+    if (nv_fast_scale(s)) {
+        const float y6 = rcp_refined(six_s);
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            float v[8];
+            unpack(i, v);
+            uint32_t w;
+            const uint32_t b = nvfp4_unit_fast(v, um[i], s, six_s, y6, w);
+            store(lane + 64 * i, w, b);
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < U; ++i) {
+            float v[8];
+            unpack(i, v);
+            const float bm = fmaxf(um[i], xor1(um[i]));
+            const uint32_t b = bm == 0.0f ? 0u : e4m3x4_code_sat(bm / six_s, 0.0f, 0.0f, 0.0f) & 0xFFu;
+            store(lane + 64 * i, nvfp4_codes8(v, e4m3_value(b) * s), b);
         }
     }
 }
@@ -386,12 +551,51 @@ static unsigned grid_for(uint64_t units, unsigned cap)
     return g ? (unsigned)g : 1u;
 }
 
+// The one-wave-per-row quantizer for rows of up to 8192 bf16 or 4096 fp32 values;
+// false when the row is longer (the two-pass kernel takes it).
+template <typename T, int U>
+static void launch_rows_w(const void *x, int64_t rows, int64_t cols, int64_t ldx, uint8_t *codes, uint8_t *scales,
+                          float *tscale, int32_t *nonfinite, hipStream_t st)
+{
+    const int64_t g = (rows + 3) / 4;
+    hipLaunchKernelGGL((k_nvfp4_quant_rows_w<T, U>), dim3((unsigned)g), dim3(256), 0, st, (const T *)x, rows,
+                       (int)cols, ldx, codes, scales, tscale, nonfinite);
+}
+
+static bool launch_quant_rows_w(const void *x, bool bf, int64_t rows, int64_t cols, int64_t ldx, uint8_t *codes,
+                                uint8_t *scales, float *tscale, int32_t *nonfinite, hipStream_t st)
+{
+    const int64_t u = (cols / 8 + 63) / 64;  // units per lane
+    if ((rows + 3) / 4 > INT32_MAX || u > (bf ? 16 : 8)) return false;
+#define FP4_ROWS_W(T, U) launch_rows_w<T, U>(x, rows, cols, ldx, codes, scales, tscale, nonfinite, st)
+    if (bf) {
+        if (u <= 1) FP4_ROWS_W(uint16_t, 1);
+        else if (u <= 2) FP4_ROWS_W(uint16_t, 2);
+        else if (u <= 4) FP4_ROWS_W(uint16_t, 4);
+        else if (u <= 6) FP4_ROWS_W(uint16_t, 6);
+        else if (u <= 8) FP4_ROWS_W(uint16_t, 8);
+        else if (u <= 10) FP4_ROWS_W(uint16_t, 10);
+        else if (u <= 12) FP4_ROWS_W(uint16_t, 12);
+        else FP4_ROWS_W(uint16_t, 16);
+    } else {
+        if (u <= 1) FP4_ROWS_W(float, 1);
+        else if (u <= 2) FP4_ROWS_W(float, 2);
+        else if (u <= 4) FP4_ROWS_W(float, 4);
+        else if (u <= 6) FP4_ROWS_W(float, 6);
+        else FP4_ROWS_W(float, 8);
+    }
+#undef FP4_ROWS_W
+    return true;
+}
+
 fp4_status launch_nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                                  int64_t ldx, uint8_t *codes, uint8_t *scales, float *tscale,
                                  fp4_scale_mode mode, void *ws, int32_t *nonfinite,
                                  hipStream_t st)
 {
     const bool bf = xt == FP4_BF16;
+    if (mode == FP4_SCALE_PER_ROW && launch_quant_rows_w(x, bf, rows, cols, ldx, codes, scales, tscale, nonfinite, st))
+        return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
     if (mode == FP4_SCALE_PER_ROW) {
         const unsigned g = rows > 65536 ? 65536u : (unsigned)rows;
         if (bf)

@@ -111,9 +111,17 @@ fp4_status nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t col
                           uint8_t *codes, uint8_t *scales, float *tscale, fp4_scale_mode mode,
                           void *ws, size_t ws_bytes, int32_t *nonfinite, hipStream_t stream);
 
-/* NVFP4 dequantize: y = fl32(fl32(E2M1(c) * E4M3(s)) * tscale) (the inner
- * product is exact), stored as fp32 or rounded to nearest even into bf16 (yt).
- *  y [rows][ldy] out. */
+/* NVFP4 dequantize ("NVFP4", Technical principle: a value is its E2M1 element
+ * times its micro-block's E4M3 scale times the FP32 tensor scale; the W4A16
+ * path of the aixq.cc article, "Core difference: W4A4 vs W4A16", restores the
+ * weights to 16 bits this way):
+ *  y = fl32(fl32(E2M1(c) * E4M3(s)) * tscale) (the inner product is exact),
+ *  stored as fp32 or rounded to nearest even into bf16 (yt).
+ *  codes [rows][cols/2], scales [rows][cols/16], tscale [1] (FP4_SCALE_PER_TENSOR)
+ *  or [rows] (FP4_SCALE_PER_ROW): device, read only.  cols % 16 == 0.
+ *  y [rows][ldy] out (ldy >= cols, 16-byte aligned rows), caller-owned.
+ * Errors (host, nothing launched): FP4_ERR_NULL, FP4_ERR_SHAPE, FP4_ERR_LAYOUT,
+ * FP4_ERR_DTYPE as for nvfp4_quantize. */
 fp4_status nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tscale,
                             fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
                             fp4_dtype yt, int64_t ldy, hipStream_t stream);
@@ -148,7 +156,10 @@ fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
  * gemm_w4a16 gives on the row-major weight, bit for bit), so one packed weight
  * serves both.  Same arithmetic and tolerance as gemm_w4a16 (each weight widened
  * exactly to E2M1 * E4M3 in bfloat16, fp32 accumulation, times w_tscale).
- * FP4_ERR_SHAPE for M * lda or N * K / 2 bytes of 2 GiB or more when M > 16. */
+ * FP4_ERR_SHAPE, checked on the host before anything is launched, for any M
+ * when A spans 2 GiB or more (M * lda * 2 or (M - 1) * lda * 2 + 2 K bytes) or
+ * the weight codes do (N * K / 2 bytes): both kernels address the operands with
+ * 32-bit byte offsets. */
 fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
                              const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,
                              fp4_dtype ct, int64_t ldc, hipStream_t stream);
@@ -203,7 +214,13 @@ fp4_status mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t col
                           uint8_t *codes, uint8_t *scales, fp4_mx_rule rule, int32_t *nonfinite,
                           hipStream_t stream);
 
-/* MXFP4 dequantize: y = E2M1(c) * 2^(s-127) (exact when in range), fp32 or bf16. */
+/* MXFP4 dequantize (eefocus.com edge-FP4 article, "FP4 as the next core
+ * standard": each 32-element block shares one E8M0 power-of-two scale):
+ *  y = E2M1(c) * 2^(s-127) (exact when in range), fp32, or bf16 by round to
+ *  nearest even.  codes [rows][cols/2], scales [rows][cols/32]: device, read
+ *  only; cols % 32 == 0.  y [rows][ldy] out (ldy >= cols, 16-byte aligned rows).
+ * Errors (host, nothing launched): FP4_ERR_NULL, FP4_ERR_SHAPE, FP4_ERR_LAYOUT,
+ * FP4_ERR_DTYPE. */
 fp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t rows,
                             int64_t cols, void *y, fp4_dtype yt, int64_t ldy, hipStream_t stream);
 
@@ -246,7 +263,8 @@ fp4_status mxfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
 /* MXFP4 W4A16 on a weight in the MXFP4 decode layout: C = A . W^T, K % 128 == 0;
  * the decode GEMV for 1 <= M <= 16 (K <= 8192), the prefill GEMM on the same
  * layout for larger M (mxfp4_gemm_w4a16's result, bit for bit).  Arithmetic and
- * tolerance as mxfp4_gemm_w4a16. */
+ * tolerance as mxfp4_gemm_w4a16.  FP4_ERR_SHAPE for the same 2 GiB limits as
+ * gemm_w4a16_decode, for any M, checked before anything is launched. */
 fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, const uint8_t *w_codes_p,
                                    const uint8_t *w_scales_p, int64_t N, void *c, fp4_dtype ct, int64_t ldc,
                                    hipStream_t stream);
@@ -341,8 +359,10 @@ fp4_status mxfp4_gemm_w4a8_prequant_seg(const uint8_t *a_codes, const uint8_t *a
  * and the output dtype check out, touching nothing (A, W, C may be null then).
  * groups <= 65536.
  * Errors (checked on the host, nothing launched): FP4_ERR_SHAPE for K not a
- * multiple of 64 (NVFP4) or 128 (MXFP4), A past 2 GiB or one group's weight
- * codes past 2 GiB; FP4_ERR_NULL, FP4_ERR_LAYOUT as the other GEMMs.
+ * multiple of 64 (NVFP4) or 128 (MXFP4), A past 2 GiB (its bf16 rows, or for
+ * W4A4 its packed codes), one group's weight codes past 2 GiB, or a tile grid of
+ * 2^31 workgroups or more; FP4_ERR_NULL, FP4_ERR_LAYOUT as the other GEMMs.
+ * nvfp4_grouped_gemm_w4a4 checks all of these before its quantizer runs.
  * Tolerance as the ungrouped GEMMs, row by row. */
 
 /* NVFP4 weights, bf16 A [a_rows][lda]: each weight widened exactly to bf16,

@@ -202,9 +202,19 @@ def test_decode_layout_validation(L):
     assert gd(lda=128) == LAYOUT
     assert gd(ws=FAKE + 4) == LAYOUT
     assert gd(ct=9) == DTYPE
+    # 32-bit byte offsets in both kernels: refused for every M, before any device call
+    assert gd(M=1, K=8192, lda=8192, N=524288, ldc=524288) == SHAPE          # weight codes of exactly 2 GiB
+    assert gd(M=1, K=8192, lda=8192, N=1048576, ldc=1048576) == SHAPE         # 4 GiB: sizes would wrap
+    assert gd(M=16, K=256, lda=1 << 26) == SHAPE                 # A spans 15 * 2^27 bytes
+    assert gd(M=17, K=256, lda=1 << 26) == SHAPE
+    assert L.mxfp4_gemm_w4a16_decode(FAKE, 1, 8192, 8192, FAKE, FAKE, 524288, FAKE, 1, 524288, None) == SHAPE
+    assert L.mxfp4_gemm_w4a16_decode(FAKE, 4, 256, 1 << 28, FAKE, FAKE, 32, FAKE, 1, 32, None) == SHAPE
     if not torch.cuda.is_available():
         # M > 16 is the prefill GEMM on the same layout, with no K <= 8192 limit
         assert gd() == NO_DEVICE and gd(M=17) == NO_DEVICE and gd(M=4096, K=8320, lda=8320) == NO_DEVICE
+        # just under the limits
+        assert gd(M=1, K=8192, lda=8192, N=524287, ldc=524287) == NO_DEVICE
+        assert gd(M=2, K=256, lda=(1 << 29) - 256) == NO_DEVICE
 
 
 def test_mxfp4_validation(L):
@@ -406,6 +416,12 @@ def test_grouped_validation(L):
 
     assert q(work_bytes=100) == WORKSPACE
     assert q(groups=0) == SHAPE
+    # the grouped kernel's 2 GiB limits are checked before the quantizer would run
+    # (no device here: a limit checked after the launch would report NO_DEVICE)
+    big = (1 << 33) // 256                               # A's packed codes of 2^32 bytes
+    assert q(a_rows=big, rows=big, ridx=None, work_bytes=1 << 40) == SHAPE
+    assert q(N=(1 << 31) // 128, ldc=(1 << 31) // 128) == SHAPE   # one expert's codes of 2 GiB
+    assert g(a_rows=1 << 22, lda=256) == SHAPE           # bf16 A of 2 GiB
 
     def qp(**kw):
         a = dict(ac=FAKE, asc=FAKE, at=FAKE, a_rows=64, K=256, ridx=FAKE, offs=FAKE, groups=4, rows=128,
@@ -415,6 +431,7 @@ def test_grouped_validation(L):
 
     assert qp(at=None) == NULL
     assert qp(K=40) == SHAPE
+    assert qp(a_rows=big, rows=big, ridx=None) == SHAPE
     if not torch.cuda.is_available():
         assert g() == NO_DEVICE and q() == NO_DEVICE and qp() == NO_DEVICE
     assert g(rows=0, a=None, c=None, wc=None, ws=None, wt=None, ridx=None, a_rows=0) == 0   # empty: no-op

@@ -130,6 +130,44 @@ def test_midpoints_and_neighbours(seed):
     _nv_check(x, "tensor", f"midpoints seed {seed}")
 
 
+def _midpoint_full_scale(seed, per_row):
+    """fp32 tensor whose tensor (or row) scale has a full 24-bit mantissa, so the
+    block steps d = fl32(E4M3(b) s) do too; elements sit on t d rounded to fp32 and
+    up to two ulps either side, t an E2M1 grid point or midpoint, so each code is
+    decided by the last bit of the correctly rounded quotient fl32(x / d)."""
+    rng = np.random.default_rng(seed)
+    rows, nb = 48, 24
+    thr = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0], np.float32)
+    n_s = rows if per_row else 1
+    amax = ((1 + rng.random(n_s)) * 2.0 ** rng.integers(-12, 13, n_s)).astype(np.float32)
+    s = (amax / np.float32(2688.0)).astype(np.float32)
+    x = np.empty((rows, nb, 16), np.float32)
+    for r in range(rows):
+        sr = s[r if per_row else 0]
+        for j in range(nb):
+            b = int(rng.integers(1, 0x77))                      # E4M3 bytes up to 240, subnormals included
+            bv = np.float32(oracle.e4m3_decode(b))
+            d = np.float32(bv * sr)
+            v = (rng.choice(thr, 16) * d).astype(np.float32)
+            for _ in range(2):
+                step = rng.integers(-1, 2, 16)
+                v = np.where(step > 0, np.nextafter(v, np.float32(np.inf)), v)
+                v = np.where(step < 0, np.nextafter(v, np.float32(0)), v)
+            v[0] = np.float32(bv * np.float32(6.0 * sr))        # the block maximum picks byte b
+            v *= np.where(rng.random(16) < 0.5, -1, 1).astype(np.float32)
+            x[r, j] = rng.permutation(v)
+        x[r if per_row else 0, 0, 0] = amax[r if per_row else 0]
+    return x.reshape(rows, nb * 16)
+
+
+@pytest.mark.parametrize("seed", [4, 5, 6])
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_midpoints_full_mantissa_scale(seed, mode):
+    x = _midpoint_full_scale(seed, mode == "row")
+    _nv_check(x, mode, f"full-mantissa midpoints seed {seed}")
+    _nv_check(to_bf16_bits(x), mode, f"full-mantissa midpoints seed {seed} as bf16")
+
+
 def test_subnormal_zero_and_signed_zero_blocks():
     rng = np.random.default_rng(9)
     x = weights(8, 256, 1.0, 0.0, 1.0, seed=9)
@@ -144,10 +182,35 @@ def test_subnormal_zero_and_signed_zero_blocks():
     _nv_check(x, "row", "special blocks per row")
 
 
-@pytest.mark.parametrize("scale", [1e-38, 1e-30, 1e30, 3e36])
-def test_tiny_and_huge_tensors(scale):
+# the quantizers switch from the shared-reciprocal division to the IEEE division
+# when the tensor scale leaves [2^-50, 2^50]: amax 2688 * 2^-50 ~ 2.39e-12 and
+# 2688 * 2^50 ~ 3.03e18; both sides of each edge are covered
+@pytest.mark.parametrize("scale", [1e-38, 1e-30, 2.0e-13, 2.2e-13, 2.6e-13, 3e-12, 2.7e17, 3.1e17, 1e30, 3e36])
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_tiny_and_huge_tensors(scale, mode):
     x = (weights(4, 64, 1.0, 0.05, 10.0, seed=5) * np.float32(scale)).astype(np.float32)
-    _nv_check(x, "tensor", f"scaled by {scale}")
+    _nv_check(x, mode, f"scaled by {scale}")
+    if mode == "row":
+        _nv_check(to_bf16_bits(x), mode, f"scaled by {scale}, bf16")
+
+
+@pytest.mark.parametrize("edge", [-50, 50])
+@pytest.mark.parametrize("mode", ["tensor", "row"])
+def test_scale_at_fast_path_edges(edge, mode):
+    """Rows whose amax puts s = amax / 2688 one ulp inside, on and one ulp outside 2^edge."""
+    rows = []
+    for k, base in enumerate(weights(9, 128, 1.0, 0.05, 10.0, seed=21)):
+        target = np.float32(2.0 ** edge * 2688.0)
+        amax = [np.nextafter(target, np.float32(0)), target, np.nextafter(target, np.float32(np.inf))][k % 3]
+        r = (base / np.abs(base).max() * amax).astype(np.float32)
+        r[np.argmax(np.abs(r))] = amax
+        rows.append(r)
+    x = np.stack(rows)
+    if mode == "tensor":
+        for r in x:
+            _nv_check(r[None, :], mode, f"edge 2^{edge}")
+    else:
+        _nv_check(x, mode, f"edge 2^{edge}")
 
 
 def test_all_zero_tensor():
