@@ -52,6 +52,7 @@ def parse():
     ap.add_argument("--steps", type=int, default=500)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--rotate", type=int, default=12, help="weight copies cycled through")
+    ap.add_argument("--trials", type=int, default=5, help="timed repetitions of the K steps (value: their median)")
     ap.add_argument("--comp-iters", type=int, default=20, help="timed launches per component")
     ap.add_argument("--skip-components", action="store_true")
     ap.add_argument("--skip-cpu", action="store_true")
@@ -92,12 +93,16 @@ def measured_traffic(Ms):
 
 
 class Timer:
-    """HIP events on torch's current stream, which is the stream the library launches on."""
+    """HIP events on torch's current stream, which is the stream the library launches on.
+    The timed loops replay library calls recorded by fp4.prepare(): the binding's
+    argument checks run once, when a call is prepared, so a short kernel is not timed
+    behind the Python that launches it."""
 
     def __init__(self, torch):
         self.torch = torch
+        self.clock = ClockSampler()
 
-    def per_launch(self, fn, iters, warmup=3, warm_s=0.05):
+    def per_launch(self, fn, iters, warmup=3, warm_s=0.05, sample_clock=False):
         """Seconds per launch over `iters` launches, after `warmup` launches and at
         least `warm_s` seconds of them (so heavy kernels are timed at the clock they
         sustain, not while it ramps up)."""
@@ -112,12 +117,66 @@ class Timer:
         torch.cuda.synchronize()
         s = torch.cuda.Event(enable_timing=True)
         e = torch.cuda.Event(enable_timing=True)
+        if sample_clock:
+            self.clock.start()
         s.record()
         for i in range(iters):
             fn(i)
         e.record()
         e.synchronize()
+        if sample_clock:
+            self.clock.stop()
         return s.elapsed_time(e) * 1e-3 / iters   # seconds per launch
+
+
+class ClockSampler:
+    """The shader clock while a timed loop runs, read from the driver's sysfs
+    (pp_dpm_sclk: the current level carries a '*') every few ms in a thread.  Empty
+    where the file is not readable."""
+
+    def __init__(self):
+        import glob
+
+        self.files = [f for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+                      if os.access(f, os.R_OK)]
+        self.samples = []
+        self._run = False
+        self._thread = None
+
+    def _read(self):
+        for f in self.files:
+            try:
+                for line in open(f):
+                    if "*" in line:
+                        return float(line.split(":")[1].split("Mhz")[0].split("MHz")[0].strip())
+            except (OSError, ValueError, IndexError):
+                continue
+        return None
+
+    def _loop(self):
+        while self._run:
+            v = self._read()
+            if v:
+                self.samples.append(v)
+            time.sleep(0.002)
+
+    def start(self):
+        import threading
+
+        if not self.files:
+            return
+        self._run = True
+        self._thread = threading.Thread(target=self._loop, daemon=True)
+        self._thread.start()
+
+    def stop(self):
+        self._run = False
+        if self._thread is not None:
+            self._thread.join()
+            self._thread = None
+
+    def median_mhz(self):
+        return float(np.median(self.samples)) if self.samples else None
 
 
 def main():
@@ -170,29 +229,35 @@ def main():
     acts = {M: torch.from_numpy(wl.activations_bf16(M).view(np.int16)).view(torch.bfloat16).to(dev)
             for M in wl.M}
     outs = {M: torch.empty(M, N, dtype=torch.bfloat16, device=dev) for M in wl.M}
+    # the library calls of every (weight copy, M), prepared once (checks made then)
+    dec_calls = {(c, M): fp4.prepare(lambda c=c, M=M: fp4.gemm_w4a16_decode(acts[M], dcopies[c], out=outs[M]))
+                 for c in range(R) for M in wl.M}
 
     # every GEMV call reads its own weight copy (12 x 50 MB > the 256 MB Infinity
     # Cache), as the distinct layers of a decode step would: no call finds its
     # weights in a cache
     def step(i):
         for j, M in enumerate(wl.M):
-            fp4.gemm_w4a16_decode(acts[M], dcopies[(len(wl.M) * i + j) % R], out=outs[M])
+            dec_calls[((len(wl.M) * i + j) % R, M)]()
 
     # ------------------------------------------------------------ the step --
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    s = torch.cuda.Event(enable_timing=True)
-    e = torch.cuda.Event(enable_timing=True)
-    s.record()
-    for i in range(args.steps):
-        step(i)
-    e.record()
-    e.synchronize()
+    trials = []
+    for _ in range(args.trials):
+        s = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        s.record()
+        for i in range(args.steps):
+            step(i)
+        e.record()
+        e.synchronize()
+        trials.append(s.elapsed_time(e) / args.steps)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_per_step = s.elapsed_time(e) / args.steps
+    ms_per_step = float(np.median(trials))
     step_bytes = sum(decode_bytes(M) for M in wl.M)
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     assert torch.isfinite(outs[16].float()).all()
@@ -202,13 +267,12 @@ def main():
     dec, dec_rm = {}, {}
     it = max(args.steps, 30)
     for M in wl.M:
-        t = T.per_launch(lambda i, M=M: fp4.gemm_w4a16_decode(acts[M], dcopies[i % R], out=outs[M]),
-                         iters=it, warmup=5)
+        t = T.per_launch(lambda i, M=M: dec_calls[(i % R, M)](), iters=it, warmup=5)
         dec[M] = {"us": t * 1e6, "GB/s": decode_bytes(M) / t / 1e9,
                   "frac_hbm": decode_bytes(M) / t / HBM_PEAK, "bytes": decode_bytes(M)}
         if not args.only_decode:
-            t = T.per_launch(lambda i, M=M: fp4.gemm_w4a16(acts[M], copies[i % R], out=outs[M]),
-                             iters=it, warmup=5)
+            rm = [fp4.prepare(lambda c=c, M=M: fp4.gemm_w4a16(acts[M], copies[c], out=outs[M])) for c in range(R)]
+            t = T.per_launch(lambda i: rm[i % R](), iters=it, warmup=5)
             dec_rm[M] = {"us": t * 1e6, "GB/s": decode_bytes(M) / t / 1e9,
                          "frac_hbm": decode_bytes(M) / t / HBM_PEAK}
     mean_bytes = sum(decode_bytes(M) for M in wl.M) / len(wl.M)
@@ -230,6 +294,8 @@ def main():
                    "weight_layout": "decode layout (segment-major [K/128][N][64] codes, [K/128][N][8] scales)",
                    "activations": "bf16 N(0,1)", "output": "bf16",
                    "weight_copies_rotated": R, "wall_s_timed_region": round(wall, 4)},
+        "trials": {"n": args.trials, "ms_per_step": [round(t, 5) for t in trials],
+                   "value_is": "median over the trials of the step time"},
         "roofline": roofline,
         "decode_per_M": {str(M): {k: round(v, 4) if isinstance(v, float) else v for k, v in d.items()}
                          for M, d in dec.items()},
@@ -239,11 +305,28 @@ def main():
 
     if not args.only_decode and not args.skip_components:
         result["components"] = components(args, torch, fp4, T, dev, w32, wq)
+        mhz = T.clock.median_mhz()
+        result["sclk"] = {"median_mhz_during_gemm_loops": mhz, "samples": len(T.clock.samples),
+                          "spec_mhz": 2400.0,
+                          "note": "fractions of peak in the components are at 2.4 GHz; *_frac_at_sclk "
+                                  "rescale the MFMA peaks to the sampled clock" if mhz else
+                                  "the driver's clock file was not readable: no clock samples"}
+        if mhz:
+            for comp in result["components"].values():
+                for k in list(comp):
+                    if "frac" in k and "mfma" in k and isinstance(comp[k], float):
+                        comp[k + "_at_sclk"] = round(comp[k] * 2400.0 / mhz, 4)
 
     if not args.only_decode and not args.skip_cpu:
-        result["cpu_baseline"] = cpu_baseline(wl, wq)
+        result["cpu_baseline"] = cpu_baseline(wl, wq, w_np)
 
     print(json.dumps(result))
+
+
+def prepared(fp4, thunk):
+    """A timing loop body that replays the library calls of `thunk` (see fp4.prepare)."""
+    call = fp4.prepare(thunk)
+    return lambda i: call()
 
 
 def components(args, torch, fp4, T, dev, w32, wq):
@@ -271,13 +354,36 @@ def components(args, torch, fp4, T, dev, w32, wq):
 def quant_components(fp4, T, dev, w32, wq, it, out):
     import torch
 
+    from synthetic import WORKLOADS
+
+    # C1: the tiny round trip (256 x 256 fp32 weight quantized per tensor,
+    # dequantized, W4A16 GEMM with 4 bf16 rows, fp32 out): latency of each call
+    wl1 = WORKLOADS["tiny_roundtrip_256"]
+    w1 = torch.from_numpy(wl1.weights()).to(dev)
+    a1 = torch.from_numpy(wl1.activations_bf16(4).view(np.int16)).view(torch.bfloat16).to(dev)
+    p1 = fp4.nvfp4_quantize(w1)
+    y1 = torch.empty(256, 256, dtype=torch.float32, device=dev)
+    c1 = torch.empty(4, 256, dtype=torch.float32, device=dev)
+    ws1 = torch.empty(fp4.lib().nvfp4_quantize_workspace(256, 256, 0), dtype=torch.uint8, device=dev)
+    t_q1 = T.per_launch(prepared(fp4, lambda: fp4.nvfp4_quantize(w1, out=p1, workspace=ws1)), it)
+    t_d1 = T.per_launch(prepared(fp4, lambda: fp4.nvfp4_dequantize(p1, out=y1)), it)
+    t_g1 = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a16(a1, p1, out=c1)), it)
+    chain = fp4.prepare(lambda: (fp4.nvfp4_quantize(w1, out=p1, workspace=ws1), fp4.nvfp4_dequantize(p1, out=y1),
+                                 fp4.gemm_w4a16(a1, p1, out=c1)))
+    t_all1 = T.per_launch(lambda i: chain(), it)
+    out["c1_tiny_roundtrip_256"] = {
+        "quantize_us": t_q1 * 1e6, "dequantize_us": t_d1 * 1e6, "gemm_w4a16_us": t_g1 * 1e6,
+        "all_three_us": t_all1 * 1e6,
+        "note": "latency per call, back-to-back launches (the configuration is a correctness case)"}
+
     # weight quantize (fp32 -> NVFP4, per tensor: amax pass + quantize pass)
     w32b = w32.clone()   # two fp32 copies (712 MB) exceed the Infinity Cache
     ws = torch.empty(fp4.lib().nvfp4_quantize_workspace(N, K, 0), dtype=torch.uint8, device=dev)
     qo = fp4.PackedNVFP4(torch.empty_like(wq.codes), torch.empty_like(wq.scales),
                          torch.empty_like(wq.tscale), N, K)
     srcs = [w32, w32b]
-    t = T.per_launch(lambda i: fp4.nvfp4_quantize(srcs[i % 2], out=qo, workspace=ws), it)
+    pq = [fp4.prepare(lambda x=x: fp4.nvfp4_quantize(x, out=qo, workspace=ws)) for x in srcs]
+    t = T.per_launch(lambda i: pq[i % 2](), it)
     b = 2 * N * K * 4 + N * K // 2 + N * K // 16 + 4
     out["weight_quantize_fp32_17408x5120"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
                                               "frac_hbm": b / t / HBM_PEAK, "bytes": b}
@@ -285,7 +391,7 @@ def quant_components(fp4, T, dev, w32, wq, it, out):
 
     # dequantize to bf16
     y = torch.empty(N, K, dtype=torch.bfloat16, device=dev)
-    t = T.per_launch(lambda i: fp4.nvfp4_dequantize(wq, out=y), it)
+    t = T.per_launch(prepared(fp4, lambda: fp4.nvfp4_dequantize(wq, out=y)), it)
     b = N * K // 2 + N * K // 16 + 4 + N * K * 2
     out["dequantize_bf16_17408x5120"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
                                          "frac_hbm": b / t / HBM_PEAK, "bytes": b}
@@ -298,10 +404,10 @@ def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     a = torch.from_numpy(wl3.activations_bf16(M).view(np.int16)).view(torch.bfloat16).to(dev)
     c = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     fl = 2.0 * M * N * K
-    t = T.per_launch(lambda i: fp4.gemm_w4a16(a, wq, out=c), it)
+    t = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a16(a, wq, out=c)), it, sample_clock=True)
     # the same GEMMs on the weight in the decode layout (one packed weight for decode and prefill)
     wd = fp4.nvfp4_pack_decode(wq)
-    t_d = T.per_launch(lambda i: fp4.gemm_w4a16_decode(a, wd, out=c), it)
+    t_d = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a16_decode(a, wd, out=c)), it)
     out["prefill_w4a16_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
                                   "decode_layout_us": t_d * 1e6, "decode_layout_TFLOP/s": fl / t_d / 1e12,
                                   "decode_layout_frac_bf16_mfma": fl / t_d / BF16_PEAK,
@@ -309,14 +415,23 @@ def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     # activation quantization alone (per row) and the fused W4A4 call
     wsa = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     pa = fp4.w4a4_packed_a(wsa, M, K, "row")
-    t_q = T.per_launch(lambda i: fp4.nvfp4_quantize(a, mode="row", out=pa), it)
+    t_q = T.per_launch(prepared(fp4, lambda: fp4.nvfp4_quantize(a, mode="row", out=pa)), it)
     bq = M * K * 2 + M * K // 2 + M * K // 16 + 4 * M
-    t_g = T.per_launch(lambda i: fp4.gemm_nvfp4_prequant(pa, wq, out=c), it)
-    t_all = T.per_launch(lambda i: fp4.gemm_w4a4(a, wq, a_mode="row", out=c, workspace=wsa), it)
-    t_gd = T.per_launch(lambda i: fp4.gemm_nvfp4_prequant_seg(pa, wd, out=c), it)
-    t_alld = T.per_launch(lambda i: fp4.gemm_w4a4_seg(a, wd, a_mode="row", out=c, workspace=wsa), it)
+    # the same on inputs that are not in any cache: 8 rotating copies (336 MB > the
+    # 256 MB Infinity Cache); the figure above is the activation as a previous
+    # kernel leaves it, resident in the Infinity Cache
+    a_cold = [a.clone() for _ in range(8)]
+    pq = [fp4.prepare(lambda x=x: fp4.nvfp4_quantize(x, mode="row", out=pa)) for x in a_cold]
+    t_qc = T.per_launch(lambda i: pq[i % 8](), max(it, 40))
+    del a_cold, pq
+    t_g = T.per_launch(prepared(fp4, lambda: fp4.gemm_nvfp4_prequant(pa, wq, out=c)), it, sample_clock=True)
+    t_all = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a4(a, wq, a_mode="row", out=c, workspace=wsa)), it)
+    t_gd = T.per_launch(prepared(fp4, lambda: fp4.gemm_nvfp4_prequant_seg(pa, wd, out=c)), it)
+    t_alld = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a4_seg(a, wd, a_mode="row", out=c, workspace=wsa)), it)
     out["prefill_w4a4_m4096"] = {
         "quant_us": t_q * 1e6, "quant_GB/s": bq / t_q / 1e9, "quant_frac_hbm": bq / t_q / HBM_PEAK,
+        "quant_cold_us": t_qc * 1e6, "quant_cold_GB/s": bq / t_qc / 1e9, "quant_cold_frac_hbm": bq / t_qc / HBM_PEAK,
+        "quant_bytes": bq,
         "gemm_us": t_g * 1e6, "gemm_TFLOP/s": fl / t_g / 1e12, "gemm_frac_bf16_mfma": fl / t_g / BF16_PEAK,
         "total_us": t_all * 1e6, "total_TFLOP/s": fl / t_all / 1e12,
         "decode_layout_gemm_us": t_gd * 1e6, "decode_layout_gemm_TFLOP/s": fl / t_gd / 1e12,
@@ -338,8 +453,8 @@ def mx16_components(torch, fp4, T, dev, w32, wl3, it, out):
     for M in wl2.M:
         am = torch.from_numpy(wl2.activations_bf16(M).view(np.int16)).view(torch.bfloat16).to(dev)
         om = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-        t = T.per_launch(lambda i, am=am, om=om: fp4.mxfp4_gemm_w4a16_decode(am, mcopies[i % 12], out=om),
-                         max(it, 30), warmup=5)
+        pm = [fp4.prepare(lambda c=c, am=am, om=om: fp4.mxfp4_gemm_w4a16_decode(am, c, out=om)) for c in mcopies]
+        t = T.per_launch(lambda i, pm=pm: pm[i % 12](), max(it, 30), warmup=5)
         b = M * K * 2 + N * K // 2 + N * K // 32 + M * N * 2
         mxd[str(M)] = {"us": round(t * 1e6, 4), "GB/s": round(b / t / 1e9, 1), "frac_hbm": round(b / t / HBM_PEAK, 4),
                        "bytes": b}
@@ -349,8 +464,8 @@ def mx16_components(torch, fp4, T, dev, w32, wl3, it, out):
     a = torch.from_numpy(wl3.activations_bf16(4096).view(np.int16)).view(torch.bfloat16).to(dev)
     c = torch.empty(4096, N, dtype=torch.bfloat16, device=dev)
     fl = 2.0 * 4096 * N * K
-    t = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a16(a, wmx, out=c), it)
-    t_d = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a16_decode(a, md0, out=c), it)
+    t = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a16(a, wmx, out=c)), it)
+    t_d = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a16_decode(a, md0, out=c)), it)
     out["mxfp4_w4a16_prefill_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
                                         "decode_layout_us": t_d * 1e6, "decode_layout_TFLOP/s": fl / t_d / 1e12,
                                         "flop": fl, "mfma": "bf16 32x32x16 (MXFP4 widened exactly to bf16)"}
@@ -372,31 +487,31 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
     fl = 2.0 * M * N * K
     wsm = torch.empty(fp4.lib().mxfp4_gemm_w4a4_workspace(M, K), dtype=torch.uint8, device=dev)
     pam = fp4.mxfp4_packed_a(wsm, M, K)
-    t_mq = T.per_launch(lambda i: fp4.mxfp4_quantize(a, out=pam), it)
-    t_mg = T.per_launch(lambda i: fp4.mxfp4_gemm_prequant(pam, wmx, out=c), it)
-    t_mall = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a4(a, wmx, out=c, workspace=wsm), it)
+    t_mq = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_quantize(a, out=pam)), it)
+    t_mg = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_prequant(pam, wmx, out=c)), it, sample_clock=True)
+    t_mall = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a4(a, wmx, out=c, workspace=wsm)), it)
     c_mx = c.clone()
     # the same GEMM with W in the decode (segment-major) layout and A quantized into it
     wmd = fp4.mxfp4_pack_decode(wmx)
     wss = fp4.mxfp4_gemm_w4a4_seg_workspace(M, K, dev)
     pas = fp4.mxfp4_seg_packed_a(wss, M, K)
     fp4.mxfp4_gemm_w4a4_seg(a, wmd, out=c, workspace=wss)
-    t_sg = T.per_launch(lambda i: fp4.mxfp4_gemm_prequant_seg(pas, wmd, out=c), it)
-    t_sall = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a4_seg(a, wmd, out=c, workspace=wss), it)
+    t_sg = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_prequant_seg(pas, wmd, out=c)), it, sample_clock=True)
+    t_sall = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a4_seg(a, wmd, out=c, workspace=wss)), it)
     torch.cuda.synchronize()
     seg_equal = bool(torch.equal(c.view(torch.int16), c_mx.view(torch.int16)))
     wsn = fp4.gemm_w4a4_workspace(M, K, "row", dev)
-    t_nall = T.per_launch(lambda i: fp4.gemm_w4a4(a, wnv, a_mode="row", out=c, workspace=wsn), it)
+    t_nall = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a4(a, wnv, a_mode="row", out=c, workspace=wsn)), it)
     c_nv = c.clone()
     # W4A8: the same MXFP4 weights, activations as MXFP8
     ws8 = fp4.mxfp4_gemm_w4a8_workspace(M, K, dev)
     pa8 = fp4.mxfp8_packed_a(ws8, M, K)
-    t_8q = T.per_launch(lambda i: fp4.mxfp8_quantize(a, out=pa8), it)
-    t_8g = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_prequant(pa8, wmx, out=c), it)
-    t_8all = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8(a, wmx, out=c, workspace=ws8), it)
+    t_8q = T.per_launch(prepared(fp4, lambda: fp4.mxfp8_quantize(a, out=pa8)), it)
+    t_8g = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a8_prequant(pa8, wmx, out=c)), it)
+    t_8all = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a8(a, wmx, out=c, workspace=ws8)), it)
     c_a8 = c.clone()
-    t_8sg = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_prequant_seg(pa8, wmd, out=c), it)
-    t_8sall = T.per_launch(lambda i: fp4.mxfp4_gemm_w4a8_seg(a, wmd, out=c, workspace=ws8), it)
+    t_8sg = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a8_prequant_seg(pa8, wmd, out=c)), it)
+    t_8sall = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a8_seg(a, wmd, out=c, workspace=ws8)), it)
     torch.cuda.synchronize()
     w4a8_seg_equal = bool(torch.equal(c.view(torch.int16), c_a8.view(torch.int16)))
     torch.cuda.synchronize()
@@ -450,9 +565,9 @@ def moe_components(args, torch, fp4, T, dev):
     c = torch.empty(rows, wlm.N, dtype=torch.bfloat16, device=dev)
     wsg = fp4.nvfp4_grouped_gemm_w4a4_workspace(wlm.tokens, wlm.K, dev)
     fl = 2.0 * rows * wlm.N * wlm.K
-    t_gnv = T.per_launch(lambda i: fp4.nvfp4_grouped_gemm_w4a16(a, env, go, ri, out=c), it)
-    t_gmx = T.per_launch(lambda i: fp4.mxfp4_grouped_gemm_w4a16(a, emx, go, ri, out=c), it)
-    t_g44 = T.per_launch(lambda i: fp4.nvfp4_grouped_gemm_w4a4(a, env, go, ri, out=c, workspace=wsg), it)
+    t_gnv = T.per_launch(prepared(fp4, lambda: fp4.nvfp4_grouped_gemm_w4a16(a, env, go, ri, out=c)), it)
+    t_gmx = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_grouped_gemm_w4a16(a, emx, go, ri, out=c)), it)
+    t_g44 = T.per_launch(prepared(fp4, lambda: fp4.nvfp4_grouped_gemm_w4a4(a, env, go, ri, out=c, workspace=wsg)), it)
     loads = np.diff(offs)
     out["moe_grouped_" + wlm.name] = {
         "rows": rows, "experts": wlm.experts, "empty_experts": int((loads == 0).sum()),
@@ -465,12 +580,21 @@ def moe_components(args, torch, fp4, T, dev):
     return out
 
 
-def cpu_baseline(wl, wq):
-    """The oracle as it stands (dequantize W to fp64 in C with OpenMP, then numpy
-    float64 matmul), timed on whole decode steps (M = 1, 4, 16), repeated
-    until ~15 s of host time."""
-    import oracle
+def cpu_baseline(wl, wq, w_np):
+    """The oracle as it stands, timed on the host cores of this machine: the whole
+    decode step (the `value` workload) plus one leg per other kernel of the path.
 
+    * decode step: dequantize W to fp64 in C (OpenMP) and a numpy float64 product,
+      for M = 1, 4 and 16, repeated for about 8 s; GB/s over the step's bytes;
+    * quantizers and the dequantizer at full size, once each; GB/s over the same
+      algorithmic bytes as the GPU figures;
+    * the prefill GEMMs on a 128-row slice of A, scaled by M / 128 to the full M
+      (labelled extrapolated); GFLOP/s over 2 M N K.  The oracle also forms the
+      tolerance term sum |a w|, a second product, which these figures do not count."""
+    import oracle
+    from synthetic import WORKLOADS
+
+    cores = len(os.sched_getaffinity(0))
     codes = wq.codes.cpu().numpy()
     scales = wq.scales.cpu().numpy()
     ts = wq.tscale.cpu().numpy()
@@ -481,15 +605,52 @@ def cpu_baseline(wl, wq):
             oracle.gemm_w4a16_ref(acts[M], codes, scales, ts)
         reps += 1
         el = time.perf_counter() - t0
-        if el > 15.0 or reps >= 40:
+        if el > 8.0 or reps >= 40:
             break
     per_step = el / reps
     b = sum(decode_bytes(M) for M in wl.M)
-    return {"value": round(b / per_step / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+    legs = {}
+
+    def timed(fn):
+        t = time.perf_counter()
+        fn()
+        return time.perf_counter() - t
+
+    bw = 2 * N * K * 4 + N * K // 2 + N * K // 16 + 4
+    t = timed(lambda: oracle.nvfp4_quantize(w_np))
+    legs["weight_quantize_fp32_17408x5120"] = {"s": round(t, 3), "GB/s": round(bw / t / 1e9, 3), "bytes": bw}
+    bd = N * K // 2 + N * K // 16 + 4 + N * K * 4
+    t = timed(lambda: oracle.nvfp4_dequantize(codes, scales, ts))
+    legs["dequantize_fp32_17408x5120"] = {"s": round(t, 3), "GB/s": round(bd / t / 1e9, 3), "bytes": bd}
+    a4 = WORKLOADS["prefill_w4a4_m4096"].activations_bf16(4096)
+    bq = 4096 * K * 2 + 4096 * K // 2 + 4096 * K // 16 + 4 * 4096
+    t = timed(lambda: oracle.nvfp4_quantize(a4, per_row=True))
+    legs["activation_quantize_per_row_4096x5120"] = {"s": round(t, 3), "GB/s": round(bq / t / 1e9, 3), "bytes": bq}
+    a8 = WORKLOADS["mx_vs_nv_w4a4_m8192"].activations_bf16(8192)
+    bm = 8192 * K * 2 + 8192 * K // 2 + 8192 * K // 32
+    t = timed(lambda: oracle.mxfp4_quantize(a8))
+    legs["mxfp4_quantize_8192x5120"] = {"s": round(t, 3), "GB/s": round(bm / t / 1e9, 3), "bytes": bm}
+
+    wb = oracle.f32_to_bf16_bits(w_np)                       # the C5 weights: fp32 -> bf16, then each format
+    mc, ms = oracle.mxfp4_quantize(wb)
+    nc, ns, nt = oracle.nvfp4_quantize(wb)
+    sl = 128
+    gemms = {
+        "prefill_w4a16_m4096": (4096, lambda: oracle.gemm_w4a16_ref(a4[:sl], codes, scales, ts)),
+        "prefill_w4a4_m4096": (4096, lambda: oracle.gemm_w4a4_ref(a4[:sl], codes, scales, ts, a_per_row=True)),
+        "mxfp4_w4a4_m8192": (8192, lambda: oracle.mxfp4_gemm_w4a4_ref(a8[:sl], mc, ms)),
+        "nvfp4_w4a4_m8192": (8192, lambda: oracle.gemm_w4a4_ref(a8[:sl], nc, ns, nt, a_per_row=True)),
+    }
+    for name, (M, fn) in gemms.items():
+        t = timed(fn)
+        legs[name] = {"slice_rows": sl, "slice_s": round(t, 3), "extrapolated_s": round(t * M / sl, 2),
+                      "GFLOP/s": round(2.0 * sl * N * K / t / 1e9, 2), "extrapolated": True}
+    return {"value": round(b / per_step / 1e9, 4), "unit": "GB/s", "cores": cores,
+            "threads": oracle.num_threads(), "kind": "oracle",
             "sample": f"{reps} full decode step(s) (M=1,4,16 on the 17408x5120 NVFP4 weight): "
                       f"{per_step:.2f} s per step on the host; OpenMP threads for dequantization, "
-                      "numpy BLAS for the fp64 product"}
+                      "numpy BLAS for the fp64 product",
+            "legs": legs}
 
 
 if __name__ == "__main__":

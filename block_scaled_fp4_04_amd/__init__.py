@@ -124,11 +124,60 @@ def _check(s: int):
         raise Fp4Error(s, status_str(s))
 
 
+_recording = None  # list of (function, arguments) while prepare() records
+_recording_keep = []  # the tensors behind the recorded pointers
+
+
+def _run(fn, *args):
+    """Every library call goes through here: made at once, or recorded by prepare()."""
+    if _recording is not None:
+        _recording.append((fn, args))
+        return
+    _check(fn(*args))
+
+
+class Prepared:
+    """Library calls recorded by prepare(), replayed with the same pointers, sizes and
+    stream.  It holds the tensors the calls use, so their memory stays valid."""
+
+    def __init__(self, calls, keep):
+        self._calls = calls
+        self._keep = keep
+
+    def __call__(self, *_ignored):
+        for fn, args in self._calls:
+            s = fn(*args)
+            if s != 0:
+                raise Fp4Error(s, status_str(s))
+
+
+def prepare(thunk, *keep) -> Prepared:
+    """Runs `thunk` (one or more calls of this module) with every argument check made
+    and the library calls recorded instead of launched, and returns a callable that
+    launches exactly those calls again: the same device pointers, sizes and stream,
+    without the Python-side checks and allocation.  For tight loops (decode steps,
+    benchmarks) where the checks would cost more than a short kernel.  The callable
+    holds every tensor whose memory the calls use (and what the thunk returns), so
+    that memory stays valid; the tensors' contents may change between calls."""
+    global _recording, _recording_keep
+    if _recording is not None:
+        raise RuntimeError("prepare() calls do not nest")
+    _recording, _recording_keep = [], []
+    try:
+        result = thunk()
+        calls, held = _recording, _recording_keep
+    finally:
+        _recording, _recording_keep = None, []
+    return Prepared(calls, (result, keep, held))
+
+
 def _stream():
     return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
 
 
 def _ptr(t):
+    if t is not None and _recording is not None:
+        _recording_keep.append(t)  # prepare(): the replayed calls keep using this memory
     return ctypes.c_void_p(0 if t is None else t.data_ptr())
 
 
@@ -302,8 +351,8 @@ def nvfp4_quantize(x: torch.Tensor, mode="tensor", nonfinite: torch.Tensor | Non
     wsb = L.nvfp4_quantize_workspace(rows, cols, m)
     workspace = _workspace(workspace, wsb, x) if wsb else workspace
     _need_cuda(x, nonfinite, out.codes, out.scales, out.tscale, workspace)
-    _check(L.nvfp4_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
-                            _ptr(out.tscale), m, _ptr(workspace), wsb, _ptr(nonfinite), _stream()))
+    _run(L.nvfp4_quantize, _ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
+                            _ptr(out.tscale), m, _ptr(workspace), wsb, _ptr(nonfinite), _stream())
     return out
 
 
@@ -312,9 +361,9 @@ def nvfp4_dequantize(p: PackedNVFP4, dtype=torch.float32, out: torch.Tensor | No
     p.check("p")
     out = _out(out, p.rows, p.cols, dtype, p.codes)
     _need_cuda(p.codes, p.scales, p.tscale, out)
-    _check(L.nvfp4_dequantize(_ptr(p.codes), _ptr(p.scales), _ptr(p.tscale),
+    _run(L.nvfp4_dequantize, _ptr(p.codes), _ptr(p.scales), _ptr(p.tscale),
                               PER_ROW if p.per_row else PER_TENSOR, p.rows, p.cols, _ptr(out),
-                              _out_dt(out.dtype), _ld(out), _stream()))
+                              _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -342,8 +391,8 @@ def gemm_w4a16(a: torch.Tensor, w: PackedNVFP4, dtype=torch.bfloat16,
     _weight_nv(w, K)
     out = _out(out, M, w.rows, dtype, a)
     _need_cuda(a, w.codes, w.scales, w.tscale, out)
-    _check(L.gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
-                        _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    _run(L.gemm_w4a16, _ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                        _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -380,8 +429,8 @@ def nvfp4_pack_decode(w: PackedNVFP4, out: DecodeNVFP4 | None = None) -> DecodeN
         raise ValueError("out does not describe this weight")
     out.check("out")
     _need_cuda(w.codes, w.scales, out.codes, out.scales)
-    _check(L.nvfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
-                               _stream()))
+    _run(L.nvfp4_pack_decode, _ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
+                               _stream())
     return out
 
 
@@ -395,8 +444,8 @@ def gemm_w4a16_decode(a: torch.Tensor, w: DecodeNVFP4, dtype=torch.bfloat16,
     _k_match(K, w.cols)
     out = _out(out, M, w.rows, dtype, a)
     _need_cuda(a, w.codes, w.scales, w.tscale, out)
-    _check(L.gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
-                               _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    _run(L.gemm_w4a16_decode, _ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+                               _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -425,9 +474,9 @@ def _w4a4(fn_name: str, a, w, a_mode, dtype, out, workspace, w_check):
     out = _out(out, M, w.rows, dtype, a)
     workspace = _workspace(workspace, L.gemm_w4a4_workspace(M, K, m), a)
     _need_cuda(a, w.codes, w.scales, w.tscale, out, workspace)
-    _check(getattr(L, fn_name)(_ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+    _run(getattr(L, fn_name), _ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                                _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                               _stream()))
+                               _stream())
     return out
 
 
@@ -443,10 +492,10 @@ def _prequant_nv(fn_name: str, a: PackedNVFP4, w, dtype, out):
     _k_match(a.cols, w.cols)
     out = _out(out, a.rows, w.rows, dtype, a.codes)
     _need_cuda(a.codes, a.scales, a.tscale, w.codes, w.scales, w.tscale, out)
-    _check(getattr(L, fn_name)(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
+    _run(getattr(L, fn_name), _ptr(a.codes), _ptr(a.scales), _ptr(a.tscale),
                                PER_ROW if a.per_row else PER_TENSOR, a.rows, a.cols,
                                _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
-                               _out_dt(out.dtype), _ld(out), _stream()))
+                               _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -490,8 +539,8 @@ def mxfp4_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None =
     if nonfinite is not None and (nonfinite.dtype != torch.int32 or nonfinite.numel() < 1):
         raise ValueError("nonfinite must be an int32 tensor of at least one element")
     _need_cuda(x, nonfinite, out.codes, out.scales)
-    _check(L.mxfp4_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
-                            _rule(rule), _ptr(nonfinite), _stream()))
+    _run(L.mxfp4_quantize, _ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
+                            _rule(rule), _ptr(nonfinite), _stream())
     return out
 
 
@@ -500,8 +549,8 @@ def mxfp4_dequantize(p: PackedMXFP4, dtype=torch.float32, out: torch.Tensor | No
     p.check("p")
     out = _out(out, p.rows, p.cols, dtype, p.codes)
     _need_cuda(p.codes, p.scales, out)
-    _check(L.mxfp4_dequantize(_ptr(p.codes), _ptr(p.scales), p.rows, p.cols, _ptr(out),
-                              _out_dt(out.dtype), _ld(out), _stream()))
+    _run(L.mxfp4_dequantize, _ptr(p.codes), _ptr(p.scales), p.rows, p.cols, _ptr(out),
+                              _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -519,9 +568,9 @@ def _mx_full(fn_name: str, ws_name: str, a, w, rule, dtype, out, workspace, w_ch
     out = _out(out, M, w.rows, dtype, a)
     workspace = _workspace(workspace, getattr(L, ws_name)(M, K), a)
     _need_cuda(a, w.codes, w.scales, out, workspace)
-    _check(getattr(L, fn_name)(_ptr(a), M, K, _ld(a), r, _ptr(w.codes), _ptr(w.scales), w.rows,
+    _run(getattr(L, fn_name), _ptr(a), M, K, _ld(a), r, _ptr(w.codes), _ptr(w.scales), w.rows,
                                _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                               _stream()))
+                               _stream())
     return out
 
 
@@ -531,8 +580,8 @@ def _mx_prequant(fn_name: str, a, w, dtype, out):
     _k_match(a.cols, w.cols)
     out = _out(out, a.rows, w.rows, dtype, a.codes)
     _need_cuda(a.codes, a.scales, w.codes, w.scales, out)
-    _check(getattr(L, fn_name)(_ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes), _ptr(w.scales),
-                               w.rows, _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    _run(getattr(L, fn_name), _ptr(a.codes), _ptr(a.scales), a.rows, a.cols, _ptr(w.codes), _ptr(w.scales),
+                               w.rows, _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -561,8 +610,8 @@ def mxfp4_gemm_w4a16(a: torch.Tensor, w: PackedMXFP4, dtype=torch.bfloat16,
     _weight_mx(w, K)
     out = _out(out, M, w.rows, dtype, a)
     _need_cuda(a, w.codes, w.scales, out)
-    _check(L.mxfp4_gemm_w4a16(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
-                              _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    _run(L.mxfp4_gemm_w4a16, _ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
+                              _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -599,8 +648,8 @@ def mxfp4_pack_decode(w: PackedMXFP4, out: DecodeMXFP4 | None = None) -> DecodeM
         raise ValueError("out does not describe this weight")
     out.check("out")
     _need_cuda(w.codes, w.scales, out.codes, out.scales)
-    _check(L.mxfp4_pack_decode(_ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
-                               _stream()))
+    _run(L.mxfp4_pack_decode, _ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
+                               _stream())
     return out
 
 
@@ -638,8 +687,8 @@ def mxfp4_gemm_w4a16_decode(a: torch.Tensor, w: DecodeMXFP4, dtype=torch.bfloat1
     _weight_mx_dec(w, K)
     out = _out(out, M, w.rows, dtype, a)
     _need_cuda(a, w.codes, w.scales, out)
-    _check(L.mxfp4_gemm_w4a16_decode(_ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
-                                     _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+    _run(L.mxfp4_gemm_w4a16_decode, _ptr(a), M, K, _ld(a), _ptr(w.codes), _ptr(w.scales), w.rows,
+                                     _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -672,8 +721,8 @@ def mxfp8_quantize(x: torch.Tensor, rule="ocp", nonfinite: torch.Tensor | None =
     if nonfinite is not None and (nonfinite.dtype != torch.int32 or nonfinite.numel() < 1):
         raise ValueError("nonfinite must be an int32 tensor of at least one element")
     _need_cuda(x, nonfinite, out.codes, out.scales)
-    _check(L.mxfp8_quantize(_ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
-                            _rule(rule), _ptr(nonfinite), _stream()))
+    _run(L.mxfp8_quantize, _ptr(x), _dt(x), rows, cols, _ld(x), _ptr(out.codes), _ptr(out.scales),
+                            _rule(rule), _ptr(nonfinite), _stream())
     return out
 
 
@@ -795,9 +844,9 @@ def nvfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch
     rows, groups = _grouped_common(a_rows, K, w, group_offs, row_index)
     out = _out(out, rows, w.rows, dtype, a)
     _need_cuda(a, w.codes, w.scales, w.tscale, group_offs, row_index, out)
-    _check(L.nvfp4_grouped_gemm_w4a16(_ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
+    _run(L.nvfp4_grouped_gemm_w4a16, _ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
                                       groups, rows, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
-                                      _ptr(out), _out_dt(out.dtype), _ld(out), _stream()))
+                                      _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -810,9 +859,9 @@ def mxfp4_grouped_gemm_w4a16(a: torch.Tensor, w: ExpertsMXFP4, group_offs: torch
     rows, groups = _grouped_common(a_rows, K, w, group_offs, row_index)
     out = _out(out, rows, w.rows, dtype, a)
     _need_cuda(a, w.codes, w.scales, group_offs, row_index, out)
-    _check(L.mxfp4_grouped_gemm_w4a16(_ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
+    _run(L.mxfp4_grouped_gemm_w4a16, _ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
                                       groups, rows, _ptr(w.codes), _ptr(w.scales), w.rows, _ptr(out),
-                                      _out_dt(out.dtype), _ld(out), _stream()))
+                                      _out_dt(out.dtype), _ld(out), _stream())
     return out
 
 
@@ -830,10 +879,10 @@ def nvfp4_grouped_gemm_w4a4(a: torch.Tensor, w: ExpertsNVFP4, group_offs: torch.
     out = _out(out, rows, w.rows, dtype, a)
     workspace = _workspace(workspace, L.nvfp4_grouped_gemm_w4a4_workspace(a_rows, K), a)
     _need_cuda(a, w.codes, w.scales, w.tscale, group_offs, row_index, out, workspace)
-    _check(L.nvfp4_grouped_gemm_w4a4(_ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
+    _run(L.nvfp4_grouped_gemm_w4a4, _ptr(a), a_rows, K, _ld(a), _ptr(row_index), _ptr(group_offs),
                                      groups, rows, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
                                      _ptr(out), _out_dt(out.dtype), _ld(out), _ptr(workspace), workspace.numel(),
-                                     _stream()))
+                                     _stream())
     return out
 
 
@@ -848,8 +897,8 @@ def nvfp4_grouped_gemm_w4a4_prequant(a: PackedNVFP4, w: ExpertsNVFP4, group_offs
     rows, groups = _grouped_common(a.rows, a.cols, w, group_offs, row_index)
     out = _out(out, rows, w.rows, dtype, a.codes)
     _need_cuda(a.codes, a.scales, a.tscale, w.codes, w.scales, w.tscale, group_offs, row_index, out)
-    _check(L.nvfp4_grouped_gemm_w4a4_prequant(_ptr(a.codes), _ptr(a.scales), _ptr(a.tscale), a.rows, a.cols,
+    _run(L.nvfp4_grouped_gemm_w4a4_prequant, _ptr(a.codes), _ptr(a.scales), _ptr(a.tscale), a.rows, a.cols,
                                               _ptr(row_index), _ptr(group_offs), groups, rows, _ptr(w.codes),
                                               _ptr(w.scales), _ptr(w.tscale), w.rows, _ptr(out),
-                                              _out_dt(out.dtype), _ld(out), _stream()))
+                                              _out_dt(out.dtype), _ld(out), _stream())
     return out

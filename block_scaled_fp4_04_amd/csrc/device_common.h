@@ -119,6 +119,21 @@ __device__ __forceinline__ float wave_max(float v)
     return v;
 }
 
+// Maximum over the 64 lanes of a wave (non-negative values), returned wave-uniform:
+// DPP within each row of 16 lanes, then the four row maxima read as scalars.
+__device__ __forceinline__ float wave_max_dpp(float v)
+{
+    v = fmaxf(v, xor1(v));
+    v = fmaxf(v, xor2(v));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x141, 0xF, 0xF, false)));  // row_half_mirror
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x140, 0xF, 0xF, false)));  // row_mirror
+    const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+    const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+    const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+    const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+    return fmaxf(fmaxf(r0, r1), fmaxf(r2, r3));
+}
+
 // 32-bit division by a run-time constant (Granlund-Montgomery round-up method;
 // exact for n, d < 2^31).
 struct FastDiv {

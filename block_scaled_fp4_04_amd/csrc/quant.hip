@@ -60,6 +60,20 @@ __device__ __forceinline__ float amax8(const float v[8], int &bad)
     return m;
 }
 
+// Streaming (non-temporal) stores for the quantizers' outputs: each byte is written
+// once and read, if at all, by a later kernel, so it need not stay in the caches.
+// (The dequantizers keep ordinary stores: theirs cover 16 bytes of every 32 or 64
+// per instruction, and as streaming stores those ran at half the rate.)
+__device__ __forceinline__ void st_nt8(uint32_t v, uint8_t *p) { __builtin_nontemporal_store((uint8_t)v, p); }
+__device__ __forceinline__ void st_nt32(uint32_t v, uint8_t *p)
+{
+    __builtin_nontemporal_store(v, reinterpret_cast<uint32_t *>(p));
+}
+__device__ __forceinline__ void st_nt64(uint32_t lo, uint32_t hi, uint8_t *p)
+{
+    __builtin_nontemporal_store(u32x2{lo, hi}, reinterpret_cast<u32x2 *>(p));
+}
+
 // ------------------------------------------- division by a shared divisor --
 //
 // Every value of a 16-block is divided by the same step d = fl32(E4M3(b) s), and
@@ -86,11 +100,23 @@ __device__ __forceinline__ float rcp_refined(float b)
     return __builtin_fmaf(__builtin_fmaf(-b, y0, 1.0f), y0, y0);
 }
 
+// Each correction is written q - (b q - a) y: the same value as q + (a - b q) y
+// (round to nearest is symmetric, so the remainder is only negated), but a
+// numerator of -0 then gives -0 (the sum -0 + -0), where the other order gives +0;
+// so the quotient carries the sign of a in every case, as the division does.
 __device__ __forceinline__ float div_refined(float a, float b, float y)
 {
     const float q0 = a * y;
-    const float q1 = __builtin_fmaf(__builtin_fmaf(-b, q0, a), y, q0);
-    return __builtin_fmaf(__builtin_fmaf(-b, q1, a), y, q1);
+    const float q1 = __builtin_fmaf(-__builtin_fmaf(b, q0, -a), y, q0);
+    return __builtin_fmaf(-__builtin_fmaf(b, q1, -a), y, q1);
+}
+
+// E4M3FN byte of one non-negative value (round to nearest even, saturating at 448).
+__device__ __forceinline__ uint32_t e4m3_code_sat1(float q)
+{
+    typedef short v2i16 __attribute__((ext_vector_type(2)));
+    const v2i16 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(v2i16{0, 0}, fminf(q, 448.0f), 0.0f, 1.0f, false);
+    return (uint32_t)(uint16_t)r[0] & 0xFFu;
 }
 
 // The E4M3 block byte and the codes of one 8-element unit (lanes 2i, 2i + 1 hold
@@ -102,13 +128,13 @@ __device__ __forceinline__ uint32_t nvfp4_unit_fast(const float v[8], float bm8,
 {
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     const float bm = fmaxf(bm8, xor1(bm8));
-    const uint32_t b = e4m3x4_code_sat(div_refined(bm, six_s, y6), 0.0f, 0.0f, 0.0f) & 0xFFu;
+    const uint32_t b = e4m3_code_sat1(div_refined(bm, six_s, y6));
     const f32x2 bv = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
     const float d = b ? bv[0] * s : s * 0x1p20f;
     const float y = rcp_refined(d);
     float q[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = __builtin_copysignf(div_refined(__builtin_fabsf(v[i]), d, y), v[i]);
+    for (int i = 0; i < 8; ++i) q[i] = div_refined(v[i], d, y);
     code_word = e2m1x8_code(q);
     return b;
 }
@@ -205,11 +231,11 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_tensor(const T *__restrict_
         if (fast) {
             int dummy = 0;
             const uint32_t b = nvfp4_unit_fast(v, amax8(v, dummy), s, six_s, y6, w);
-            if ((c8 & 1u) == 0u) *sp = (uint8_t)b;
+            if ((c8 & 1u) == 0u) st_nt8(b, sp);
         } else {
             nvfp4_unit(v, s, six_s, &w, sp, (c8 & 1u) == 0u);
         }
-        *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
+        st_nt32(w, codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
     }
 }
 
@@ -253,9 +279,10 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_rows(const T *__restrict__ 
     }
 }
 
-// Per-row mode for rows of at most 512 U elements: one wave per row, four rows per
-// workgroup.  Lane l owns the 8-element units l, l + 64, ..., l + 64 (U - 1) of
-// its row; all U loads go out at once (a buffer descriptor over the row returns
+// Per-row mode for rows of at most 1024 U elements: one wave per row, four rows
+// per workgroup.  Lane l owns the 16-blocks l, l + 64, ..., l + 64 (U - 1) of its
+// row, so each block's byte, step and reciprocal are formed once, by one lane.
+// All loads of the row go out at once (a buffer descriptor over the row returns
 // zeros past its end), the row maximum is a wave reduction, and the row is
 // quantized from registers: it is read from memory once and no barrier is
 // needed.  bf16 rows keep their packed bits (maxima on the 16-bit magnitudes,
@@ -267,92 +294,116 @@ __global__ __launch_bounds__(256) void k_nvfp4_quant_rows_w(const T *__restrict_
                                                             int32_t *__restrict__ nonfinite)
 {
     constexpr bool BF = sizeof(T) == 2;
-    constexpr int WPU = BF ? 1 : 2;  // 16-byte loads per unit
+    constexpr int LPB = BF ? 2 : 4;  // 16-byte loads per block
     const int lane = threadIdx.x & 63;
     const int64_t r = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     if (r >= rows) return;  // whole waves
-    const int units = cols >> 3;
+    const int blocks = cols >> 4;
     const __amdgpu_buffer_rsrc_t rx =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<T *>(x + r * ldx), (short)0, cols * (int)sizeof(T), 0x00020000);
-    u32x4 raw[U][WPU];
+    u32x4 raw[U][LPB];
 #pragma unroll
     for (int i = 0; i < U; ++i)
 #pragma unroll
-        for (int h = 0; h < WPU; ++h)
-            raw[i][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, (lane + 64 * i) * 16 * WPU + 16 * h, 0, 0);
+        for (int h = 0; h < LPB; ++h)
+            raw[i][h] = __builtin_amdgcn_raw_buffer_load_b128(rx, (lane + 64 * i) * 16 * LPB + 16 * h, 0, 0);
 
-    float um[U];  // max |v| of each unit
+    float bmax[U];  // max |v| of each block
     float m = 0.0f;
     int bad = 0;
 #pragma unroll
     for (int i = 0; i < U; ++i) {
         if constexpr (BF) {
             typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
-            u16x2 h[4];
+            u16x2 h[8];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                const uint32_t mag = raw[i][0][k] & 0x7FFF7FFFu;
+            for (int k = 0; k < 8; ++k) {
+                const uint32_t mag = raw[i][k >> 2][k & 3] & 0x7FFF7FFFu;
                 __builtin_memcpy(&h[k], &mag, 4);
             }
-            const u16x2 t = __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]),
-                                                      __builtin_elementwise_max(h[2], h[3]));
+            const u16x2 t = __builtin_elementwise_max(
+                __builtin_elementwise_max(__builtin_elementwise_max(h[0], h[1]), __builtin_elementwise_max(h[2], h[3])),
+                __builtin_elementwise_max(__builtin_elementwise_max(h[4], h[5]), __builtin_elementwise_max(h[6], h[7])));
             const uint32_t mb = t[0] > t[1] ? t[0] : t[1];
             bad |= mb >= 0x7F80u;
-            um[i] = __uint_as_float(mb << 16);
+            bmax[i] = __uint_as_float(mb << 16);
         } else {
-            float v[8];
+            float a = 0.0f;
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                v[k] = __uint_as_float(raw[i][0][k]);
-                v[4 + k] = __uint_as_float(raw[i][1][k]);
+            for (int k = 0; k < 16; ++k) {
+                const float v = __builtin_fabsf(__uint_as_float(raw[i][k >> 2][k & 3]));
+                bad |= !__builtin_isfinite(v);
+                a = fmaxf(a, v);
             }
-            um[i] = amax8(v, bad);
+            bmax[i] = a;
         }
-        m = fmaxf(m, um[i]);
+        m = fmaxf(m, bmax[i]);
     }
     if (bad && nonfinite) *nonfinite = 1;
-    m = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(wave_max(m))));  // every lane holds it
+    m = wave_max_dpp(m);
     const float s = m / 2688.0f;
     const float six_s = 6.0f * s;
     if (lane == 0) tscale[r] = s;
     uint8_t *cr = codes + r * (cols / 2);
     uint8_t *sr = scales + r * (cols / 16);
-    auto unpack = [&](int i, float (&v)[8]) {
+    auto unpack = [&](int i, float (&v)[16]) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < 8; ++k) {
             if constexpr (BF) {
-                v[2 * k] = __uint_as_float(raw[i][0][k] << 16);
-                v[2 * k + 1] = __uint_as_float(raw[i][0][k] & 0xFFFF0000u);
+                const uint32_t w = raw[i][k >> 2][k & 3];
+                v[2 * k] = __uint_as_float(w << 16);
+                v[2 * k + 1] = __uint_as_float(w & 0xFFFF0000u);
             } else {
-                v[k] = __uint_as_float(raw[i][0][k]);
-                v[4 + k] = __uint_as_float(raw[i][1][k]);
+                v[k] = __uint_as_float(raw[i][k >> 2][k & 3]);
+                v[8 + k] = __uint_as_float(raw[i][2 + (k >> 2)][k & 3]);
             }
         }
     };
-    auto store = [&](int u, uint32_t w, uint32_t b) {
-        if (u < units) {
-            *reinterpret_cast<uint32_t *>(cr + u * 4) = w;
-            if ((u & 1) == 0) sr[u >> 1] = (uint8_t)b;
+    // Streaming (non-temporal) stores: 8 code bytes per lane (512 contiguous bytes a
+    // wave), and when a row's scale count is a multiple of 4, the scale bytes of
+    // lanes 4j .. 4j + 3 gathered into one dword that lane 4j stores (every dword
+    // then lies inside its row and is 4-byte aligned); byte stores otherwise.
+    const bool dword_scales = (blocks & 3) == 0;
+    auto store = [&](int blk, uint32_t w0, uint32_t w1, uint32_t b) {
+        uint32_t sw = b;
+        if (dword_scales) {
+            const uint32_t b1 = __builtin_amdgcn_mov_dpp((int)b, 0x39, 0xF, 0xF, false);  // quad_perm [1,2,3,0]
+            const uint32_t b2 = __builtin_amdgcn_mov_dpp((int)b, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+            const uint32_t b3 = __builtin_amdgcn_mov_dpp((int)b, 0x93, 0xF, 0xF, false);  // [3,0,1,2]
+            sw = b | (b1 << 8) | (b2 << 16) | (b3 << 24);
+        }
+        if (blk < blocks) {
+            st_nt64(w0, w1, cr + blk * 8);
+            if (!dword_scales) st_nt8(b, sr + blk);
+            else if ((lane & 3) == 0) st_nt32(sw, sr + blk);
         }
     };
     if (nv_fast_scale(s)) {
         const float y6 = rcp_refined(six_s);
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            float v[8];
+            float v[16];
             unpack(i, v);
-            uint32_t w;
-            const uint32_t b = nvfp4_unit_fast(v, um[i], s, six_s, y6, w);
-            store(lane + 64 * i, w, b);
+            // E4M3 byte of the block; a byte of 0 divides by s 2^20 instead of 0, so
+            // every quotient is below 2^-27 and each code is the value's sign alone
+            const uint32_t b = e4m3_code_sat1(div_refined(bmax[i], six_s, y6));
+            typedef float f32x2 __attribute__((ext_vector_type(2)));
+            const f32x2 bv = __builtin_amdgcn_cvt_pk_f32_fp8((int)b, false);
+            const float d = b ? bv[0] * s : s * 0x1p20f;
+            const float y = rcp_refined(d);
+            float q[2][8];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) q[k >> 3][k & 7] = div_refined(v[k], d, y);
+            store(lane + 64 * i, e2m1x8_code(q[0]), e2m1x8_code(q[1]), b);
         }
     } else {
 #pragma unroll
         for (int i = 0; i < U; ++i) {
-            float v[8];
+            float v[16];
             unpack(i, v);
-            const float bm = fmaxf(um[i], xor1(um[i]));
-            const uint32_t b = bm == 0.0f ? 0u : e4m3x4_code_sat(bm / six_s, 0.0f, 0.0f, 0.0f) & 0xFFu;
-            store(lane + 64 * i, nvfp4_codes8(v, e4m3_value(b) * s), b);
+            const uint32_t b = bmax[i] == 0.0f ? 0u : e4m3_code_sat1(bmax[i] / six_s);
+            const float d = e4m3_value(b) * s;
+            store(lane + 64 * i, nvfp4_codes8(v, d), nvfp4_codes8(v + 8, d), b);
         }
     }
 }
@@ -451,11 +502,11 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, ui
         }
         if (SEG) {
             const int64_t piece = (int64_t)(c8 >> 4) * rows + r;  // (segment, row)
-            *reinterpret_cast<uint32_t *>(codes + piece * 64 + (c8 & 15u) * 4) = w;
-            if ((c8 & 3u) == 0u) scales[piece * 4 + ((c8 >> 2) & 3u)] = (uint8_t)byte;
+            st_nt32(w, codes + piece * 64 + (c8 & 15u) * 4);
+            if ((c8 & 3u) == 0u) st_nt8(byte, scales + piece * 4 + ((c8 >> 2) & 3u));
         } else {
-            *reinterpret_cast<uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4) = w;
-            if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
+            st_nt32(w, codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
+            if ((c8 & 3u) == 0u) st_nt8(byte, scales + (int64_t)r * (cols / 32) + (c8 >> 2));
         }
     }
     if (bad && nonfinite) *nonfinite = 1;
@@ -506,8 +557,8 @@ __global__ __launch_bounds__(256) void k_mxfp8_quant(const T *__restrict__ x, ui
                                                     0x05040100u) & 0x80808080u;
         const uint32_t lo = e4m3x4_code_sat(a[0], a[1], a[2], a[3]) | s_lo;
         const uint32_t hi = e4m3x4_code_sat(a[4], a[5], a[6], a[7]) | s_hi;
-        *reinterpret_cast<uint2 *>(codes + (int64_t)r * cols + (int64_t)c8 * 8) = make_uint2(lo, hi);
-        if ((c8 & 3u) == 0u) scales[(int64_t)r * (cols / 32) + (c8 >> 2)] = (uint8_t)byte;
+        st_nt64(lo, hi, codes + (int64_t)r * cols + (int64_t)c8 * 8);
+        if ((c8 & 3u) == 0u) st_nt8(byte, scales + (int64_t)r * (cols / 32) + (c8 >> 2));
     }
     if (bad && nonfinite) *nonfinite = 1;
 }
@@ -565,24 +616,21 @@ static void launch_rows_w(const void *x, int64_t rows, int64_t cols, int64_t ldx
 static bool launch_quant_rows_w(const void *x, bool bf, int64_t rows, int64_t cols, int64_t ldx, uint8_t *codes,
                                 uint8_t *scales, float *tscale, int32_t *nonfinite, hipStream_t st)
 {
-    const int64_t u = (cols / 8 + 63) / 64;  // units per lane
-    if ((rows + 3) / 4 > INT32_MAX || u > (bf ? 16 : 8)) return false;
+    const int64_t u = (cols / 16 + 63) / 64;  // 16-blocks per lane
+    if ((rows + 3) / 4 > INT32_MAX || u > (bf ? 8 : 4)) return false;
 #define FP4_ROWS_W(T, U) launch_rows_w<T, U>(x, rows, cols, ldx, codes, scales, tscale, nonfinite, st)
     if (bf) {
         if (u <= 1) FP4_ROWS_W(uint16_t, 1);
         else if (u <= 2) FP4_ROWS_W(uint16_t, 2);
+        else if (u <= 3) FP4_ROWS_W(uint16_t, 3);
         else if (u <= 4) FP4_ROWS_W(uint16_t, 4);
+        else if (u <= 5) FP4_ROWS_W(uint16_t, 5);
         else if (u <= 6) FP4_ROWS_W(uint16_t, 6);
-        else if (u <= 8) FP4_ROWS_W(uint16_t, 8);
-        else if (u <= 10) FP4_ROWS_W(uint16_t, 10);
-        else if (u <= 12) FP4_ROWS_W(uint16_t, 12);
-        else FP4_ROWS_W(uint16_t, 16);
+        else FP4_ROWS_W(uint16_t, 8);
     } else {
         if (u <= 1) FP4_ROWS_W(float, 1);
         else if (u <= 2) FP4_ROWS_W(float, 2);
-        else if (u <= 4) FP4_ROWS_W(float, 4);
-        else if (u <= 6) FP4_ROWS_W(float, 6);
-        else FP4_ROWS_W(float, 8);
+        else FP4_ROWS_W(float, 4);
     }
 #undef FP4_ROWS_W
     return true;

@@ -3,7 +3,8 @@
  *
  * The kernels divide every value a of a block by the block step b as
  *     y  = y0 + y0 (1 - b y0)            (y0: the hardware reciprocal of b)
- *     q0 = a y;  q1 = q0 + (a - b q0) y;  q = q1 + (a - b q1) y   (each "+" an FMA)
+ *     q0 = a y;  q1 = q0 - (b q0 - a) y;  q = q1 - (b q1 - a) y   (each step an FMA)
+ * and expect q to carry the sign of a, also for a = -0.
  * This program checks, for divisors b in [2^-59, 2^59] and numerators that
  * matter for the codes, that q equals the correctly rounded a / b for every y0
  * within one ulp of 1/b (the hardware reciprocal's stated accuracy), on random
@@ -31,8 +32,8 @@ static float refine(float b, float y0) { return fmaf(fmaf(-b, y0, 1.0f), y0, y0)
 static float divr(float a, float b, float y)
 {
     volatile float q0 = a * y;
-    float q1 = fmaf(fmaf(-b, q0, a), y, q0);
-    return fmaf(fmaf(-b, q1, a), y, q1);
+    float q1 = fmaf(-fmaf(b, q0, -a), y, q0);
+    return fmaf(-fmaf(b, q1, -a), y, q1);
 }
 
 int main(int argc, char **argv)
@@ -74,12 +75,14 @@ int main(int argc, char **argv)
                 break;
             }
             if (!isfinite(a)) continue;
+            if ((k >> 40) & 1) a = -a;  /* both signs, -0 included */
             const float want = a / b;
             for (int m = 0; m < 3; ++m) {
                 const float got = divr(a, b, refine(b, ys[m]));
                 ++checked;
                 const int tiny = fabsf(want) < 0x1p-11f;
-                if (tiny ? !(fabsf(got) < 0.125f) : ubits(got) != ubits(want)) {
+                const int sign_ok = signbit(got) == signbit(want);
+                if (!sign_ok || (tiny ? !(fabsf(got) < 0.125f) : ubits(got) != ubits(want))) {
                     if (bad < 5)
                         fprintf(stderr, "mismatch a=%a b=%a y0=%a got %a want %a\n", a, b, ys[m], got, want);
                     ++bad;

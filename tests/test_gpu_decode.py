@@ -173,3 +173,38 @@ def test_decode_gemv_full_size(M):
     c2 = fp4().gemm_w4a16(bf16bits_to_dev(a), _packed_nv(oc, os_, ot), dtype=torch.bfloat16)
     torch.cuda.synchronize()
     assert_gemm_close(c2, ref, tol, f"row-major M={M}")
+
+
+def test_prepared_calls_replay_the_same_launches():
+    """fp4.prepare records the library calls of a thunk (checks made once) and
+    replays them: the replayed GEMV and W4A4 calls (the latter with a workspace the
+    wrapper allocated inside the thunk) give the eager results, call after call,
+    and see new contents of the same input tensors."""
+    m = fp4()
+    N, K = 1000, 1024
+    w = weights(N, K, 0.02, 0.001, 20.0, seed=41)
+    oc, os_, ot = oracle.nvfp4_quantize(w)
+    wp = _packed_nv(oc, os_, ot)
+    wd = m.nvfp4_pack_decode(wp)
+    a_bits = to_bf16_bits(activations_f32(16, K, seed=42))
+    a = bf16bits_to_dev(a_bits)
+    out = torch.empty(16, N, dtype=torch.float32, device=dev())
+    gemv = m.prepare(lambda: m.gemm_w4a16_decode(a, wd, out=out))
+    w4a4 = m.prepare(lambda: m.gemm_w4a4(a, wp, dtype=torch.float32))   # output and workspace made inside
+    eager = m.gemm_w4a16_decode(a, wd, dtype=torch.float32)
+    eager4 = m.gemm_w4a4(a, wp, dtype=torch.float32)
+    torch.cuda.synchronize()
+    c4 = w4a4._keep[0]
+    for rep in range(3):
+        out.zero_()
+        c4.zero_()
+        gemv()
+        w4a4()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager), f"replay {rep}"
+        assert torch.equal(c4, eager4), f"replay {rep}"
+    a.mul_(-1)                                   # new contents, same memory
+    gemv()
+    fresh = m.gemm_w4a16_decode(a, wd, dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(out, fresh) and not torch.equal(out, eager)
