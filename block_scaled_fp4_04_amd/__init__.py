@@ -61,6 +61,7 @@ def _declare(L):
         "gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p, sz, p]),
         "gemm_nvfp4_w4a4_prequant": (i32, [p, p, p, i32, i64, i64, p, p, p, i64, p, i32, i64, p]),
         "gemm_w4a4_seg": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p, sz, p]),
+        "gemm_w4a4_noalloc": (i32, [p, i64, i64, i64, i32, p, p, p, i64, p, i32, i64, p]),
         "gemm_nvfp4_w4a4_prequant_seg": (i32, [p, p, p, i32, i64, i64, p, p, p, i64, p, i32, i64, p]),
         "mxfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, i32, p, p]),
         "mxfp4_dequantize": (i32, [p, p, i64, i64, p, i32, i64, p]),
@@ -484,6 +485,22 @@ def gemm_w4a4(a: torch.Tensor, w: PackedNVFP4, a_mode="row", dtype=torch.bfloat1
               out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """NVFP4 W4A4: quantize bf16 A on the device (per row by default), then C = A_q . W^T."""
     return _w4a4("gemm_w4a4", a, w, a_mode, dtype, out, workspace, _weight_nv)
+
+
+def gemm_w4a4_noalloc(a: torch.Tensor, w: PackedNVFP4, a_mode="row", dtype=torch.bfloat16,
+                      out: torch.Tensor | None = None) -> torch.Tensor:
+    """gemm_w4a4 with A's packed form in the library's own device scratch (32 MiB per
+    device): the library allocates nothing.  Pass `out` to allocate nothing here either.
+    Calls that overlap on one device race for the scratch."""
+    L = lib()
+    M, K = _bf16_a(a, "gemm_w4a4_noalloc")
+    _weight_nv(w, K)
+    m = _mode(a_mode)
+    out = _out(out, M, w.rows, dtype, a)
+    _need_cuda(a, w.codes, w.scales, w.tscale, out)
+    _run(L.gemm_w4a4_noalloc, _ptr(a), M, K, _ld(a), m, _ptr(w.codes), _ptr(w.scales), _ptr(w.tscale), w.rows,
+         _ptr(out), _out_dt(out.dtype), _ld(out), _stream())
+    return out
 
 
 def _prequant_nv(fn_name: str, a: PackedNVFP4, w, dtype, out):

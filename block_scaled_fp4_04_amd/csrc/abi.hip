@@ -441,6 +441,67 @@ fp4_status gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_s
     return w4a4_full(a, M, K, lda, a_mode, w_codes_p, w_scales_p, w_tscale, N, c, ct, ldc, ws, ws_bytes, true, stream);
 }
 
+}  // extern "C"
+
+// ------------------------------------------------ W4A4 without allocation --
+//
+// gemm_w4a4_noalloc keeps A's packed form in `scratch`, a device array of the
+// library itself, instead of a caller's workspace.  Each device holds its own
+// copy from the time the library's code is loaded on it until the process ends.
+// In host code `scratch` names a host-side stand-in, never device memory: its
+// device address is looked up once per device (hipGetSymbolAddress, with that
+// device current) and only that address is passed to kernels.  Nothing in it
+// needs clearing between calls: the quantizer writes every byte the GEMM reads
+// (codes, scales, tensor scales and, per tensor, all amax partials it reduces).
+
+namespace {
+
+constexpr size_t kNoallocScratchBytes = size_t(32) << 20;
+
+static __device__ __align__(256) uint8_t scratch[kNoallocScratchBytes];
+
+std::atomic<uintptr_t> g_scratch_addr[kMaxDevices];  // 0 until looked up on that device
+
+// The device address of the current device's `scratch`, or null on failure.
+void *scratch_on_current_device()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    uintptr_t p = g_scratch_addr[dev].load(std::memory_order_acquire);
+    if (!p) {
+        void *q = nullptr;
+        if (hipGetSymbolAddress(&q, HIP_SYMBOL(scratch)) != hipSuccess || !q) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        p = reinterpret_cast<uintptr_t>(q);
+        g_scratch_addr[dev].store(p, std::memory_order_release);  // racing first calls store the same address
+    }
+    return reinterpret_cast<void *>(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+fp4_status gemm_w4a4_noalloc(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                             const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale, int64_t N,
+                             void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream)
+{
+    if (a_mode != FP4_SCALE_PER_TENSOR && a_mode != FP4_SCALE_PER_ROW) return FP4_ERR_DTYPE;
+    FP4_TRY(check_gemm_common(M, K, N, 16, c, ct, ldc));
+    FP4_TRY(check_matrix(a, M, K, lda, 2));
+    if (M * K > kMaxFlatElems) return FP4_ERR_SHAPE;
+    FP4_TRY(check_packed(w_codes, w_scales));
+    if (!w_tscale) return FP4_ERR_NULL;
+    if (gemm_w4a4_workspace(M, K, a_mode) > kNoallocScratchBytes) return FP4_ERR_WORKSPACE;
+    FP4_TRY(check_device());
+    void *ws = scratch_on_current_device();
+    if (!ws) return FP4_ERR_HIP;
+    return w4a4_full(a, M, K, lda, a_mode, w_codes, w_scales, w_tscale, N, c, ct, ldc, ws, kNoallocScratchBytes, false,
+                     stream);
+}
+
 // ------------------------------------------------------------------ MXFP4 --
 
 fp4_status mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols, int64_t ldx,

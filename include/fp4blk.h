@@ -200,6 +200,24 @@ fp4_status gemm_nvfp4_w4a4_prequant(const uint8_t *a_codes, const uint8_t *a_sca
 fp4_status gemm_w4a4_seg(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
                          const uint8_t *w_codes_p, const uint8_t *w_scales_p, const float *w_tscale, int64_t N,
                          void *c, fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): gemm_w4a4 with A's
+ * packed NVFP4 form kept in the library's own device scratch instead of a
+ * caller's workspace.  The scratch is 32 MiB (33,554,432 bytes) per device, held
+ * from the time the library's code is loaded on the device until the process
+ * ends.  Arguments as gemm_w4a4 without ws / ws_bytes (W row-major); the result
+ * is gemm_w4a4's, bit for bit.  FP4_ERR_WORKSPACE when gemm_w4a4_workspace(M, K,
+ * a_mode) exceeds 32 MiB (M * K up to about 29.6 million with per-row scales),
+ * checked on the host before anything is launched; other errors as gemm_w4a4.
+ * The call allocates and frees nothing.  Every call on a device uses that
+ * device's one scratch: calls that overlap on one device (two streams, or two
+ * host threads without ordering) race and give unspecified results; calls
+ * ordered on one stream do not.  A's packed form stays in the scratch until the
+ * next call, but its address is not part of this interface. */
+fp4_status gemm_w4a4_noalloc(const void *a, int64_t M, int64_t K, int64_t lda, fp4_scale_mode a_mode,
+                             const uint8_t *w_codes, const uint8_t *w_scales, const float *w_tscale, int64_t N,
+                             void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream);
 fp4_status gemm_nvfp4_w4a4_prequant_seg(const uint8_t *a_codes, const uint8_t *a_scales, const float *a_tscale,
                                         fp4_scale_mode a_mode, int64_t M, int64_t K, const uint8_t *w_codes_p,
                                         const uint8_t *w_scales_p, const float *w_tscale, int64_t N, void *c,

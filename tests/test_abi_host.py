@@ -445,3 +445,24 @@ def test_python_binding_fails_loudly_without_library(tmp_path, monkeypatch):
     monkeypatch.setattr(fp4, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="no fallback"):
         fp4.lib()
+
+
+def test_noalloc_validation(L):
+    import torch
+
+    def na(**kw):
+        a = dict(a=FAKE, M=64, K=256, lda=256, mode=1, wc=FAKE, ws=FAKE, wt=FAKE, N=32, c=FAKE, ct=1, ldc=32,
+                 stream=None)
+        a.update(kw)
+        return L.gemm_w4a4_noalloc(*a.values())
+
+    assert na(a=None) == NULL
+    assert na(wt=None) == NULL
+    assert na(K=40, lda=40) == SHAPE
+    assert na(mode=7) == DTYPE
+    assert na(ldc=16) == LAYOUT
+    # beyond the 32 MiB scratch: refused on the host, before any device call
+    assert na(M=12000, K=5120, lda=5120) == WORKSPACE
+    assert na(M=4096, K=16384, lda=16384) == WORKSPACE
+    if not torch.cuda.is_available():
+        assert na() == NO_DEVICE and na(M=8192, K=5120, lda=5120) == NO_DEVICE
