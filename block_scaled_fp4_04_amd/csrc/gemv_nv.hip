@@ -108,8 +108,11 @@ __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale 
 // in bf16); each NVFP4 block's four steps accumulate from zero and the partial is
 // multiplied by the lane's E4M3 scale, so the scale costs 4 FMAs per 16 codes
 // instead of a multiply per code.  The four K-quarters are summed across lanes
-// at the end.  The activation rows (4 x K bf16) are staged in LDS once per
-// workgroup: the lanes 4 p + i of a wave all need row i.
+// at the end (lane-swap instructions, no LDS).  The activation rows (4 x K bf16)
+// are staged in LDS once per workgroup: the lanes 4 p + i of a wave all need
+// row i.  (Loading each wave's fragments from memory instead, with no
+// workgroup barrier, was about 1 us slower at M = 4: 20 more memory
+// instructions per wave, 4 lanes reading each address.)
 template <int S, int NT, bool M4, bool MX>
 __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
 {
@@ -133,6 +136,9 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     const __amdgpu_buffer_rsrc_t rc = gv_rsrc(g.w_codes, (uint32_t)((int64_t)nseg * N * 64));
     constexpr int SB = MX ? 4 : 8;  // scale bytes per row and segment
     const __amdgpu_buffer_rsrc_t rs = gv_rsrc(g.w_scales, (uint32_t)((int64_t)nseg * N * SB));
+    // the tensor scale is read now, not in the epilogue, where its load would wait
+    // behind the weight stream
+    const float ts = MX ? 1.0f : *g.w_tscale;
 
     // unit u = (segment u / NT, tile u % NT): the lane's 32 codes (row n, K 32 grp ..)
     // and their scale byte(s); rows past the workgroup's range and segments the
@@ -294,11 +300,17 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         if (t < nt) {
             f32x4 v = M4 && !MX ? acc[t][0] : acc[t][0] + acc[t][1];
             if constexpr (M4) {
-                // sum the four K-quarters (lanes l, l ^ 16, l ^ 32, l ^ 48)
+                // sum the four K-quarters (lanes l, l ^ 16, l ^ 32, l ^ 48): each swap
+                // returns the value with its rows of 16 (or halves of 32) exchanged,
+                // and the two results add up to lane l's and its partner's
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    v[i] += __shfl_xor(v[i], 16);
-                    v[i] += __shfl_xor(v[i], 32);
+                    const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i]),
+                                                                      false, false);
+                    v[i] = __uint_as_float(h16[0]) + __uint_as_float(h16[1]);
+                    const auto h32 = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i]),
+                                                                      false, false);
+                    v[i] = __uint_as_float(h32[0]) + __uint_as_float(h32[1]);
                 }
             }
             red[t][wave][lane] = v;
@@ -312,7 +324,6 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         f32x4 sum = red[wave][0][lane];
 #pragma unroll
         for (int w = 1; w < W; ++w) sum += red[wave][w][lane];
-        const float ts = MX ? 1.f : *g.w_tscale;  // MXFP4 has no tensor scale
         const int col = r_lo + 16 * wave + n;
         if (col < r_hi) {
 #pragma unroll
