@@ -62,6 +62,9 @@ def parse():
     ap.add_argument("--only-moe", action="store_true", help="grouped (MoE) GEMM components only (profiling runs)")
     ap.add_argument("--only", choices=COMPONENT_GROUPS, default=None,
                     help="with --only-components: one group of components (profiling runs)")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="only the fixed-cost / streaming-rate split: a load-only read and the decode GEMV "
+                         "at 1x, 2x and 4x the weight bytes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -205,6 +208,10 @@ def main():
         print(json.dumps({"copy_bytes": src.numel()}))
         return
 
+    if args.ceiling:
+        print(json.dumps(ceiling(args, torch, fp4, T, dev)))
+        return
+
     if args.only_moe:
         print(json.dumps({"components": {k: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                                                 for kk, vv in v.items()}
@@ -329,6 +336,68 @@ def prepared(fp4, thunk):
     return lambda i: call()
 
 
+def ceiling(args, torch, fp4, T, dev):
+    """Per-launch time against bytes per launch, at 1x, 2x and 4x the decode weight's
+    50.1 MB: for a load-only kernel that reads the bytes once and does nothing else
+    (fp4.read_ceiling), and for the decode GEMV at K = 3072, 5120 and 8192.  A
+    straight-line fit splits each into a fixed cost per launch (the intercept) and a
+    streaming rate (the slope).  Every launch reads its own copy from a rotation
+    whose total exceeds twice the 256 MB Infinity Cache."""
+    R = max(4, args.rotate)
+    wbytes = N * K // 2 + N * K // 16
+    it = max(args.steps, 100)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    res = {"workload": "read: the decode weight's bytes (N = 17408, K = 5120: codes + scales) x {1, 2, 4}; "
+                       "GEMV: N = 17408 at K = 3072, 5120, 8192",
+           "rotated_copies": R, "launches_timed": it, "read": {}, "gemv": {}}
+
+    def fit(xs, ys):
+        b, a = np.polyfit(np.asarray(xs, float), np.asarray(ys, float), 1)
+        return {"fixed_us": round(float(a), 3), "stream_TBps": round(1e-6 / float(b), 3)}  # b: us per byte
+
+    for grid in (1024, 2048):
+        xs, ys = [], []
+        for mult in (1, 2, 4):
+            bufs = [torch.randint(0, 256, (wbytes * mult,), dtype=torch.uint8, device=dev) for _ in range(R)]
+            calls = [fp4.prepare(lambda b=b: fp4.read_ceiling(b, grid, sink)) for b in bufs]
+            t = T.per_launch(lambda i: calls[i % R](), iters=it, warmup=5)
+            res["read"][f"grid{grid}_x{mult}"] = {"bytes": wbytes * mult, "us": round(t * 1e6, 3),
+                                                  "TBps": round(wbytes * mult / t / 1e12, 3),
+                                                  "frac_hbm": round(wbytes * mult / t / HBM_PEAK, 4)}
+            xs.append(wbytes * mult)
+            ys.append(t * 1e6)
+            del bufs, calls
+            torch.cuda.empty_cache()
+        res["read"][f"grid{grid}_fit"] = fit(xs, ys)
+
+    # the GEMV grows along K (K = 3072, 5120, 8192: 3, 5 and 8 of the 128-element
+    # segments per wave, 8192 being the decode kernel's largest K), so its launch
+    # geometry (218 workgroups of 80 weight rows) stays the same and only the bytes
+    # per row grow
+    g = torch.Generator(device="cpu").manual_seed(7)
+    for M in (1, 16):
+        xs, ys = [], []
+        for k in (3072, 5120, 8192):
+            a = (torch.randn(M, k, generator=g)).to(torch.bfloat16).to(dev)
+            w = fp4.nvfp4_quantize((torch.randn(N, k, generator=g) * 0.02).to(dev))
+            d0 = fp4.nvfp4_pack_decode(w)
+            del w
+            ds = [d0] + [fp4.DecodeNVFP4(d0.codes.clone(), d0.scales.clone(), d0.tscale, N, k) for _ in range(R - 1)]
+            out = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+            calls = [fp4.prepare(lambda d=d: fp4.gemm_w4a16_decode(a, d, out=out)) for d in ds]
+            t = T.per_launch(lambda i: calls[i % R](), iters=it, warmup=5)
+            b = M * k * 2 + N * k // 2 + N * k // 16 + 4 + M * N * 2
+            res["gemv"][f"M{M}_K{k}"] = {"K": k, "bytes": b, "us": round(t * 1e6, 3),
+                                            "TBps": round(b / t / 1e12, 3), "frac_hbm": round(b / t / HBM_PEAK, 4)}
+            assert torch.isfinite(out.float()).all()
+            xs.append(b)
+            ys.append(t * 1e6)
+            del ds, calls, d0, out
+            torch.cuda.empty_cache()
+        res["gemv"][f"M{M}_fit"] = fit(xs, ys)
+    return res
+
+
 def components(args, torch, fp4, T, dev, w32, wq):
     from synthetic import WORKLOADS
 
@@ -396,6 +465,36 @@ def quant_components(fp4, T, dev, w32, wq, it, out):
     out["dequantize_bf16_17408x5120"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
                                          "frac_hbm": b / t / HBM_PEAK, "bytes": b}
     del y
+
+    # per-row activation quantize (bf16 -> NVFP4, one tensor scale per row), 4096 x
+    # 5120, on 8 rotating copies (336 MB > the 256 MB Infinity Cache): the kernel
+    # reads its input from HBM, as its counters show
+    Ma = 4096
+    acts = [torch.randn(Ma, K, dtype=torch.float32, device=dev).to(torch.bfloat16) for _ in range(8)]
+    pa = fp4.PackedNVFP4(torch.empty(Ma, K // 2, dtype=torch.uint8, device=dev),
+                         torch.empty(Ma, K // 16, dtype=torch.uint8, device=dev),
+                         torch.empty(Ma, dtype=torch.float32, device=dev), Ma, K, True)
+    pr = [fp4.prepare(lambda x=x: fp4.nvfp4_quantize(x, mode="row", out=pa)) for x in acts]
+    t = T.per_launch(lambda i: pr[i % 8](), max(it, 40))
+    b = Ma * K * 2 + Ma * K // 2 + Ma * K // 16 + 4 * Ma
+    out["activation_quantize_rows_bf16_4096x5120_cold"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                                           "frac_hbm": b / t / HBM_PEAK, "bytes": b}
+    # MXFP4 quantize of the 8192 x 5120 bf16 activation (E8M0 per 32), cold as above
+    acts = [torch.randn(2 * Ma, K, dtype=torch.float32, device=dev).to(torch.bfloat16) for _ in range(4)]
+    pm = fp4.PackedMXFP4(torch.empty(2 * Ma, K // 2, dtype=torch.uint8, device=dev),
+                         torch.empty(2 * Ma, K // 32, dtype=torch.uint8, device=dev), 2 * Ma, K)
+    pr = [fp4.prepare(lambda x=x: fp4.mxfp4_quantize(x, out=pm)) for x in acts]
+    t = T.per_launch(lambda i: pr[i % 4](), max(it, 40))
+    b = 2 * Ma * K * 2 + 2 * Ma * K // 2 + 2 * Ma * K // 32
+    out["mxfp4_quantize_bf16_8192x5120_cold"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                                 "frac_hbm": b / t / HBM_PEAK, "bytes": b}
+    # MXFP4 dequantize of that tensor to bf16
+    y = torch.empty(2 * Ma, K, dtype=torch.bfloat16, device=dev)
+    t = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_dequantize(pm, out=y)), it)
+    b = 2 * Ma * K // 2 + 2 * Ma * K // 32 + 2 * Ma * K * 2
+    out["mxfp4_dequantize_bf16_8192x5120"] = {"us": t * 1e6, "GB/s": b / t / 1e9,
+                                              "frac_hbm": b / t / HBM_PEAK, "bytes": b}
+    del acts, pr, y
 
 
 def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):

@@ -50,6 +50,7 @@ def _declare(L):
         "fp4_status_str": (ctypes.c_char_p, [i32]),
         "fp4blk_version": (i32, []),
         "fp4blk_check_device": (i32, []),
+        "fp4blk_read_ceiling": (i32, [p, sz, i32, p, p]),
         "nvfp4_quantize_workspace": (sz, [i64, i64, i32]),
         "nvfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, p, i32, p, sz, p, p]),
         "nvfp4_dequantize": (i32, [p, p, p, i32, i64, i64, p, i32, i64, p]),
@@ -433,6 +434,19 @@ def nvfp4_pack_decode(w: PackedNVFP4, out: DecodeNVFP4 | None = None) -> DecodeN
     _run(L.nvfp4_pack_decode, _ptr(w.codes), _ptr(w.scales), N, K, _ptr(out.codes), _ptr(out.scales),
                                _stream())
     return out
+
+
+def read_ceiling(buf: torch.Tensor, grid: int, sink: torch.Tensor) -> None:
+    """Measurement aid: read every byte of `buf` (a contiguous device tensor whose
+    size is a multiple of 16 bytes) once, on `grid` workgroups, computing nothing
+    from it.  `sink` is a device int32/uint32 tensor of at least one element."""
+    L = lib()
+    if not buf.is_contiguous() or buf.numel() * buf.element_size() % 16:
+        raise ValueError("buf must be contiguous, a multiple of 16 bytes")
+    if sink.dtype not in (torch.int32, torch.uint32) or sink.numel() < 1:
+        raise ValueError("sink must hold one 32-bit integer")
+    _need_cuda(buf, sink)
+    _run(L.fp4blk_read_ceiling, _ptr(buf), buf.numel() * buf.element_size(), int(grid), _ptr(sink), _stream())
 
 
 def gemm_w4a16_decode(a: torch.Tensor, w: DecodeNVFP4, dtype=torch.bfloat16,

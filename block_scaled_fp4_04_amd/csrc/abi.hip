@@ -102,6 +102,15 @@ int fp4blk_version(void) { return 10000; }
 
 fp4_status fp4blk_check_device(void) { return check_device(); }
 
+fp4_status fp4blk_read_ceiling(const void *buf, size_t bytes, int grid, uint32_t *sink, hipStream_t stream)
+{
+    if (!buf || !sink) return FP4_ERR_NULL;
+    if (bytes == 0 || bytes % 16 != 0 || grid <= 0 || grid > 65535) return FP4_ERR_SHAPE;
+    if (!aligned16(buf)) return FP4_ERR_LAYOUT;
+    FP4_TRY(check_device());
+    return launch_read_ceiling(buf, bytes, grid, sink, stream);
+}
+
 // ------------------------------------------------------------------ NVFP4 --
 
 size_t nvfp4_quantize_workspace(int64_t rows, int64_t cols, fp4_scale_mode mode)

@@ -875,9 +875,10 @@ struct NvPipe {
     static constexpr int NA = F == kFmtNv44 ? S::NI : 1;
     typedef float f32x2 __attribute__((ext_vector_type(2)));
     u32x4 wc[S::NJ];
-    f32x2 wsc[S::NJ];
+    f32x2 wsc[S::NJ];  // W4A16: the lane's two block scales as fp32
+    f16x2 wsh[S::NJ];  // W4A4: the same as fp16 (exact), for the fp16 widening
     u32x4 ac[NA];
-    f32x2 asc[NA];
+    f16x2 ash[NA];
     uint32_t wb, wsb;  // W codes / scales of MFMA tile 0
     uint32_t ab, asb;  // A codes / scales (W4A4) or bf16 row (W4A16) of MFMA tile 0
     uint32_t ak[4];    // W4A16: swizzled 16-byte chunk of step ks in a bf16 A row
@@ -917,6 +918,9 @@ __device__ __forceinline__ void nv_pipe_raw(NvPipe<F, L, TM, TN> &p, const uint8
             // scaled conversion takes its exponent from
             const uint32_t e = st[S::kWS + p.wsb + 2 * (t & 1) + 128 * j];
             p.wsc[j][0] = __uint_as_float(e << 23);
+        } else if constexpr (F == kFmtNv44) {
+            p.wsh[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                (uint32_t)*reinterpret_cast<const uint16_t *>(st + S::kWS + p.wsb + 128 * j), 1.0f, false);
         } else {
             p.wsc[j] = __builtin_amdgcn_cvt_pk_f32_fp8(
                 (int)*reinterpret_cast<const uint16_t *>(st + S::kWS + p.wsb + 128 * j), false);
@@ -926,8 +930,8 @@ __device__ __forceinline__ void nv_pipe_raw(NvPipe<F, L, TM, TN> &p, const uint8
 #pragma unroll
         for (int i = 0; i < S::NI; ++i) {
             p.ac[i] = *reinterpret_cast<const u32x4 *>(st + S::kA + p.ab + 1024 * i);
-            p.asc[i] = __builtin_amdgcn_cvt_pk_f32_fp8(
-                (int)*reinterpret_cast<const uint16_t *>(st + S::kAS + p.asb + 128 * i), false);
+            p.ash[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
+                (uint32_t)*reinterpret_cast<const uint16_t *>(st + S::kAS + p.asb + 128 * i), 1.0f, false);
         }
     }
 }
@@ -943,26 +947,34 @@ __device__ __forceinline__ void nv_pipe_frags(const NvPipe<F, L, TM, TN> &p, con
     for (int j = 0; j < S::NJ; ++j) {
         if constexpr (F == kFmtMx16)
             wf[j] = e2m1x8_bf16_pow2(p.wc[j][KS], p.wsc[j][0]);
+        else if constexpr (F == kFmtNv44)
+            wf[j] = as_bf16x8(dq8_f16(p.wc[j][KS], KS < 2 ? p.wsh[j][0] : p.wsh[j][1]));
         else
             wf[j] = as_bf16x8(dq8_bf16(p.wc[j][KS], KS < 2 ? p.wsc[j][0] : p.wsc[j][1]));
     }
 #pragma unroll
     for (int i = 0; i < S::NI; ++i) {
         if constexpr (F == kFmtNv44)
-            af[i] = as_bf16x8(dq8_bf16(p.ac[i][KS], KS < 2 ? p.asc[i][0] : p.asc[i][1]));
+            af[i] = as_bf16x8(dq8_f16(p.ac[i][KS], KS < 2 ? p.ash[i][0] : p.ash[i][1]));
         else
             af[i] = *reinterpret_cast<const bf16x8 *>(st + S::kA + p.ab + p.ak[KS] + 4096 * i);
     }
 }
 
-template <int NI, int NJ>
+// F16: the fragments hold fp16 bits (W4A4, both operands widened exactly to fp16)
+template <int NI, int NJ, bool F16>
 __device__ __forceinline__ void nv_pipe_mfma(f32x16 (&acc)[NI][NJ], const bf16x8 (&wf)[NJ], const bf16x8 (&af)[NI])
 {
 #pragma unroll
     for (int i = 0; i < NI; ++i)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < NJ; ++j) {
+            if constexpr (F16)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, wf[j]),
+                                                                   __builtin_bit_cast(f16x8, af[i]), acc[i][j], 0, 0, 0);
+            else
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[j], af[i], acc[i][j], 0, 0, 0);
+        }
 }
 
 // Spread the NM MFMAs of a step over the widening (NV VALU) and the reads (ND)
@@ -1014,18 +1026,18 @@ __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, 
     using S = NvTile<F == 1, L, TM, TN>;
     constexpr bool A_FP4 = F == kFmtNv44;
     constexpr int NI = S::NI, NJ = S::NJ, NM = NI * NJ;
-    constexpr int NV = (F == kFmtMx16 ? 4 : 16) * (NJ + (A_FP4 ? NI : 0));  // VALU per step's widening, about
+    constexpr int NV = (F == kFmtMx16 ? 4 : A_FP4 ? 8 : 16) * (NJ + (A_FP4 ? NI : 0));  // VALU per step's widening, about
     constexpr int ND = A_FP4 ? 0 : NI;                // DS reads per step
     constexpr int P = NM >= 8 ? 4 : 1;
     bf16x8 wf1[NJ], af1[NI];
     nv_pipe_frags<F, L, TM, TN, 1>(p, cur, wf1, af1);
-    nv_pipe_mfma<NI, NJ>(acc, wf, af);
+    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf, af);
     nv_pipe_interleave<NM, NV, ND>();
     nv_pipe_frags<F, L, TM, TN, 2>(p, cur, wf, af);
-    nv_pipe_mfma<NI, NJ>(acc, wf1, af1);
+    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf1, af1);
     nv_pipe_interleave<NM, NV, ND>();
     nv_pipe_frags<F, L, TM, TN, 3>(p, cur, wf1, af1);
-    nv_pipe_mfma<NI, NJ>(acc, wf, af);
+    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf, af);
     nv_pipe_interleave<NM, NV, ND>();
     nv_wait_vm<S::kDma>();
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0)
@@ -1033,7 +1045,7 @@ __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, 
     nv_pipe_raw<F, L, TM, TN>(p, nxt, t + 1);
     nv_ring_dma<F, L, TM, TN>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
     nv_pipe_frags<F, L, TM, TN, 0>(p, nxt, wf, af);
-    nv_pipe_mfma<NI, NJ>(acc, wf1, af1);
+    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf1, af1);
     nv_pipe_interleave<NM, NV, ND, 2 * (A_FP4 ? NI + NJ : NJ), S::kDma, P>();
 }
 

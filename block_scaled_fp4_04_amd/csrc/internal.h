@@ -29,6 +29,8 @@ fp4_status launch_nvfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int6
 fp4_status launch_nvfp4_dequantize(const uint8_t *codes, const uint8_t *scales, const float *tscale,
                                    fp4_scale_mode mode, int64_t rows, int64_t cols, void *y,
                                    fp4_dtype yt, int64_t ldy, hipStream_t st);
+// load-only pass over bytes (a multiple of 16) at buf on grid x 512 threads (measure.hip)
+fp4_status launch_read_ceiling(const void *buf, size_t bytes, int grid, uint32_t *sink, hipStream_t st);
 fp4_status launch_mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t cols,
                                  int64_t ldx, uint8_t *codes, uint8_t *scales, fp4_mx_rule rule,
                                  int32_t *nonfinite, hipStream_t st);

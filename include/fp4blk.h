@@ -418,6 +418,19 @@ fp4_status nvfp4_grouped_gemm_w4a4_prequant(const uint8_t *a_codes, const uint8_
                                             const uint8_t *w_scales, const float *w_tscale, int64_t N,
                                             void *c, fp4_dtype ct, int64_t ldc, hipStream_t stream);
 
+/* ---------------------------------------------------------- measurement --
+ * fp4blk_read_ceiling: reads `bytes` bytes at `buf` once, with `grid`
+ * workgroups of 512 threads striding over 16-byte words, and computes nothing
+ * from them.  Its duration is the reference for the decode GEMV, which streams
+ * its weight exactly once per call and is therefore bound by memory bandwidth
+ * (edge-FP4 article, eefocus.com, section on the trade-offs of compute, memory
+ * and precision).  A measurement aid, not part of the quantization path.
+ * buf: device, 16-byte aligned; bytes: > 0, a multiple of 16; grid: 1..65535;
+ * sink: device uint32, written only in the (practically never taken) case that
+ * the XOR of all words equals a fixed constant.  FP4_ERR_NULL / _SHAPE /
+ * _LAYOUT on bad arguments, nothing launched. */
+fp4_status fp4blk_read_ceiling(const void *buf, size_t bytes, int grid, uint32_t *sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

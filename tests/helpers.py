@@ -56,3 +56,21 @@ def assert_gemm_close(c: torch.Tensor | np.ndarray, ref: np.ndarray, tol: np.nda
     assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside 2e-3*sum|aw|; worst ratio "
                            f"{(err / np.maximum(lim, 1e-300)).max():.3g}")
     assert np.isfinite(got).all(), what
+
+
+def sample_rows(M: int, n: int = 256, seed: int = 0) -> np.ndarray:
+    """Rows 0 and M - 1 and n distinct others, drawn with a seeded generator, sorted."""
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, M - 1], rng.choice(M, min(n, M), replace=False)]))
+
+
+def assert_bf16_is_rounded(c_bf16: torch.Tensor, c_f32: torch.Tensor, what: str) -> None:
+    """A bf16 output equals the fp32 output of the same call rounded to nearest even,
+    element for element (the kernels accumulate in fp32 the same way for both)."""
+    assert c_bf16.dtype == torch.bfloat16 and c_f32.dtype == torch.float32
+    want = c_f32.to(torch.bfloat16)
+    same = c_bf16.view(torch.int16) == want.view(torch.int16)
+    if not bool(same.all()):
+        bad = (~same).nonzero()[:3].tolist()
+        raise AssertionError(f"{what}: {int((~same).sum())} bf16 outputs differ from the rounded fp32 "
+                             f"output, first at {bad}")

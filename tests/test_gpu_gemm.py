@@ -12,7 +12,8 @@ import pytest
 import torch
 
 import oracle
-from helpers import assert_gemm_close, bf16bits_to_dev, dev, f32_to_dev, log
+from helpers import (assert_bf16_is_rounded, assert_gemm_close, bf16bits_to_dev, dev, f32_to_dev, log,
+                     sample_rows)
 from synthetic import WORKLOADS, activations_f32, to_bf16_bits, weights
 
 pytestmark = pytest.mark.gpu
@@ -217,61 +218,75 @@ def _full_weights():
 
 @pytest.mark.parametrize("M", [1, 4, 16])
 def test_decode_gemv_full_size(M):
+    """fp32 output, every element under 2e-3 * sum|a w|; the bf16 output (the form
+    the benchmark times) is that result rounded to nearest even, element for element."""
     wl = WORKLOADS["decode_gemv_k5120_n17408"]
     log(f"decode GEMV full size M={M} N=17408 K=5120")
     _, (oc, os_, ot) = _full_weights()
     a = wl.activations_bf16(M)
-    c = fp4().gemm_w4a16(bf16bits_to_dev(a), _packed_nv(oc, os_, ot), dtype=torch.bfloat16)
+    w = _packed_nv(oc, os_, ot)
+    c = fp4().gemm_w4a16(bf16bits_to_dev(a), w, dtype=torch.float32)
+    cb = fp4().gemm_w4a16(bf16bits_to_dev(a), w, dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot)
     assert_gemm_close(c, ref, tol, f"decode M={M}")
+    assert_bf16_is_rounded(cb, c, f"decode M={M} bf16")
 
 
-def _sample_rows(M, n=48, seed=0):
-    rng = np.random.default_rng(seed)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, n, replace=False)]))
-    return rows
+def _full_size_check(c32, cb, ref_fn, rows, what):
+    """c32 / cb: the fp32 and bf16 outputs of one call on the full workload.  The
+    sampled rows of c32 against the oracle under the literal bound; all of cb
+    against c32 rounded to bf16."""
+    ref, tol = ref_fn(rows)
+    assert_gemm_close(c32[torch.from_numpy(rows).to(dev())], ref, tol, what)
+    assert_bf16_is_rounded(cb, c32, what + " bf16")
 
 
 def test_prefill_w4a16_full_size_sampled():
     wl = WORKLOADS["prefill_w4a16_m4096"]
-    log("prefill W4A16 full size M=4096 N=17408 K=5120 (sampled rows vs oracle)")
+    log("prefill W4A16 full size M=4096 N=17408 K=5120 (256 sampled rows vs oracle)")
     _, (oc, os_, ot) = _full_weights()
     a = wl.activations_bf16(4096)
-    c = fp4().gemm_w4a16(bf16bits_to_dev(a), _packed_nv(oc, os_, ot), dtype=torch.bfloat16)
+    ad, w = bf16bits_to_dev(a), _packed_nv(oc, os_, ot)
+    c = fp4().gemm_w4a16(ad, w, dtype=torch.float32)
+    cb = fp4().gemm_w4a16(ad, w, dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = _sample_rows(4096)
-    ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot, rows=rows)
-    assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, "prefill w4a16 sampled")
+    _full_size_check(c, cb, lambda r: oracle.gemm_w4a16_ref(a, oc, os_, ot, rows=r), sample_rows(4096),
+                     "prefill w4a16 sampled")
 
 
 def test_prefill_w4a4_full_size_sampled():
     wl = WORKLOADS["prefill_w4a4_m4096"]
-    log("prefill W4A4 full size M=4096 N=17408 K=5120 (sampled rows vs oracle)")
+    log("prefill W4A4 full size M=4096 N=17408 K=5120 (256 sampled rows vs oracle)")
     _, (oc, os_, ot) = _full_weights()
     a = wl.activations_bf16(4096)
-    c = fp4().gemm_w4a4(bf16bits_to_dev(a), _packed_nv(oc, os_, ot), a_mode="row", dtype=torch.bfloat16)
+    ad, w = bf16bits_to_dev(a), _packed_nv(oc, os_, ot)
+    c = fp4().gemm_w4a4(ad, w, a_mode="row", dtype=torch.float32)
+    cb = fp4().gemm_w4a4(ad, w, a_mode="row", dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = _sample_rows(4096, seed=1)
-    ref, tol = oracle.gemm_w4a4_ref(a, oc, os_, ot, a_per_row=True, rows=rows)
-    assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, "prefill w4a4 sampled")
+    _full_size_check(c, cb, lambda r: oracle.gemm_w4a4_ref(a, oc, os_, ot, a_per_row=True, rows=r),
+                     sample_rows(4096, seed=1), "prefill w4a4 sampled")
 
 
 def test_mx_vs_nv_full_size_sampled():
     wl = WORKLOADS["mx_vs_nv_w4a4_m8192"]
-    log("MXFP4 vs NVFP4 W4A4 full size M=8192 N=17408 K=5120 (sampled rows vs oracle)")
+    log("MXFP4 vs NVFP4 W4A4 full size M=8192 N=17408 K=5120 (256 sampled rows vs oracle)")
     w, _ = _full_weights()
     wb = to_bf16_bits(w)
     a = wl.activations_bf16(8192)
     ad = bf16bits_to_dev(a)
+    rows = sample_rows(8192, seed=2)
     wc, wsc = oracle.mxfp4_quantize(wb)
-    cm = fp4().mxfp4_gemm_w4a4(ad, _packed_mx(wc, wsc), dtype=torch.bfloat16)
-    nc, ns, nt = oracle.nvfp4_quantize(wb)
-    cn = fp4().gemm_w4a4(ad, _packed_nv(nc, ns, nt), a_mode="row", dtype=torch.bfloat16)
+    wm = _packed_mx(wc, wsc)
+    cm = fp4().mxfp4_gemm_w4a4(ad, wm, dtype=torch.float32)
+    cmb = fp4().mxfp4_gemm_w4a4(ad, wm, dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rows = _sample_rows(8192, seed=2)
-    rt = torch.from_numpy(rows).to(dev())
-    refm, tolm = oracle.mxfp4_gemm_w4a4_ref(a, wc, wsc, rows=rows)
-    assert_gemm_close(cm[rt], refm, tolm, "mxfp4 sampled")
-    refn, toln = oracle.gemm_w4a4_ref(a, nc, ns, nt, a_per_row=True, rows=rows)
-    assert_gemm_close(cn[rt], refn, toln, "nvfp4 w4a4 sampled")
+    _full_size_check(cm, cmb, lambda r: oracle.mxfp4_gemm_w4a4_ref(a, wc, wsc, rows=r), rows, "mxfp4 sampled")
+    del cm, cmb
+    nc, ns, nt = oracle.nvfp4_quantize(wb)
+    wn = _packed_nv(nc, ns, nt)
+    cn = fp4().gemm_w4a4(ad, wn, a_mode="row", dtype=torch.float32)
+    cnb = fp4().gemm_w4a4(ad, wn, a_mode="row", dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    _full_size_check(cn, cnb, lambda r: oracle.gemm_w4a4_ref(a, nc, ns, nt, a_per_row=True, rows=r), rows,
+                     "nvfp4 w4a4 sampled")

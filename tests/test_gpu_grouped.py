@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import assert_gemm_close, bf16bits_to_dev, dev, log
+from helpers import assert_bf16_is_rounded, assert_gemm_close, bf16bits_to_dev, dev, log
 from synthetic import MOE_WORKLOADS, activations_f32, group_by_expert, moe_routing, to_bf16_bits, weights
 
 pytestmark = pytest.mark.gpu
@@ -170,11 +170,13 @@ def test_grouped_full_size_sampled(fmt):
             wc, wsc, wts = oracle.nvfp4_quantize(w[e])
             assert ts[e] == wts[0]
         assert np.array_equal(codes[e], wc) and np.array_equal(scales[e], wsc)
-    c = _run(fmt, a, dw, offs, ridx, torch.bfloat16)
+    c = _run(fmt, a, dw, offs, ridx, torch.float32)
+    cb = _run(fmt, a, dw, offs, ridx, torch.bfloat16)
     torch.cuda.synchronize()
+    assert_bf16_is_rounded(cb, c, f"grouped {fmt}")
     rng = np.random.default_rng(6)
     live = np.nonzero(np.diff(offs))[0]
     edge = np.concatenate([offs[live], offs[live + 1] - 1])          # first and last row of every group
-    rows = np.unique(np.concatenate([edge, rng.choice(int(offs[-1]), 200, replace=False)]))
+    rows = np.unique(np.concatenate([edge, rng.choice(int(offs[-1]), 256, replace=False)]))
     ref, tol = _ref(fmt, a, codes, scales, ts, offs, ridx, rows)
     assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, f"grouped {fmt} sampled")

@@ -14,7 +14,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import assert_gemm_close, bf16bits_to_dev, dev, log
+from helpers import assert_bf16_is_rounded, assert_gemm_close, bf16bits_to_dev, dev, log, sample_rows
 from synthetic import WORKLOADS, activations_f32, to_bf16_bits, weights
 
 pytestmark = pytest.mark.gpu
@@ -174,20 +174,25 @@ def test_mxfp4_decode_full_size(M):
     wc, wsc = _full_mx()
     a = wl.activations_bf16(M)
     d = fp4().mxfp4_pack_decode(_packed_mx(wc, wsc))
-    c = fp4().mxfp4_gemm_w4a16_decode(bf16bits_to_dev(a), d, dtype=torch.bfloat16)
+    ad = bf16bits_to_dev(a)
+    c = fp4().mxfp4_gemm_w4a16_decode(ad, d, dtype=torch.float32)
+    cb = fp4().mxfp4_gemm_w4a16_decode(ad, d, dtype=torch.bfloat16)
     torch.cuda.synchronize()
     ref, tol = oracle.mxfp4_gemm_w4a16_ref(a, wc, wsc)
     assert_gemm_close(c, ref, tol, f"mxfp4 decode M={M}")
+    assert_bf16_is_rounded(cb, c, f"mxfp4 decode M={M}")
 
 
 def test_mxfp4_prefill_full_size_sampled():
     wl = WORKLOADS["prefill_w4a16_m4096"]
-    log("MXFP4 W4A16 prefill full size M=4096 N=17408 K=5120 (sampled rows vs oracle)")
+    log("MXFP4 W4A16 prefill full size M=4096 N=17408 K=5120 (256 sampled rows vs oracle)")
     wc, wsc = _full_mx()
     a = wl.activations_bf16(4096)
-    c = fp4().mxfp4_gemm_w4a16(bf16bits_to_dev(a), _packed_mx(wc, wsc), dtype=torch.bfloat16)
+    ad, w = bf16bits_to_dev(a), _packed_mx(wc, wsc)
+    c = fp4().mxfp4_gemm_w4a16(ad, w, dtype=torch.float32)
+    cb = fp4().mxfp4_gemm_w4a16(ad, w, dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(2)
-    rows = np.unique(np.concatenate([[0, 4095], rng.choice(4096, 48, replace=False)]))
+    rows = sample_rows(4096, seed=2)
     ref, tol = oracle.mxfp4_gemm_w4a16_ref(a, wc, wsc, rows=rows)
     assert_gemm_close(c[torch.from_numpy(rows).to(dev())], ref, tol, "mxfp4 prefill sampled")
+    assert_bf16_is_rounded(cb, c, "mxfp4 prefill")

@@ -20,7 +20,7 @@ import pytest
 import torch
 
 import oracle
-from helpers import assert_gemm_close, bf16bits_to_dev, dev, log
+from helpers import assert_bf16_is_rounded, assert_gemm_close, bf16bits_to_dev, dev, log, sample_rows
 from synthetic import WORKLOADS, activations_f32, to_bf16_bits, weights
 
 pytestmark = pytest.mark.gpu
@@ -128,7 +128,7 @@ def test_mxfp4_seg_exact_when_scales_are_powers_of_two(M, N, K):
 def test_mxfp4_seg_full_size():
     wl = WORKLOADS["mx_vs_nv_w4a4_m8192"]
     M, N, K = 8192, wl.N, wl.K
-    log(f"mxfp4_gemm_w4a4_seg full size M={M} N={N} K={K} (all of C vs the row-major kernel, sampled rows vs oracle)")
+    log(f"mxfp4_gemm_w4a4_seg full size M={M} N={N} K={K} (all of C vs the row-major kernel, 256 sampled rows vs oracle)")
     w = WORKLOADS["decode_gemv_k5120_n17408"].weights()
     wb = to_bf16_bits(w)
     a = wl.activations_bf16(M)
@@ -136,11 +136,14 @@ def test_mxfp4_seg_full_size():
     wp = _packed_mx(wc, wsc)
     wd = fp4().mxfp4_pack_decode(wp)
     ad = bf16bits_to_dev(a)
-    cs = fp4().mxfp4_gemm_w4a4_seg(ad, wd, dtype=torch.bfloat16)
-    cr = fp4().mxfp4_gemm_w4a4(ad, wp, dtype=torch.bfloat16)
+    cs = fp4().mxfp4_gemm_w4a4_seg(ad, wd, dtype=torch.float32)
+    cr = fp4().mxfp4_gemm_w4a4(ad, wp, dtype=torch.float32)
     torch.cuda.synchronize()
-    assert torch.equal(cs.view(torch.int16), cr.view(torch.int16))
-    rng = np.random.default_rng(4)
-    rows = np.unique(np.concatenate([[0, M - 1], rng.choice(M, 48, replace=False)]))
+    assert torch.equal(cs, cr)
+    del cr
+    csb = fp4().mxfp4_gemm_w4a4_seg(ad, wd, dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert_bf16_is_rounded(csb, cs, "mxfp4 seg full size")
+    rows = sample_rows(M, seed=4)
     ref, tol = oracle.mxfp4_gemm_w4a4_ref(a, wc, wsc, rows=rows)
     assert_gemm_close(cs[torch.from_numpy(rows).to(dev())], ref, tol, "mxfp4 seg full size sampled")
