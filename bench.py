@@ -507,9 +507,16 @@ def prefill_components(torch, fp4, T, dev, wq, wl3, it, out):
     # the same GEMMs on the weight in the decode layout (one packed weight for decode and prefill)
     wd = fp4.nvfp4_pack_decode(wq)
     t_d = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a16_decode(a, wd, out=c)), it)
+    # yardstick: the same product as a dense bf16 GEMM in the vendor library
+    # (torch.matmul -> hipBLASLt), the weight already widened to bf16 in HBM
+    wb16 = fp4.nvfp4_dequantize(wq, torch.bfloat16)
+    t_ref = T.per_launch(lambda i: torch.matmul(a, wb16.t(), out=c), it)
+    del wb16
     out["prefill_w4a16_m4096"] = {"us": t * 1e6, "TFLOP/s": fl / t / 1e12, "frac_bf16_mfma": fl / t / BF16_PEAK,
                                   "decode_layout_us": t_d * 1e6, "decode_layout_TFLOP/s": fl / t_d / 1e12,
                                   "decode_layout_frac_bf16_mfma": fl / t_d / BF16_PEAK,
+                                  "dense_bf16_library_us": t_ref * 1e6,
+                                  "dense_bf16_library_frac_bf16_mfma": fl / t_ref / BF16_PEAK,
                                   "flop": fl, "mfma": "bf16 32x32x16 (NVFP4 widened exactly to bf16)"}
     # activation quantization alone (per row) and the fused W4A4 call
     wsa = fp4.gemm_w4a4_workspace(M, K, "row", dev)

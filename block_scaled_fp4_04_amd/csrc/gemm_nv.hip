@@ -772,6 +772,29 @@ __global__ __launch_bounds__(256) void k_nv_gemm(NvGemmArgs g)
 // the last K % 3 stages peeled; copies of stages past K go through size-0
 // descriptors (zeros, nothing read).
 constexpr int kRK = 64;  // K elements per stage
+// 8 E2M1 codes times one E4M3 block scale -> 8 fp16, exact.  An E2M1 magnitude
+// has at most 2 significant bits and an E4M3 value at most 4, so their product
+// has at most 6 (fp16 keeps 11), and it lies in [2^-10, 2688], inside fp16's
+// normal range: the packed fp16 multiply never rounds.  (bf16 would hold the
+// product too, but gfx950 has no packed bf16 multiply: the bf16 form above
+// multiplies in fp32 and packs, 16 VALU per 8 elements against 8 here.)
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+__device__ __forceinline__ uint4 dq8_f16(uint32_t codes, _Float16 bs)
+{
+    const f16x2 s = {bs, bs};
+    const f16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s;
+    const f16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s;
+    const f16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s;
+    const f16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s;
+    uint4 r;
+    __builtin_memcpy(&r.x, &p0, 4);
+    __builtin_memcpy(&r.y, &p1, 4);
+    __builtin_memcpy(&r.z, &p2, 4);
+    __builtin_memcpy(&r.w, &p3, 4);
+    return r;
+}
+
 // Operand formats of the ring kernel (template parameter F): W4A16 with NVFP4
 // weights, W4A4 with NVFP4 on both sides, W4A16 with MXFP4 weights.
 constexpr int kFmtNv16 = 0, kFmtNv44 = 1, kFmtMx16 = 2;

@@ -574,10 +574,32 @@ __global__ __launch_bounds__(256) void k_mxfp4_dequant(const uint8_t *__restrict
         const uint32_t c8 = u - r * cv.d;
         const uint32_t w = *reinterpret_cast<const uint32_t *>(codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
         const int k = (int)scales[(int64_t)r * (cols / 32) + (c8 >> 2)] - 127;
+        const int64_t off = (int64_t)r * ldy + (int64_t)c8 * 8;
+        if (k >= -120 && k <= 120) {
+            // E2M1 times 2^k with every result normal and finite: the scaled
+            // conversion applies exactly 2^k (it takes the exponent field of its
+            // fp32 scale operand), 2 elements per instruction
+            const float sc = __uint_as_float((uint32_t)(k + 127) << 23);
+            if (OUT_BF16) {
+                *reinterpret_cast<bf16x8 *>(reinterpret_cast<uint16_t *>(y) + off) = e2m1x8_bf16_pow2(w, sc);
+            } else {
+                typedef float f32x2 __attribute__((ext_vector_type(2)));
+                const f32x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 0);
+                const f32x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 1);
+                const f32x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 2);
+                const f32x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, sc, 3);
+                float *yp = reinterpret_cast<float *>(y) + off;
+                *reinterpret_cast<float4 *>(yp) = make_float4(p0[0], p0[1], p1[0], p1[1]);
+                *reinterpret_cast<float4 *>(yp + 4) = make_float4(p2[0], p2[1], p3[0], p3[1]);
+            }
+            continue;
+        }
+        // the extreme scales (subnormal or overflowing results) one element at a
+        // time; the E8M0 byte 0xFF encodes NaN, which every element then takes
         float o[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) o[i] = __builtin_amdgcn_ldexpf(e2m1_value(w >> (4 * i)), k);
-        const int64_t off = (int64_t)r * ldy + (int64_t)c8 * 8;
+        for (int i = 0; i < 8; ++i)
+            o[i] = k == 128 ? __uint_as_float(0x7FC00000u) : __builtin_amdgcn_ldexpf(e2m1_value(w >> (4 * i)), k);
         if (OUT_BF16) {
             uint4 p;
             p.x = f32_to_bf16_rne(o[0]) | (f32_to_bf16_rne(o[1]) << 16);

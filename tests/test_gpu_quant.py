@@ -326,6 +326,28 @@ def test_mxfp4_dequantize():
     assert np.array_equal(bf16_tensor_bits(y16), oracle.f32_to_bf16_bits(yo))
 
 
+def test_mxfp4_dequantize_every_scale_and_code():
+    """Every E8M0 byte (0..254 and the NaN byte 0xFF) with all 16 codes in both
+    nibble positions: fp32 and bf16 bits equal the oracle's (subnormal results at
+    the low end, overflow to infinity at the high end, NaN for 0xFF)."""
+    rows, cols = 256, 64
+    codes = np.empty((rows, cols // 2), np.uint8)
+    lo = np.arange(32, dtype=np.uint8) % 16
+    hi = (np.arange(32, dtype=np.uint8) * 7 + 3) % 16
+    codes[:] = lo | (hi << 4)
+    scales = np.repeat(np.arange(256, dtype=np.uint8)[:, None], cols // 32, axis=1)
+    p = fp4().PackedMXFP4(torch.from_numpy(codes).to(dev()), torch.from_numpy(scales).to(dev()), rows, cols)
+    y32 = fp4().mxfp4_dequantize(p, torch.float32)
+    y16 = fp4().mxfp4_dequantize(p, torch.bfloat16)
+    torch.cuda.synchronize()
+    yo = oracle.mxfp4_dequantize(codes, scales)
+    assert np.isnan(yo[255]).all() and np.isinf(yo[254]).any() and (yo[0] != 0).any()
+    got = y32.cpu().numpy().view(np.uint32)
+    bad = np.argwhere(got != yo.view(np.uint32))
+    assert bad.size == 0, f"{len(bad)} fp32 mismatches, first (row = scale byte, col) {bad[:4].tolist()}"
+    assert np.array_equal(bf16_tensor_bits(y16), oracle.f32_to_bf16_bits(yo))
+
+
 def test_mxfp4_full_size_activations():
     wl = WORKLOADS["mx_vs_nv_w4a4_m8192"]
     _mx_check(wl.activations_bf16(8192), "ocp", "activations 8192x5120 bf16")
