@@ -355,7 +355,7 @@ def ceiling(args, torch, fp4, T, dev):
         b, a = np.polyfit(np.asarray(xs, float), np.asarray(ys, float), 1)
         return {"fixed_us": round(float(a), 3), "stream_TBps": round(1e-6 / float(b), 3)}  # b: us per byte
 
-    for grid in (1024, 2048):
+    for grid in (256, 512, 1024, 2048):  # 1, 2, 4, 8 workgroups of 8 waves per CU
         xs, ys = [], []
         for mult in (1, 2, 4):
             bufs = [torch.randint(0, 256, (wbytes * mult,), dtype=torch.uint8, device=dev) for _ in range(R)]

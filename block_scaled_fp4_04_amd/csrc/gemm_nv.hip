@@ -823,13 +823,17 @@ struct NvTile {
     static constexpr int nW = TN * 2 / 256;
     static constexpr int kDma = nA + nW + 1 + (A_FP4 ? 1 : 0);
     // epilogue: the two row halves of the tile are staged through two stage
-    // buffers, R rows at a time (rows padded by 16 bytes)
+    // buffers, R rows at a time (rows padded by 16 bytes).  128 x 256 tiles stage
+    // 32 rows a round, so that their stage stays at the size the K loop needs and
+    // two workgroups fit in a CU's LDS (bf16 output)
     static constexpr int H = TM / 2;
-    static constexpr int epi_rows(int es) { return (es == 2 ? 64 : 32) < H ? (es == 2 ? 64 : 32) : H; }
+    static constexpr bool kTwoPerCu = TM == 128 && TN == 256;
+    static constexpr int epi_rows(int es) { return kTwoPerCu ? 32 : (es == 2 ? 64 : 32) < H ? (es == 2 ? 64 : 32) : H; }
     static constexpr int epi_pitch(int es) { return TN * es + 16; }
-    static constexpr int kEpi = epi_rows(2) * epi_pitch(2) > epi_rows(4) * epi_pitch(4)
-                                    ? epi_rows(2) * epi_pitch(2) : epi_rows(4) * epi_pitch(4);
-    static constexpr int kStage = kUsed > kEpi ? kUsed : kEpi;
+    static constexpr int stage_bytes(int es)
+    {
+        return kUsed > epi_rows(es) * epi_pitch(es) ? kUsed : epi_rows(es) * epi_pitch(es);
+    }
 };
 
 struct NvRingDma {
@@ -1088,7 +1092,7 @@ __device__ __forceinline__ void nv_ring_epilogue(
     constexpr int pitch = S::epi_pitch(es);
     constexpr int R = S::epi_rows(es);
     constexpr int kPer = 16 / es, kChunks = TN / kPer;
-    static_assert(R * pitch <= S::kStage, "epilogue staging");
+    static_assert(R * pitch <= S::stage_bytes(es), "epilogue staging");
     constexpr bool A_FP4 = F == kFmtNv44;
     const int M = (int)g.M, N = (int)g.N;
     const float wt = F == kFmtMx16 ? 1.f : g.w_tscale[0];  // MXFP4 has no tensor scale
@@ -1217,15 +1221,17 @@ __device__ __forceinline__ bool nv_group_tile(const NvGemmArgs &g, int b, int &e
 // GR: the grouped form (one weight per group, rows by group offsets, optional
 // row gather from A; see NvGemmArgs)
 template <int F, int L, typename OutT, int TM, int TN, bool GR = false>
-__global__ __launch_bounds__(256) void k_nv_gemm_ring(NvGemmArgs g)
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(TM == 128 && TN == 256 ? 2 : 1)))
+void k_nv_gemm_ring(NvGemmArgs g)
 {
     using S = NvTile<F == 1, L, TM, TN>;
     constexpr bool A_FP4 = F == kFmtNv44;
     constexpr int kWsRow = F == kFmtMx16 ? 32 : 16;  // K elements per weight scale byte
     constexpr int NI = S::NI, NJ = S::NJ;
-    __shared__ __align__(16) uint8_t s0[S::kStage];
-    __shared__ __align__(16) uint8_t s1[S::kStage];
-    __shared__ __align__(16) uint8_t s2[S::kStage];
+    constexpr int kStage = S::stage_bytes((int)sizeof(OutT));
+    __shared__ __align__(16) uint8_t s0[kStage];
+    __shared__ __align__(16) uint8_t s1[kStage];
+    __shared__ __align__(16) uint8_t s2[kStage];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int N = (int)g.N, K = (int)g.K;

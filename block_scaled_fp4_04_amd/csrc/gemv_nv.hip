@@ -117,7 +117,7 @@ template <int S, int NT, bool M4, bool MX>
 __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
 {
     constexpr int W = kGvWaves;
-    constexpr int D = M4 ? 8 : 5;  // units (tile, segment) of weight loads in flight
+    constexpr int D = M4 ? 8 : 4;  // units (tile, segment) of weight loads in flight (measured best: 3..8 tried)
     __shared__ f32x4 red[NT][W][64];
     __shared__ __align__(16) uint16_t alds[M4 ? 4 * 1024 * S : 8];  // M4: A rows 0..3, K <= 1024 S
     __shared__ __align__(16) uint8_t a16[M4 ? 16 : W * 2 * 4096];    // M > 4: per wave, two segments of A
