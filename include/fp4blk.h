@@ -41,8 +41,12 @@
  *
  * Conventions:
  *  - Every data pointer is a DEVICE pointer owned by the caller.  The library
- *    allocates and frees nothing and keeps no mutable global state apart from a
- *    per-device "is this a gfx950" cache; calls are thread-safe.
+ *    allocates and frees nothing.  Its only global state is per-device and
+ *    written once per device with atomics (whether the device is a gfx950, its
+ *    CU count, which kernels had their LDS limit raised, the device address of
+ *    the scratch array of gemm_w4a4_noalloc), plus that scratch array itself;
+ *    calls are thread-safe, except that calls of gemm_w4a4_noalloc that
+ *    overlap on one device share its scratch.
  *  - Every call is asynchronous on `stream` (0 = the null stream) and never
  *    synchronizes the host.
  *  - Arguments are validated on the host before anything is launched; on an
@@ -235,7 +239,7 @@ fp4_status mxfp4_quantize(const void *x, fp4_dtype xt, int64_t rows, int64_t col
 /* MXFP4 dequantize (eefocus.com edge-FP4 article, "FP4 as the next core
  * standard": each 32-element block shares one E8M0 power-of-two scale):
  *  y = E2M1(c) * 2^(s-127) (exact when in range), fp32, or bf16 by round to
- *  nearest even.  codes [rows][cols/2], scales [rows][cols/32]: device, read
+ *  nearest even; the scale byte 0xFF (E8M0's NaN) gives NaN for its block.  codes [rows][cols/2], scales [rows][cols/32]: device, read
  *  only; cols % 32 == 0.  y [rows][ldy] out (ldy >= cols, 16-byte aligned rows).
  * Errors (host, nothing launched): FP4_ERR_NULL, FP4_ERR_SHAPE, FP4_ERR_LAYOUT,
  * FP4_ERR_DTYPE. */
