@@ -113,7 +113,9 @@ __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale 
 // row i.  (Loading each wave's fragments from memory instead, with no
 // workgroup barrier, was about 1 us slower at M = 4: 20 more memory
 // instructions per wave, 4 lanes reading each address.)
-template <int S, int NT, bool M4, bool MX>
+// M1 (with M4): exactly one activation row; of the four rows the 4x4x4 blocks
+// produce only row 0 is scaled, reduced and stored.
+template <int S, int NT, bool M4, bool MX, bool M1 = false>
 __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
 {
     constexpr int W = kGvWaves;
@@ -143,15 +145,28 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     // unit u = (segment u / NT, tile u % NT): the lane's 32 codes (row n, K 32 grp ..)
     // and their scale byte(s); rows past the workgroup's range and segments the
     // wave does not own read nothing
+    // The lane's byte offsets within a segment, per tile (fixed for the whole
+    // walk: rows past the range get kGvOut), and the segment's start as the scalar
+    // offset; a segment the wave does not own goes through size-0 descriptors.
+    // So a unit's loads take no vector arithmetic.  Offsets stay below 2^32: the
+    // segment starts are below the codes' size (< 2^31, checked on the host).
+    uint32_t vo_c[NT], vo_s[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) {
+        const int row = r_lo + 16 * t + n;
+        vo_c[t] = row < r_hi ? (uint32_t)row * 64u + 16u * grp : kGvOut;
+        vo_s[t] = row < r_hi ? (uint32_t)row * SB + (MX ? 1u : 2u) * grp : kGvOut;
+    }
+    const __amdgpu_buffer_rsrc_t rc0 = gv_rsrc(g.w_codes, 0), rs0 = gv_rsrc(g.w_scales, 0);
     auto issue = [&](int u, u32x4 &c, uint32_t &sc) {
         const int s = u / NT, t = u % NT;
-        const bool ok = s < ns && r_lo + 16 * t + n < r_hi;
-        const int64_t e = (int64_t)(seg0 + s) * N + r_lo + 16 * t + n;
-        c = __builtin_amdgcn_raw_buffer_load_b128(rc, (int)(ok ? (uint32_t)(e * 64 + 16 * grp) : kGvOut), 0, 0);
+        const bool own = s < ns;  // wave-uniform
+        const int seg = own ? seg0 + s : 0;
+        c = __builtin_amdgcn_raw_buffer_load_b128(own ? rc : rc0, (int)vo_c[t], seg * N * 64, 0);
         if constexpr (MX)
-            sc = __builtin_amdgcn_raw_buffer_load_b8(rs, (int)(ok ? (uint32_t)(e * SB + grp) : kGvOut), 0, 0);
+            sc = __builtin_amdgcn_raw_buffer_load_b8(own ? rs : rs0, (int)vo_s[t], seg * N * SB, 0);
         else
-            sc = __builtin_amdgcn_raw_buffer_load_b16(rs, (int)(ok ? (uint32_t)(e * SB + 2 * grp) : kGvOut), 0, 0);
+            sc = __builtin_amdgcn_raw_buffer_load_b16(own ? rs : rs0, (int)vo_s[t], seg * N * SB, 0);
     };
     // activation fragments of segment s: A row arow (zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8).
     // M <= 4 reads them from the workgroup's staged rows.  M > 4 copies each
@@ -249,7 +264,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
 #pragma unroll
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
-                    for (int i = 0; i < 4; ++i) acc0[i] = __builtin_fmaf(part[blk][i], bs[blk], acc0[i]);
+                    for (int i = 0; i < (M1 ? 1 : 4); ++i) acc0[i] = __builtin_fmaf(part[blk][i], bs[blk], acc0[i]);
             }
         } else if constexpr (MX) {
             const float msc = __uint_as_float(sc << 23);
@@ -304,7 +319,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
                 // returns the value with its rows of 16 (or halves of 32) exchanged,
                 // and the two results add up to lane l's and its partner's
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
+                for (int i = 0; i < (M1 ? 1 : 4); ++i) {
                     const auto h16 = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i]),
                                                                       false, false);
                     v[i] = __uint_as_float(h16[0]) + __uint_as_float(h16[1]);
@@ -357,7 +372,9 @@ fp4_status launch_pack_decode(const uint8_t *codes, const uint8_t *scales, int64
 template <int S, int NT, bool MX>
 static void launch_gemv(const GemvArgs &g, unsigned grid, hipStream_t st)
 {
-    if (g.M <= 4)
+    if (g.M == 1 && !MX)
+        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX, true>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    else if (g.M <= 4)
         hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
     else
         hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, false, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
