@@ -466,3 +466,23 @@ def test_noalloc_validation(L):
     assert na(M=4096, K=16384, lda=16384) == WORKSPACE
     if not torch.cuda.is_available():
         assert na() == NO_DEVICE and na(M=8192, K=5120, lda=5120) == NO_DEVICE
+
+
+def test_read_ceiling_validation(L):
+    """The measurement entry point refuses bad arguments on the host, before any
+    device call: null pointers, a size that is zero or not a multiple of 16, a grid
+    out of range, a misaligned buffer."""
+    import torch
+
+    def rc(buf=FAKE, nbytes=1 << 20, grid=256, sink=FAKE):
+        return L.fp4blk_read_ceiling(buf, nbytes, grid, sink, None)
+
+    assert rc(buf=None) == NULL
+    assert rc(sink=None) == NULL
+    assert rc(nbytes=0) == SHAPE
+    assert rc(nbytes=1000) == SHAPE
+    assert rc(grid=0) == SHAPE
+    assert rc(grid=65536) == SHAPE
+    assert rc(buf=FAKE + 8) == LAYOUT
+    if not torch.cuda.is_available():
+        assert rc() == NO_DEVICE

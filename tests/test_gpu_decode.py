@@ -216,3 +216,18 @@ def test_prepared_calls_replay_the_same_launches():
     fresh = m.gemm_w4a16_decode(a, wd, dtype=torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(out, fresh) and not torch.equal(out, eager)
+
+
+def test_read_ceiling_runs_and_reads_nothing_back():
+    """The measurement kernel reads its buffer and leaves the sink alone (the sink
+    is written only when the XOR of all words hits one fixed constant, which this
+    buffer's words do not)."""
+    log("fp4blk_read_ceiling on 1 MiB + 16 bytes")
+    buf = torch.zeros((1 << 20) + 16, dtype=torch.uint8, device=dev())
+    sink = torch.zeros(1, dtype=torch.int32, device=dev())
+    for grid in (1, 7, 256, 2048):
+        fp4().read_ceiling(buf, grid, sink)
+    torch.cuda.synchronize()
+    assert int(sink.item()) == 0
+    with pytest.raises(ValueError):
+        fp4().read_ceiling(buf[:1000], 16, sink)
