@@ -81,6 +81,23 @@ __device__ __forceinline__ void nv_wait_vm_gv()
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// the same for a count that is a compile-time constant only once the walk is
+// unrolled (the switch then folds to one wait)
+__device__ __forceinline__ void nv_wait_vm_gv_n(int n)
+{
+    switch (n) {
+    case 0: nv_wait_vm_gv<0>(); break;
+    case 1: nv_wait_vm_gv<1>(); break;
+    case 2: nv_wait_vm_gv<2>(); break;
+    case 3: nv_wait_vm_gv<3>(); break;
+    case 4: nv_wait_vm_gv<4>(); break;
+    case 5: nv_wait_vm_gv<5>(); break;
+    case 6: nv_wait_vm_gv<6>(); break;
+    case 7: nv_wait_vm_gv<7>(); break;
+    default: nv_wait_vm_gv<8>(); break;
+    }
+}
+
 // E2M1 x 4 (two code bytes, low nibble first) -> bf16 x 4, times the power of two
 // in `scale`'s exponent field (1.0: unscaled); exact.
 __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale = 1.0f)
@@ -123,6 +140,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     __shared__ f32x4 red[NT][W][64];
     __shared__ __align__(16) uint16_t alds[M4 ? 4 * 1024 * S : 8];  // M4: A rows 0..3, K <= 1024 S
     __shared__ __align__(16) uint8_t a16[M4 ? 16 : W * 2 * 4096];    // M > 4: per wave, two segments of A
+    __shared__ __align__(16) uint8_t sclds[W][M4 ? 16 : 1024];       // M > 4, per wave: one segment's block scales
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int n = lane & 15, grp = lane >> 4;
@@ -145,10 +163,10 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     // unit u = (segment u / NT, tile u % NT): the lane's 32 codes (row n, K 32 grp ..)
     // and their scale byte(s); rows past the workgroup's range and segments the
     // wave does not own read nothing
-    // The lane's byte offsets within a segment, per tile (fixed for the whole
+    // The lane's code byte offset within a segment, per tile (fixed for the whole
     // walk: rows past the range get kGvOut), and the segment's start as the scalar
     // offset; a segment the wave does not own goes through size-0 descriptors.
-    // So a unit's loads take no vector arithmetic.  Offsets stay below 2^32: the
+    // So a unit's load takes no vector arithmetic.  Offsets stay below 2^32: the
     // segment starts are below the codes' size (< 2^31, checked on the host).
     uint32_t vo_c[NT], vo_s[NT];
 #pragma unroll
@@ -158,15 +176,41 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         vo_s[t] = row < r_hi ? (uint32_t)row * SB + (MX ? 1u : 2u) * grp : kGvOut;
     }
     const __amdgpu_buffer_rsrc_t rc0 = gv_rsrc(g.w_codes, 0), rs0 = gv_rsrc(g.w_scales, 0);
+    // M <= 4: a unit loads its codes and its lane's scale byte(s).  M > 4 takes the
+    // scales per segment instead (below).
     auto issue = [&](int u, u32x4 &c, uint32_t &sc) {
         const int s = u / NT, t = u % NT;
         const bool own = s < ns;  // wave-uniform
         const int seg = own ? seg0 + s : 0;
         c = __builtin_amdgcn_raw_buffer_load_b128(own ? rc : rc0, (int)vo_c[t], seg * N * 64, 0);
+        if constexpr (M4) {
+            if constexpr (MX)
+                sc = __builtin_amdgcn_raw_buffer_load_b8(own ? rs : rs0, (int)vo_s[t], seg * N * SB, 0);
+            else
+                sc = __builtin_amdgcn_raw_buffer_load_b16(own ? rs : rs0, (int)vo_s[t], seg * N * SB, 0);
+        }
+    };
+    // M > 4: block scales per segment.  The workgroup's rows are consecutive, so one
+    // segment's scale bytes of all its tiles are one run of 16 NT SB bytes (640 for
+    // NVFP4 with 5 tiles): one 16-byte load per lane fetches them (lanes past the
+    // run read nothing), the wave parks them in its LDS slot, and each unit reads
+    // its lane's byte(s) back.  This takes one load instruction per unit off the
+    // address unit (13.5 -> 13.1 us at M = 16); at M <= 4, whose units are shorter,
+    // the per-unit LDS read cost more than it saved (11.0 -> 11.3 us at M = 1).
+    constexpr int kScLanes = (16 * NT * SB + 15) / 16;
+    auto sc_load = [&](int s) -> u32x4 {
+        const bool own = s < ns;
+        const int seg = own ? seg0 + s : 0;
+        const uint32_t off = lane < kScLanes ? 16u * lane : kGvOut;
+        return __builtin_amdgcn_raw_buffer_load_b128(own ? rs : rs0, (int)off, (seg * N + r_lo) * SB, 0);
+    };
+    auto sc_park = [&](const u32x4 &v) { *reinterpret_cast<u32x4 *>(&sclds[wave][16 * lane]) = v; };
+    auto sc_read = [&](int t) -> uint32_t {
+        const int b = (16 * t + n) * SB + (MX ? 1 : 2) * grp;
         if constexpr (MX)
-            sc = __builtin_amdgcn_raw_buffer_load_b8(own ? rs : rs0, (int)vo_s[t], seg * N * SB, 0);
+            return sclds[wave][b];
         else
-            sc = __builtin_amdgcn_raw_buffer_load_b16(own ? rs : rs0, (int)vo_s[t], seg * N * SB, 0);
+            return *reinterpret_cast<const uint16_t *>(&sclds[wave][b]);
     };
     // activation fragments of segment s: A row arow (zero past M), K 128 (seg0 + s) + 32 grp + 8 j + [0, 8).
     // M <= 4 reads them from the workgroup's staged rows.  M > 4 copies each
@@ -203,7 +247,8 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     };
 
     u32x4 bc[D];
-    uint32_t bsc[D];
+    uint32_t bsc[D];  // M <= 4: the units' scale byte(s)
+    u32x4 scv;        // M > 4: the next segment's scale run, in flight
     if constexpr (M4) {
         // the A loads go out first, then the first units' weight loads, so waiting
         // for A does not wait for them
@@ -217,7 +262,8 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
             ach[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
         }
 #pragma unroll
-        for (int k = 0; k < D - 1; ++k) issue(k, bc[k], bsc[k]);
+        for (int k = 0; k < D - 1; ++k)
+            if (k < S * NT) issue(k, bc[k], bsc[k]);
 #pragma unroll
         for (int c = 0; c < S; ++c) {
             const int idx = (int)threadIdx.x + 64 * W * c;
@@ -230,10 +276,15 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     if constexpr (M4) {
         frags(0, af[0]);
     } else {
+        // the scale run goes out before the copy, in a scheduling region of its
+        // own, so that only code loads follow the copy (the wait counts below)
+        scv = sc_load(0);
+        __builtin_amdgcn_sched_barrier(0);
         a_dma(0, 0);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int k = 0; k < D - 1; ++k) issue(k, bc[k], bsc[k]);
+        for (int k = 0; k < D - 1; ++k)
+            if (k < S * NT) issue(k, bc[k], bsc[k]);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -290,22 +341,37 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         if constexpr (M4) {
             if (s + 1 < S) frags(s + 1, af[(s + 1) & 1]);
         } else {
-            // segment s's copy is older than every load issued after it: the 2 (D - 1)
-            // of the first units before segment 0, then 2 NT per segment (each unit
-            // issues its two loads, past the end too, where they read nothing)
-            if (s == 0) nv_wait_vm_gv<2 * (D - 1)>();
-            else nv_wait_vm_gv<2 * NT>();
+            // segment s's copy is older than every load issued after it: the code
+            // loads of the units the walk looks ahead to, D - 1 before segment 0 and
+            // NT per segment, fewer at the end of the walk, where units past the last
+            // are not loaded (the compiler would drop loads whose data go unused,
+            // and the counts must be exact; the next segment's scale run goes out
+            // before its copy)
+            const int ahead = s == 0 ? min(D - 1, S * NT) : max(0, min(NT, S * NT - ((s - 1) * NT + D - 1)));
+            nv_wait_vm_gv_n(ahead);
             __builtin_amdgcn_sched_barrier(0);
             frags16(s & 1, af[s & 1]);
+            // segment s's scales to the LDS slot (the wave's reads of segment s - 1's
+            // are older: a wave's LDS operations complete in order), the next run out
+            sc_park(scv);
+            if (s + 1 < S) scv = sc_load(s + 1);
+            __builtin_amdgcn_sched_barrier(0);
             if (s + 1 < S) a_dma(s + 1, (s + 1) & 1);
             __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int t = 0; t < NT; ++t) {
             const int u = s * NT + t;
-            if (!M4 || u + D - 1 < S * NT) issue(u + D - 1, bc[(u + D - 1) % D], bsc[(u + D - 1) % D]);
+            if (u + D - 1 < S * NT) issue(u + D - 1, bc[(u + D - 1) % D], bsc[(u + D - 1) % D]);
             __builtin_amdgcn_sched_barrier(0);
-            if (t < nt) unit(af[s & 1], bc[u % D], bsc[u % D], acc[t][0], acc[t][1]);
+            if (t < nt) {
+                uint32_t sc;
+                if constexpr (M4)
+                    sc = bsc[u % D];
+                else
+                    sc = sc_read(t);
+                unit(af[s & 1], bc[u % D], sc, acc[t][0], acc[t][1]);
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
