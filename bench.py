@@ -65,6 +65,9 @@ def parse():
     ap.add_argument("--ceiling", action="store_true",
                     help="only the fixed-cost / streaming-rate split: a load-only read and the decode GEMV "
                          "at 1x, 2x and 4x the weight bytes")
+    ap.add_argument("--ceiling-short", action="store_true",
+                    help="with --ceiling: only the read at one workgroup per CU over 1x the bytes and the GEMV "
+                         "at K = 5120 (counter runs: one configuration per kernel)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 512 MiB device copy (counter calibration)")
     return ap.parse_args()
@@ -355,9 +358,10 @@ def ceiling(args, torch, fp4, T, dev):
         b, a = np.polyfit(np.asarray(xs, float), np.asarray(ys, float), 1)
         return {"fixed_us": round(float(a), 3), "stream_TBps": round(1e-6 / float(b), 3)}  # b: us per byte
 
-    for grid in (256, 512, 1024, 2048):  # 1, 2, 4, 8 workgroups of 8 waves per CU
+    short = args.ceiling_short
+    for grid in ((256,) if short else (256, 512, 1024, 2048)):  # 1, 2, 4, 8 workgroups of 8 waves per CU
         xs, ys = [], []
-        for mult in (1, 2, 4):
+        for mult in ((1,) if short else (1, 2, 4)):
             bufs = [torch.randint(0, 256, (wbytes * mult,), dtype=torch.uint8, device=dev) for _ in range(R)]
             calls = [fp4.prepare(lambda b=b: fp4.read_ceiling(b, grid, sink)) for b in bufs]
             t = T.per_launch(lambda i: calls[i % R](), iters=it, warmup=5)
@@ -368,7 +372,8 @@ def ceiling(args, torch, fp4, T, dev):
             ys.append(t * 1e6)
             del bufs, calls
             torch.cuda.empty_cache()
-        res["read"][f"grid{grid}_fit"] = fit(xs, ys)
+        if not short:
+            res["read"][f"grid{grid}_fit"] = fit(xs, ys)
 
     # the GEMV grows along K (K = 3072, 5120, 8192: 3, 5 and 8 of the 128-element
     # segments per wave, 8192 being the decode kernel's largest K), so its launch
@@ -377,7 +382,7 @@ def ceiling(args, torch, fp4, T, dev):
     g = torch.Generator(device="cpu").manual_seed(7)
     for M in (1, 16):
         xs, ys = [], []
-        for k in (3072, 5120, 8192):
+        for k in ((5120,) if short else (3072, 5120, 8192)):
             a = (torch.randn(M, k, generator=g)).to(torch.bfloat16).to(dev)
             w = fp4.nvfp4_quantize((torch.randn(N, k, generator=g) * 0.02).to(dev))
             d0 = fp4.nvfp4_pack_decode(w)
@@ -394,7 +399,8 @@ def ceiling(args, torch, fp4, T, dev):
             ys.append(t * 1e6)
             del ds, calls, d0, out
             torch.cuda.empty_cache()
-        res["gemv"][f"M{M}_fit"] = fit(xs, ys)
+        if not short:
+            res["gemv"][f"M{M}_fit"] = fit(xs, ys)
     return res
 
 
