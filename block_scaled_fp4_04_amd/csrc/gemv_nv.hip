@@ -221,12 +221,16 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     // memory touches 32; the chunk swizzle lets each 16-lane group of a fragment
     // read hit 16 different bank groups.
     const int arow = M4 ? (lane & 3) : n;
+    // A segment the wave does not own reads a valid one and selects zeros, with
+    // no branch: the walk then has none at all, and the accumulators keep their
+    // registers from unit to unit (around a branch the compiler copied them whole).
     auto frags = [&](int s, bf16x8 (&dst)[4]) {
+        const bool own = s < ns;  // wave-uniform
+        const int sg = min(seg0 + s, nseg - 1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            bf16x8 v = {};
-            if (s < ns) v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * (seg0 + s) + 32 * grp + 8 * j);
-            dst[j] = v;
+            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * sg + 32 * grp + 8 * j);
+            dst[j] = own ? v : bf16x8{};
         }
     };
     typedef __attribute__((address_space(3))) void gv_lds_void;
@@ -333,9 +337,10 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         }
     };
 
-    // the walk: fully unrolled, so every buffer is a fixed register set and no
-    // load in flight crosses a loop back edge; units of tiles at or past nt are
-    // neither loaded (their rows lie past the range) nor multiplied
+    // the walk: fully unrolled and free of branches, so every buffer is a fixed
+    // register set and no load in flight crosses a loop back edge.  Units of tiles
+    // at or past nt (rows past the range) and of segments the wave does not own
+    // read nothing and multiply zero codes: their sums are zero or never stored.
 #pragma unroll
     for (int s = 0; s < S; ++s) {
         if constexpr (M4) {
@@ -364,7 +369,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
             const int u = s * NT + t;
             if (u + D - 1 < S * NT) issue(u + D - 1, bc[(u + D - 1) % D], bsc[(u + D - 1) % D]);
             __builtin_amdgcn_sched_barrier(0);
-            if (t < nt) {
+            {
                 uint32_t sc;
                 if constexpr (M4)
                     sc = bsc[u % D];
