@@ -80,6 +80,35 @@ def test_decode_gemv(M, N, K, out):
     assert_gemm_close(c, ref, tol, f"decode {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("M", [1, 4, 16])
+def test_decode_infinite_activation_stays_in_its_row(M):
+    """An infinite activation of row 0 in the last K segment (K = 1152: nine
+    segments, so waves 5-7 of a workgroup own none and read that segment's
+    position for nothing): row 0 of C is +-inf where the weight at that K is
+    nonzero and NaN where it is zero, exactly as the fp64 product gives, and every
+    other row is finite and within the GEMM bound (a wave that multiplied the
+    infinity by its zero codes would turn all of row 0 into NaN)."""
+    N, K, k0 = 300, 1152, 1100
+    log(f"gemm_w4a16_decode M={M} N={N} K={K} with A[0, {k0}] = +inf")
+    w = weights(N, K, 0.02, 0.001, 20.0, seed=91 + M)
+    a = to_bf16_bits(activations_f32(M, K, 0.005, 30.0, seed=92 + M))
+    a[0, k0] = 0x7F80  # +inf in bf16
+    oc, os_, ot = oracle.nvfp4_quantize(w)
+    d = fp4().nvfp4_pack_decode(_packed_nv(oc, os_, ot))
+    with np.errstate(invalid="ignore"):  # inf * 0 in the reference product
+        ref, tol = oracle.gemm_w4a16_ref(a, oc, os_, ot)
+    assert np.isnan(ref[0]).any() and np.isinf(ref[0]).any()  # both kinds occur
+    for dt in (torch.float32, torch.bfloat16):
+        c = fp4().gemm_w4a16_decode(bf16bits_to_dev(a), d, dtype=dt)
+        torch.cuda.synchronize()
+        got = c.float().cpu().numpy().astype(np.float64)
+        assert np.array_equal(np.isnan(got[0]), np.isnan(ref[0])), "NaN positions of row 0"
+        inf = np.isinf(ref[0])
+        assert np.array_equal(np.isinf(got[0]), inf) and np.array_equal(np.sign(got[0][inf]), np.sign(ref[0][inf]))
+        if M > 1:
+            assert_gemm_close(c[1:], ref[1:], tol[1:], f"decode rows 1.. with inf in row 0, {dt}")
+
+
 def _grid_vals(rng, shape, top_every):
     """E2M1 grid values with a +-6 every `top_every` elements (so every 16-block of
     the weight gets the same scale byte)."""
