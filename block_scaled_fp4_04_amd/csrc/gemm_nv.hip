@@ -932,8 +932,10 @@ __device__ __forceinline__ void nv_pipe_init(NvPipe<F, L, TM, TN> &p, int wave, 
 }
 
 // read the stage's packed rows (codes + scales) into registers
-// (t: the stage's index; MXFP4 picks its E8M0 byte pair by t's parity)
-template <int F, int L, int TM, int TN>
+// (t: the stage's index; MXFP4 picks its E8M0 byte pair by t's parity).
+// NIL: the wave's 32-row blocks that hold rows of the tile (the others are
+// neither read nor multiplied; grouped tiles past their group's last row)
+template <int F, int L, int TM, int TN, int NIL = NvTile<F == 1, L, TM, TN>::NI>
 __device__ __forceinline__ void nv_pipe_raw(NvPipe<F, L, TM, TN> &p, const uint8_t *st, int t)
 {
     using S = NvTile<F == 1, L, TM, TN>;
@@ -955,7 +957,7 @@ __device__ __forceinline__ void nv_pipe_raw(NvPipe<F, L, TM, TN> &p, const uint8
     }
     if constexpr (F == kFmtNv44) {
 #pragma unroll
-        for (int i = 0; i < S::NI; ++i) {
+        for (int i = 0; i < NIL; ++i) {
             p.ac[i] = *reinterpret_cast<const u32x4 *>(st + S::kA + p.ab + 1024 * i);
             p.ash[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(
                 (uint32_t)*reinterpret_cast<const uint16_t *>(st + S::kAS + p.asb + 128 * i), 1.0f, false);
@@ -964,7 +966,7 @@ __device__ __forceinline__ void nv_pipe_raw(NvPipe<F, L, TM, TN> &p, const uint8
 }
 
 // fragments of step ks: lane half h holds K = 32 h + 8 ks + [0, 8) of the stage
-template <int F, int L, int TM, int TN, int KS>
+template <int F, int L, int TM, int TN, int KS, int NIL = NvTile<F == 1, L, TM, TN>::NI>
 __device__ __forceinline__ void nv_pipe_frags(const NvPipe<F, L, TM, TN> &p, const uint8_t *st,
                                               bf16x8 (&wf)[NvTile<F == 1, L, TM, TN>::NJ],
                                               bf16x8 (&af)[NvTile<F == 1, L, TM, TN>::NI])
@@ -980,7 +982,7 @@ __device__ __forceinline__ void nv_pipe_frags(const NvPipe<F, L, TM, TN> &p, con
             wf[j] = as_bf16x8(dq8_bf16(p.wc[j][KS], KS < 2 ? p.wsc[j][0] : p.wsc[j][1]));
     }
 #pragma unroll
-    for (int i = 0; i < S::NI; ++i) {
+    for (int i = 0; i < NIL; ++i) {
         if constexpr (F == kFmtNv44)
             af[i] = as_bf16x8(dq8_f16(p.ac[i][KS], KS < 2 ? p.ash[i][0] : p.ash[i][1]));
         else
@@ -988,12 +990,13 @@ __device__ __forceinline__ void nv_pipe_frags(const NvPipe<F, L, TM, TN> &p, con
     }
 }
 
-// F16: the fragments hold fp16 bits (W4A4, both operands widened exactly to fp16)
-template <int NI, int NJ, bool F16>
+// F16: the fragments hold fp16 bits (W4A4, both operands widened exactly to fp16);
+// row blocks NIL .. NI - 1 are left alone
+template <int NI, int NJ, bool F16, int NIL = NI>
 __device__ __forceinline__ void nv_pipe_mfma(f32x16 (&acc)[NI][NJ], const bf16x8 (&wf)[NJ], const bf16x8 (&af)[NI])
 {
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
+    for (int i = 0; i < NIL; ++i)
 #pragma unroll
         for (int j = 0; j < NJ; ++j) {
             if constexpr (F16)
@@ -1043,7 +1046,7 @@ __device__ __forceinline__ void nv_wait_vm()
 // returned, and a barrier extends both to every wave, so `cur` is free: the copy
 // of stage t + 3 starts into it.  Step 3 multiplies while stage t + 1's packed
 // rows and step-0 fragments are read from `nxt`.  One basic block per stage.
-template <int F, int L, int TM, int TN>
+template <int F, int L, int TM, int TN, int NIL = NvTile<F == 1, L, TM, TN>::NI>
 __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, int t, int nk, const NvRingDma &d,
                                               const NvRingDma &dz, int wave, NvPipe<F, L, TM, TN> &p,
                                               f32x16 (&acc)[NvTile<F == 1, L, TM, TN>::NI][NvTile<F == 1, L, TM, TN>::NJ],
@@ -1052,28 +1055,52 @@ __device__ __forceinline__ void nv_pipe_stage(uint8_t *cur, const uint8_t *nxt, 
 {
     using S = NvTile<F == 1, L, TM, TN>;
     constexpr bool A_FP4 = F == kFmtNv44;
-    constexpr int NI = S::NI, NJ = S::NJ, NM = NI * NJ;
-    constexpr int NV = (F == kFmtMx16 ? 4 : A_FP4 ? 8 : 16) * (NJ + (A_FP4 ? NI : 0));  // VALU per step's widening, about
-    constexpr int ND = A_FP4 ? 0 : NI;                // DS reads per step
+    constexpr int NI = S::NI, NJ = S::NJ, NM = NIL * NJ;
+    static_assert(NIL >= 1 && NIL <= NI, "live row blocks");
+    constexpr int NV = (F == kFmtMx16 ? 4 : A_FP4 ? 8 : 16) * (NJ + (A_FP4 ? NIL : 0));  // VALU per step's widening, about
+    constexpr int ND = A_FP4 ? 0 : NIL;               // DS reads per step
     constexpr int P = NM >= 8 ? 4 : 1;
     bf16x8 wf1[NJ], af1[NI];
-    nv_pipe_frags<F, L, TM, TN, 1>(p, cur, wf1, af1);
-    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf, af);
+    nv_pipe_frags<F, L, TM, TN, 1, NIL>(p, cur, wf1, af1);
+    nv_pipe_mfma<NI, NJ, A_FP4, NIL>(acc, wf, af);
     nv_pipe_interleave<NM, NV, ND>();
-    nv_pipe_frags<F, L, TM, TN, 2>(p, cur, wf, af);
-    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf1, af1);
+    nv_pipe_frags<F, L, TM, TN, 2, NIL>(p, cur, wf, af);
+    nv_pipe_mfma<NI, NJ, A_FP4, NIL>(acc, wf1, af1);
     nv_pipe_interleave<NM, NV, ND>();
-    nv_pipe_frags<F, L, TM, TN, 3>(p, cur, wf1, af1);
-    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf, af);
+    nv_pipe_frags<F, L, TM, TN, 3, NIL>(p, cur, wf1, af1);
+    nv_pipe_mfma<NI, NJ, A_FP4, NIL>(acc, wf, af);
     nv_pipe_interleave<NM, NV, ND>();
     nv_wait_vm<S::kDma>();
     __builtin_amdgcn_s_waitcnt((0xF) | (0x3 << 14) | (7 << 4));  // lgkmcnt(0)
     asm volatile("s_barrier" ::: "memory");
-    nv_pipe_raw<F, L, TM, TN>(p, nxt, t + 1);
+    nv_pipe_raw<F, L, TM, TN, NIL>(p, nxt, t + 1);
     nv_ring_dma<F, L, TM, TN>(cur, t + 3 < nk ? d : dz, (t + 3 < nk ? t + 3 : 0) * kRK, wave);
-    nv_pipe_frags<F, L, TM, TN, 0>(p, nxt, wf, af);
-    nv_pipe_mfma<NI, NJ, A_FP4>(acc, wf1, af1);
-    nv_pipe_interleave<NM, NV, ND, 2 * (A_FP4 ? NI + NJ : NJ), S::kDma, P>();
+    nv_pipe_frags<F, L, TM, TN, 0, NIL>(p, nxt, wf, af);
+    nv_pipe_mfma<NI, NJ, A_FP4, NIL>(acc, wf1, af1);
+    nv_pipe_interleave<NM, NV, ND, 2 * (A_FP4 ? NIL + NJ : NJ), S::kDma, P>();
+}
+
+// The K loop of a tile: the first stage's fragments, then the stages in threes
+// (the three LDS stages rotate), then the last one or two (no copies left to
+// start).  Every variant runs the same copies and barriers, so waves of one
+// workgroup may take different NIL.
+template <int F, int L, int TM, int TN, int NIL>
+__device__ __forceinline__ void nv_ring_kloop(uint8_t *s0, uint8_t *s1, uint8_t *s2, int nk, const NvRingDma &d,
+                                              const NvRingDma &dz, int wave, NvPipe<F, L, TM, TN> &p,
+                                              f32x16 (&acc)[NvTile<F == 1, L, TM, TN>::NI][NvTile<F == 1, L, TM, TN>::NJ])
+{
+    using S = NvTile<F == 1, L, TM, TN>;
+    bf16x8 wf[S::NJ], af[S::NI];
+    nv_pipe_raw<F, L, TM, TN, NIL>(p, s0, 0);
+    nv_pipe_frags<F, L, TM, TN, 0, NIL>(p, s0, wf, af);
+    const int nfull = nk - nk % 3;
+    for (int t = 0; t < nfull; t += 3) {
+        nv_pipe_stage<F, L, TM, TN, NIL>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<F, L, TM, TN, NIL>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
+        nv_pipe_stage<F, L, TM, TN, NIL>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
+    }
+    if (nk % 3 >= 1) nv_pipe_stage<F, L, TM, TN, NIL>(s0, s1, nfull, nk, d, dz, wave, p, acc, wf, af);
+    if (nk % 3 == 2) nv_pipe_stage<F, L, TM, TN, NIL>(s1, s2, nfull + 1, nk, d, dz, wave, p, acc, wf, af);
 }
 
 // Epilogue: lane l holds output row r0 + 32 i + l % 32, columns
@@ -1340,18 +1367,23 @@ void k_nv_gemm_ring(NvGemmArgs g)
     nv_ring_dma<F, L, TM, TN>(s2, nk > 2 ? d : dz, nk > 2 ? 2 * kRK : 0, wave);
     nv_wait_vm<2 * S::kDma>();
     asm volatile("s_barrier" ::: "memory");
-    bf16x8 wf[NJ], af[NI];
-    nv_pipe_raw<F, L, TM, TN>(p, s0, 0);
-    nv_pipe_frags<F, L, TM, TN, 0>(p, s0, wf, af);
-    const int nfull = nk - nk % 3;
-    for (int t = 0; t < nfull; t += 3) {
-        nv_pipe_stage<F, L, TM, TN>(s0, s1, t, nk, d, dz, wave, p, acc, wf, af);
-        nv_pipe_stage<F, L, TM, TN>(s1, s2, t + 1, nk, d, dz, wave, p, acc, wf, af);
-        nv_pipe_stage<F, L, TM, TN>(s2, s0, t + 2, nk, d, dz, wave, p, acc, wf, af);
+    // A grouped 128-row tile multiplies only the 32-row blocks that hold rows of
+    // its group (the group's last tile is on average half empty): each wave
+    // picks the K loop for its live blocks
+    if constexpr (GR && TM == 128) {
+        const int live = min(TM, M - m0) - S::row0(wave);  // rows of this wave's blocks
+        const int nil = min(NI, max(1, (live + 31) / 32));
+        if (nil == 1) nv_ring_kloop<F, L, TM, TN, 1>(s0, s1, s2, nk, d, dz, wave, p, acc);
+        else if constexpr (NI > 2) {
+            if (nil == 2) nv_ring_kloop<F, L, TM, TN, 2>(s0, s1, s2, nk, d, dz, wave, p, acc);
+            else if (nil == 3) nv_ring_kloop<F, L, TM, TN, 3>(s0, s1, s2, nk, d, dz, wave, p, acc);
+            else nv_ring_kloop<F, L, TM, TN, NI>(s0, s1, s2, nk, d, dz, wave, p, acc);
+        } else {
+            nv_ring_kloop<F, L, TM, TN, NI>(s0, s1, s2, nk, d, dz, wave, p, acc);
+        }
+    } else {
+        nv_ring_kloop<F, L, TM, TN, NI>(s0, s1, s2, nk, d, dz, wave, p, acc);
     }
-    // the last one or two stages (no copies left to start)
-    if (nk % 3 >= 1) nv_pipe_stage<F, L, TM, TN>(s0, s1, nfull, nk, d, dz, wave, p, acc, wf, af);
-    if (nk % 3 == 2) nv_pipe_stage<F, L, TM, TN>(s1, s2, nfull + 1, nk, d, dz, wave, p, acc, wf, af);
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
