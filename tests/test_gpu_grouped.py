@@ -115,6 +115,25 @@ def test_grouped_bf16_output_and_one_busy_group(fmt):
     assert_gemm_close(c, ref, tol, f"grouped one busy group {fmt}")
 
 
+@pytest.mark.parametrize("fmt", ["nv16", "mx", "nv44"])
+def test_grouped_every_live_row_block_count(fmt):
+    """Groups whose last 128-row tile holds 1, 31, 32, 33, 64, 65, 96, 97, 127, 128
+    and 129 + 63 rows: each count of live 32-row blocks (1-4 of a wave's 4 in the
+    W4A16 layout; 0-2 of each wave's 2 in W4A4's 2 x 2 split) and both sides of
+    every block boundary, with the rows gathered and fp32 C."""
+    sizes = [1, 31, 32, 33, 64, 65, 96, 97, 127, 128, 192]
+    E, K, N = len(sizes), 256, 300
+    offs = np.concatenate([[0], np.cumsum(sizes)]).astype(np.int32)
+    T = int(offs[-1])
+    ridx = np.random.default_rng(4).permutation(T).astype(np.int32)
+    a = to_bf16_bits(activations_f32(T, K, 0.005, 30.0, seed=6))
+    codes, scales, ts, dw = _experts("mx" if fmt == "mx" else "nv", E, N, K, seed=13)
+    c = _run(fmt, a, dw, offs, ridx, torch.float32)
+    torch.cuda.synchronize()
+    ref, tol = _ref(fmt, a, codes, scales, ts, offs, ridx)
+    assert_gemm_close(c, ref, tol, f"grouped live row blocks {fmt}")
+
+
 def test_grouped_exact_tile_multiples():
     """Groups of exactly 128 and 256 rows, N = 512: no ragged tile anywhere."""
     E, K, N = 3, 256, 512
