@@ -324,6 +324,11 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
                 for (int blk = 0; blk < 2; ++blk)
 #pragma unroll
                     for (int i = 0; i < (M1 ? 1 : 4); ++i) acc0[i] = __builtin_fmaf(part[blk][i], bs[blk], acc0[i]);
+                // the sums are formed here, in the unit: left free, the compiler
+                // deferred these FMAs to later units and kept every unit's
+                // partials live (about 8 more registers per unit, and spills)
+#pragma unroll
+                for (int i = 0; i < (M1 ? 1 : 4); ++i) asm volatile("" : "+v"(acc0[i]));
             }
         } else if constexpr (MX) {
             const float msc = __uint_as_float(sc << 23);
