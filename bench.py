@@ -376,7 +376,7 @@ def ceiling(args, torch, fp4, T, dev):
             res["read"][f"grid{grid}_fit"] = fit(xs, ys)
 
     # the GEMV grows along K (K = 3072, 5120, 8192: 3, 5 and 8 of the 128-element
-    # segments per wave, 8192 being the decode kernel's largest K), so its launch
+    # segments per wave, 8192 the largest K walked in one chunk), so its launch
     # geometry (218 workgroups of 80 weight rows) stays the same and only the bytes
     # per row grow
     g = torch.Generator(device="cpu").manual_seed(7)

@@ -242,7 +242,6 @@ fp4_status gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t lda, c
                              fp4_dtype ct, int64_t ldc, hipStream_t stream)
 {
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
-    if (M <= 16 && K > 8192) return FP4_ERR_SHAPE;
     FP4_TRY(check_matrix(a, M, K, lda, 2));
     FP4_TRY(check_decode_limits(M, K, lda, N));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));
@@ -279,7 +278,6 @@ fp4_status mxfp4_gemm_w4a16_decode(const void *a, int64_t M, int64_t K, int64_t 
                                    hipStream_t stream)
 {
     FP4_TRY(check_gemm_common(M, K, N, 128, c, ct, ldc));
-    if (M <= 16 && K > 8192) return FP4_ERR_SHAPE;
     FP4_TRY(check_matrix(a, M, K, lda, 2));
     FP4_TRY(check_decode_limits(M, K, lda, N));
     FP4_TRY(check_packed(w_codes_p, w_scales_p));

@@ -146,8 +146,11 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     const int n = lane & 15, grp = lane >> 4;
     const int M = g.M, N = g.N;
     const int nseg = g.K >> 7;
-    const int seg0 = wave * S;
-    const int ns = max(0, min(S, nseg - seg0));  // this wave's segments
+    // K runs in chunks of 8 S segments (one when K <= 1024 S): the wave owns
+    // segments seg0 .. seg0 + ns - 1 of the current chunk, which starts at segment
+    // segb and spans wch K elements
+    const int nch = (nseg + W * S - 1) / (W * S);
+    int segb = 0, seg0 = wave * S, ns = max(0, min(S, nseg - seg0)), wch = min(g.K, 1024 * S);
     const int r_lo = blockIdx.x * g.rows_per_wg;
     const int r_hi = min(r_lo + g.rows_per_wg, N);
     const int nt = (r_hi - r_lo + 15) >> 4;      // <= NT
@@ -233,7 +236,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         const int sg = min(seg0 + s, nseg - 1);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(alds + arow * g.K + 128 * sg + 32 * grp + 8 * j);
+            const bf16x8 v = *reinterpret_cast<const bf16x8 *>(alds + arow * wch + 128 * (sg - segb) + 32 * grp + 8 * j);
             dst[j] = own ? v : bf16x8{};
         }
     };
@@ -254,19 +257,32 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
             dst[j] = *reinterpret_cast<const bf16x8 *>(a16 + 8192 * wave + 4096 * b + 256 * n + 16 * ((4 * grp + j) ^ n));
     };
 
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    f32x4 acc[NT][2];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
     u32x4 bc[D];
     uint32_t bsc[D];  // M <= 4: the units' scale byte(s)
     u32x4 scv;        // M > 4: the next segment's scale run, in flight
+    for (int ch = 0; ch < nch; ++ch) {
+    segb = ch * W * S;
+    seg0 = segb + wave * S;
+    ns = max(0, min(S, nseg - seg0));
+    wch = min(1024 * S, g.K - 128 * segb);
     if constexpr (M4) {
         // the A loads go out first, then the first units' weight loads, so waiting
-        // for A does not wait for them
-        const int cpr = g.K >> 3;  // 16-byte chunks per row; 4 cpr <= 512 S = 64 W S / 8 chunks
+        // for A does not wait for them; a later chunk overwrites the staged rows
+        // only once every wave has read the previous chunk's
+        if (ch > 0) __syncthreads();
+        const int cpr = wch >> 3;  // 16-byte chunks per row; 4 cpr <= 512 S = 64 W S / 8 chunks
         u32x4 ach[S];
 #pragma unroll
         for (int c = 0; c < S; ++c) {
             const int idx = (int)threadIdx.x + 64 * W * c;
             const int row = idx / cpr, col = idx - row * cpr;
-            const uint32_t off = (row < M && row < 4) ? (uint32_t)(((int64_t)row * g.lda + 8 * col) * 2) : kGvOut;
+            const uint32_t off =
+                (row < M && row < 4) ? (uint32_t)(((int64_t)row * g.lda + 128 * segb + 8 * col) * 2) : kGvOut;
             ach[c] = __builtin_amdgcn_raw_buffer_load_b128(ra, (int)off, 0, 0);
         }
 #pragma unroll
@@ -296,10 +312,6 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
         __builtin_amdgcn_sched_barrier(0);
     }
 
-    typedef float f32x2 __attribute__((ext_vector_type(2)));
-    f32x4 acc[NT][2];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one unit: the lane's 32 codes c with scale byte(s) sc against fragments a
     auto unit = [&](const bf16x8 (&a)[4], const u32x4 &c, uint32_t sc, f32x4 &acc0, f32x4 &acc1) {
@@ -399,6 +411,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
             __builtin_amdgcn_sched_barrier(0);
         }
     }
+    }  // chunks
 
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
@@ -508,7 +521,10 @@ int device_cu_count()
 fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st)
 {
     const int nseg = g.K / 128;
-    const int S = (nseg + kGvWaves - 1) / kGvWaves;
+    // segments per wave and chunk: K beyond 1024 * 8 runs in chunks of 8 S
+    // segments, S chosen so the chunks come out as even as they go
+    const int nch = (nseg + 8 * kGvWaves - 1) / (8 * kGvWaves);
+    const int S = (nseg + kGvWaves * nch - 1) / (kGvWaves * nch);
     // whole 16-row tiles per workgroup, all workgroups in one round (at most one
     // per CU): a workgroup's last tile is multiplied in full whether or not its
     // rows exist, and that math is not hidden under the loads, so fewer, full

@@ -155,7 +155,7 @@ fp4_status nvfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
                              uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream);
 
 /* W4A16 (aixq.cc article, "Core difference: W4A4 vs W4A16") on a weight in the
- * decode layout: C = A . W^T, K % 128 == 0.  1 <= M <= 16 (K <= 8192) runs the
+ * decode layout: C = A . W^T, K % 128 == 0.  1 <= M <= 16 (any such K) runs the
  * decode GEMV; larger M the prefill GEMM reading the same layout (the result
  * gemm_w4a16 gives on the row-major weight, bit for bit), so one packed weight
  * serves both.  Same arithmetic and tolerance as gemm_w4a16 (each weight widened
@@ -283,7 +283,7 @@ fp4_status mxfp4_pack_decode(const uint8_t *codes, const uint8_t *scales, int64_
                              uint8_t *codes_p, uint8_t *scales_p, hipStream_t stream);
 
 /* MXFP4 W4A16 on a weight in the MXFP4 decode layout: C = A . W^T, K % 128 == 0;
- * the decode GEMV for 1 <= M <= 16 (K <= 8192), the prefill GEMM on the same
+ * the decode GEMV for 1 <= M <= 16 (any such K), the prefill GEMM on the same
  * layout for larger M (mxfp4_gemm_w4a16's result, bit for bit).  Arithmetic and
  * tolerance as mxfp4_gemm_w4a16.  FP4_ERR_SHAPE for the same 2 GiB limits as
  * gemm_w4a16_decode, for any M, checked before anything is launched. */

@@ -197,7 +197,6 @@ def test_decode_layout_validation(L):
     assert gd(a=None) == NULL
     assert gd(wt=None) == NULL
     assert gd(K=192, lda=192) == SHAPE
-    assert gd(K=8320, lda=8320) == SHAPE   # the GEMV (M <= 16) takes K <= 8192
     assert gd(M=17, K=192, lda=192) == SHAPE
     assert gd(lda=128) == LAYOUT
     assert gd(ws=FAKE + 4) == LAYOUT
@@ -210,8 +209,9 @@ def test_decode_layout_validation(L):
     assert L.mxfp4_gemm_w4a16_decode(FAKE, 1, 8192, 8192, FAKE, FAKE, 524288, FAKE, 1, 524288, None) == SHAPE
     assert L.mxfp4_gemm_w4a16_decode(FAKE, 4, 256, 1 << 28, FAKE, FAKE, 32, FAKE, 1, 32, None) == SHAPE
     if not torch.cuda.is_available():
-        # M > 16 is the prefill GEMM on the same layout, with no K <= 8192 limit
+        # any K % 128 == 0 at every M (the GEMV runs K past 8192 in chunks)
         assert gd() == NO_DEVICE and gd(M=17) == NO_DEVICE and gd(M=4096, K=8320, lda=8320) == NO_DEVICE
+        assert gd(K=8320, lda=8320) == NO_DEVICE and gd(M=16, K=28672, lda=28672) == NO_DEVICE
         # just under the limits
         assert gd(M=1, K=8192, lda=8192, N=524287, ldc=524287) == NO_DEVICE
         assert gd(M=2, K=256, lda=(1 << 29) - 256) == NO_DEVICE
@@ -268,12 +268,12 @@ def test_mxfp4_w4a16_validation(L):
         a.update(kw)
         return L.mxfp4_gemm_w4a16_decode(*a.values())
 
-    assert gd(K=8320, lda=8320) == SHAPE
     assert gd(M=40, K=96, lda=96) == SHAPE
     assert gd(c=None) == NULL
     if not torch.cuda.is_available():
         assert g() == NO_DEVICE and pk() == NO_DEVICE and gd() == NO_DEVICE
         assert gd(M=17) == NO_DEVICE and gd(M=300, K=8320, lda=8320) == NO_DEVICE
+        assert gd(K=8320, lda=8320) == NO_DEVICE  # the GEMV takes K past 8192 in chunks
 
 
 def test_mxfp4_segment_major_gemm_validation(L):

@@ -5,7 +5,7 @@ segment-major rearrangement of the oracle's row-major codes and scales, written
 here with numpy reshapes.  gemm_w4a16_decode must meet the GEMM bound
 |C - C_ref| <= 2e-3 * sum_k |a w| against the oracle's fp64 product, over
 shapes that cover one and many 16-row tiles, ragged row counts per workgroup,
-waves with no K segment (K / 128 < 8), the largest K (8192), more workgroups
+waves with no K segment (K / 128 < 8), K past 8192 (run in chunks), more workgroups
 than CUs, and the full decode workload; with grid-valued operands the fp32
 result is exact and must equal the oracle bit for bit.
 """
@@ -63,6 +63,9 @@ SHAPES = [
     (3, 1000, 8192), (1, 4097, 2048), (16, 1, 128), (7, 40000, 256), (16, 2000, 1152),
     # 3, 4, 6 and 7 16-row tiles per workgroup on a 256-CU part
     (16, 9600, 256), (1, 14400, 256), (5, 22400, 128), (4, 27200, 384),
+    # K past 8192, in chunks of 8 S segments: 2 chunks of 40 and 32 segments
+    # (K = 9216), 2 of 56 (14336), 3 of 48, 48 and 33 (16512)
+    (1, 700, 9216), (4, 300, 14336), (16, 530, 14336), (2, 100, 16512), (16, 64, 16512),
 ]
 
 
