@@ -132,7 +132,10 @@ __device__ __forceinline__ bf16x4 e2m1x4_bf16(uint32_t w, int half, float scale 
 // instructions per wave, 4 lanes reading each address.)
 // M1 (with M4): exactly one activation row; of the four rows the 4x4x4 blocks
 // produce only row 0 is scaled, reduced and stored.
-template <int S, int NT, bool M4, bool MX, bool M1 = false>
+// CH: K spans more than one chunk (K > 1024 S).  Kept a template flag: as a
+// runtime loop even of one pass, the chunk loop made the compiler carry the
+// accumulators through a loop with copies (2-4% slower at K = 5120).
+template <int S, int NT, bool M4, bool MX, bool M1 = false, bool CH = false>
 __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
 {
     constexpr int W = kGvWaves;
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(64 * kGvWaves, 1) void k_nv_gemv_dec(GemvArgs g)
     u32x4 bc[D];
     uint32_t bsc[D];  // M <= 4: the units' scale byte(s)
     u32x4 scv;        // M > 4: the next segment's scale run, in flight
-    for (int ch = 0; ch < nch; ++ch) {
+    for (int ch = 0; ch < (CH ? nch : 1); ++ch) {
     segb = ch * W * S;
     seg0 = segb + wave * S;
     ns = max(0, min(S, nseg - seg0));
@@ -472,15 +475,29 @@ fp4_status launch_pack_decode(const uint8_t *codes, const uint8_t *scales, int64
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
+template <int S, int NT, bool MX, bool CH>
+static void launch_gemv_ch(const GemvArgs &g, unsigned grid, hipStream_t st)
+{
+    if (g.M == 1 && !MX)
+        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX, true, CH>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    else if (g.M <= 4)
+        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX, false, CH>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, false, MX, false, CH>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+}
+
+// more than one chunk only arises with S >= 5 (K > 8192 gives at least 65
+// segments over chunks of 8 S), so only those S have the chunked form
 template <int S, int NT, bool MX>
 static void launch_gemv(const GemvArgs &g, unsigned grid, hipStream_t st)
 {
-    if (g.M == 1 && !MX)
-        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX, true>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
-    else if (g.M <= 4)
-        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, true, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
-    else
-        hipLaunchKernelGGL((k_nv_gemv_dec<S, NT, false, MX>), dim3(grid), dim3(64 * kGvWaves), 0, st, g);
+    if constexpr (S >= 5) {
+        if (g.K > 1024 * S) {
+            launch_gemv_ch<S, NT, MX, true>(g, grid, st);
+            return;
+        }
+    }
+    launch_gemv_ch<S, NT, MX, false>(g, grid, st);
 }
 
 template <int S, int NT>
@@ -525,6 +542,7 @@ fp4_status launch_gemv_decode(GemvArgs g, hipStream_t st)
     // segments, S chosen so the chunks come out as even as they go
     const int nch = (nseg + 8 * kGvWaves - 1) / (8 * kGvWaves);
     const int S = (nseg + kGvWaves * nch - 1) / (kGvWaves * nch);
+    if (nch > 1 && S < 5) return FP4_ERR_SHAPE;  // cannot happen (see launch_gemv); never run a partial K
     // whole 16-row tiles per workgroup, all workgroups in one round (at most one
     // per CU): a workgroup's last tile is multiplied in full whether or not its
     // rows exist, and that math is not hidden under the loads, so fewer, full
