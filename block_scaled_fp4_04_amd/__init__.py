@@ -67,6 +67,7 @@ def _declare(L):
         "mxfp4_quantize": (i32, [p, i32, i64, i64, i64, p, p, i32, p, p]),
         "mxfp4_dequantize": (i32, [p, p, i64, i64, p, i32, i64, p]),
         "mxfp4_gemm_w4a4_workspace": (sz, [i64, i64]),
+        "mxfp4_gemm_w4a4_a_segment_major": (i32, [i64, i64, i64]),
         "mxfp4_gemm_w4a4": (i32, [p, i64, i64, i64, i32, p, p, i64, p, i32, i64, p, sz, p]),
         "mxfp4_gemm_prequant": (i32, [p, p, i64, i64, p, p, i64, p, i32, i64, p]),
         "mxfp4_gemm_w4a4_seg_workspace": (sz, [i64, i64]),
@@ -621,8 +622,12 @@ def mxfp4_gemm_w4a4(a: torch.Tensor, w: PackedMXFP4, rule="ocp", dtype=torch.bfl
     return _mx_full("mxfp4_gemm_w4a4", "mxfp4_gemm_w4a4_workspace", a, w, rule, dtype, out, workspace, _weight_mx)
 
 
-def mxfp4_packed_a(ws: torch.Tensor, M: int, K: int) -> PackedMXFP4:
-    """Views of A's MXFP4 form inside an mxfp4_gemm_w4a4 workspace."""
+def mxfp4_packed_a(ws: torch.Tensor, M: int, K: int, N: int):
+    """Views of A's MXFP4 form inside the workspace of an mxfp4_gemm_w4a4 call
+    with W of N rows: segment-major (DecodeMXFP4) or row-major (PackedMXFP4), as
+    the library reports for those sizes."""
+    if lib().mxfp4_gemm_w4a4_a_segment_major(M, N, K):
+        return mxfp4_seg_packed_a(ws, M, K)
     cb = (M * (K // 2) + 255) // 256 * 256
     return PackedMXFP4(ws[:M * K // 2].view(M, K // 2), ws[cb:cb + M * K // 32].view(M, K // 32), M, K)
 

@@ -564,6 +564,11 @@ fp4_status mxfp4_gemm_prequant(const uint8_t *a_codes, const uint8_t *a_scales, 
     return launch_mxfp4_gemm(g, stream);
 }
 
+int mxfp4_gemm_w4a4_a_segment_major(int64_t M, int64_t N, int64_t K)
+{
+    return M > 0 && N > 0 && K > 0 && K % 128 == 0 && codes_under_2gib(M, N, K / 2) ? 1 : 0;
+}
+
 fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
                            const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
                            fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,
@@ -578,7 +583,15 @@ fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4
     FP4_TRY(check_device());
     uint8_t *ac = reinterpret_cast<uint8_t *>(ws);
     uint8_t *as = ac + align256((size_t)M * (size_t)(K / 2));
-    FP4_TRY(launch_mxfp4_quantize(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
+    // A's packed form lives only in the workspace, so its layout is this call's
+    // choice: segment-major (each 256-row panel's 128-K segment one contiguous
+    // 16 KiB run) whenever the segment kernel applies, with W read row-major by
+    // the same kernel; the products and their order, and so C, are the same
+    const bool seg = mxfp4_gemm_w4a4_a_segment_major(M, N, K) != 0;
+    if (seg)
+        FP4_TRY(launch_mxfp4_quantize_seg(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
+    else
+        FP4_TRY(launch_mxfp4_quantize(a, FP4_BF16, M, K, lda, ac, as, rule, nullptr, stream));
     MxGemmArgs g{};
     g.a_codes = ac;
     g.a_scales = as;
@@ -590,7 +603,7 @@ fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4
     g.c = c;
     g.c_bf16 = ct == FP4_BF16;
     g.ldc = ldc;
-    return launch_mxfp4_gemm(g, stream);
+    return seg ? launch_mxfp4_gemm_seg_wrow(g, stream) : launch_mxfp4_gemm(g, stream);
 }
 
 // ------------------------------------------- MXFP4 W4A4, segment-major ----

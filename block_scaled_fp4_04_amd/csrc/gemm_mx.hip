@@ -1049,7 +1049,12 @@ __device__ __forceinline__ void mq_epilogue(const f32x16 (&acc)[4][2], uint8_t *
     }
 }
 
-template <typename OutT>
+// AROW / WROW: that operand is row-major instead (codes [rows][K/2], E8M0
+// [rows][K/32]): a row's 128-K segment is then the 64 bytes at row K/2 + 64 s and
+// its 4 scale bytes at row K/32 + 4 s, so only the copies' row stride and
+// segment step change; the slots, fragments and contraction order are the same,
+// and so is every output bit.
+template <typename OutT, bool AROW = false, bool WROW = false>
 __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
 {
     __shared__ __align__(16) uint8_t q0[kQSlot];
@@ -1075,16 +1080,17 @@ __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
         const int q = 128 * wave + 64 * i + lane;
         const int r = q >> 2;
         const int c = (q & 3) ^ ((r >> 2) & 3);
-        d.a[i] = (uint32_t)min(m0 + r, M - 1) * 64u + 16 * c;
-        d.w[i] = (uint32_t)min(n0 + r, N - 1) * 64u + 16 * c;
+        d.a[i] = (uint32_t)min(m0 + r, M - 1) * (AROW ? (uint32_t)(K / 2) : 64u) + 16 * c;
+        d.w[i] = (uint32_t)min(n0 + r, N - 1) * (WROW ? (uint32_t)(K / 2) : 64u) + 16 * c;
     }
+    const bool srow = wave < 4 ? AROW : WROW;  // this wave copies A's (waves 0-3) or W's scale bytes
     {
         const int r = 64 * (wave & 3) + lane;
-        d.s = (uint32_t)(wave < 4 ? min(m0 + r, M - 1) : min(n0 + r, N - 1)) * 4u;
+        d.s = (uint32_t)(wave < 4 ? min(m0 + r, M - 1) : min(n0 + r, N - 1)) * (srow ? (uint32_t)(K / 32) : 4u);
     }
-    d.seg_a = (uint32_t)M * 64u;
-    d.seg_w = (uint32_t)N * 64u;
-    d.seg_s = (uint32_t)(wave < 4 ? M : N) * 4u;
+    d.seg_a = AROW ? 64u : (uint32_t)M * 64u;
+    d.seg_w = WROW ? 64u : (uint32_t)N * 64u;
+    d.seg_s = srow ? 4u : (uint32_t)(wave < 4 ? M : N) * 4u;
     dz = d;
     dz.ra = mx2_rsrc(g.a_codes, 0);
     dz.rw = mx2_rsrc(g.w_codes, 0);
@@ -1134,17 +1140,30 @@ __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
     mq_epilogue<OutT>(acc, q0, q1, q2, q3, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
 }
 
-fp4_status launch_mxfp4_gemm_seg(const MxGemmArgs &g, hipStream_t st)
+template <bool AROW, bool WROW>
+static fp4_status launch_seg_layout(const MxGemmArgs &g, hipStream_t st)
 {
     // 32-bit byte offsets and descriptor sizes
     if (g.K % kQK != 0 || g.M * (g.K / 2) >= (int64_t(1) << 31) || g.N * (g.K / 2) >= (int64_t(1) << 31))
         return FP4_ERR_SHAPE;
     const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
     if (g.c_bf16)
-        hipLaunchKernelGGL(k_mx_gemm_seg<__bf16>, dim3(tiles), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_mx_gemm_seg<__bf16, AROW, WROW>), dim3(tiles), dim3(512), 0, st, g);
     else
-        hipLaunchKernelGGL(k_mx_gemm_seg<float>, dim3(tiles), dim3(512), 0, st, g);
+        hipLaunchKernelGGL((k_mx_gemm_seg<float, AROW, WROW>), dim3(tiles), dim3(512), 0, st, g);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+}
+
+fp4_status launch_mxfp4_gemm_seg(const MxGemmArgs &g, hipStream_t st) { return launch_seg_layout<false, false>(g, st); }
+
+fp4_status launch_mxfp4_gemm_seg_wrow(const MxGemmArgs &g, hipStream_t st)
+{
+    return launch_seg_layout<false, true>(g, st);
+}
+
+fp4_status launch_mxfp4_gemm_seg_rows(const MxGemmArgs &g, hipStream_t st)
+{
+    return launch_seg_layout<true, true>(g, st);
 }
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)

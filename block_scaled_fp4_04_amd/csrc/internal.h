@@ -139,6 +139,9 @@ fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st);
 // Both operands segment-major (codes [K/128][rows][64], scales [K/128][rows][4]);
 // K % 128 == 0
 fp4_status launch_mxfp4_gemm_seg(const MxGemmArgs &g, hipStream_t st);
+// The same kernel with W row-major (A segment-major), or with both row-major
+fp4_status launch_mxfp4_gemm_seg_wrow(const MxGemmArgs &g, hipStream_t st);
+fp4_status launch_mxfp4_gemm_seg_rows(const MxGemmArgs &g, hipStream_t st);
 // W4A8: A MXFP8 (E4M3 bytes [M][K], E8M0 [M][K/32]), W MXFP4; K % 128 == 0
 fp4_status launch_mxfp4_gemm_w4a8(const MxGemmArgs &g, hipStream_t st);
 

@@ -501,9 +501,12 @@ __global__ __launch_bounds__(256) void k_mxfp4_quant(const T *__restrict__ x, ui
             w = e2m1x8_code(q);
         }
         if (SEG) {
+            // plain stores: a lane group writes 64 bytes, half of a cache line, and as
+            // streaming stores those half lines took the kernel from 28.5 to 45.5 us
+            // (8192 x 5120); the row-major form writes whole lines and streams them
             const int64_t piece = (int64_t)(c8 >> 4) * rows + r;  // (segment, row)
-            st_nt32(w, codes + piece * 64 + (c8 & 15u) * 4);
-            if ((c8 & 3u) == 0u) st_nt8(byte, scales + piece * 4 + ((c8 >> 2) & 3u));
+            *reinterpret_cast<uint32_t *>(codes + piece * 64 + (c8 & 15u) * 4) = w;
+            if ((c8 & 3u) == 0u) scales[piece * 4 + ((c8 >> 2) & 3u)] = (uint8_t)byte;
         } else {
             st_nt32(w, codes + (int64_t)r * (cols / 2) + (int64_t)c8 * 4);
             if ((c8 & 3u) == 0u) st_nt8(byte, scales + (int64_t)r * (cols / 32) + (c8 >> 2));

@@ -249,9 +249,19 @@ fp4_status mxfp4_dequantize(const uint8_t *codes, const uint8_t *scales, int64_t
 /* Workspace bytes mxfp4_gemm_w4a4 needs: A's codes | scales, 256-byte aligned. */
 size_t mxfp4_gemm_w4a4_workspace(int64_t M, int64_t K);
 
+/* 1 if mxfp4_gemm_w4a4 leaves A's MXFP4 form in its workspace segment-major
+ * (codes [K/128][M][64], E8M0 [K/128][M][4], as mxfp4_gemm_w4a4_seg does): when
+ * K % 128 == 0 and A's and W's codes are each under 2 GiB.  0: row-major
+ * (codes [M][K/2], E8M0 [M][K/32]).  Either way the bytes are those of
+ * mxfp4_quantize(A); only their order differs. */
+int mxfp4_gemm_w4a4_a_segment_major(int64_t M, int64_t N, int64_t K);
+
 /* MXFP4 W4A4 GEMM: A (bf16) is quantized to MXFP4 with `rule` into `ws`, then
  * C = A_q . W^T on gfx950's block-scaled FP4 matrix instruction (E8M0 scale per
- * 32 K-elements per row, the MX block), fp32 accumulation.  W [N][K] MXFP4. */
+ * 32 K-elements per row, the MX block), fp32 accumulation.  W [N][K] MXFP4.
+ * A's form in `ws` is segment-major where mxfp4_gemm_w4a4_a_segment_major says
+ * so (the kernel then reads W's 64-byte row pieces per 128-K segment, A's
+ * panels as contiguous runs); the result is the same bit for bit. */
 fp4_status mxfp4_gemm_w4a4(const void *a, int64_t M, int64_t K, int64_t lda, fp4_mx_rule rule,
                            const uint8_t *w_codes, const uint8_t *w_scales, int64_t N, void *c,
                            fp4_dtype ct, int64_t ldc, void *ws, size_t ws_bytes,

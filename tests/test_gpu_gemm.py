@@ -116,8 +116,12 @@ def test_mxfp4_w4a4(M, N, K, rule):
     c = fp4().mxfp4_gemm_w4a4(bf16bits_to_dev(a), _packed_mx(wc, wsc), rule=rule,
                               dtype=torch.float32, workspace=ws)
     torch.cuda.synchronize()
-    pa = fp4().mxfp4_packed_a(ws, M, K)
+    pa = fp4().mxfp4_packed_a(ws, M, K, N)
     ac, asc = oracle.mxfp4_quantize(a, r)
+    if K % 128 == 0:  # the workspace holds A segment-major: [K/128][M][64] and [K/128][M][4]
+        assert pa.codes.shape == (K // 128, M, 64)
+        ac = ac.reshape(M, K // 128, 64).transpose(1, 0, 2)
+        asc = asc.reshape(M, K // 128, 4).transpose(1, 0, 2)
     assert np.array_equal(pa.codes.cpu().numpy(), ac) and np.array_equal(pa.scales.cpu().numpy(), asc)
     ref, tol = oracle.mxfp4_gemm_w4a4_ref(a, wc, wsc, r)
     assert_gemm_close(c, ref, tol, f"mxfp4 {M}x{N}x{K}")
