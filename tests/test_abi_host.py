@@ -486,3 +486,19 @@ def test_read_ceiling_validation(L):
     assert rc(buf=FAKE + 8) == LAYOUT
     if not torch.cuda.is_available():
         assert rc() == NO_DEVICE
+
+
+def test_mxfp4_w4a4_workspace_layout_query(L):
+    """mxfp4_gemm_w4a4 keeps A segment-major in its workspace exactly when K is a
+    multiple of 128 and both operands' codes stay under 2 GiB (the segment
+    kernel's 32-bit offsets); row-major otherwise.  A host-only query."""
+    seg = L.mxfp4_gemm_w4a4_a_segment_major
+    assert seg(8192, 17408, 5120) == 1
+    assert seg(1, 1, 128) == 1
+    assert seg(300, 520, 96) == 0                         # K % 128 != 0
+    assert seg(300, 520, 1056) == 0
+    assert seg((1 << 31) // 64, 16, 128) == 0             # A's codes exactly 2 GiB
+    assert seg((1 << 31) // 64 - 1, 16, 128) == 1
+    assert seg(16, (1 << 31) // 2560 + 1, 5120) == 0      # W's codes past 2 GiB
+    assert seg(16, (1 << 31) // 2560, 5120) == 1
+    assert seg(0, 16, 128) == 0 and seg(16, 0, 128) == 0 and seg(16, 16, 0) == 0
