@@ -1415,7 +1415,9 @@ static void launch_ring(const NvGemmArgs &g, hipStream_t st)
 // 256 x 256 tiles; when the last round of tiles would leave most CUs idle, the
 // tile columns of that round go to a second launch of 128 x 128 tiles, provided
 // they fit in one round (for M = 4096, N = 17408: 1024 large tiles, four full
-// rounds on 256 CUs, then 256 small tiles for the last 1024 columns).
+// rounds on 256 CUs, then 256 small tiles for the last 1024 columns), else of
+// 128 x 256 tiles if those fit (M = 8192: eight full rounds, then 256 tiles of
+// 128 x 256 where a ninth round of 128 large tiles left half the CUs idle).
 template <int F, int L>
 static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
 {
@@ -1426,7 +1428,8 @@ static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
         const int64_t cols = tiles / cus * cus / tm;  // 256-wide column blocks kept on large tiles
         const int64_t n_split = cols * 256;
         const int64_t small = ((g.M + 127) / 128) * ((g.N - n_split + 127) / 128);
-        if (cols >= 1 && n_split < g.N && small <= cus) {
+        const int64_t mid = ((g.M + 127) / 128) * ((g.N - n_split + 255) / 256);
+        if (cols >= 1 && n_split < g.N && (small <= cus || mid <= cus)) {
             NvGemmArgs big = g;
             big.N = n_split;
             launch_ring<F, L, 256, 256>(big, st);
@@ -1439,7 +1442,10 @@ static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
                 rest.w_scales = g.w_scales + n_split * (g.K / (F == kFmtMx16 ? 32 : 16));
             }
             rest.c = reinterpret_cast<uint8_t *>(g.c) + n_split * (g.c_bf16 ? 2 : 4);
-            launch_ring<F, 0, 128, 128>(rest, st);
+            if (small <= cus)
+                launch_ring<F, 0, 128, 128>(rest, st);
+            else
+                launch_ring<F, L, 128, 256>(rest, st);  // M = 8192, N = 17408: 256 tiles of 128 x 256
             return;
         }
     }

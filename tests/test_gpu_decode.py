@@ -143,7 +143,7 @@ def test_decode_exact_when_operands_are_grid_values(M, N, K):
 # to forty segments, and a grid whose last round of columns runs as a second
 # launch of 128 x 128 tiles (500 x 33000: its weight rows start at row 32768)
 PREFILL = [(17, 260, 1024), (40, 70, 128), (300, 520, 5120), (257, 513, 1280), (513, 260, 640),
-           (500, 33000, 128)]
+           (500, 33000, 128), (1100, 16900, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL)

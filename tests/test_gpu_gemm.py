@@ -57,6 +57,9 @@ SHAPES = [
     (40, 70, 64), (300, 300, 128), (257, 513, 192), (513, 260, 320),
     # 258 tiles of 256 x 256: the last 232 columns run as 128 x 128 tiles in a second launch
     (500, 33000, 128),
+    # 335 tiles of 256 x 256: the last 3844 columns run as 144 tiles of 128 x 256 (128 x 128
+    # tiles would not fit in one round on 256 CUs), ragged in M and N
+    (1100, 16900, 256),
 ]
 
 
@@ -75,7 +78,8 @@ def test_w4a16(M, N, K, out):
 
 @pytest.mark.parametrize("M,N,K", [(1, 48, 64), (4, 517, 5120), (16, 300, 1040), (17, 260, 1040),
                                    (300, 520, 5120), (513, 130, 96),
-                                   (40, 70, 64), (257, 513, 192), (513, 260, 320), (500, 33000, 128)])
+                                   (40, 70, 64), (257, 513, 192), (513, 260, 320), (500, 33000, 128),
+                                   (1100, 16900, 256)])
 @pytest.mark.parametrize("a_mode", ["row", "tensor"])
 def test_w4a4(M, N, K, a_mode):
     log(f"gemm_w4a4 M={M} N={N} K={K} a_mode={a_mode}")

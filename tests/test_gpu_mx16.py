@@ -47,7 +47,7 @@ def _case(M, N, K, seed):
 # prefill GEMM: one to many 256 x 256 tiles, ragged M and N, K stages 2..80, and a
 # grid with a last round that runs as 128 x 128 tiles (500 x 33000)
 PREFILL = [(1, 16, 128), (5, 100, 384), (40, 70, 128), (300, 520, 5120), (257, 513, 1280),
-           (513, 260, 640), (500, 33000, 128), (16, 300, 1024)]
+           (513, 260, 640), (500, 33000, 128), (16, 300, 1024), (1100, 16900, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", PREFILL)
@@ -141,7 +141,7 @@ def test_mxfp4_decode_exact_with_grid_operands(M, N, K):
 # M > 16 on the MXFP4 decode layout: the prefill GEMM reading it (a second launch
 # of 128 x 128 tiles for the last columns of 500 x 33000)
 @pytest.mark.parametrize("M,N,K", [(17, 260, 1024), (40, 70, 128), (300, 520, 5120), (513, 260, 640),
-                                   (500, 33000, 128)])
+                                   (500, 33000, 128), (1100, 16900, 256)])
 @pytest.mark.parametrize("out", ["bf16", "f32"])
 def test_mxfp4_decode_layout_prefill(M, N, K, out):
     log(f"mxfp4_gemm_w4a16_decode (prefill, M > 16) M={M} N={N} K={K} out={out}")
