@@ -601,7 +601,11 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
     pam = fp4.mxfp4_quantize(a)  # A row-major, for the GEMM half on its own
     t_mq = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_quantize(a, out=pam)), it)
     t_mg = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_prequant(pam, wmx, out=c)), it, sample_clock=True)
+    torch.cuda.synchronize()
+    c_2s = c.clone()  # the row-major two-stage kernel
     t_mall = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a4(a, wmx, out=c, workspace=wsm)), it)
+    torch.cuda.synchronize()
+    canon_equal = bool(torch.equal(c.view(torch.int16), c_2s.view(torch.int16)))
     c_mx = c.clone()
     # the same GEMM with W in the decode (segment-major) layout and A quantized into it
     wmd = fp4.mxfp4_pack_decode(wmx)
@@ -611,7 +615,7 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
     t_sg = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_prequant_seg(pas, wmd, out=c)), it, sample_clock=True)
     t_sall = T.per_launch(prepared(fp4, lambda: fp4.mxfp4_gemm_w4a4_seg(a, wmd, out=c, workspace=wss)), it)
     torch.cuda.synchronize()
-    seg_equal = bool(torch.equal(c.view(torch.int16), c_mx.view(torch.int16)))
+    seg_equal = bool(torch.equal(c.view(torch.int16), c_2s.view(torch.int16))) and canon_equal
     wsn = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     t_nall = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a4(a, wnv, a_mode="row", out=c, workspace=wsn)), it)
     c_nv = c.clone()
@@ -654,7 +658,7 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
         "w4a8_seg_gemm_frac_fp8_mfma": fl / t_8sg / FP8_PEAK, "w4a8_seg_total_us": t_8sall * 1e6,
         "w4a8_seg_equals_row_major": w4a8_seg_equal,
         "error_vs_bf16_product_64_rows": err}
-    del a, c, c_mx, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8, wmd, wss
+    del a, c, c_mx, c_2s, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8, wmd, wss
 
 
 def moe_components(args, torch, fp4, T, dev):

@@ -8,8 +8,10 @@ same layout.  Checks:
   - the workspace's A equals the oracle's MXFP4 quantization of A rearranged by
     the layout's definition (a numpy reshape), bit for bit;
   - C meets |C - C_ref| <= 2e-3 * sum_k |a w| against the oracle's fp64 product;
-  - C equals mxfp4_gemm_w4a4 on the row-major operands bit for bit (the kernels
-    contract the same 64-element K steps in the same order);
+  - C equals mxfp4_gemm_w4a4 on the row-major W (the same kernel reading W
+    row-major) and mxfp4_gemm_prequant on row-major A and W (the two-stage
+    row-major kernel) bit for bit: the kernels contract the same 64-element K
+    steps in the same order;
   - with grid-valued operands and power-of-two scales the fp32 C equals the
     oracle exactly;
   - at the full M = 8192, N = 17408, K = 5120 workload: equal to the row-major
@@ -83,6 +85,9 @@ def test_mxfp4_seg_gemm(M, N, K, rule):
     ref, tol = oracle.mxfp4_gemm_w4a4_ref(a, wc, wsc, r)
     assert_gemm_close(c, ref, tol, f"mxfp4 seg {M}x{N}x{K}")
     assert torch.equal(c, c_rm), "segment-major and row-major kernels differ"
+    c_2s = fp4().mxfp4_gemm_prequant(_packed_mx(ac, asc), wp, dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(c, c_2s), "segment kernel and two-stage row-major kernel differ"
 
 
 @pytest.mark.parametrize("M,N,K", [(33, 300, 640), (300, 260, 1024)])
