@@ -285,12 +285,12 @@ __device__ __forceinline__ void mx2_put(uint8_t *row, int col, const f32x16 &a, 
 // Store `rows` staged rows of width 256 elements (pitch bytes apart in `st`) to
 // output rows m_first.. and columns n0..; the NT threads take 16-byte chunks in
 // order.
-template <typename T, int NT = 256>
+template <typename T, int NT = 256, int COLS = 256>
 __device__ __forceinline__ void mx2_flush(const uint8_t *st, int pitch, int rows, const MxGemmArgs &g, int m_first,
                                           int n0, int tid)
 {
     constexpr int kPer = 16 / (int)sizeof(T);              // elements per chunk
-    constexpr int kChunks = 256 / kPer;                    // chunks per row
+    constexpr int kChunks = COLS / kPer;                   // chunks per row
     const int M = (int)g.M, N = (int)g.N;
     for (int q = tid; q < rows * kChunks; q += NT) {
         const int r = q / kChunks, ch = q % kChunks;
@@ -934,32 +934,34 @@ struct MqLds {
     uint32_t la[2], lw[2], lsa, lsw, hsh;
 };
 
+template <int NJ>
 __device__ __forceinline__ void mq_frags(const uint8_t *st, uint32_t la, uint32_t lw, Mx2Frag &f)
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const i32x4 *>(st + la + 2048 * i);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) f.w[j] = *reinterpret_cast<const i32x4 *>(st + lw + 2048 * j);
+    for (int j = 0; j < NJ; ++j) f.w[j] = *reinterpret_cast<const i32x4 *>(st + lw + 2048 * j);
 }
 
 // the lane's E8M0 bytes of the slot: byte 0 = step 0's block (2 * 0 + h), byte 2 =
 // step 1's (2 + h), h the lane half
+template <int NJ>
 __device__ __forceinline__ void mq_scales(const uint8_t *st, const MqLds &o, uint32_t (&sa)[4], uint32_t (&sw)[2])
 {
 #pragma unroll
     for (int i = 0; i < 4; ++i) sa[i] = (*reinterpret_cast<const uint32_t *>(st + o.lsa + 128 * i) >> o.hsh) & 0x00FF00FFu;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sw[j] = (*reinterpret_cast<const uint32_t *>(st + o.lsw + 128 * j) >> o.hsh) & 0x00FF00FFu;
+    for (int j = 0; j < NJ; ++j) sw[j] = (*reinterpret_cast<const uint32_t *>(st + o.lsw + 128 * j) >> o.hsh) & 0x00FF00FFu;
 }
 
-template <int KS, int I0, int I1>
-__device__ __forceinline__ void mq_mfma(f32x16 (&acc)[4][2], const Mx2Frag &f, const uint32_t (&sa)[4],
+template <int KS, int I0, int I1, int NJ>
+__device__ __forceinline__ void mq_mfma(f32x16 (&acc)[4][NJ], const Mx2Frag &f, const uint32_t (&sa)[4],
                                         const uint32_t (&sw)[2])
 {
 #pragma unroll
     for (int i = I0; i < I1; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < NJ; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(mx2_wide(f.w[j]), mx2_wide(f.a[i]), acc[i][j],
                                                                         4, 4, 2 * KS, (int)sw[j], 2 * KS, (int)sa[i]);
 }
@@ -968,31 +970,33 @@ __device__ __forceinline__ void mq_mfma(f32x16 (&acc)[4][2], const Mx2Frag &f, c
 // s + 3) into `dst`, which the previous barrier freed, spread among the MFMAs; at
 // the barrier slot s + 1 (`nxt`) must have landed, while the 10 copies of slots
 // s + 2 and s + 3 may still be in flight.  One basic block.
+template <int NJ>
 __device__ __forceinline__ void mq_slot(const uint8_t *cur, const uint8_t *nxt, uint8_t *dst, const MqDma &d,
-                                        int seg, const MqLds &o, int wave, f32x16 (&acc)[4][2], Mx2Frag &f0,
+                                        int seg, const MqLds &o, int wave, f32x16 (&acc)[4][NJ], Mx2Frag &f0,
                                         Mx2Frag &f1, uint32_t (&sa)[4], uint32_t (&sw)[2])
 {
-    // step 0: 8 MFMAs, the 6 reads of step 1's fragments, 3 copies
-    mq_frags(cur, o.la[1], o.lw[1], f1);
-    mq_mfma<0, 0, 4>(acc, f0, sa, sw);
+    constexpr int nm = 4 * NJ;  // MFMAs per step
+    // step 0: nm MFMAs, the 4 + NJ reads of step 1's fragments, 3 copies
+    mq_frags<NJ>(cur, o.la[1], o.lw[1], f1);
+    mq_mfma<0, 0, 4, NJ>(acc, f0, sa, sw);
     mq_dma<0>(dst, d, seg, wave);
     mq_dma<1>(dst, d, seg, wave);
     mq_dma<2>(dst, d, seg, wave);
 #pragma unroll
-    for (int t = 0; t < 8; ++t) {
+    for (int t = 0; t < nm; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                       // MFMA
-        if (t < 6) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);            // DS read
-        if (t == 1 || t == 4 || t == 7) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
+        if (t < 4 + NJ) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);       // DS read
+        if (t == 1 || t == nm / 2 || t == nm - 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
     }
     __builtin_amdgcn_sched_barrier(0);
-    // step 1, first half: 4 MFMAs, 2 copies
-    mq_mfma<1, 0, 2>(acc, f1, sa, sw);
+    // step 1, first half: nm / 2 MFMAs, 2 copies
+    mq_mfma<1, 0, 2, NJ>(acc, f1, sa, sw);
     mq_dma<3>(dst, d, seg, wave);
     mq_dma<4>(dst, d, seg, wave);
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < nm / 2; ++t) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        if (t == 0 || t == 2) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+        if (t == 0 || t == nm / 4) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
     // slot s + 1 has landed (vmcnt 10) and this wave's reads of `cur` returned; the
@@ -1000,21 +1004,21 @@ __device__ __forceinline__ void mq_slot(const uint8_t *cur, const uint8_t *nxt, 
     __builtin_amdgcn_s_waitcnt(((2 * kQDma) & 15) | (7 << 4));
     asm volatile("s_barrier" ::: "memory");
     uint32_t na[4], nw[2];
-    mq_scales(nxt, o, na, nw);
-    mq_frags(nxt, o.la[0], o.lw[0], f0);
-    mq_mfma<1, 2, 4>(acc, f1, sa, sw);
+    mq_scales<NJ>(nxt, o, na, nw);
+    mq_frags<NJ>(nxt, o.la[0], o.lw[0], f0);
+    mq_mfma<1, 2, 4, NJ>(acc, f1, sa, sw);
 #pragma unroll
     for (int i = 0; i < 4; ++i) sa[i] = na[i];
 #pragma unroll
-    for (int j = 0; j < 2; ++j) sw[j] = nw[j];
+    for (int j = 0; j < NJ; ++j) sw[j] = nw[j];
     __builtin_amdgcn_sched_barrier(0);
 }
 
 // Epilogue through the four slots: bf16 stages 64 tile rows per slot (slots 0, 1
 // rows 0..127 from the waves with wm = 0, slots 2, 3 rows 128..255), one round;
 // fp32 32 rows per slot, two rounds.
-template <typename T>
-__device__ __forceinline__ void mq_epilogue(const f32x16 (&acc)[4][2], uint8_t *q0, uint8_t *q1, uint8_t *q2,
+template <typename T, int NJ>
+__device__ __forceinline__ void mq_epilogue(const f32x16 (&acc)[4][NJ], uint8_t *q0, uint8_t *q1, uint8_t *q2,
                                             uint8_t *q3, const MxGemmArgs &g, int m0, int n0, int wm, int wn,
                                             int lane, int tid)
 {
@@ -1030,21 +1034,21 @@ __device__ __forceinline__ void mq_epilogue(const f32x16 (&acc)[4][2], uint8_t *
             const int rr = sizeof(T) == 2 ? 32 * i : 32 * i - 64 * rd;  // row within the round's two slots
             const int sub = rr / rows;
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+            for (int j = 0; j < NJ; ++j) {
                 uint8_t *slot = wm ? (sub ? q3 : q2) : (sub ? q1 : q0);
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq)
-                    mx2_put<T>(slot + (rr % rows + (lane & 31)) * pitch, wn * 64 + j * 32 + 8 * gq + 4 * (lane >> 5),
-                               acc[i][j], gq);
+                    mx2_put<T>(slot + (rr % rows + (lane & 31)) * pitch,
+                               wn * 32 * NJ + j * 32 + 8 * gq + 4 * (lane >> 5), acc[i][j], gq);
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
         __syncthreads();
         const int mr = m0 + (sizeof(T) == 4 ? 64 * rd : 0);
-        mx2_flush<T, 512>(q0, pitch, rows, g, mr, n0, tid);
-        mx2_flush<T, 512>(q1, pitch, rows, g, mr + rows, n0, tid);
-        mx2_flush<T, 512>(q2, pitch, rows, g, mr + 128, n0, tid);
-        mx2_flush<T, 512>(q3, pitch, rows, g, mr + 128 + rows, n0, tid);
+        mx2_flush<T, 512, 128 * NJ>(q0, pitch, rows, g, mr, n0, tid);
+        mx2_flush<T, 512, 128 * NJ>(q1, pitch, rows, g, mr + rows, n0, tid);
+        mx2_flush<T, 512, 128 * NJ>(q2, pitch, rows, g, mr + 128, n0, tid);
+        mx2_flush<T, 512, 128 * NJ>(q3, pitch, rows, g, mr + 128 + rows, n0, tid);
         if (rd + 1 < rounds) __syncthreads();
     }
 }
@@ -1054,9 +1058,16 @@ __device__ __forceinline__ void mq_epilogue(const f32x16 (&acc)[4][2], uint8_t *
 // its 4 scale bytes at row K/32 + 4 s, so only the copies' row stride and
 // segment step change; the slots, fragments and contraction order are the same,
 // and so is every output bit.
-template <typename OutT, bool AROW = false, bool WROW = false>
+// TN = 128: tiles of 256 x 128 for a last round that 256 x 256 tiles would leave
+// half empty; each wave then owns 128 x 32, the copies of W rows 128..255 and
+// their scale bytes read nothing (they keep every wave's copy count, which the
+// slot waits count), and the same K steps are contracted in the same order.
+constexpr uint32_t kMqOut = 0x80000000u;  // an offset past every descriptor's size
+template <typename OutT, bool AROW = false, bool WROW = false, int TN = 256>
 __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
 {
+    static_assert(TN == 256 || TN == 128, "tile width");
+    constexpr int NJ = TN / 128;  // 32-column blocks per wave
     __shared__ __align__(16) uint8_t q0[kQSlot];
     __shared__ __align__(16) uint8_t q1[kQSlot];
     __shared__ __align__(16) uint8_t q2[kQSlot];
@@ -1065,32 +1076,37 @@ __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 2, wn = wave & 3;
     const int M = (int)g.M, N = (int)g.N, K = (int)g.K;
-    const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + MBN - 1) / MBN;
+    const int tiles_m = (M + MBM - 1) / MBM, tiles_n = (N + TN - 1) / TN;
     int tm, tn;
     mx_tile_of(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
-    const int m0 = tm * MBM, n0 = tn * MBN;
+    const int m0 = tm * MBM, n0 = tn * TN;
     const int nk = K / kQK;
+    // W rows w_row0 .. w_row0 + N - 1 of a weight of wrows rows
+    const int w_row0 = (int)g.w_row0, wrows = (int)(g.w_rows ? g.w_rows : g.N);
 
     MqDma d, dz;
     d.ra = mx2_rsrc(g.a_codes, g.M * (g.K / 2));
-    d.rw = mx2_rsrc(g.w_codes, g.N * (g.K / 2));
-    d.rs = wave < 4 ? mx2_rsrc(g.a_scales, g.M * (g.K / 32)) : mx2_rsrc(g.w_scales, g.N * (g.K / 32));
+    d.rw = mx2_rsrc(g.w_codes, (int64_t)wrows * (g.K / 2));
+    d.rs = wave < 4 ? mx2_rsrc(g.a_scales, g.M * (g.K / 32)) : mx2_rsrc(g.w_scales, (int64_t)wrows * (g.K / 32));
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int q = 128 * wave + 64 * i + lane;
         const int r = q >> 2;
         const int c = (q & 3) ^ ((r >> 2) & 3);
         d.a[i] = (uint32_t)min(m0 + r, M - 1) * (AROW ? (uint32_t)(K / 2) : 64u) + 16 * c;
-        d.w[i] = (uint32_t)min(n0 + r, N - 1) * (WROW ? (uint32_t)(K / 2) : 64u) + 16 * c;
+        d.w[i] = r < TN ? (uint32_t)(w_row0 + min(n0 + r, N - 1)) * (WROW ? (uint32_t)(K / 2) : 64u) + 16 * c
+                        : kMqOut;
     }
     const bool srow = wave < 4 ? AROW : WROW;  // this wave copies A's (waves 0-3) or W's scale bytes
     {
         const int r = 64 * (wave & 3) + lane;
-        d.s = (uint32_t)(wave < 4 ? min(m0 + r, M - 1) : min(n0 + r, N - 1)) * (srow ? (uint32_t)(K / 32) : 4u);
+        const uint32_t step = srow ? (uint32_t)(K / 32) : 4u;
+        d.s = wave < 4 ? (uint32_t)min(m0 + r, M - 1) * step
+                       : (r < TN ? (uint32_t)(w_row0 + min(n0 + r, N - 1)) * step : kMqOut);
     }
     d.seg_a = AROW ? 64u : (uint32_t)M * 64u;
-    d.seg_w = WROW ? 64u : (uint32_t)N * 64u;
-    d.seg_s = srow ? 4u : (uint32_t)(wave < 4 ? M : N) * 4u;
+    d.seg_w = WROW ? 64u : (uint32_t)wrows * 64u;
+    d.seg_s = srow ? 4u : (uint32_t)(wave < 4 ? M : wrows) * 4u;
     dz = d;
     dz.ra = mx2_rsrc(g.a_codes, 0);
     dz.rw = mx2_rsrc(g.w_codes, 0);
@@ -1099,7 +1115,7 @@ __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
     MqLds o;
     {
         const int h = lane >> 5, l = lane & 31;
-        const int ra = wm * 128 + l, rw = wn * 64 + l;
+        const int ra = wm * 128 + l, rw = wn * 32 * NJ + l;
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
             o.la[ks] = 64 * ra + 16 * ((2 * ks + h) ^ ((ra >> 2) & 3));
@@ -1110,11 +1126,11 @@ __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
         o.hsh = 8 * h;
     }
 
-    f32x16 acc[4][2];
+    f32x16 acc[4][NJ];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = f32x16{};
+        for (int j = 0; j < NJ; ++j) acc[i][j] = f32x16{};
 
     const int T = (nk + 3) & ~3, ph = T - nk;
     auto seg_of = [&](int t) { return max(t - ph, 0); };
@@ -1126,31 +1142,60 @@ __global__ __launch_bounds__(512) void k_mx_gemm_seg(MxGemmArgs g)
     asm volatile("s_barrier" ::: "memory");
     Mx2Frag f0, f1;
     uint32_t sa[4], sw[2];
-    mq_scales(q0, o, sa, sw);
-    mq_frags(q0, o.la[0], o.lw[0], f0);
+    mq_scales<NJ>(q0, o, sa, sw);
+    mq_frags<NJ>(q0, o.la[0], o.lw[0], f0);
     for (int t = 0; t < T; t += 4) {
-        mq_slot(q0, q1, q3, slot_d(t + 3), seg_of(t + 3), o, wave, acc, f0, f1, sa, sw);
-        mq_slot(q1, q2, q0, slot_d(t + 4), seg_of(t + 4), o, wave, acc, f0, f1, sa, sw);
-        mq_slot(q2, q3, q1, slot_d(t + 5), seg_of(t + 5), o, wave, acc, f0, f1, sa, sw);
-        mq_slot(q3, q0, q2, slot_d(t + 6), seg_of(t + 6), o, wave, acc, f0, f1, sa, sw);
+        mq_slot<NJ>(q0, q1, q3, slot_d(t + 3), seg_of(t + 3), o, wave, acc, f0, f1, sa, sw);
+        mq_slot<NJ>(q1, q2, q0, slot_d(t + 4), seg_of(t + 4), o, wave, acc, f0, f1, sa, sw);
+        mq_slot<NJ>(q2, q3, q1, slot_d(t + 5), seg_of(t + 5), o, wave, acc, f0, f1, sa, sw);
+        mq_slot<NJ>(q3, q0, q2, slot_d(t + 6), seg_of(t + 6), o, wave, acc, f0, f1, sa, sw);
     }
     __builtin_amdgcn_s_waitcnt(0);  // the last (empty) copies landed
     __syncthreads();
     const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-    mq_epilogue<OutT>(acc, q0, q1, q2, q3, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
+    mq_epilogue<OutT, NJ>(acc, q0, q1, q2, q3, g, m0, n0, wm, wn, lane_e, 64 * wave + lane_e);
 }
 
+template <bool AROW, bool WROW, int TN>
+static void launch_seg_tiles(const MxGemmArgs &g, hipStream_t st)
+{
+    const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + TN - 1) / TN));
+    if (g.c_bf16)
+        hipLaunchKernelGGL((k_mx_gemm_seg<__bf16, AROW, WROW, TN>), dim3(tiles), dim3(512), 0, st, g);
+    else
+        hipLaunchKernelGGL((k_mx_gemm_seg<float, AROW, WROW, TN>), dim3(tiles), dim3(512), 0, st, g);
+}
+
+// 256 x 256 tiles; when their last round would be at most half full and the
+// columns of that round fit one round of 256 x 128 tiles, those columns go to a
+// second launch of 256 x 128 tiles (M = 8192, N = 17408: eight rounds of large
+// tiles over 16384 columns, then 256 tiles over the last 1024).
 template <bool AROW, bool WROW>
 static fp4_status launch_seg_layout(const MxGemmArgs &g, hipStream_t st)
 {
     // 32-bit byte offsets and descriptor sizes
     if (g.K % kQK != 0 || g.M * (g.K / 2) >= (int64_t(1) << 31) || g.N * (g.K / 2) >= (int64_t(1) << 31))
         return FP4_ERR_SHAPE;
-    const int tiles = (int)(((g.M + MBM - 1) / MBM) * ((g.N + MBN - 1) / MBN));
-    if (g.c_bf16)
-        hipLaunchKernelGGL((k_mx_gemm_seg<__bf16, AROW, WROW>), dim3(tiles), dim3(512), 0, st, g);
-    else
-        hipLaunchKernelGGL((k_mx_gemm_seg<float, AROW, WROW>), dim3(tiles), dim3(512), 0, st, g);
+    MxGemmArgs a = g;
+    a.w_row0 = 0;
+    a.w_rows = g.N;
+    const int64_t cus = device_cu_count();
+    const int64_t tm = (g.M + MBM - 1) / MBM, tn = (g.N + MBN - 1) / MBN, tiles = tm * tn, rem = tiles % cus;
+    if (tiles > cus && rem != 0 && rem <= cus / 2) {
+        const int64_t n_split = tiles / cus * cus / tm * MBN;  // columns kept on large tiles
+        if (n_split >= MBN && n_split < g.N && tm * ((g.N - n_split + 127) / 128) <= cus) {
+            MxGemmArgs big = a;
+            big.N = n_split;
+            launch_seg_tiles<AROW, WROW, 256>(big, st);
+            MxGemmArgs rest = a;
+            rest.N = g.N - n_split;
+            rest.w_row0 = n_split;
+            rest.c = reinterpret_cast<uint8_t *>(g.c) + n_split * (g.c_bf16 ? 2 : 4);
+            launch_seg_tiles<AROW, WROW, 128>(rest, st);
+            return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
+        }
+    }
+    launch_seg_tiles<AROW, WROW, 256>(a, st);
     return hipGetLastError() == hipSuccess ? FP4_OK : FP4_ERR_HIP;
 }
 
@@ -1161,10 +1206,6 @@ fp4_status launch_mxfp4_gemm_seg_wrow(const MxGemmArgs &g, hipStream_t st)
     return launch_seg_layout<false, true>(g, st);
 }
 
-fp4_status launch_mxfp4_gemm_seg_rows(const MxGemmArgs &g, hipStream_t st)
-{
-    return launch_seg_layout<true, true>(g, st);
-}
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st)
 {

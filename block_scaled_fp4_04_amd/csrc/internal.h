@@ -133,15 +133,18 @@ struct MxGemmArgs {
     int c_bf16;
     int64_t ldc;
     int w_seg;  // W4A8: W in the segment-major layout ([K/128][N][64], [K/128][N][4])
+    // segment kernel: this launch's N columns are W rows w_row0 .. w_row0 + N - 1
+    // of a weight of w_rows rows (0: the launch's N), so a launch can take the
+    // last columns of a weight whose segment-major layout interleaves all rows
+    int64_t w_row0, w_rows;
 };
 
 fp4_status launch_mxfp4_gemm(const MxGemmArgs &g, hipStream_t st);
 // Both operands segment-major (codes [K/128][rows][64], scales [K/128][rows][4]);
 // K % 128 == 0
 fp4_status launch_mxfp4_gemm_seg(const MxGemmArgs &g, hipStream_t st);
-// The same kernel with W row-major (A segment-major), or with both row-major
+// The same kernel with W row-major (A segment-major)
 fp4_status launch_mxfp4_gemm_seg_wrow(const MxGemmArgs &g, hipStream_t st);
-fp4_status launch_mxfp4_gemm_seg_rows(const MxGemmArgs &g, hipStream_t st);
 // W4A8: A MXFP8 (E4M3 bytes [M][K], E8M0 [M][K/32]), W MXFP4; K % 128 == 0
 fp4_status launch_mxfp4_gemm_w4a8(const MxGemmArgs &g, hipStream_t st);
 

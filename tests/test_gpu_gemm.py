@@ -109,7 +109,7 @@ def test_w4a4(M, N, K, a_mode):
 # other K the prefetch kernel with a masked K tail.
 @pytest.mark.parametrize("M,N,K", [(1, 32, 64), (5, 100, 96), (16, 300, 1056), (17, 260, 1024),
                                    (300, 520, 5120), (513, 130, 160), (256, 256, 128),
-                                   (70, 300, 768), (257, 513, 1280), (9, 40, 256)])
+                                   (70, 300, 768), (257, 513, 1280), (9, 40, 256), (1100, 16900, 256)])
 @pytest.mark.parametrize("rule", ["ocp", "ceil"])
 def test_mxfp4_w4a4(M, N, K, rule):
     log(f"mxfp4_gemm_w4a4 M={M} N={N} K={K} rule={rule}")

@@ -61,7 +61,10 @@ def _case(M, N, K, seed):
 # one to many 256 x 256 tiles, ragged M and N; K = 1..40 segments, so 0..3
 # leading zero slots fill the ring of four
 SHAPES = [(1, 32, 128), (5, 100, 384), (16, 300, 1152), (17, 260, 1024), (70, 300, 768),
-          (256, 256, 128), (257, 513, 1280), (513, 130, 640), (300, 520, 5120), (40, 1000, 2688)]
+          (256, 256, 128), (257, 513, 1280), (513, 130, 640), (300, 520, 5120), (40, 1000, 2688),
+          # 335 tiles of 256 x 256 on 256 CUs: the last 3844 columns run as 155 tiles of
+          # 256 x 128 in a second launch
+          (1100, 16900, 256)]
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)
