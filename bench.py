@@ -619,6 +619,12 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
     wsn = fp4.gemm_w4a4_workspace(M, K, "row", dev)
     t_nall = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a4(a, wnv, a_mode="row", out=c, workspace=wsn)), it)
     c_nv = c.clone()
+    # the same with the NVFP4 weight in the decode layout (the layout the decode GEMV reads)
+    wnd = fp4.nvfp4_pack_decode(wnv)
+    t_nsall = T.per_launch(prepared(fp4, lambda: fp4.gemm_w4a4_seg(a, wnd, a_mode="row", out=c,
+                                                                    workspace=wsn)), it)
+    torch.cuda.synchronize()
+    nv_seg_equal = bool(torch.equal(c.view(torch.int16), c_nv.view(torch.int16)))
     # W4A8: the same MXFP4 weights, activations as MXFP8
     ws8 = fp4.mxfp4_gemm_w4a8_workspace(M, K, dev)
     pa8 = fp4.mxfp8_packed_a(ws8, M, K)
@@ -651,6 +657,8 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
         "mxfp4_seg_equals_row_major": seg_equal,
         "nvfp4_total_us": t_nall * 1e6, "nvfp4_total_TFLOP/s": fl / t_nall / 1e12,
         "nvfp4_frac_bf16_mfma": fl / t_nall / BF16_PEAK,
+        "nvfp4_seg_total_us": t_nsall * 1e6, "nvfp4_seg_total_TFLOP/s": fl / t_nsall / 1e12,
+        "nvfp4_seg_frac_bf16_mfma": fl / t_nsall / BF16_PEAK, "nvfp4_seg_equals_row_major": nv_seg_equal,
         "w4a8_quant_us": t_8q * 1e6, "w4a8_gemm_us": t_8g * 1e6,
         "w4a8_gemm_TFLOP/s": fl / t_8g / 1e12, "w4a8_gemm_frac_fp8_mfma": fl / t_8g / FP8_PEAK,
         "w4a8_total_us": t_8all * 1e6, "w4a8_total_TFLOP/s": fl / t_8all / 1e12,
@@ -658,7 +666,7 @@ def m8192_components(torch, fp4, T, dev, w32, it, out):
         "w4a8_seg_gemm_frac_fp8_mfma": fl / t_8sg / FP8_PEAK, "w4a8_seg_total_us": t_8sall * 1e6,
         "w4a8_seg_equals_row_major": w4a8_seg_equal,
         "error_vs_bf16_product_64_rows": err}
-    del a, c, c_mx, c_2s, c_nv, c_a8, wmx, wnv, wsm, wsn, ws8, wmd, wss
+    del a, c, c_mx, c_2s, c_nv, c_a8, wmx, wnv, wnd, wsm, wsn, ws8, wmd, wss
 
 
 def moe_components(args, torch, fp4, T, dev):
