@@ -298,3 +298,41 @@ def test_mx_vs_nv_full_size_sampled():
     torch.cuda.synchronize()
     _full_size_check(cn, cnb, lambda r: oracle.gemm_w4a4_ref(a, nc, ns, nt, a_per_row=True, rows=r), rows,
                      "nvfp4 w4a4 sampled")
+
+
+@pytest.mark.parametrize("entry", ["w4a16", "w4a4", "w4a16_decode", "mxfp4_w4a4", "mxfp4_seg"])
+def test_split_launch_guard_band(entry):
+    """1100 x 16900 x 256 runs as two launches (the last columns on smaller tiles,
+    written at a column offset of the output): into a view of a larger bf16 buffer,
+    nothing outside the view changes and the view equals the same call's output
+    into a tensor of its own."""
+    M, N, K = 1100, 16900, 256
+    log(f"split launch guard band {entry}")
+    w, a = _case(M, N, K, seed=1234)
+    ad = bf16bits_to_dev(a)
+    if entry.startswith("mxfp4"):
+        wc, wsc = oracle.mxfp4_quantize(to_bf16_bits(w))
+        wp = _packed_mx(wc, wsc)
+        if entry == "mxfp4_seg":
+            wd = fp4().mxfp4_pack_decode(wp)
+            call = lambda out: fp4().mxfp4_gemm_w4a4_seg(ad, wd, out=out)
+        else:
+            call = lambda out: fp4().mxfp4_gemm_w4a4(ad, wp, out=out)
+    else:
+        oc, os_, ot = oracle.nvfp4_quantize(w)
+        wp = _packed_nv(oc, os_, ot)
+        if entry == "w4a16":
+            call = lambda out: fp4().gemm_w4a16(ad, wp, out=out)
+        elif entry == "w4a16_decode":
+            wd = fp4().nvfp4_pack_decode(wp)
+            call = lambda out: fp4().gemm_w4a16_decode(ad, wd, out=out)
+        else:
+            call = lambda out: fp4().gemm_w4a4(ad, wp, a_mode="row", out=out)
+    big = torch.full((M + 3, N + 40), -7.0, dtype=torch.bfloat16, device=dev())
+    view = big[:M, :N]
+    call(view)
+    own = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+    call(own)
+    torch.cuda.synchronize()
+    assert torch.all(big[:M, N:] == -7.0) and torch.all(big[M:, :] == -7.0)
+    assert torch.equal(view.view(torch.int16), own.view(torch.int16))
