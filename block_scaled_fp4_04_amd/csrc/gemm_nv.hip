@@ -392,6 +392,8 @@ __device__ __forceinline__ void persist_lane_init(PersistLane<S> &pl, int K, int
 }
 
 // DMA one tile (rows t0 .. t0 + 15, clamped to n_hi - 1) of the wave's K slice into buf.
+// The weight copies carry the non-temporal hint (cache policy 2): each weight byte
+// is read once per call.
 template <int S>
 __device__ __forceinline__ void persist_issue(uint8_t *buf, const uint8_t *__restrict__ wc,
                                               const uint8_t *__restrict__ wsc, int t0, int n_hi,
@@ -403,11 +405,11 @@ __device__ __forceinline__ void persist_issue(uint8_t *buf, const uint8_t *__res
     if (t0 + 16 <= n_hi) {
 #pragma unroll
         for (int t = 0; t < C::kCodeInstr; ++t)
-            __builtin_amdgcn_global_load_lds(cbase + pl.code_off[t], (lds_void *)(buf + t * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(cbase + pl.code_off[t], (lds_void *)(buf + t * 1024), 16, 0, 2);
 #pragma unroll
         for (int t = 0; t < C::kScaleInstr; ++t)
             __builtin_amdgcn_global_load_lds(sbase + pl.scale_off[t],
-                                             (lds_void *)(buf + C::kCodeBytes + t * 256), 4, 0, 0);
+                                             (lds_void *)(buf + C::kCodeBytes + t * 256), 4, 0, 2);
     } else {
         // partial last tile: rows past n_hi re-read row n_hi - 1 (never stored)
         const int last = n_hi - 1 - t0;
@@ -415,13 +417,13 @@ __device__ __forceinline__ void persist_issue(uint8_t *buf, const uint8_t *__res
         for (int t = 0; t < C::kCodeInstr; ++t) {
             const int back = max((int)pl.code_row[t] - last, 0);
             __builtin_amdgcn_global_load_lds(cbase + pl.code_off[t] - (int64_t)back * (K / 2),
-                                             (lds_void *)(buf + t * 1024), 16, 0, 0);
+                                             (lds_void *)(buf + t * 1024), 16, 0, 2);
         }
 #pragma unroll
         for (int t = 0; t < C::kScaleInstr; ++t) {
             const int back = max((int)pl.scale_row[t] - last, 0);
             __builtin_amdgcn_global_load_lds(sbase + pl.scale_off[t] - (int64_t)back * (K / 16),
-                                             (lds_void *)(buf + C::kCodeBytes + t * 256), 4, 0, 0);
+                                             (lds_void *)(buf + C::kCodeBytes + t * 256), 4, 0, 2);
         }
     }
 }
