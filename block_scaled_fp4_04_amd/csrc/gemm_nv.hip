@@ -1445,7 +1445,7 @@ static void launch_ring_split(const NvGemmArgs &g, hipStream_t st)
             }
             rest.c = reinterpret_cast<uint8_t *>(g.c) + n_split * (g.c_bf16 ? 2 : 4);
             if (small <= cus)
-                launch_ring<F, 0, 128, 128>(rest, st);
+                launch_ring<F, L, 128, 128>(rest, st);  // W4A16: each wave 128 rows x 32 columns
             else
                 launch_ring<F, L, 128, 256>(rest, st);  // M = 8192, N = 17408: 256 tiles of 128 x 256
             return;
